@@ -1,0 +1,169 @@
+/*
+ * moe_layer.h -- C ABI of the MI355X (gfx950) LatentMoE layer forward.
+ *
+ * The layer (Kimi K3 and the New Open-Weights Moat, section "Sparse
+ * computation: latent experts and routing" and section "How the router picks
+ * 16 of 896", Fig. 2):
+ *
+ *   xq    = MXFP8(x)                                  per token, blocks of 32
+ *   z     = deq(xq) deq(W_down)^T                     model width -> latent
+ *   s     = sigmoid(z W_router^T + logit_bias)        one score per routed expert
+ *   ids   = top_k(s + selection_bias)                 ties -> lower expert id
+ *   gates = s[ids] / sum(s[ids])                      bias not in the gates
+ *   per expert e, on the tokens routed to it (stable, token order):
+ *       h   = SiLU(zq W_gate_e^T) * (zq W_up_e^T),  hq = MXFP8(h)
+ *       y_e = deq(hq) deq(W_down_e)^T
+ *   y_lat = sum_j gates[j] y_e[j]                     gate-weighted combine
+ *   y     = deq(MXFP8(y_lat)) deq(W_up)^T
+ *         + sum_s deq(MXFP8(SiLU(xq W_gate_s^T) * (xq W_up_s^T))) deq(W_down_s)^T
+ *
+ * Number formats (Kimi K3: 2.8 Trillion Parameters, Four Bits at a Time,
+ * section "Four bits from the start"; Moat page, section "Precision and
+ * deployment", Fig. 6): weights are MXFP4 (E2M1 elements), activations MXFP8
+ * (E4M3, OCP "FN" variant), 32 elements per block sharing one E8M0 scale.
+ * The router weight is fp32 and is not quantised.
+ *
+ * Storage of an MX tensor [rows][K] (blocks run along K, the contraction dim):
+ *   E2M1 codes: [rows][K/2] bytes, element 2i in the low nibble of byte i;
+ *   E4M3 codes: [rows][K] bytes;
+ *   scales:     [rows][K/32] bytes, E8M0 (value 2^(c-127)).
+ * Weight matrices are stored [out][in] (nn.Linear orientation).
+ *
+ * All tensor pointers are DEVICE pointers unless stated otherwise.  Every
+ * call is asynchronous on the given HIP stream (a hipStream_t passed as
+ * void*, NULL = the null stream); no call synchronises the host, allocates
+ * device memory or copies between host and device.  Pointers stay owned by
+ * the caller.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every entry point returns one of these (0 = success). */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, k > E, ...            */
+  MOE_ERR_UNSUPPORTED = -2, /* valid layer this build does not run (see create) */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  MOE_ERR_HIP = -4          /* a HIP launch reported an error                 */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* Layer shape.  d_model, d_latent, d_ff_routed, d_ff_shared must be positive
+ * multiples of 128 (whole MFMA K-steps); 1 <= top_k <= n_routed <= 4096;
+ * 0 <= n_shared <= 8; 1 <= max_tokens <= 2^20.  The Kimi-K3 width is
+ * {7168, 3584, 896, 16, 2, 3072, 3072, T}. */
+typedef struct {
+  int32_t d_model;     /* d:  model width                        */
+  int32_t d_latent;    /* L:  routed latent width                */
+  int32_t n_routed;    /* E:  routed experts                     */
+  int32_t top_k;       /* k:  experts kept per token             */
+  int32_t n_shared;    /* S:  always-on shared experts           */
+  int32_t d_ff_routed; /* F:  routed-expert intermediate width   */
+  int32_t d_ff_shared; /* Fs: shared-expert intermediate width   */
+  int32_t max_tokens;  /* largest T a forward call may pass      */
+} moe_layer_config;
+
+/* One MXFP4 (E2M1) tensor: packed codes and E8M0 scales, device memory. */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+} moe_mx_tensor;
+
+/* Layer weights.  Non-owning: every buffer must outlive the handle and must
+ * not change while a forward that reads it is in flight.  Expert tensors are
+ * the E (or S) matrices stored back to back. */
+typedef struct {
+  moe_mx_tensor w_down;            /* [L][d]      latent down-projection        */
+  moe_mx_tensor w_up;              /* [d][L]      latent up-projection          */
+  const float* w_router;           /* [E][L] fp32 router                        */
+  const float* router_logit_bias;  /* [E] added to the logits, or NULL (zeros)  */
+  const float* selection_bias;     /* [E] added for selection only, or NULL     */
+  moe_mx_tensor w_gate_e;          /* [E][F][L]   routed gate projections       */
+  moe_mx_tensor w_up_e;            /* [E][F][L]   routed up projections         */
+  moe_mx_tensor w_down_e;          /* [E][L][F]   routed down projections       */
+  moe_mx_tensor w_gate_s;          /* [S][Fs][d]  shared gate projections       */
+  moe_mx_tensor w_up_s;            /* [S][Fs][d]  shared up projections         */
+  moe_mx_tensor w_down_s;          /* [S][d][Fs]  shared down projections       */
+} moe_layer_weights;
+
+/* Optional device-side copies of the forward's intermediates, for testing.
+ * Every member may be NULL; non-NULL members are filled by the forward (on
+ * the same stream) with the sizes shown, for the T of that call.  Rows in
+ * "sorted order" are the (token, slot) pairs stably sorted by expert. */
+typedef struct {
+  uint8_t* xq_codes;   uint8_t* xq_scales;   /* [T][d], [T][d/32]            */
+  float* z;                                  /* [T][L] fp32 latent           */
+  uint8_t* zq_codes;   uint8_t* zq_scales;   /* [T][L], [T][L/32]            */
+  float* logits;                             /* [T][E] router logits (+bias) */
+  int32_t* ids;        float* gates;         /* [T][k] slot order            */
+  int32_t* counts;                           /* [E] pairs per expert         */
+  int32_t* offsets;                          /* [E+1] exclusive prefix sum   */
+  int32_t* pair_of_row;                      /* [T*k] pair t*k+j of sorted row */
+  int32_t* row_of_pair;                      /* [T*k] sorted row of pair     */
+  float* h;                                  /* [T*k][F] SiLU(gate)*up, sorted rows */
+  uint8_t* hq_codes;   uint8_t* hq_scales;   /* [T*k][F], [T*k][F/32] sorted */
+  float* y_e;                                /* [T*k][L] expert outputs, sorted */
+  float* y_lat;                              /* [T][L] combined latent       */
+  uint8_t* yq_codes;   uint8_t* yq_scales;   /* [T][L], [T][L/32]            */
+  float* hs;                                 /* [S][T][Fs] shared hidden, fp32 */
+  uint8_t* hs_codes;   uint8_t* hs_scales;   /* [S][T][Fs], [S][T][Fs/32]    */
+} moe_layer_trace;
+
+typedef struct moe_layer* moe_layer_t;
+
+/* Validate the shape and record the (non-owning) weight pointers.  Host-side
+ * only: launches nothing.  *out is written only on success.
+ * Errors: MOE_ERR_INVALID_ARG for null pointers (the two biases may be NULL;
+ * the shared tensors may be NULL when n_shared == 0) or out-of-range sizes;
+ * MOE_ERR_UNSUPPORTED when a width is not a multiple of 128. */
+int moe_layer_create(const moe_layer_config* cfg, const moe_layer_weights* w, moe_layer_t* out);
+
+/* Device workspace, in bytes, that a forward over T tokens needs
+ * (0 <= T <= cfg->max_tokens).  Pure function of (cfg, T).
+ * Errors: MOE_ERR_INVALID_ARG (cfg or bytes NULL, T out of range). */
+int moe_layer_workspace_size(const moe_layer_config* cfg, int32_t T, size_t* bytes);
+
+/* The forward pass: y[T][d] (fp32, fully overwritten) from x[T][d] (fp32).
+ * ws must be a device buffer of at least moe_layer_workspace_size(T) bytes,
+ * 256-byte aligned; it is scratch owned by the caller and must not be shared
+ * by two forwards in flight at once.  T == 0 returns MOE_OK and launches
+ * nothing.  trace may be NULL.
+ * Errors: MOE_ERR_INVALID_ARG (null handle/x/y, T < 0 or T > max_tokens),
+ * MOE_ERR_WORKSPACE (ws NULL, misaligned or too small), MOE_ERR_HIP (a launch
+ * failed; the stream's contents are then undefined). */
+int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y,
+                      void* ws, size_t ws_bytes, void* stream, const moe_layer_trace* trace);
+
+/* Free the host-side handle (the weights are not touched).  NULL is a no-op. */
+int moe_layer_destroy(moe_layer_t layer);
+
+/* MX block quantisation of an fp32 matrix in[rows][K] (Four Bits at a Time,
+ * "Four bits from the start": shared exponent floor(log2(amax)) - emax,
+ * elements rounded to nearest, ties to even, saturating; scale clamped to the
+ * E8M0 range).  fmt 0 = E4M3 (codes [rows][K]), 1 = E2M1 (packed codes
+ * [rows][K/2]); scales [rows][K/32].  K must be a positive multiple of 32.
+ * Used by the forward for activations and by callers to encode weights. */
+int moe_mx_quantize(const float* in, int64_t rows, int32_t K, int32_t fmt,
+                    uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Dense MX GEMM c[M][N] = deq(a) deq(b)^T in fp32, a = E4M3 [M][K],
+ * b = E2M1 [N][K] (layout as above), K a positive multiple of 128.  This is the
+ * block-scaled matrix-core kernel the layer's projections run on, exposed for
+ * stage-level checks. */
+int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                const uint8_t* b_scales, int32_t M, int32_t N, int32_t K, float* c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_H */

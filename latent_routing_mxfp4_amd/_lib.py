@@ -1,0 +1,145 @@
+"""ctypes binding of ``libmoe_layer.so`` (declared in ``include/moe_layer.h``).
+
+Argument marshalling only: every computation happens in the HIP library.
+Functions keep the C names; a non-zero status raises ``MoEError``.  Pointers
+are plain integers (device addresses, e.g. ``tensor.data_ptr()``), streams are
+``hipStream_t`` handles as integers (``torch.cuda.current_stream().cuda_stream``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_layer.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+EXPORTED = (
+    "moe_status_string",
+    "moe_layer_create",
+    "moe_layer_workspace_size",
+    "moe_layer_forward",
+    "moe_layer_destroy",
+    "moe_mx_quantize",
+    "moe_mx_gemm",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_string(status)} ({status})")
+
+
+class MoeLayerConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "d_model", "d_latent", "n_routed", "top_k", "n_shared", "d_ff_routed", "d_ff_shared", "max_tokens")]
+
+
+class MoeMxTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class MoeLayerWeights(ctypes.Structure):
+    _fields_ = [
+        ("w_down", MoeMxTensor),
+        ("w_up", MoeMxTensor),
+        ("w_router", ctypes.c_void_p),
+        ("router_logit_bias", ctypes.c_void_p),
+        ("selection_bias", ctypes.c_void_p),
+        ("w_gate_e", MoeMxTensor),
+        ("w_up_e", MoeMxTensor),
+        ("w_down_e", MoeMxTensor),
+        ("w_gate_s", MoeMxTensor),
+        ("w_up_s", MoeMxTensor),
+        ("w_down_s", MoeMxTensor),
+    ]
+
+
+TRACE_FIELDS = (
+    "xq_codes", "xq_scales", "z", "zq_codes", "zq_scales", "logits", "ids", "gates", "counts", "offsets",
+    "pair_of_row", "row_of_pair", "h", "hq_codes", "hq_scales", "y_e", "y_lat", "yq_codes", "yq_scales",
+    "hs", "hs_codes", "hs_scales",
+)
+
+
+class MoeLayerTrace(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in TRACE_FIELDS]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_layer_create.restype = ctypes.c_int
+    lib.moe_layer_create.argtypes = [ctypes.POINTER(MoeLayerConfig), ctypes.POINTER(MoeLayerWeights),
+                                     ctypes.POINTER(vp)]
+    lib.moe_layer_workspace_size.restype = ctypes.c_int
+    lib.moe_layer_workspace_size.argtypes = [ctypes.POINTER(MoeLayerConfig), i32, ctypes.POINTER(sz)]
+    lib.moe_layer_forward.restype = ctypes.c_int
+    lib.moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, sz, vp, ctypes.POINTER(MoeLayerTrace)]
+    lib.moe_layer_destroy.restype = ctypes.c_int
+    lib.moe_layer_destroy.argtypes = [vp]
+    lib.moe_mx_quantize.restype = ctypes.c_int
+    lib.moe_mx_quantize.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.moe_mx_gemm.restype = ctypes.c_int
+    lib.moe_mx_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def moe_status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def moe_layer_create(cfg: MoeLayerConfig, weights: MoeLayerWeights) -> int:
+    h = ctypes.c_void_p()
+    _check(load().moe_layer_create(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(h)), "moe_layer_create")
+    return h.value
+
+
+def moe_layer_workspace_size(cfg: MoeLayerConfig, T: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().moe_layer_workspace_size(ctypes.byref(cfg), int(T), ctypes.byref(n)), "moe_layer_workspace_size")
+    return n.value
+
+
+def moe_layer_forward(handle: int, x: int, T: int, y: int, ws: int, ws_bytes: int, stream: int = 0,
+                      trace: MoeLayerTrace | None = None) -> None:
+    tr = ctypes.byref(trace) if trace is not None else None
+    _check(load().moe_layer_forward(handle, x, int(T), y, ws, int(ws_bytes), stream, tr), "moe_layer_forward")
+
+
+def moe_layer_destroy(handle: int) -> None:
+    _check(load().moe_layer_destroy(handle), "moe_layer_destroy")
+
+
+def moe_mx_quantize(src: int, rows: int, K: int, fmt: int, codes: int, scales: int, stream: int = 0) -> None:
+    _check(load().moe_mx_quantize(src, int(rows), int(K), int(fmt), codes, scales, stream), "moe_mx_quantize")
+
+
+def moe_mx_gemm(a_codes: int, a_scales: int, b_codes: int, b_scales: int, M: int, N: int, K: int, c: int,
+                stream: int = 0) -> None:
+    _check(load().moe_mx_gemm(a_codes, a_scales, b_codes, b_scales, int(M), int(N), int(K), c, stream),
+           "moe_mx_gemm")

@@ -1,0 +1,86 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- MX quantisation (mx_quant.hip) -----------------------------------------
+// fmt 0: E4M3 codes [rows][K]; fmt 1: E2M1 packed codes [rows][K/2].
+hipError_t launch_quantize(const float* in, int64_t rows, int K, int fmt, uint8_t* codes,
+                           uint8_t* scales, hipStream_t s);
+
+// ---- Router (router.hip) ----------------------------------------------------
+// logits[T][E] = z[T][L] w[E][L]^T (+ bias[E]) in fp32 on the fp32 matrix cores.
+hipError_t launch_router_logits(const float* z, const float* w, const float* logit_bias, int T, int E,
+                                int L, float* logits, hipStream_t s);
+// Per token: s = sigmoid(logit), key = s + sel_bias, top-k by (key desc, id asc),
+// gates = s / sum(s over the k winners).
+hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
+                       float* gates, hipStream_t s);
+
+// ---- Dispatch (permute.hip) -------------------------------------------------
+size_t dispatch_scratch_ints(int T, int E);
+// counts[E], offsets[E+1], row_of_pair[T*k], pair_of_row[T*k], and, for each of
+// the two M-tile heights mt0/mt1, mtile_start_x[E+1] (prefix of ceil(count/mt)).
+hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* scratch, int32_t* counts,
+                           int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row, int mt0,
+                           int32_t* mtile_start0, int mt1, int32_t* mtile_start1, hipStream_t s);
+
+// ---- MX GEMM (mx_gemm.hip) --------------------------------------------------
+enum Epilogue : int {
+  EPI_F32 = 0,         // c = acc (fp32)
+  EPI_F32_QUANT = 1,   // c = acc and q = MXFP8(acc) along N
+  EPI_SWIGLU_QUANT = 2 // q = MXFP8(SiLU(acc_gate) * acc_up) along N
+};
+
+struct GemmSeg {
+  const uint8_t* a;    // E4M3 codes, row stride lda bytes
+  const uint8_t* as;   // scales, row stride lda/32
+  int64_t lda;         // = K of this segment (codes bytes per row)
+  const uint8_t* b;    // E2M1 packed codes of group 0: [N][K/2]
+  const uint8_t* bs;   // scales of group 0: [N][K/32]
+  const uint8_t* b2;   // second matrix (the "up" half of a SwiGLU), or null
+  const uint8_t* b2s;
+  int64_t b_gstride;   // bytes between groups' code matrices
+  int64_t bs_gstride;  // bytes between groups' scale matrices
+  int K;
+};
+
+struct GemmArgs {
+  int nseg;
+  GemmSeg seg[9];           // K segments (up to 1 + 8 shared experts)
+  // Groups.  Routed: rows of group g are [offsets[g], offsets[g+1]) and its
+  // M-tiles are [mtile_start[g], mtile_start[g+1]).  Dense: G groups of M rows.
+  const int32_t* offsets;      // null => dense
+  const int32_t* mtile_start;  // routed only
+  int G;
+  int M;                       // dense rows per group
+  int N;                       // output columns (per matrix)
+  const int32_t* gather;       // routed A-row gather: A row = gather[row] / gather_div (null = row)
+  int gather_div;
+  // Outputs: row index is the sorted row (routed) or m (dense, + g * c_gstride rows).
+  float* c;
+  int64_t ldc;
+  int64_t c_gstride;           // elements between dense groups' outputs
+  uint8_t* q;                  // E4M3 codes [rows][N]
+  uint8_t* qs;                 // scales [rows][N/32]
+  int64_t q_gstride;           // bytes between dense groups' code outputs
+  int64_t qs_gstride;
+  int max_mtiles;              // upper bound of M-tiles (grid size / n-tiles)
+};
+
+// M-tile height of the small-M (decode) and large-M configurations.
+int gemm_mtile(bool small_m);
+
+// Launch the grouped/dense MX GEMM with an automatically chosen tile shape.
+hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, bool small_m, hipStream_t s);
+
+// ---- Combine (combine.hip) --------------------------------------------------
+// y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then
+// yq = MXFP8(y_lat) per row; y_lat_out may be null.
+hipError_t launch_combine(const float* y_e, const float* gates, const int32_t* row_of_pair, int T, int k,
+                          int L, float* y_lat_out, uint8_t* yq, uint8_t* yqs, hipStream_t s);
+
+}  // namespace moe

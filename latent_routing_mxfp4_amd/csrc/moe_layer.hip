@@ -1,0 +1,406 @@
+// moe_layer.hip -- the C ABI: validation, workspace plan and the launch sequence
+// of one LatentMoE forward on a single HIP stream.
+//
+// Launch sequence (all asynchronous, no host synchronisation, no allocation):
+//   1. quantise x to MXFP8                                   mx_quant
+//   2. z = xq W_down^T (fp32) and zq = MXFP8(z)               mx_gemm (dense, F32_QUANT)
+//   3. logits = z W_router^T + logit_bias                     router_logits (fp32 MFMA)
+//   4. ids, gates = top-k(sigmoid + selection bias)           topk
+//   5. counts, offsets, stable permutation, M-tile prefix     dispatch (count/scan/scatter)
+//   6. hq = MXFP8(SiLU(zq_e W_gate_e^T) * (zq_e W_up_e^T))    mx_gemm (grouped, SWIGLU_QUANT,
+//                                                             rows gathered through the permutation)
+//   7. y_e = hq_e W_down_e^T                                  mx_gemm (grouped, F32)
+//   8. y_lat = sum_j gate_j y_e[row(t,j)], yq = MXFP8(y_lat)   combine
+//   9. hs_s = MXFP8(SiLU(xq W_gate_s^T) * (xq W_up_s^T))      mx_gemm (dense groups, SWIGLU_QUANT)
+//  10. y = yq W_up^T + sum_s hs_s W_down_s^T                  mx_gemm (dense, 1+S K-segments)
+// Step 10 runs the up-projection and every shared down-projection as one
+// GEMM whose K dimension is the concatenation [L | Fs | Fs ...], so the sum of
+// the routed and shared branches (Moat page, Fig. 2) happens in the fp32
+// accumulators instead of an extra pass over y.
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/moe_layer.h"
+#include "kernels.hpp"
+
+struct moe_layer {
+  moe_layer_config cfg;
+  moe_layer_weights w;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+struct Plan {
+  size_t xq, xqs, z, zq, zqs, logits, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye, ylat,
+      yq, yqs, hs, hss, total;
+};
+
+Plan make_plan(const moe_layer_config& c, int64_t T) {
+  const int64_t d = c.d_model, L = c.d_latent, E = c.n_routed, k = c.top_k, F = c.d_ff_routed,
+                S = c.n_shared, Fs = c.n_shared > 0 ? c.d_ff_shared : 0;
+  const int64_t P = T * k;
+  Plan p;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  p.xq = take(T * d);
+  p.xqs = take(T * d / 32);
+  p.z = take(T * L * 4);
+  p.zq = take(T * L);
+  p.zqs = take(T * L / 32);
+  p.logits = take(T * E * 4);
+  p.ids = take(P * 4);
+  p.gates = take(P * 4);
+  p.dscr = take(moe::dispatch_scratch_ints((int)T, (int)E) * 4);
+  p.counts = take(E * 4);
+  p.offsets = take((E + 1) * 4);
+  p.ms0 = take((E + 1) * 4);
+  p.ms1 = take((E + 1) * 4);
+  p.rop = take(P * 4);
+  p.por = take(P * 4);
+  p.hq = take(P * F);
+  p.hqs = take(P * F / 32);
+  p.ye = take(P * L * 4);
+  p.ylat = take(T * L * 4);
+  p.yq = take(T * L);
+  p.yqs = take(T * L / 32);
+  p.hs = take(S * T * Fs);
+  p.hss = take(S * T * Fs / 32);
+  p.total = o;
+  return p;
+}
+
+int check_config(const moe_layer_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->d_model <= 0 || c->d_latent <= 0 || c->d_ff_routed <= 0 || c->n_routed <= 0 || c->top_k <= 0 ||
+      c->n_shared < 0 || c->max_tokens <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->top_k > c->n_routed || c->n_shared > 8 || c->max_tokens > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  if (c->n_shared > 0 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->n_routed > 4096 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model % 128 || c->d_latent % 128 || c->d_ff_routed % 128) return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared > 0 && c->d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
+  if (c->d_model > (1 << 16) || c->d_latent > (1 << 16) || c->d_ff_routed > (1 << 16) ||
+      (c->n_shared > 0 && c->d_ff_shared > (1 << 16)))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+inline bool mx_ok(const moe_mx_tensor& t) { return t.codes != nullptr && t.scales != nullptr; }
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline bool mx_aligned(const moe_mx_tensor& t) { return aligned(t.codes, 16) && aligned(t.scales, 4); }
+
+template <class T>
+inline T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported layer shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int moe_layer_create(const moe_layer_config* cfg, const moe_layer_weights* w, moe_layer_t* out) {
+  if (!cfg || !w || !out) return MOE_ERR_INVALID_ARG;
+  int st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!mx_ok(w->w_down) || !mx_ok(w->w_up) || !w->w_router || !mx_ok(w->w_gate_e) || !mx_ok(w->w_up_e) ||
+      !mx_ok(w->w_down_e))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && (!mx_ok(w->w_gate_s) || !mx_ok(w->w_up_s) || !mx_ok(w->w_down_s)))
+    return MOE_ERR_INVALID_ARG;
+  if (!mx_aligned(w->w_down) || !mx_aligned(w->w_up) || !mx_aligned(w->w_gate_e) || !mx_aligned(w->w_up_e) ||
+      !mx_aligned(w->w_down_e) || !aligned(w->w_router, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->n_shared > 0 && (!mx_aligned(w->w_gate_s) || !mx_aligned(w->w_up_s) || !mx_aligned(w->w_down_s)))
+    return MOE_ERR_INVALID_ARG;
+  moe_layer* h = new (std::nothrow) moe_layer;
+  if (!h) return MOE_ERR_INVALID_ARG;
+  h->cfg = *cfg;
+  h->w = *w;
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_layer_workspace_size(const moe_layer_config* cfg, int32_t T, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  int st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > cfg->max_tokens) return MOE_ERR_INVALID_ARG;
+  *bytes = make_plan(*cfg, T).total;
+  return MOE_OK;
+}
+
+int moe_layer_destroy(moe_layer_t layer) {
+  delete layer;
+  return MOE_OK;
+}
+
+#define MOE_HIP(expr)                                 \
+  do {                                                \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;     \
+  } while (0)
+
+int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes,
+                      void* stream, const moe_layer_trace* tr) {
+  if (!layer) return MOE_ERR_INVALID_ARG;
+  const moe_layer_config& c = layer->cfg;
+  if (T < 0 || T > c.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  const Plan pl = make_plan(c, T);
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < pl.total) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_layer_weights& w = layer->w;
+  const int d = c.d_model, L = c.d_latent, E = c.n_routed, k = c.top_k, F = c.d_ff_routed, S = c.n_shared,
+            Fs = c.d_ff_shared;
+  const int64_t P = (int64_t)T * k;
+
+  uint8_t* xq = at<uint8_t>(ws, pl.xq);
+  uint8_t* xqs = at<uint8_t>(ws, pl.xqs);
+  float* z = at<float>(ws, pl.z);
+  uint8_t* zq = at<uint8_t>(ws, pl.zq);
+  uint8_t* zqs = at<uint8_t>(ws, pl.zqs);
+  float* logits = at<float>(ws, pl.logits);
+  int32_t* ids = at<int32_t>(ws, pl.ids);
+  float* gates = at<float>(ws, pl.gates);
+  int32_t* dscr = at<int32_t>(ws, pl.dscr);
+  int32_t* counts = at<int32_t>(ws, pl.counts);
+  int32_t* offsets = at<int32_t>(ws, pl.offsets);
+  int32_t* ms0 = at<int32_t>(ws, pl.ms0);
+  int32_t* ms1 = at<int32_t>(ws, pl.ms1);
+  int32_t* rop = at<int32_t>(ws, pl.rop);
+  int32_t* por = at<int32_t>(ws, pl.por);
+  uint8_t* hq = at<uint8_t>(ws, pl.hq);
+  uint8_t* hqs = at<uint8_t>(ws, pl.hqs);
+  float* ye = at<float>(ws, pl.ye);
+  float* ylat = at<float>(ws, pl.ylat);
+  uint8_t* yq = at<uint8_t>(ws, pl.yq);
+  uint8_t* yqs = at<uint8_t>(ws, pl.yqs);
+  uint8_t* hs = at<uint8_t>(ws, pl.hs);
+  uint8_t* hss = at<uint8_t>(ws, pl.hss);
+
+  const bool small_dense = T <= 256;
+  const bool small_routed = P <= (int64_t)32 * E;
+  const int mt_small = moe::gemm_mtile(true), mt_big = moe::gemm_mtile(false);
+
+  // 1. xq
+  MOE_HIP(moe::launch_quantize(x, T, d, 0, xq, xqs, s));
+
+  // 2. z, zq
+  {
+    moe::GemmArgs a = {};
+    a.nseg = 1;
+    a.seg[0] = {xq, xqs, d, w.w_down.codes, w.w_down.scales, nullptr, nullptr, 0, 0, d};
+    a.G = 1;
+    a.M = T;
+    a.N = L;
+    a.c = z;
+    a.ldc = L;
+    a.q = zq;
+    a.qs = zqs;
+    a.max_mtiles = (T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense);
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32_QUANT, small_dense, s));
+  }
+
+  // 3-4. router
+  MOE_HIP(moe::launch_router_logits(z, w.w_router, w.router_logit_bias, T, E, L, logits, s));
+  MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, ids, gates, s));
+
+  // 5. dispatch
+  MOE_HIP(moe::launch_dispatch(ids, T, E, k, dscr, counts, offsets, rop, por, mt_small, ms0, mt_big, ms1, s));
+
+  const int mt_r = small_routed ? mt_small : mt_big;
+  const int32_t* ms_r = small_routed ? ms0 : ms1;
+  const int64_t max_mt_r = P / mt_r + (P < E ? P : E) + 1;
+
+  // 6. routed GEMM1 + SwiGLU + MXFP8
+  {
+    moe::GemmArgs a = {};
+    a.nseg = 1;
+    a.seg[0] = {zq,
+                zqs,
+                L,
+                w.w_gate_e.codes,
+                w.w_gate_e.scales,
+                w.w_up_e.codes,
+                w.w_up_e.scales,
+                (int64_t)F * L / 2,
+                (int64_t)F * L / 32,
+                L};
+    a.offsets = offsets;
+    a.mtile_start = ms_r;
+    a.G = E;
+    a.N = F;
+    a.gather = por;
+    a.gather_div = k;
+    a.c = tr ? tr->h : nullptr;
+    a.ldc = F;
+    a.q = hq;
+    a.qs = hqs;
+    a.max_mtiles = (int)max_mt_r;
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, small_routed, s));
+  }
+
+  // 7. routed GEMM2
+  {
+    moe::GemmArgs a = {};
+    a.nseg = 1;
+    a.seg[0] = {hq, hqs, F, w.w_down_e.codes, w.w_down_e.scales, nullptr, nullptr, (int64_t)L * F / 2,
+                (int64_t)L * F / 32, F};
+    a.offsets = offsets;
+    a.mtile_start = ms_r;
+    a.G = E;
+    a.N = L;
+    a.c = ye;
+    a.ldc = L;
+    a.max_mtiles = (int)max_mt_r;
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, small_routed, s));
+  }
+
+  // 8. combine
+  MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, ylat, yq, yqs, s));
+
+  // 9. shared experts, first half
+  if (S > 0) {
+    moe::GemmArgs a = {};
+    a.nseg = 1;
+    a.seg[0] = {xq,
+                xqs,
+                d,
+                w.w_gate_s.codes,
+                w.w_gate_s.scales,
+                w.w_up_s.codes,
+                w.w_up_s.scales,
+                (int64_t)Fs * d / 2,
+                (int64_t)Fs * d / 32,
+                d};
+    a.G = S;
+    a.M = T;
+    a.N = Fs;
+    a.c = tr ? tr->hs : nullptr;
+    a.ldc = Fs;
+    a.c_gstride = (int64_t)T * Fs;
+    a.q = hs;
+    a.qs = hss;
+    a.q_gstride = (int64_t)T * Fs;
+    a.qs_gstride = (int64_t)T * Fs / 32;
+    a.max_mtiles = S * ((T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense));
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, small_dense, s));
+  }
+
+  // 10. y = up-projection + shared down-projections (one K-concatenated GEMM)
+  {
+    moe::GemmArgs a = {};
+    a.nseg = 1 + S;
+    a.seg[0] = {yq, yqs, L, w.w_up.codes, w.w_up.scales, nullptr, nullptr, 0, 0, L};
+    for (int i = 0; i < S; ++i)
+      a.seg[1 + i] = {hs + (int64_t)i * T * Fs,
+                      hss + (int64_t)i * T * Fs / 32,
+                      Fs,
+                      w.w_down_s.codes + (int64_t)i * d * Fs / 2,
+                      w.w_down_s.scales + (int64_t)i * d * Fs / 32,
+                      nullptr,
+                      nullptr,
+                      0,
+                      0,
+                      Fs};
+    a.G = 1;
+    a.M = T;
+    a.N = d;
+    a.c = y;
+    a.ldc = d;
+    a.max_mtiles = (T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense);
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, small_dense, s));
+  }
+
+  // Optional trace copies.
+  if (tr) {
+    auto cp = [&](void* dst, const void* src, size_t n) -> hipError_t {
+      if (!dst || n == 0) return hipSuccess;
+      return hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s);
+    };
+    const size_t Ts = (size_t)T, Ps = (size_t)P;
+    MOE_HIP(cp(tr->xq_codes, xq, Ts * d));
+    MOE_HIP(cp(tr->xq_scales, xqs, Ts * d / 32));
+    MOE_HIP(cp(tr->z, z, Ts * L * 4));
+    MOE_HIP(cp(tr->zq_codes, zq, Ts * L));
+    MOE_HIP(cp(tr->zq_scales, zqs, Ts * L / 32));
+    MOE_HIP(cp(tr->logits, logits, Ts * E * 4));
+    MOE_HIP(cp(tr->ids, ids, Ps * 4));
+    MOE_HIP(cp(tr->gates, gates, Ps * 4));
+    MOE_HIP(cp(tr->counts, counts, (size_t)E * 4));
+    MOE_HIP(cp(tr->offsets, offsets, (size_t)(E + 1) * 4));
+    MOE_HIP(cp(tr->pair_of_row, por, Ps * 4));
+    MOE_HIP(cp(tr->row_of_pair, rop, Ps * 4));
+    MOE_HIP(cp(tr->hq_codes, hq, Ps * F));
+    MOE_HIP(cp(tr->hq_scales, hqs, Ps * F / 32));
+    MOE_HIP(cp(tr->y_e, ye, Ps * L * 4));
+    MOE_HIP(cp(tr->y_lat, ylat, Ts * L * 4));
+    MOE_HIP(cp(tr->yq_codes, yq, Ts * L));
+    MOE_HIP(cp(tr->yq_scales, yqs, Ts * L / 32));
+    if (S > 0) {
+      MOE_HIP(cp(tr->hs_codes, hs, (size_t)S * Ts * Fs));
+      MOE_HIP(cp(tr->hs_scales, hss, (size_t)S * Ts * Fs / 32));
+    }
+  }
+  return MOE_OK;
+}
+
+int moe_mx_quantize(const float* in, int64_t rows, int32_t K, int32_t fmt, uint8_t* codes, uint8_t* scales,
+                    void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 || (fmt != 0 && fmt != 1)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!in || !codes || !scales || !aligned(in, 16) || !aligned(codes, fmt == 0 ? 4 : 2))
+    return MOE_ERR_INVALID_ARG;
+  if (rows > ((int64_t)1 << 40) / K) return MOE_ERR_INVALID_ARG;
+  if (moe::launch_quantize(in, rows, K, fmt, codes, scales, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                int32_t M, int32_t N, int32_t K, float* c, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 128) return MOE_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return MOE_OK;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MOE_ERR_INVALID_ARG;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
+    return MOE_ERR_INVALID_ARG;
+  const bool small = M <= 256;
+  moe::GemmArgs a = {};
+  a.nseg = 1;
+  a.seg[0] = {a_codes, a_scales, K, b_codes, b_scales, nullptr, nullptr, 0, 0, K};
+  a.G = 1;
+  a.M = M;
+  a.N = N;
+  a.c = c;
+  a.ldc = N;
+  a.max_mtiles = (M + moe::gemm_mtile(small) - 1) / moe::gemm_mtile(small);
+  if (moe::launch_mx_gemm(a, moe::EPI_F32, small, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// mx_device.hpp -- device helpers shared by the gfx950 kernels: MX encoding in
+// integer arithmetic, wave reductions, and the block-scaled MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// MX encoding.  Four Bits at a Time, "Four bits from the start": the shared
+// exponent of a block is floor(log2(amax)) minus the element format's largest
+// exponent; elements are the value divided by 2^e, clipped to the largest grid
+// magnitude and rounded to the nearest grid point.  Everything below is exact
+// integer work on the fp32 bit pattern, so the result does not depend on the
+// rounding mode of any float operation.
+
+// floor(log2(|a|)) of a nonzero fp32 bit pattern (sign ignored).
+__device__ __forceinline__ int floor_log2_bits(uint32_t mag) {
+  uint32_t ex = mag >> 23;
+  if (ex) return (int)ex - 127;
+  return -149 + (31 - __clz(mag));  // subnormal: mag * 2^-149
+}
+
+// E8M0 code of a block with maximum magnitude amax (fp32 bits, sign cleared).
+// EMAX = 8 for E4M3, 2 for E2M1.  amax == 0 gives code 0 (the clamp floor).
+template <int EMAX>
+__device__ __forceinline__ int mx_scale_code(uint32_t amax_bits) {
+  if (amax_bits == 0) return 0;
+  int e = floor_log2_bits(amax_bits) - EMAX;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return e + 127;
+}
+
+// Element code of fp32 v under block exponent e = scale_code - 127.
+// MB mantissa bits, EMIN smallest normal exponent, MAXC largest finite
+// magnitude code, SBIT sign position.  Round to nearest, ties to even code.
+template <int MB, int EMIN, int MAXC, int SBIT>
+__device__ __forceinline__ uint32_t mx_encode(float v, int e) {
+  uint32_t b = __float_as_uint(v);
+  uint32_t sign = (b >> 31) << SBIT;
+  uint32_t mag = b & 0x7fffffffu;
+  if (mag == 0) return sign;
+  uint32_t ex = mag >> 23;
+  uint32_t M;   // integer significand: |v| = M * 2^E0
+  int E0, fl;
+  if (ex) {
+    M = (mag & 0x7fffffu) | 0x800000u;
+    E0 = (int)ex - 150;
+    fl = (int)ex - 127;
+  } else {
+    M = mag;
+    E0 = -149;
+    fl = -149 + (31 - __clz(mag));
+  }
+  int fly = fl - e;                       // floor(log2(|v| / 2^e))
+  int bin = fly > EMIN ? fly : EMIN;      // binade of the grid step
+  int sh = bin - MB + e - E0;             // q = M / 2^sh, rounded
+  uint32_t q;
+  if (sh <= 0) {
+    q = M << (-sh);                       // not reached for e >= -127; kept exact anyway
+  } else if (sh >= 32) {
+    q = 0;                                // below half a step
+  } else {
+    uint32_t qt = M >> sh;
+    uint32_t rem = M & ((1u << sh) - 1u);
+    uint32_t half = 1u << (sh - 1);
+    q = qt + ((rem > half) | ((rem == half) & (qt & 1u)));
+  }
+  uint32_t code = (uint32_t)(bin - EMIN) * (1u << MB) + q;
+  code = code > (uint32_t)MAXC ? (uint32_t)MAXC : code;
+  return sign | code;
+}
+
+__device__ __forceinline__ uint32_t enc_e4m3(float v, int e) { return mx_encode<3, -6, 0x7E, 7>(v, e); }
+__device__ __forceinline__ uint32_t enc_e2m1(float v, int e) { return mx_encode<1, 0, 0x7, 3>(v, e); }
+
+// ---------------------------------------------------------------------------
+// Wave helpers.
+
+// Max over aligned groups of W lanes (W a power of two <= 64), via xor shuffles.
+template <int W>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) {
+    uint32_t w = (uint32_t)__shfl_xor((int)v, o, kWave);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Block-scaled MFMA, 16x16x128, A = E4M3, B = E2M1, fp32 accumulate.
+//
+// Operand layout (64 lanes, lane l, r = l % 16, g = l / 16):
+//   A: row r, K elements [32g, 32g+32)  -> 32 bytes (8 dwords)
+//   B: col r, K elements [32g, 32g+32)  -> 16 bytes (4 dwords, low 4 of 8)
+//   scale_a / scale_b: bits [7:0] = E8M0 of that lane's 32-element block
+//   D: col r, rows 4g .. 4g+3           -> 4 floats
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma_f8f4(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, /*A fmt E4M3*/ 0, /*B fmt E2M1*/ 4,
+                                                          0, sa, 0, sb);
+}
+
+}  // namespace moe

@@ -1,0 +1,274 @@
+// mx_gemm.hip -- grouped / dense block-scaled GEMM on the gfx950 matrix cores.
+//
+// C = deq(A) deq(B)^T with A an MXFP8 (E4M3) activation matrix and B an MXFP4
+// (E2M1) weight matrix [N][K], both blocked by 32 along K.  The MX scales are
+// applied inside v_mfma_scale_f32_16x16x128_f8f6f4, so the weights are consumed
+// as stored, never expanded to a wider copy (Kimi K3 open-weights serving,
+// section "Native MXFP4": kernels should consume that representation).
+//
+// The same kernel runs
+//   * the routed experts as one grouped GEMM over ragged, runtime-sized
+//     segments (Four Bits at a Time, "What has to change in the serving
+//     stacks": up to 896 runtime-sized groups per layer) -- the group of an
+//     M-tile is found from the device-side prefix of M-tiles per expert, so
+//     nothing is read back to the host;
+//   * the dense projections (latent down/up) and the shared experts.
+//
+// Work decomposition: a workgroup of 4 waves owns an (MT x NT) output tile;
+// the waves split the N columns, each wave computes MT x (16*NW) with
+// MW x NW 16x16 MFMA tiles (two accumulators per tile for SwiGLU: gate and
+// up).  Operands go straight from global memory into the MFMA register
+// layout, one 16-byte load per lane per E2M1 fragment, two per E4M3 fragment,
+// one dword of 4 block scales per row per K-step.  The K loop is software
+// pipelined one K-step deep.
+//
+// Epilogues: fp32 store; fp32 store plus MXFP8 quantisation along N; or
+// h = SiLU(gate) * up quantised to MXFP8 (the expert hidden state; h itself is
+// also stored in fp32 when an output pointer is given, for tracing), where the
+// 32-column block of a row sits in one wave (two adjacent 16-column tiles x 16
+// lanes), so its maximum is a 16-lane xor reduction.
+#include "kernels.hpp"
+#include "mx_device.hpp"
+
+namespace moe {
+
+namespace {
+
+struct Frag8 {  // E4M3 A fragment: 32 bytes per lane
+  uint4 lo, hi;
+};
+
+__device__ __forceinline__ v8i as_v8i(const Frag8& f) {
+  v8i r;
+  r[0] = (int)f.lo.x; r[1] = (int)f.lo.y; r[2] = (int)f.lo.z; r[3] = (int)f.lo.w;
+  r[4] = (int)f.hi.x; r[5] = (int)f.hi.y; r[6] = (int)f.hi.z; r[7] = (int)f.hi.w;
+  return r;
+}
+
+__device__ __forceinline__ v8i as_v8i(const uint4& f) {
+  v8i r;
+  r[0] = (int)f.x; r[1] = (int)f.y; r[2] = (int)f.z; r[3] = (int)f.w;
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+}  // namespace
+
+template <int MW, int NW, int EPI>
+__global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
+  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
+  constexpr int NB = SWI ? 2 : 1;
+  constexpr int MT = 16 * MW;
+  constexpr int NT = 4 * 16 * NW;
+  static_assert(EPI == EPI_F32 || NW % 2 == 0, "quantising epilogues need whole 32-column blocks per wave");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int n_ntiles = (p.N + NT - 1) / NT;
+  const int gm = blockIdx.x / n_ntiles;
+  const int nt = blockIdx.x - gm * n_ntiles;
+
+  int g, m0, rows, row_base;
+  if (p.offsets) {
+    const int total = p.mtile_start[p.G];
+    if (gm >= total) return;
+    int lo = 0, hi = p.G;  // mtile_start[lo] <= gm < mtile_start[hi]
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (p.mtile_start[mid] <= gm) lo = mid; else hi = mid;
+    }
+    g = lo;
+    row_base = p.offsets[g];
+    rows = p.offsets[g + 1] - row_base;
+    m0 = (gm - p.mtile_start[g]) * MT;
+  } else {
+    const int mpg = (p.M + MT - 1) / MT;
+    g = gm / mpg;
+    if (g >= p.G) return;
+    m0 = (gm - g * mpg) * MT;
+    rows = p.M;
+    row_base = 0;
+  }
+  const int n0 = nt * NT + wave * 16 * NW;
+
+  // Rows of A this lane feeds (clamped into the group; results of clamped rows are dropped).
+  int64_t arow[MW];
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi) {
+    int r = m0 + 16 * mi + r16;
+    r = r < rows ? r : rows - 1;
+    int sr = row_base + r;
+    if (p.offsets) arow[mi] = p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr;
+    else arow[mi] = r;
+  }
+  int bcol[NW];
+#pragma unroll
+  for (int ni = 0; ni < NW; ++ni) {
+    int c = n0 + 16 * ni + r16;
+    bcol[ni] = c < p.N ? c : p.N - 1;
+  }
+
+  v4f acc[MW][NW][NB];
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) acc[mi][ni][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSeg& sg = p.seg[s];
+    const int K = sg.K;
+    const int ksteps = K >> 7;
+    const int64_t lds = sg.lda >> 5;
+    const uint8_t* ap[MW];
+    const uint32_t* asp[MW];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi) {
+      ap[mi] = sg.a + arow[mi] * sg.lda + 32 * g4;
+      asp[mi] = reinterpret_cast<const uint32_t*>(sg.as + arow[mi] * lds);
+    }
+    const uint8_t* bp[NW][NB];
+    const uint32_t* bsp[NW][NB];
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni) {
+#pragma unroll
+      for (int h = 0; h < NB; ++h) {
+        const uint8_t* bb = h == 0 ? sg.b : sg.b2;
+        const uint8_t* bbs = h == 0 ? sg.bs : sg.b2s;
+        bp[ni][h] = bb + (int64_t)g * sg.b_gstride + (int64_t)bcol[ni] * (K >> 1) + 16 * g4;
+        bsp[ni][h] = reinterpret_cast<const uint32_t*>(bbs + (int64_t)g * sg.bs_gstride + (int64_t)bcol[ni] * (K >> 5));
+      }
+    }
+
+    Frag8 fa[MW];
+    uint32_t sa[MW];
+    uint4 fb[NW][NB];
+    uint32_t sb[NW][NB];
+    auto load = [&](int ks) {
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi) {
+        const uint4* q = reinterpret_cast<const uint4*>(ap[mi] + 128 * ks);
+        fa[mi].lo = q[0];
+        fa[mi].hi = q[1];
+        sa[mi] = asp[mi][ks] >> (8 * g4);
+      }
+#pragma unroll
+      for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+        for (int h = 0; h < NB; ++h) {
+          fb[ni][h] = *reinterpret_cast<const uint4*>(bp[ni][h] + 64 * ks);
+          sb[ni][h] = bsp[ni][h][ks] >> (8 * g4);
+        }
+    };
+
+    load(0);
+    for (int ks = 0; ks < ksteps; ++ks) {
+      Frag8 ca[MW];
+      uint32_t csa[MW];
+      uint4 cb[NW][NB];
+      uint32_t csb[NW][NB];
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi) { ca[mi] = fa[mi]; csa[mi] = sa[mi]; }
+#pragma unroll
+      for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+        for (int h = 0; h < NB; ++h) { cb[ni][h] = fb[ni][h]; csb[ni][h] = sb[ni][h]; }
+      if (ks + 1 < ksteps) load(ks + 1);
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi) {
+        const v8i av = as_v8i(ca[mi]);
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+          for (int h = 0; h < NB; ++h)
+            acc[mi][ni][h] = mfma_f8f4(av, as_v8i(cb[ni][h]), acc[mi][ni][h], (int)csa[mi], (int)csb[ni][h]);
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const bool dense = p.offsets == nullptr;
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + 16 * mi + 4 * g4 + i;
+      const bool rok = row < rows;
+      const int64_t orow = dense ? row : (int64_t)row_base + row;
+      if (EPI == EPI_F32 || EPI == EPI_F32_QUANT) {
+        float* crow = p.c + (dense ? (int64_t)g * p.c_gstride : 0) + orow * p.ldc;
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni) {
+          const int col = n0 + 16 * ni + r16;
+          if (rok && col < p.N) crow[col] = acc[mi][ni][0][i];
+        }
+      }
+      if (EPI == EPI_F32_QUANT || EPI == EPI_SWIGLU_QUANT) {
+        uint8_t* qrow = p.q + (dense ? (int64_t)g * p.q_gstride : 0) + orow * p.N;
+        uint8_t* qsrow = p.qs + (dense ? (int64_t)g * p.qs_gstride : 0) + orow * (p.N >> 5);
+#pragma unroll
+        for (int b = 0; b < NW / 2; ++b) {
+          float v0, v1;
+          if (SWI) {
+            v0 = silu(acc[mi][2 * b][0][i]) * acc[mi][2 * b][1][i];
+            v1 = silu(acc[mi][2 * b + 1][0][i]) * acc[mi][2 * b + 1][1][i];
+            if (p.c != nullptr && rok && n0 + 32 * b < p.N) {  // optional fp32 copy of h (tracing)
+              float* crow = p.c + (dense ? (int64_t)g * p.c_gstride : 0) + orow * p.ldc;
+              crow[n0 + 32 * b + r16] = v0;
+              crow[n0 + 32 * b + 16 + r16] = v1;
+            }
+          } else {
+            v0 = acc[mi][2 * b][0][i];
+            v1 = acc[mi][2 * b + 1][0][i];
+          }
+          uint32_t m = max(__float_as_uint(v0) & 0x7fffffffu, __float_as_uint(v1) & 0x7fffffffu);
+          m = group_max_u32<16>(m);
+          const int sc = mx_scale_code<8>(m);
+          const int e = sc - 127;
+          const int cb = n0 + 32 * b;
+          if (rok && cb < p.N) {
+            qrow[cb + r16] = (uint8_t)enc_e4m3(v0, e);
+            qrow[cb + 16 + r16] = (uint8_t)enc_e4m3(v1, e);
+            if (r16 == 0) qsrow[cb >> 5] = (uint8_t)sc;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MW, int NW, int EPI>
+static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  constexpr int NT = 4 * 16 * NW;
+  const int n_ntiles = (a.N + NT - 1) / NT;
+  const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  mx_gemm_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+int gemm_mtile(bool small_m) { return small_m ? 16 : 64; }
+
+hipError_t launch_mx_gemm(const GemmArgs& a, int epi, bool small_m, hipStream_t s) {
+  if (small_m) {
+    switch (epi) {
+      case EPI_F32: return launch_cfg<1, 2, EPI_F32>(a, s);
+      case EPI_F32_QUANT: return launch_cfg<1, 2, EPI_F32_QUANT>(a, s);
+      default: return launch_cfg<1, 2, EPI_SWIGLU_QUANT>(a, s);
+    }
+  }
+  switch (epi) {
+    case EPI_F32: return launch_cfg<4, 2, EPI_F32>(a, s);
+    case EPI_F32_QUANT: return launch_cfg<4, 2, EPI_F32_QUANT>(a, s);
+    default: return launch_cfg<4, 2, EPI_SWIGLU_QUANT>(a, s);
+  }
+}
+
+}  // namespace moe

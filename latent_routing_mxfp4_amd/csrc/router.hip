@@ -1,0 +1,164 @@
+// router.hip -- sigmoid router on the latent and top-k selection.
+//
+// Kimi K3 and the New Open-Weights Moat, "How the router picks 16 of 896"
+// (Fig. 2): every routed expert gets a sigmoid score; selection takes the top
+// k of score + a per-expert selection bias; the winners' raw scores,
+// normalised by their sum, are the mixture weights.  Four Bits at a Time,
+// "The shape of the model": routing runs in the latent space.
+//
+// Two kernels:
+//   router_logits: logits[T][E] = z[T][L] W[E][L]^T (+ logit bias), fp32 in
+//     and out, on the fp32 matrix cores (v_mfma_f32_16x16x4f32) with 64x64
+//     tiles staged through LDS.
+//   topk: one wave per token; the E selection keys sit in LDS, each lane keeps
+//     the best key of its strided slice, and k rounds of a 64-lane
+//     (key desc, id asc) reduction pick the winners in slot order; only the
+//     winning lane rescans its slice.  k <= 64 (slot j is held by lane j).
+#include <float.h>
+
+#include "kernels.hpp"
+#include "mx_device.hpp"
+
+namespace moe {
+
+namespace {
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+constexpr int RT = 64;   // tokens per tile
+constexpr int RE = 64;   // experts per tile
+constexpr int RK = 32;   // K chunk
+constexpr int RPAD = 4;  // LDS row padding (floats)
+}  // namespace
+
+__global__ void __launch_bounds__(256) router_logits_kernel(const float* __restrict__ z,
+                                                           const float* __restrict__ w,
+                                                           const float* __restrict__ bias, int T, int E,
+                                                           int L, float* __restrict__ logits) {
+  __shared__ float zs[RT][RK + RPAD];
+  __shared__ float ws[RE][RK + RPAD];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int t0 = blockIdx.y * RT, e0 = blockIdx.x * RE;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;  // wave's 32x32 sub-tile
+
+  v4f_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = v4f_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < L; k0 += RK) {
+    // 64 rows x 32 floats = 512 float4 per operand; 2 per thread.
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int f = tid + 256 * it;
+      const int r = f >> 3, c4 = (f & 7) * 4;
+      float4 vz = make_float4(0.f, 0.f, 0.f, 0.f), vw = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t0 + r < T) vz = *reinterpret_cast<const float4*>(z + (int64_t)(t0 + r) * L + k0 + c4);
+      if (e0 + r < E) vw = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + r) * L + k0 + c4);
+      zs[r][c4 + 0] = vz.x; zs[r][c4 + 1] = vz.y; zs[r][c4 + 2] = vz.z; zs[r][c4 + 3] = vz.w;
+      ws[r][c4 + 0] = vw.x; ws[r][c4 + 1] = vw.y; ws[r][c4 + 2] = vw.z; ws[r][c4 + 3] = vw.w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < RK; kk += 4) {
+      float a0 = zs[wm + r16][kk + g4], a1 = zs[wm + 16 + r16][kk + g4];
+      float b0 = ws[wn + r16][kk + g4], b1 = ws[wn + 16 + r16][kk + g4];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int e = e0 + wn + 16 * b + r16;
+      if (e >= E) continue;
+      const float bb = bias ? bias[e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wm + 16 * a + 4 * g4 + i;
+        if (t < T) logits[(int64_t)t * E + e] = acc[a][b][i] + bb;
+      }
+    }
+}
+
+hipError_t launch_router_logits(const float* z, const float* w, const float* bias, int T, int E, int L,
+                                float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT);
+  router_logits_kernel<<<grid, dim3(256), 0, s>>>(z, w, bias, T, E, L, logits);
+  return hipGetLastError();
+}
+
+namespace {
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// (key desc, id asc) "better than"
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+}  // namespace
+
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
+                                                  const float* __restrict__ sel_bias, int T, int E, int k,
+                                                  int32_t* __restrict__ ids, float* __restrict__ gates) {
+  extern __shared__ float keys_smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // no block-level barrier below
+  float* keys = keys_smem + (int64_t)wave * E;
+  const float* lrow = logits + (int64_t)t * E;
+
+  float bk = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int e = lane; e < E; e += 64) {
+    float key = sigmoidf(lrow[e]);
+    if (sel_bias) key += sel_bias[e];
+    key = fmaxf(key, -FLT_MAX);  // NaN / -inf inputs rank last but stay above "taken" (-inf)
+    keys[e] = key;
+    if (better(key, e, bk, bi)) { bk = key; bi = e; }
+  }
+  float ssum = 0.f;
+  float mys = 0.f;  // raw score of the winner of slot `lane`
+  int myid = 0;
+  for (int r = 0; r < k; ++r) {
+    float wk = bk;
+    int wi = bi;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      float ok = __shfl_xor(wk, o, 64);
+      int oi = __shfl_xor(wi, o, 64);
+      if (better(ok, oi, wk, wi)) { wk = ok; wi = oi; }
+    }
+    const float sw = sigmoidf(lrow[wi]);
+    ssum += sw;  // every lane adds the same values in the same (slot) order
+    if (lane == r) { mys = sw; myid = wi; }
+    if ((wi & 63) == lane) {  // owner marks it taken and rescans its slice
+      keys[wi] = -INFINITY;
+      bk = -INFINITY;
+      bi = 0x7fffffff;
+      for (int e = lane; e < E; e += 64) {
+        const float key = keys[e];
+        if (better(key, e, bk, bi)) { bk = key; bi = e; }
+      }
+    }
+  }
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = myid;
+    gates[(int64_t)t * k + lane] = mys / ssum;
+  }
+}
+
+hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
+                       float* gates, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const size_t smem = (size_t)4 * E * sizeof(float);
+  topk_kernel<<<dim3((T + 3) / 4), dim3(256), smem, s>>>(logits, sel_bias, T, E, k, ids, gates);
+  return hipGetLastError();
+}
+
+}  // namespace moe

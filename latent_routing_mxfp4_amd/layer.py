@@ -1,0 +1,210 @@
+"""PyTorch-facing wrapper of the HIP LatentMoE layer.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+layer runs in ``libmoe_layer.so``.  Nothing here computes layer values.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from concurrent.futures import ThreadPoolExecutor
+from typing import Callable, Dict, Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _lib
+
+FMT_E4M3 = 0
+FMT_E2M1 = 1
+
+ROUTED = ("w_gate_e", "w_up_e", "w_down_e")
+SHARED = ("w_gate_s", "w_up_s", "w_down_s")
+DENSE = ("w_down", "w_up")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    d_model: int
+    d_latent: int
+    n_routed: int
+    top_k: int
+    n_shared: int
+    d_ff_routed: int
+    d_ff_shared: int
+
+    @classmethod
+    def of(cls, cfg) -> "LayerShape":
+        return cls(cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k, cfg.n_shared, cfg.d_ff_routed,
+                   cfg.d_ff_shared)
+
+    def matrix_shape(self, name: str) -> Tuple[int, int]:
+        d, L, F, Fs = self.d_model, self.d_latent, self.d_ff_routed, self.d_ff_shared
+        return {"w_down": (L, d), "w_up": (d, L), "w_gate_e": (F, L), "w_up_e": (F, L), "w_down_e": (L, F),
+                "w_gate_s": (Fs, d), "w_up_s": (Fs, d), "w_down_s": (d, Fs)}[name]
+
+    def count(self, name: str) -> int:
+        return self.n_routed if name in ROUTED else self.n_shared if name in SHARED else 1
+
+    def c_config(self, max_tokens: int) -> _lib.MoeLayerConfig:
+        return _lib.MoeLayerConfig(self.d_model, self.d_latent, self.n_routed, self.top_k, self.n_shared,
+                                   self.d_ff_routed, self.d_ff_shared, int(max_tokens))
+
+
+# --------------------------------------------------------------------------- MX helpers
+
+
+def mx_quantize(x: torch.Tensor, fmt: int, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """MX-encode an fp32 CUDA tensor along its last axis; returns (codes, scales)."""
+    assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous()
+    K = x.shape[-1]
+    rows = x.numel() // K if K else 0
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], K if fmt == FMT_E4M3 else K // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    _lib.moe_mx_quantize(x.data_ptr(), rows, K, fmt, codes.data_ptr(), scales.data_ptr(), _stream())
+    return codes, scales
+
+
+def mx_gemm(a_codes, a_scales, b_codes, b_scales) -> torch.Tensor:
+    """fp32 deq(a) @ deq(b)^T with a E4M3 [M][K], b packed E2M1 [N][K/2]."""
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    c = torch.empty(M, N, dtype=torch.float32, device=a_codes.device)
+    _lib.moe_mx_gemm(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(), M, N, K,
+                     c.data_ptr(), _stream())
+    return c
+
+
+def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray], device="cuda",
+                   extra: Optional[Dict[str, Optional[np.ndarray]]] = None, workers: int = 8) -> Dict:
+    """MXFP4-encode every weight matrix on the GPU.
+
+    ``host_fp32(name, index)`` returns the fp32 ``[out][in]`` matrix (numpy);
+    matrices are produced by a thread pool, copied to the device one at a
+    time through a staging buffer and encoded with ``moe_mx_quantize``.
+    ``extra`` carries the fp32 router (``w_router``) and the optional biases.
+    """
+    out: Dict = {}
+    jobs = []
+    for name in DENSE + ROUTED + SHARED:
+        n = shape.count(name)
+        if n == 0:
+            out[name] = None
+            continue
+        r, c = shape.matrix_shape(name)
+        codes = torch.empty(n, r, c // 2, dtype=torch.uint8, device=device)
+        scales = torch.empty(n, r, c // 32, dtype=torch.uint8, device=device)
+        out[name] = (codes if name in ROUTED + SHARED else codes[0], scales if name in ROUTED + SHARED else scales[0])
+        jobs += [(name, i, codes[i], scales[i]) for i in range(n)]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [ex.submit(host_fp32, name, i) for (name, i, _, _) in jobs[:2 * workers]]
+        nxt = len(futs)
+        for j, (name, i, codes, scales) in enumerate(jobs):
+            host = futs[j].result()
+            futs[j] = None
+            if nxt < len(jobs):
+                futs.append(ex.submit(host_fp32, jobs[nxt][0], jobs[nxt][1]))
+                nxt += 1
+            dev = torch.from_numpy(np.ascontiguousarray(host, dtype=np.float32)).to(device, non_blocking=False)
+            mx_quantize(dev, FMT_E2M1, out=(codes, scales))
+    extra = extra or {}
+    for k in ("w_router", "router_logit_bias", "selection_bias"):
+        v = extra.get(k)
+        out[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(device)
+    torch.cuda.synchronize()
+    return out
+
+
+# --------------------------------------------------------------------------- the layer
+
+
+class LatentMoE:
+    """Handle around ``moe_layer_create`` / ``moe_layer_forward``.
+
+    ``weights`` maps each weight name to ``(codes, scales)`` CUDA uint8 tensors
+    (routed/shared groups with a leading expert axis), ``w_router`` to an fp32
+    tensor, and the optional biases to fp32 tensors or None.
+    """
+
+    def __init__(self, shape: LayerShape, weights: Dict, max_tokens: int):
+        self.shape = shape
+        self.max_tokens = int(max_tokens)
+        self.weights = weights  # keep the tensors alive: the handle does not own them
+        self._cfg = shape.c_config(max_tokens)
+
+        def mx(name):
+            v = weights.get(name)
+            if v is None:
+                return _lib.MoeMxTensor(None, None)
+            return _lib.MoeMxTensor(v[0].data_ptr(), v[1].data_ptr())
+
+        self._w = _lib.MoeLayerWeights(
+            mx("w_down"), mx("w_up"), _ptr(weights["w_router"]), _ptr(weights.get("router_logit_bias")),
+            _ptr(weights.get("selection_bias")), mx("w_gate_e"), mx("w_up_e"), mx("w_down_e"), mx("w_gate_s"),
+            mx("w_up_s"), mx("w_down_s"))
+        self.handle = _lib.moe_layer_create(self._cfg, self._w)
+        self._ws: Optional[torch.Tensor] = None
+
+    def workspace_bytes(self, T: int) -> int:
+        return _lib.moe_layer_workspace_size(self._cfg, T)
+
+    def workspace(self, T: int) -> torch.Tensor:
+        need = self.workspace_bytes(T)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def trace_buffers(self, T: int) -> Dict[str, torch.Tensor]:
+        s = self.shape
+        d, L, E, k, F, S, Fs = s.d_model, s.d_latent, s.n_routed, s.top_k, s.d_ff_routed, s.n_shared, s.d_ff_shared
+        P = T * k
+        u8, i32, f32 = torch.uint8, torch.int32, torch.float32
+        shapes = {
+            "xq_codes": ((T, d), u8), "xq_scales": ((T, d // 32), u8), "z": ((T, L), f32),
+            "zq_codes": ((T, L), u8), "zq_scales": ((T, L // 32), u8), "logits": ((T, E), f32),
+            "ids": ((T, k), i32), "gates": ((T, k), f32), "counts": ((E,), i32), "offsets": ((E + 1,), i32),
+            "pair_of_row": ((P,), i32), "row_of_pair": ((P,), i32), "h": ((P, F), f32), "hq_codes": ((P, F), u8),
+            "hq_scales": ((P, F // 32), u8), "y_e": ((P, L), f32), "y_lat": ((T, L), f32),
+            "yq_codes": ((T, L), u8), "yq_scales": ((T, L // 32), u8),
+        }
+        if S > 0:
+            shapes["hs"] = ((S, T, Fs), f32)
+            shapes["hs_codes"] = ((S, T, Fs), u8)
+            shapes["hs_scales"] = ((S, T, Fs // 32), u8)
+        return {n: torch.empty(sh, dtype=dt, device="cuda") for n, (sh, dt) in shapes.items()}
+
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, trace: Optional[Dict] = None,
+                stream: Optional[int] = None) -> torch.Tensor:
+        assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() == 2
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty_like(x)
+        ws = self.workspace(T)
+        tr = None
+        if trace is not None:
+            tr = _lib.MoeLayerTrace(*[_ptr(trace.get(n)) for n in _lib.TRACE_FIELDS])
+        _lib.moe_layer_forward(self.handle, x.data_ptr(), T, y.data_ptr(), ws.data_ptr(), ws.numel(),
+                               _stream() if stream is None else stream, tr)
+        return y
+
+    def close(self) -> None:
+        if self.handle:
+            _lib.moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -163,15 +163,17 @@ def dispatch(ids: np.ndarray, n_experts: int) -> Dispatch:
 # --------------------------------------------------------------------------- experts
 
 
-def swiglu_expert(aq: MXTensor, wg: MXTensor, wu: MXTensor, wd: MXTensor, decide=np.float32):
+def swiglu_expert(aq: MXTensor, wg: MXTensor, wu: MXTensor, wd: MXTensor, decide=np.float32, full=False):
     """down(SiLU(gate a) * (up a)) with MXFP8 re-quantisation of the hidden h.
 
-    Returns (y, h, hq).
+    Returns (y, h, hq), plus (g, u) when ``full``.
     """
     g = mm(aq, wg)
     u = mm(aq, wu)
     h = silu(g) * u
     hq = quant(h, "e4m3", decide)
+    if full:
+        return mm(hq, wd), h, hq, g, u
     return mm(hq, wd), h, hq
 
 
@@ -186,12 +188,16 @@ class Trace:
     routing: Routing
     disp: Dispatch
     h_rows: np.ndarray        # [T*k][F] fp64, in sorted-row order
+    g_rows: np.ndarray        # [T*k][F] gate pre-activation, sorted rows
+    u_rows: np.ndarray        # [T*k][F] up projection, sorted rows
     hq_rows: MXTensor         # [T*k][F]
     ye_rows: np.ndarray       # [T*k][L]
     y_lat: np.ndarray         # [T][L]
     yq: MXTensor
     y_up: np.ndarray
     h_shared: list
+    g_shared: list
+    u_shared: list
     hq_shared: list
     y_shared: list
     y: np.ndarray
@@ -218,7 +224,7 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
     P = T * top_k
     F = None
     ye_rows = np.zeros((P, L))
-    h_rows = None
+    h_rows = g_rows = u_rows = None
     hq_codes = hq_scales = None
     for e in range(E):                                              # step 7
         lo, hi = disp.offsets[e], disp.offsets[e + 1]
@@ -229,14 +235,18 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
         else:
             wg, wu, wd = W.w_gate_e[e], W.w_up_e[e], W.w_down_e[e]
         toks = disp.pair_of_row[lo:hi] // top_k
-        ye, h, hq = swiglu_expert(zq[toks], wg, wu, wd, decide)
+        ye, h, hq, g, u = swiglu_expert(zq[toks], wg, wu, wd, decide, full=True)
         if h_rows is None:
             F = h.shape[1]
             h_rows = np.zeros((P, F))
+            g_rows = np.zeros((P, F))
+            u_rows = np.zeros((P, F))
             hq_codes = np.zeros((P, F), np.uint8)
             hq_scales = np.zeros((P, F // mx.BLOCK), np.uint8)
         ye_rows[lo:hi] = ye
         h_rows[lo:hi] = h
+        g_rows[lo:hi] = g
+        u_rows[lo:hi] = u
         hq_codes[lo:hi] = hq.codes
         hq_scales[lo:hi] = hq.scales
 
@@ -249,16 +259,19 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
     y_up = mm(yq, W.w_up)
 
     y = y_up.copy()                                                 # step 10
-    hs_l, hsq_l, ys_l = [], [], []
+    hs_l, hsq_l, ys_l, gs_l, us_l = [], [], [], [], []
     for s in range(len(W.w_gate_s)):
-        ys, hs, hsq = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide)
+        ys, hs, hsq, gs, us = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide, full=True)
         y += ys
         hs_l.append(hs)
+        gs_l.append(gs)
+        us_l.append(us)
         hsq_l.append(hsq)
         ys_l.append(ys)
 
     hq_rows = MXTensor(hq_codes, hq_scales, "e4m3") if hq_codes is not None else None
-    return Trace(xq, z, zq, r, disp, h_rows, hq_rows, ye_rows, y_lat, yq, y_up, hs_l, hsq_l, ys_l, y)
+    return Trace(xq, z, zq, r, disp, h_rows, g_rows, u_rows, hq_rows, ye_rows, y_lat, yq, y_up, hs_l, gs_l, us_l,
+                 hsq_l, ys_l, y)
 
 
 def forward_dense_mask(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32) -> np.ndarray:

@@ -1,0 +1,45 @@
+"""GPU-side helpers for the parity tests: build a seeded layer on the device
+through the HIP library and run it with a full trace."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import synth
+from latent_routing_mxfp4_amd import layer as LY
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_weights(cfg, selection_bias=None, workers=8):
+    shape = LY.LayerShape.of(cfg)
+    extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg),
+             "selection_bias": selection_bias}
+    return shape, LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra, workers=workers)
+
+
+def gpu_layer(cfg, max_tokens=None, selection_bias=None, weights=None):
+    if weights is None:
+        shape, weights = gpu_weights(cfg, selection_bias)
+    else:
+        shape = LY.LayerShape.of(cfg)
+    return LY.LatentMoE(shape, weights, max_tokens or cfg.T), weights
+
+
+def run_traced(layer, x_np: np.ndarray):
+    T = x_np.shape[0]
+    x = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).cuda()
+    tr = layer.trace_buffers(T)
+    y = layer.forward(x, trace=tr)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), {k: v.cpu().numpy() for k, v in tr.items()}
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()

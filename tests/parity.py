@@ -1,0 +1,160 @@
+"""Comparison of a GPU layer trace with the oracle's independent fp64 chain.
+
+Rules (all expected values come from the oracle run on the same seeded inputs):
+
+* MX codes of inputs (x) and weights: bit-exact.
+* fp32 GEMM outputs (z, h, y): within the fp32 accumulation bound
+  K * 2^-24 * ||a_row|| * ||b_row|| (Cauchy-Schwarz on sum |a_i b_i|) plus one
+  rounding of the value, wherever the GEMM inputs agree bit-exactly.
+* MX codes of computed tensors (zq, hq, yq, hs): equal to the oracle's codes
+  except where a rounding boundary (element midpoint or block power of two)
+  lies between the oracle's value and the GPU's fp32 value; those are
+  counted as flagged, never as failures.
+* expert ids: the same set per token unless the oracle's gap between the k-th
+  and (k+1)-th selection key is below 1e-6 (flagged near-tie); gates of
+  unflagged tokens within 1e-6.
+* dispatch: counts, offsets and the permutation equal the stable sort of the
+  GPU's own ids (exactly the oracle's when no token is flagged).
+* layer output: relative L2 error <= 5e-3 and max-abs error <= 5e-2 * rms(y).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import moe, mx
+
+EPS32 = 2.0 ** -24
+NEAR_TIE = 1e-6
+REL_L2 = 5e-3
+MAXABS_FRAC = 5e-2
+
+
+def row_norms(t: moe.MXTensor) -> np.ndarray:
+    return np.sqrt((t.deq() ** 2).sum(-1))
+
+
+def gemm_bound(a: moe.MXTensor, b: moe.MXTensor, value: np.ndarray) -> np.ndarray:
+    K = a.codes.shape[-1]
+    return K * EPS32 * np.outer(row_norms(a), row_norms(b)) + EPS32 * np.abs(value)
+
+
+def straddled(ref: np.ndarray, got: np.ndarray, fmt="e4m3") -> np.ndarray:
+    """Elements whose code may legitimately differ: a boundary between ref and got."""
+    ref = np.asarray(ref, np.float64)
+    got = np.asarray(got, np.float64)
+    dev = np.abs(got - ref) * (1 + 1e-6) + 1e-300
+    return moe.ambiguous_codes(ref.astype(np.float32).astype(np.float64), dev, fmt)
+
+
+def code_report(gpu_codes, gpu_scales, ref: moe.MXTensor, ref_vals, gpu_vals, fmt="e4m3"):
+    """(unflagged mismatches, flagged mismatches) of an E4M3 code tensor."""
+    sc_g = np.repeat(gpu_scales, 32, axis=-1).reshape(gpu_codes.shape)
+    sc_r = np.repeat(ref.scales, 32, axis=-1).reshape(ref.codes.shape)
+    mism = (gpu_codes != ref.codes) | (sc_g != sc_r)
+    if gpu_vals is None:
+        return int(mism.sum()), 0
+    amb = straddled(ref_vals, gpu_vals, fmt)
+    return int((mism & ~amb).sum()), int((mism & amb).sum())
+
+
+def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray):
+    diff = y_gpu.astype(np.float64) - y_ref
+    rel = np.linalg.norm(diff) / max(np.linalg.norm(y_ref), 1e-300)
+    rms = np.sqrt((y_ref ** 2).mean())
+    return float(rel), float(np.abs(diff).max()), float(rms)
+
+
+def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict, say=print) -> dict:
+    """Assert the GPU trace against the oracle trace; returns a report."""
+    T, k, E = y.shape[0], cfg.top_k, cfg.n_routed
+    rep = {}
+
+    # 1. input codes: bit-exact
+    assert np.array_equal(tr["xq_codes"], o.xq.codes), "xq codes"
+    assert np.array_equal(tr["xq_scales"], o.xq.scales), "xq scales"
+
+    # 2. latent down-projection
+    bz = gemm_bound(o.xq, W.w_down, o.z)
+    dz = np.abs(tr["z"].astype(np.float64) - o.z)
+    assert np.all(dz <= bz), f"z outside the fp32 bound: worst ratio {np.max(dz / bz):.3g}"
+    rep["z_err_over_bound"] = float(np.max(dz / bz))
+    bad, flag = code_report(tr["zq_codes"], tr["zq_scales"], o.zq, o.z, tr["z"])
+    assert bad == 0, f"zq: {bad} unflagged code mismatches"
+    rep["zq_flagged"] = flag
+    zq_flag_tok = np.zeros(T, bool)
+    if flag:
+        m = (tr["zq_codes"] != o.zq.codes).any(1) | (tr["zq_scales"] != o.zq.scales).any(1)
+        zq_flag_tok |= m
+
+    # 3. routing
+    gi, ri = tr["ids"], o.routing.ids
+    same = np.array([set(gi[t]) == set(ri[t]) for t in range(T)])
+    near = o.routing.gap < NEAR_TIE
+    assert np.all(same | near), f"ids differ on tokens {np.where(~(same | near))[0][:10]} without a near-tie"
+    rep["near_tie_tokens"] = int(near.sum())
+    rep["ids_differ_flagged"] = int((~same).sum())
+    ok = same & ~near
+    for t in np.where(ok)[0]:
+        og = dict(zip(ri[t].tolist(), o.routing.gates[t].tolist()))
+        for j in range(k):
+            assert abs(tr["gates"][t, j] - og[int(gi[t, j])]) <= 1e-6, ("gate", t, j)
+    assert np.all(np.abs(tr["gates"].astype(np.float64).sum(1) - 1) <= 1e-6)
+    for t in range(T):
+        assert len(set(gi[t].tolist())) == k and gi[t].min() >= 0 and gi[t].max() < E
+
+    # 4. dispatch = stable sort of the GPU's ids (bit-exact)
+    d = moe.dispatch(gi, E)
+    assert np.array_equal(tr["counts"], d.counts), "counts"
+    assert np.array_equal(tr["offsets"], d.offsets), "offsets"
+    assert np.array_equal(tr["pair_of_row"], d.pair_of_row), "pair_of_row"
+    assert np.array_equal(tr["row_of_pair"], d.row_of_pair), "row_of_pair"
+
+    # 5. expert hidden states, rows whose token agrees upstream (same ids, same zq)
+    tok_ok = same & ~zq_flag_tok
+    if np.array_equal(gi, ri) and "h" in tr:
+        rows_ok = tok_ok[o.disp.pair_of_row // k]
+        g, u = o.g_rows, o.u_rows
+        # error bound of h = silu(G) U from the bounds of G and U
+        bnd_gu = np.zeros_like(g)
+        for e in range(E):
+            lo, hi = o.disp.offsets[e], o.disp.offsets[e + 1]
+            if hi == lo:
+                continue
+            toks = o.disp.pair_of_row[lo:hi] // k
+            a = o.zq[toks]
+            nb = np.sqrt((W.w_gate_e[e].deq() ** 2).sum(-1)) if W.w_gate_e else None
+            nu = np.sqrt((W.w_up_e[e].deq() ** 2).sum(-1)) if W.w_up_e else None
+            na = row_norms(a)
+            KL = a.codes.shape[-1]
+            bnd_gu[lo:hi] = KL * EPS32 * np.outer(na, np.maximum(nb, nu))
+        sg = 1 / (1 + np.exp(-g))
+        dsilu = sg * (1 + g * (1 - sg))
+        bh = (np.abs(dsilu) * np.abs(u) + np.abs(g * sg)) * (bnd_gu + EPS32 * (np.abs(g) + np.abs(u))) \
+            + 4 * EPS32 * np.abs(o.h_rows)
+        dh = np.abs(tr["h"].astype(np.float64) - o.h_rows)
+        viol = (dh > bh) & rows_ok[:, None]
+        assert not viol.any(), f"h outside bound on {viol.sum()} elements"
+        bad, flag = code_report(tr["hq_codes"], tr["hq_scales"], o.hq_rows, o.h_rows, tr["h"])
+        assert bad == 0, f"hq: {bad} unflagged code mismatches"
+        rep["hq_flagged"] = flag
+
+    # 6. combined latent codes
+    bad, flag = code_report(tr["yq_codes"], tr["yq_scales"], o.yq, o.y_lat, tr["y_lat"])
+    rep["yq_mismatch_unflagged"] = bad
+    rep["yq_flagged"] = flag
+
+    # 7. shared experts
+    for s in range(len(W.w_gate_s)):
+        bad, flag = code_report(tr["hs_codes"][s], tr["hs_scales"][s], o.hq_shared[s], o.h_shared[s],
+                                tr["hs"][s] if "hs" in tr else None)
+        assert bad == 0, f"shared {s}: {bad} unflagged code mismatches"
+        rep[f"hs{s}_flagged"] = flag
+
+    # 8. output
+    rel, maxabs, rms = output_errors(y, o.y)
+    rep.update(rel_l2=rel, max_abs=maxabs, rms=rms)
+    say("parity report:", rep)
+    assert rel <= REL_L2, f"relative L2 {rel:.3g}"
+    assert maxabs <= MAXABS_FRAC * rms, f"max abs {maxabs:.3g} vs rms {rms:.3g}"
+    return rep

@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+entry point, and rejects bad arguments before any launch."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from latent_routing_mxfp4_amd import _lib
+from tests.conftest import ROOT
+
+FAKE = 0x10000000  # aligned, never dereferenced by host-side validation
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared()
+    assert declared == set(_lib.EXPORTED)
+    for n in declared:
+        assert hasattr(lib, n), n
+
+
+def _k3(max_tokens=16384):
+    return _lib.MoeLayerConfig(7168, 3584, 896, 16, 2, 3072, 3072, max_tokens)
+
+
+def _weights(shared=True):
+    t = _lib.MoeMxTensor(FAKE, FAKE)
+    z = _lib.MoeMxTensor(None, None)
+    s = t if shared else z
+    return _lib.MoeLayerWeights(t, t, FAKE, None, None, t, t, t, s, s, s)
+
+
+def _create_status(cfg, w):
+    h = ctypes.c_void_p()
+    st = _lib.load().moe_layer_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
+    if st == 0:
+        _lib.moe_layer_destroy(h.value)
+    return st
+
+
+def test_create_accepts_k3_and_rejects_bad_shapes():
+    assert _create_status(_k3(), _weights()) == _lib.MOE_OK
+    bad = [
+        (dict(top_k=897), _lib.MOE_ERR_INVALID_ARG),
+        (dict(top_k=0), _lib.MOE_ERR_INVALID_ARG),
+        (dict(d_model=7200), _lib.MOE_ERR_UNSUPPORTED),
+        (dict(d_latent=-128), _lib.MOE_ERR_INVALID_ARG),
+        (dict(max_tokens=0), _lib.MOE_ERR_INVALID_ARG),
+        (dict(n_shared=9), _lib.MOE_ERR_INVALID_ARG),
+        (dict(n_routed=5000, top_k=16), _lib.MOE_ERR_UNSUPPORTED),
+        (dict(top_k=65, n_routed=128), _lib.MOE_ERR_UNSUPPORTED),
+    ]
+    for change, want in bad:
+        cfg = _k3()
+        for k, v in change.items():
+            setattr(cfg, k, v)
+        assert _create_status(cfg, _weights()) == want, change
+
+
+def test_create_rejects_null_and_misaligned_weights():
+    w = _weights()
+    w.w_router = None
+    assert _create_status(_k3(), w) == _lib.MOE_ERR_INVALID_ARG
+    w = _weights()
+    w.w_gate_e = _lib.MoeMxTensor(FAKE + 8, FAKE)
+    assert _create_status(_k3(), w) == _lib.MOE_ERR_INVALID_ARG
+    # shared tensors may be NULL only when there are no shared experts
+    assert _create_status(_k3(), _weights(shared=False)) == _lib.MOE_ERR_INVALID_ARG
+    cfg = _k3()
+    cfg.n_shared = 0
+    assert _create_status(cfg, _weights(shared=False)) == _lib.MOE_OK
+    h = ctypes.c_void_p()
+    assert _lib.load().moe_layer_create(None, ctypes.byref(_weights()), ctypes.byref(h)) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_size_is_monotone_and_bounded():
+    cfg = _k3()
+    sizes = [_lib.moe_layer_workspace_size(cfg, T) for T in (0, 1, 64, 4096, 16384)]
+    assert sizes == sorted(sizes)
+    assert sizes[-1] < 8 << 30  # prefill workspace stays a few GB
+    with pytest.raises(_lib.MoEError) as e:
+        _lib.moe_layer_workspace_size(cfg, 16385)
+    assert e.value.status == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_forward_argument_errors_need_no_gpu():
+    cfg = _k3(max_tokens=64)
+    h = _lib.moe_layer_create(cfg, _weights())
+    try:
+        lib = _lib.load()
+        need = _lib.moe_layer_workspace_size(cfg, 64)
+        # T == 0 is a no-op, even with null buffers
+        assert lib.moe_layer_forward(h, None, 0, None, None, 0, None, None) == _lib.MOE_OK
+        assert lib.moe_layer_forward(None, FAKE, 1, FAKE, FAKE, need, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert lib.moe_layer_forward(h, FAKE, 65, FAKE, FAKE, need, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert lib.moe_layer_forward(h, FAKE, -1, FAKE, FAKE, need, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert lib.moe_layer_forward(h, None, 8, FAKE, FAKE, need, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert lib.moe_layer_forward(h, FAKE, 64, FAKE, None, need, None, None) == _lib.MOE_ERR_WORKSPACE
+        assert lib.moe_layer_forward(h, FAKE, 64, FAKE, FAKE, need - 1, None, None) == _lib.MOE_ERR_WORKSPACE
+        assert lib.moe_layer_forward(h, FAKE, 64, FAKE, FAKE + 64, need, None, None) == _lib.MOE_ERR_WORKSPACE
+    finally:
+        _lib.moe_layer_destroy(h)
+    assert _lib.load().moe_layer_destroy(None) == _lib.MOE_OK
+
+
+def test_quantize_and_gemm_argument_errors():
+    lib = _lib.load()
+    assert lib.moe_mx_quantize(FAKE, 4, 48, 0, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_quantize(FAKE, 4, 64, 2, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_quantize(None, 4, 64, 0, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_quantize(FAKE, 0, 64, 0, FAKE, FAKE, None) == _lib.MOE_OK
+    assert lib.moe_mx_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 96, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, FAKE, None) == _lib.MOE_OK
+    assert lib.moe_mx_gemm(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert _lib.moe_status_string(-3).startswith("workspace")

@@ -1,0 +1,93 @@
+"""Layer-level GPU parity against the oracle (gfx950 only)."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe, weights
+from tests import parity
+from tests.gpu_harness import gpu_layer, gpu_weights, run_traced, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_weight_codes(cfg, gw, W):
+    from oracle import mx
+    for name in ("w_down", "w_up"):
+        c, s = gw[name]
+        ref = getattr(W, name)
+        assert np.array_equal(s.cpu().numpy(), ref.scales), name
+        assert np.array_equal(c.cpu().numpy(), mx.pack_e2m1(ref.codes)), name
+    for name in ("w_gate_e", "w_up_e", "w_down_e", "w_gate_s", "w_up_s", "w_down_s"):
+        lst = getattr(W, name)
+        if not lst:
+            continue
+        c, s = gw[name]
+        c, s = c.cpu().numpy(), s.cpu().numpy()
+        for i, ref in enumerate(lst):
+            assert np.array_equal(s[i], ref.scales), (name, i)
+            assert np.array_equal(c[i], mx.pack_e2m1(ref.codes)), (name, i)
+
+
+def _layer_case(cfg, x=None, selection_bias=None, check_codes=True):
+    say(f"layer parity {cfg.name} T={cfg.T} d={cfg.d_model} L={cfg.d_latent} E={cfg.n_routed} k={cfg.top_k}")
+    W = weights.layer(cfg, selection_bias=selection_bias)
+    lay, gw = gpu_layer(cfg, selection_bias=selection_bias)
+    if check_codes:
+        _check_weight_codes(cfg, gw, W)
+    if x is None:
+        x = synth.gen_hidden(cfg)
+    y, tr = run_traced(lay, x)
+    o = moe.forward(x, W, cfg.top_k)
+    rep = parity.check_layer(cfg, W, o, y, tr, say=say)
+    lay.close()
+    return rep, y, tr, o
+
+
+def test_tiny_layer_parity():
+    _layer_case(synth.config("tiny"))
+
+
+def test_tiny_ragged_tokens():
+    for T in (1, 5, 63, 65, 130):
+        _layer_case(synth.config("tiny", T=T), check_codes=(T == 1))
+
+
+def test_tiny_selection_bias_and_top1():
+    cfg = synth.config("tiny", T=48)
+    _layer_case(cfg, selection_bias=synth.gen_selection_bias(cfg, 0.05), check_codes=False)
+    import dataclasses
+    _layer_case(dataclasses.replace(cfg, top_k=1), check_codes=False)
+
+
+def test_zero_input_gives_zero_output():
+    cfg = synth.config("tiny", T=16)
+    lay, _ = gpu_layer(cfg)
+    y, tr = run_traced(lay, np.zeros((16, cfg.d_model), np.float32))
+    assert np.all(y == 0)
+    assert np.all(tr["ids"] == np.arange(cfg.top_k)[None, :])
+    lay.close()
+
+
+def test_determinism_two_forwards_bitwise_equal():
+    cfg = synth.config("tiny")
+    lay, _ = gpu_layer(cfg)
+    x = synth.gen_hidden(cfg)
+    y1, t1 = run_traced(lay, x)
+    y2, t2 = run_traced(lay, x)
+    assert np.array_equal(y1, y2)
+    for k in ("ids", "pair_of_row", "zq_codes", "hq_codes", "yq_codes"):
+        assert np.array_equal(t1[k], t2[k]), k
+    lay.close()
+
+
+def test_mid_layer_parity():
+    _layer_case(synth.config("mid"))
