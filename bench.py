@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""LatentMoE layer forward at Kimi-K3 width on one MI355X.
+
+One step = one full forward of the layer (MXFP8 quantise, latent
+down-projection, sigmoid router + top-16 of 896, dispatch, grouped
+MXFP4 x MXFP8 expert GEMMs with SwiGLU, combine, up-projection and the two
+shared experts) over one batch of synthetic tokens already resident in HBM.
+
+Default workload: the 16384-token prefill batch (matrix-core bound); the
+64-token decode batch (HBM bound) is measured in the same run and reported
+under "decode".  Per-stage times come from HIP events recorded by the library
+on the forward's stream inside the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_MX_TFLOPS = 5000.0        # dense MFMA at the FP8 rate (an FP8 activation operand), TFLOP/s
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+class StageEvents:
+    """MOE_TRACE_EVENTS HIP events per step, for K steps."""
+
+    def __init__(self, hip, n_steps, n_ev):
+        self.hip = hip
+        self.arrays = []
+        for _ in range(n_steps):
+            arr = (ctypes.c_void_p * n_ev)()
+            for i in range(n_ev):
+                e = ctypes.c_void_p()
+                assert hip.hipEventCreate(ctypes.byref(e)) == 0
+                arr[i] = e.value
+            self.arrays.append(arr)
+
+    def elapsed(self, step, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arrays[step][a], self.arrays[step][b]) == 0
+        return ms.value
+
+    def close(self):
+        for arr in self.arrays:
+            for e in arr:
+                self.hip.hipEventDestroy(e)
+
+
+def algorithmic_work(cfg, counts):
+    """Flops and bytes one forward must do (codes + scales; no padding, no re-reads)."""
+    T, d, L, E, k, S, F, Fs = (cfg.T, cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k, cfg.n_shared,
+                               cfg.d_ff_routed, cfg.d_ff_shared)
+    P = T * k
+    mxb = lambda n: n * 17 // 32          # E2M1 codes + E8M0 scales
+    f8b = lambda n: n * 33 // 32          # E4M3 codes + E8M0 scales
+    touched = int((counts > 0).sum())
+    w_up_e = 2 * F * L                    # gate + up elements per expert
+    w_dn_e = L * F
+    work = {
+        "touched_experts": touched,
+        # dominant kernel: routed gate/up GEMM + SwiGLU + MXFP8(h)
+        "expert_up_flops": 2.0 * P * L * 2 * F,
+        "expert_up_bytes": touched * mxb(w_up_e) + P * f8b(L) + P * f8b(F),
+        "expert_down_flops": 2.0 * P * F * L,
+        "expert_down_bytes": touched * mxb(w_dn_e) + P * f8b(F) + P * L * 4,
+    }
+    mx_flops = (2.0 * T * d * L + work["expert_up_flops"] + work["expert_down_flops"] + 2.0 * T * L * d
+                + S * (2.0 * T * d * 2 * Fs + 2.0 * T * Fs * d))
+    weight_bytes = (mxb(2 * d * L) + touched * (mxb(w_up_e) + mxb(w_dn_e)) + S * mxb(3 * d * Fs) + E * L * 4)
+    work.update(mx_flops=mx_flops, router_flops=2.0 * T * L * E, weight_bytes=weight_bytes,
+                layer_bytes=weight_bytes + T * d * 8 + P * (f8b(L) + f8b(F) * 2 + 8 * L))
+    return work
+
+
+def run_workload(name, steps, warmup, weights, hip, say):
+    import numpy as np
+    import torch
+
+    import synth
+    from latent_routing_mxfp4_amd import _lib
+    from latent_routing_mxfp4_amd import layer as LY
+
+    cfg = synth.config(name)
+    shape = LY.LayerShape.of(cfg)
+    lay = LY.LatentMoE(shape, weights, cfg.T)
+    x = torch.from_numpy(synth.gen_hidden(cfg)).cuda()
+    y = torch.empty_like(x)
+    lay.workspace(cfg.T)
+    stream = torch.cuda.current_stream().cuda_stream
+    nev = _lib.MOE_TRACE_EVENTS
+    evs = StageEvents(hip, steps, nev)
+    traces = [_lib.MoeLayerTrace(*([None] * len(_lib.TRACE_FIELDS)), ctypes.cast(a, ctypes.c_void_p))
+              for a in evs.arrays]
+    ws = lay.workspace(cfg.T)
+
+    def step(tr=None):
+        _lib.moe_layer_forward(lay.handle, x.data_ptr(), cfg.T, y.data_ptr(), ws.data_ptr(), ws.numel(), stream,
+                               tr)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(traces[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+
+    stage_ms = {}
+    for si, sname in enumerate(_lib.STAGES):
+        stage_ms[sname] = statistics.mean(evs.elapsed(i, si, si + 1) for i in range(steps))
+    evs.close()
+
+    # routing statistics of this batch (outside the timed region)
+    tb = {"counts": torch.empty(cfg.n_routed, dtype=torch.int32, device="cuda")}
+    lay.forward(x, y, trace=tb)
+    torch.cuda.synchronize()
+    counts = tb["counts"].cpu().numpy()
+    work = algorithmic_work(cfg, counts)
+    lay.close()
+    say(f"{name}: {ms_per_step:.3f} ms/step; stages (ms): " +
+        ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
+    return cfg, ms_per_step, stage_ms, work, counts
+
+
+def cpu_baseline(name, n_tokens, say):
+    """The oracle, as it stands, on the first n_tokens of the workload."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import synth
+    from oracle import moe, weights
+
+    cfg = synth.config(name)
+    x = synth.gen_hidden(cfg, T=n_tokens)
+    W = weights.layer(cfg, experts="lazy")
+    cache = weights.ExpertCache(cfg, maxsize=n_tokens * cfg.top_k + 8)
+    # find the experts the sample needs and encode them beforehand (not timed:
+    # weight encoding is load-time work on the GPU side too)
+    z = moe.mm(moe.quant(x), W.w_down)
+    r = moe.route(z, W.w_router, cfg.top_k, W.logit_bias, W.selection_bias)
+    need = sorted(set(r.ids.reshape(-1).tolist()))
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        list(ex.map(cache, need))
+    t0 = time.perf_counter()
+    moe.forward(x, W, cfg.top_k, expert_weights=cache)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        pass
+    say(f"cpu oracle: {n_tokens} tokens of {name} in {dt:.2f} s ({cores} threads)")
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of the {name} batch through the fp64 oracle forward "
+                      f"({len(need)} routed experts, weights pre-encoded outside the timed call); "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="k3_prefill", choices=["k3_prefill", "k3_decode", "k3_skew"])
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU: the layer is measured on one MI355X "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}); multi-GPU expert parallelism is not "
+              f"part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    say = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
+
+    import torch
+
+    import synth
+    from latent_routing_mxfp4_amd import layer as LY
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = _hip()
+    cfg = synth.config(args.workload)
+    t = time.perf_counter()
+    shape = LY.LayerShape.of(cfg)
+    workers = min(16, len(os.sched_getaffinity(0)))
+    extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg)}
+    weights = LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra, workers=workers)
+    say(f"K3 weights encoded on the GPU in {time.perf_counter() - t:.1f} s")
+
+    cfg, ms, stages, work, counts = run_workload(args.workload, args.steps, args.warmup, weights, hip, say)
+    value = cfg.T / (ms / 1e3)
+    dom_ms = stages["expert_up"]
+    roof = {"bound": "mfma", "achieved": work["expert_up_flops"] / (dom_ms / 1e3) / 1e12, "peak": PEAK_MX_TFLOPS,
+            "unit": "TFLOP/s", "kernel": "expert_up (routed gate/up grouped GEMM + SwiGLU + MXFP8)",
+            "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    out = {
+        "metric": "LatentMoE layer tokens/s (K3 width); HBM GB/s decode, MFMA % prefill vs peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4xmxfp8",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,1/sqrt(fan_in)) weights encoded to MXFP4)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T}, d={cfg.d_model}, latent={cfg.d_latent}, "
+                               f"E={cfg.n_routed} top-{cfg.top_k}, {cfg.n_shared} shared, "
+                               f"d_ff={cfg.d_ff_routed}", "tokens": cfg.T, "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"mx_tflops": work["mx_flops"] / (ms / 1e3) / 1e12,
+                  "mx_frac": work["mx_flops"] / (ms / 1e3) / 1e12 / PEAK_MX_TFLOPS,
+                  "stage_ms": stages, "touched_experts": work["touched_experts"],
+                  "max_expert_load": int(counts.max()), "empty_experts": int((counts == 0).sum())},
+    }
+
+    if not args.no_decode and args.workload != "k3_decode":
+        dcfg, dms, dst, dwork, dcounts = run_workload("k3_decode", args.decode_steps, args.warmup, weights, hip, say)
+        dom = dst["expert_up"]
+        droof = {"bound": "hbm", "achieved": dwork["expert_up_bytes"] / (dom / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "kernel": "expert_up", "traffic": None}
+        droof["frac"] = droof["achieved"] / droof["peak"]
+        out["decode"] = {"workload": f"{dcfg.name}: T={dcfg.T}", "value": dcfg.T / (dms / 1e3), "unit": "tokens/s",
+                         "ms_per_step": dms, "roofline": droof,
+                         "layer_gbs": dwork["layer_bytes"] / (dms / 1e3) / 1e9,
+                         "layer_hbm_frac": dwork["layer_bytes"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                         "stage_ms": dst, "touched_experts": dwork["touched_experts"]}
+    if args.workload == "k3_decode":
+        dom = stages["expert_up"]
+        out["roofline"] = {"bound": "hbm", "achieved": work["expert_up_bytes"] / (dom / 1e3) / 1e9,
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "kernel": "expert_up", "traffic": None}
+        out["roofline"]["frac"] = out["roofline"]["achieved"] / PEAK_HBM_GBS
+
+    del weights
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_tokens, say)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

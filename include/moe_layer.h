@@ -95,10 +95,30 @@ typedef struct {
   moe_mx_tensor w_down_s;          /* [S][d][Fs]  shared down projections       */
 } moe_layer_weights;
 
+/* Stage boundaries at which moe_layer_forward records the optional timing
+ * events of a trace (event i is recorded on the forward's stream right after
+ * stage i finishes launching; event 0 before the first launch). */
+enum {
+  MOE_EV_START = 0,
+  MOE_EV_QUANT_X = 1,    /* xq = MXFP8(x)                              */
+  MOE_EV_DOWN = 2,       /* z, zq: latent down-projection              */
+  MOE_EV_LOGITS = 3,     /* router logits                              */
+  MOE_EV_TOPK = 4,       /* top-k ids and gates                        */
+  MOE_EV_DISPATCH = 5,   /* counts, offsets, permutation               */
+  MOE_EV_EXPERT_UP = 6,  /* routed gate/up GEMM + SwiGLU + MXFP8       */
+  MOE_EV_EXPERT_DOWN = 7,/* routed down GEMM                           */
+  MOE_EV_COMBINE = 8,    /* gate-weighted combine + MXFP8              */
+  MOE_EV_SHARED_UP = 9,  /* shared gate/up GEMM + SwiGLU + MXFP8       */
+  MOE_EV_OUT = 10,       /* up-projection + shared down-projections    */
+  MOE_TRACE_EVENTS = 11
+};
+
 /* Optional device-side copies of the forward's intermediates, for testing.
  * Every member may be NULL; non-NULL members are filled by the forward (on
  * the same stream) with the sizes shown, for the T of that call.  Rows in
- * "sorted order" are the (token, slot) pairs stably sorted by expert. */
+ * "sorted order" are the (token, slot) pairs stably sorted by expert.
+ * `events`, if not NULL, is a HOST array of MOE_TRACE_EVENTS hipEvent_t
+ * handles (created by the caller) recorded at the stage boundaries above. */
 typedef struct {
   uint8_t* xq_codes;   uint8_t* xq_scales;   /* [T][d], [T][d/32]            */
   float* z;                                  /* [T][L] fp32 latent           */
@@ -116,6 +136,7 @@ typedef struct {
   uint8_t* yq_codes;   uint8_t* yq_scales;   /* [T][L], [T][L/32]            */
   float* hs;                                 /* [S][T][Fs] shared hidden, fp32 */
   uint8_t* hs_codes;   uint8_t* hs_scales;   /* [S][T][Fs], [S][T][Fs/32]    */
+  void* const* events;                       /* host array of hipEvent_t, or NULL */
 } moe_layer_trace;
 
 typedef struct moe_layer* moe_layer_t;

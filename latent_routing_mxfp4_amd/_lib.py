@@ -69,8 +69,13 @@ TRACE_FIELDS = (
 )
 
 
+MOE_TRACE_EVENTS = 11
+STAGES = ("quant_x", "down", "logits", "topk", "dispatch", "expert_up", "expert_down", "combine", "shared_up",
+          "out")
+
+
 class MoeLayerTrace(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in TRACE_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in TRACE_FIELDS] + [("events", ctypes.c_void_p)]
 
 
 _lib = None

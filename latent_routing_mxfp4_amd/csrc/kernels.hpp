@@ -8,8 +8,12 @@ namespace moe {
 
 // ---- MX quantisation (mx_quant.hip) -----------------------------------------
 // fmt 0: E4M3 codes [rows][K]; fmt 1: E2M1 packed codes [rows][K/2].
+// deq_bf16 (E4M3 only, may be null): bf16 [rows][K] of the dequantised values.
 hipError_t launch_quantize(const float* in, int64_t rows, int K, int fmt, uint8_t* codes,
-                           uint8_t* scales, hipStream_t s);
+                           uint8_t* scales, hipStream_t s, uint16_t* deq_bf16 = nullptr);
+// E2M1 packed [rows][K/2] + scales [rows][K/32] -> exact bf16 [rows][K].
+hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
+                                   uint16_t* out, hipStream_t s);
 
 // ---- Router (router.hip) ----------------------------------------------------
 // logits[T][E] = z[T][L] w[E][L]^T (+ bias[E]) in fp32 on the fp32 matrix cores.
@@ -73,6 +77,10 @@ struct GemmArgs {
 
 // M-tile height of the small-M (decode) and large-M configurations.
 int gemm_mtile(bool small_m);
+
+// Dense bf16 GEMM (seg[0].a = bf16 [M][K], seg[0].b = bf16 [N][K]) with the
+// fp32 + MXFP8 epilogue (EPI_F32_QUANT).
+hipError_t launch_bf16_gemm_quant(const GemmArgs& args, bool small_m, hipStream_t s);
 
 // Launch the grouped/dense MX GEMM with an automatically chosen tile shape.
 hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, bool small_m, hipStream_t s);

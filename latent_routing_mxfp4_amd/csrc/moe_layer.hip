@@ -3,7 +3,8 @@
 //
 // Launch sequence (all asynchronous, no host synchronisation, no allocation):
 //   1. quantise x to MXFP8                                   mx_quant
-//   2. z = xq W_down^T (fp32) and zq = MXFP8(z)               mx_gemm (dense, F32_QUANT)
+//   2. z = xq W_down^T (fp32) and zq = MXFP8(z)               bf16 GEMM on exactly decoded MX
+//                                                             operands (dense, F32_QUANT)
 //   3. logits = z W_router^T + logit_bias                     router_logits (fp32 MFMA)
 //   4. ids, gates = top-k(sigmoid + selection bias)           topk
 //   5. counts, offsets, stable permutation, M-tile prefix     dispatch (count/scan/scatter)
@@ -37,7 +38,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t xq, xqs, z, zq, zqs, logits, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye, ylat,
+  size_t xq, xqs, xdq, wdn16, z, zq, zqs, logits, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye, ylat,
       yq, yqs, hs, hss, total;
 };
 
@@ -54,6 +55,8 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   };
   p.xq = take(T * d);
   p.xqs = take(T * d / 32);
+  p.xdq = take(T * d * 2);
+  p.wdn16 = take(L * d * 2);
   p.z = take(T * L * 4);
   p.zq = take(T * L);
   p.zqs = take(T * L / 32);
@@ -180,6 +183,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
 
   uint8_t* xq = at<uint8_t>(ws, pl.xq);
   uint8_t* xqs = at<uint8_t>(ws, pl.xqs);
+  uint16_t* xdq = at<uint16_t>(ws, pl.xdq);
+  uint16_t* wdn16 = at<uint16_t>(ws, pl.wdn16);
   float* z = at<float>(ws, pl.z);
   uint8_t* zq = at<uint8_t>(ws, pl.zq);
   uint8_t* zqs = at<uint8_t>(ws, pl.zqs);
@@ -206,14 +211,22 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   const bool small_routed = P <= (int64_t)32 * E;
   const int mt_small = moe::gemm_mtile(true), mt_big = moe::gemm_mtile(false);
 
-  // 1. xq
-  MOE_HIP(moe::launch_quantize(x, T, d, 0, xq, xqs, s));
+  hipEvent_t const* ev = tr && tr->events ? reinterpret_cast<hipEvent_t const*>(tr->events) : nullptr;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  MOE_HIP(mark(MOE_EV_START));
 
-  // 2. z, zq
+  // 1. xq (and its exact bf16 image for the latent down-projection)
+  MOE_HIP(moe::launch_quantize(x, T, d, 0, xq, xqs, s, xdq));
+  MOE_HIP(mark(MOE_EV_QUANT_X));
+
+  // 2. z, zq: bf16 matrix cores on the exactly decoded MX operands, so that the
+  //    latent the router ranks is accurate to fp32 accumulation.
   {
+    MOE_HIP(moe::launch_decode_e2m1_bf16(w.w_down.codes, w.w_down.scales, L, d, wdn16, s));
     moe::GemmArgs a = {};
     a.nseg = 1;
-    a.seg[0] = {xq, xqs, d, w.w_down.codes, w.w_down.scales, nullptr, nullptr, 0, 0, d};
+    a.seg[0] = {reinterpret_cast<const uint8_t*>(xdq), nullptr, d, reinterpret_cast<const uint8_t*>(wdn16),
+                nullptr, nullptr, nullptr, 0, 0, d};
     a.G = 1;
     a.M = T;
     a.N = L;
@@ -222,15 +235,19 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.q = zq;
     a.qs = zqs;
     a.max_mtiles = (T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense);
-    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32_QUANT, small_dense, s));
+    MOE_HIP(moe::launch_bf16_gemm_quant(a, small_dense, s));
   }
+  MOE_HIP(mark(MOE_EV_DOWN));
 
   // 3-4. router
   MOE_HIP(moe::launch_router_logits(z, w.w_router, w.router_logit_bias, T, E, L, logits, s));
+  MOE_HIP(mark(MOE_EV_LOGITS));
   MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, ids, gates, s));
+  MOE_HIP(mark(MOE_EV_TOPK));
 
   // 5. dispatch
   MOE_HIP(moe::launch_dispatch(ids, T, E, k, dscr, counts, offsets, rop, por, mt_small, ms0, mt_big, ms1, s));
+  MOE_HIP(mark(MOE_EV_DISPATCH));
 
   const int mt_r = small_routed ? mt_small : mt_big;
   const int32_t* ms_r = small_routed ? ms0 : ms1;
@@ -263,6 +280,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.max_mtiles = (int)max_mt_r;
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, small_routed, s));
   }
+  MOE_HIP(mark(MOE_EV_EXPERT_UP));
 
   // 7. routed GEMM2
   {
@@ -279,9 +297,11 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.max_mtiles = (int)max_mt_r;
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, small_routed, s));
   }
+  MOE_HIP(mark(MOE_EV_EXPERT_DOWN));
 
   // 8. combine
   MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, ylat, yq, yqs, s));
+  MOE_HIP(mark(MOE_EV_COMBINE));
 
   // 9. shared experts, first half
   if (S > 0) {
@@ -310,6 +330,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.max_mtiles = S * ((T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense));
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, small_dense, s));
   }
+  MOE_HIP(mark(MOE_EV_SHARED_UP));
 
   // 10. y = up-projection + shared down-projections (one K-concatenated GEMM)
   {
@@ -335,6 +356,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.max_mtiles = (T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense);
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, small_dense, s));
   }
+  MOE_HIP(mark(MOE_EV_OUT));
 
   // Optional trace copies.
   if (tr) {

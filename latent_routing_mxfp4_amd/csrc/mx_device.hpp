@@ -94,11 +94,15 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
 // ---------------------------------------------------------------------------
 // Block-scaled MFMA, 16x16x128, A = E4M3, B = E2M1, fp32 accumulate.
 //
-// Operand layout (64 lanes, lane l, r = l % 16, g = l / 16):
-//   A: row r, K elements [32g, 32g+32)  -> 32 bytes (8 dwords)
-//   B: col r, K elements [32g, 32g+32)  -> 16 bytes (4 dwords, low 4 of 8)
-//   scale_a / scale_b: bits [7:0] = E8M0 of that lane's 32-element block
-//   D: col r, rows 4g .. 4g+3           -> 4 floats
+// Operand layout (64 lanes, lane l, r = l % 16, g = l / 16), established by a
+// one-tile probe against the exact product on gfx950:
+//   A (E4M3, 8 dwords): row r; bytes 0-15 = K [16g, 16g+16),
+//                       bytes 16-31 = K [64+16g, 64+16g+16)
+//   B (E2M1, low 4 of 8 dwords): col r; 32 elements K [32g, 32g+32),
+//                       element 2i in the low nibble of byte i
+//   scale_a / scale_b: bits [7:0] = E8M0 of 32-element block g of row/col r
+//                       (the scale lane need not hold that block's data)
+//   D: col r, rows 4g .. 4g+3 -> 4 floats
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 

@@ -18,7 +18,8 @@
 // the waves split the N columns, each wave computes MT x (16*NW) with
 // MW x NW 16x16 MFMA tiles (two accumulators per tile for SwiGLU: gate and
 // up).  Operands go straight from global memory into the MFMA register
-// layout, one 16-byte load per lane per E2M1 fragment, two per E4M3 fragment,
+// layout, one 16-byte load per lane per E2M1 fragment, two per E4M3 fragment
+// (the two K halves the E4M3 operand layout interleaves),
 // one dword of 4 block scales per row per K-step.  The K loop is software
 // pipelined one K-step deep.
 //
@@ -54,7 +55,110 @@ __device__ __forceinline__ v8i as_v8i(const uint4& f) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& f) {
+  union {
+    uint4 u;
+    bf16x8 b;
+  } c;
+  c.u = f;
+  return c.b;
+}
+
 }  // namespace
+
+struct Tile {
+  int g, m0, rows, row_base, n0;
+};
+
+// Map a workgroup to (group, M-tile, N-tile).  Returns false for workgroups
+// past the last M-tile (the grid is sized for the worst case).
+template <int MT, int NT>
+__device__ __forceinline__ bool decode_tile(const GemmArgs& p, int wave, int NWC, Tile& t) {
+  const int n_ntiles = (p.N + NT - 1) / NT;
+  const int gm = blockIdx.x / n_ntiles;
+  const int nt = blockIdx.x - gm * n_ntiles;
+  if (p.offsets) {
+    const int total = p.mtile_start[p.G];
+    if (gm >= total) return false;
+    int lo = 0, hi = p.G;  // mtile_start[lo] <= gm < mtile_start[hi]
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (p.mtile_start[mid] <= gm) lo = mid; else hi = mid;
+    }
+    t.g = lo;
+    t.row_base = p.offsets[lo];
+    t.rows = p.offsets[lo + 1] - t.row_base;
+    t.m0 = (gm - p.mtile_start[lo]) * MT;
+  } else {
+    const int mpg = (p.M + MT - 1) / MT;
+    t.g = gm / mpg;
+    if (t.g >= p.G) return false;
+    t.m0 = (gm - t.g * mpg) * MT;
+    t.rows = p.M;
+    t.row_base = 0;
+  }
+  t.n0 = nt * NT + wave * NWC;
+  return true;
+}
+
+// Write one wave's MW x NW accumulator tiles (16x16 each; NB accumulators per
+// tile for SwiGLU) in the epilogue's form.  Lane (r16, g4) holds column
+// n0 + 16*ni + r16 of rows m0 + 16*mi + 4*g4 + i.
+template <int MW, int NW, int NB, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const v4f (&acc)[MW][NW][NB], int r16,
+                                         int g4) {
+  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
+  const bool dense = p.offsets == nullptr;
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = t.m0 + 16 * mi + 4 * g4 + i;
+      const bool rok = row < t.rows;
+      const int64_t orow = dense ? row : (int64_t)t.row_base + row;
+      if (EPI == EPI_F32 || EPI == EPI_F32_QUANT) {
+        float* crow = p.c + (dense ? (int64_t)t.g * p.c_gstride : 0) + orow * p.ldc;
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni) {
+          const int col = t.n0 + 16 * ni + r16;
+          if (rok && col < p.N) crow[col] = acc[mi][ni][0][i];
+        }
+      }
+      if (EPI == EPI_F32_QUANT || EPI == EPI_SWIGLU_QUANT) {
+        uint8_t* qrow = p.q + (dense ? (int64_t)t.g * p.q_gstride : 0) + orow * p.N;
+        uint8_t* qsrow = p.qs + (dense ? (int64_t)t.g * p.qs_gstride : 0) + orow * (p.N >> 5);
+#pragma unroll
+        for (int b = 0; b < NW / 2; ++b) {
+          float v0, v1;
+          if (SWI) {
+            v0 = silu(acc[mi][2 * b][0][i]) * acc[mi][2 * b][NB - 1][i];
+            v1 = silu(acc[mi][2 * b + 1][0][i]) * acc[mi][2 * b + 1][NB - 1][i];
+            if (p.c != nullptr && rok && t.n0 + 32 * b < p.N) {  // optional fp32 copy of h (tracing)
+              float* crow = p.c + (dense ? (int64_t)t.g * p.c_gstride : 0) + orow * p.ldc;
+              crow[t.n0 + 32 * b + r16] = v0;
+              crow[t.n0 + 32 * b + 16 + r16] = v1;
+            }
+          } else {
+            v0 = acc[mi][2 * b][0][i];
+            v1 = acc[mi][2 * b + 1][0][i];
+          }
+          uint32_t m = max(__float_as_uint(v0) & 0x7fffffffu, __float_as_uint(v1) & 0x7fffffffu);
+          m = group_max_u32<16>(m);
+          const int sc = mx_scale_code<8>(m);
+          const int e = sc - 127;
+          const int cb = t.n0 + 32 * b;
+          if (rok && cb < p.N) {
+            qrow[cb + r16] = (uint8_t)enc_e4m3(v0, e);
+            qrow[cb + 16 + r16] = (uint8_t)enc_e4m3(v1, e);
+            if (r16 == 0) qsrow[cb >> 5] = (uint8_t)sc;
+          }
+        }
+      }
+    }
+  }
+}
 
 template <int MW, int NW, int EPI>
 __global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
@@ -68,48 +172,23 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
-
-  const int n_ntiles = (p.N + NT - 1) / NT;
-  const int gm = blockIdx.x / n_ntiles;
-  const int nt = blockIdx.x - gm * n_ntiles;
-
-  int g, m0, rows, row_base;
-  if (p.offsets) {
-    const int total = p.mtile_start[p.G];
-    if (gm >= total) return;
-    int lo = 0, hi = p.G;  // mtile_start[lo] <= gm < mtile_start[hi]
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if (p.mtile_start[mid] <= gm) lo = mid; else hi = mid;
-    }
-    g = lo;
-    row_base = p.offsets[g];
-    rows = p.offsets[g + 1] - row_base;
-    m0 = (gm - p.mtile_start[g]) * MT;
-  } else {
-    const int mpg = (p.M + MT - 1) / MT;
-    g = gm / mpg;
-    if (g >= p.G) return;
-    m0 = (gm - g * mpg) * MT;
-    rows = p.M;
-    row_base = 0;
-  }
-  const int n0 = nt * NT + wave * 16 * NW;
+  Tile t;
+  if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;
 
   // Rows of A this lane feeds (clamped into the group; results of clamped rows are dropped).
   int64_t arow[MW];
 #pragma unroll
   for (int mi = 0; mi < MW; ++mi) {
-    int r = m0 + 16 * mi + r16;
-    r = r < rows ? r : rows - 1;
-    int sr = row_base + r;
+    int r = t.m0 + 16 * mi + r16;
+    r = r < t.rows ? r : t.rows - 1;
+    int sr = t.row_base + r;
     if (p.offsets) arow[mi] = p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr;
     else arow[mi] = r;
   }
   int bcol[NW];
 #pragma unroll
   for (int ni = 0; ni < NW; ++ni) {
-    int c = n0 + 16 * ni + r16;
+    int c = t.n0 + 16 * ni + r16;
     bcol[ni] = c < p.N ? c : p.N - 1;
   }
 
@@ -130,7 +209,7 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
     const uint32_t* asp[MW];
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi) {
-      ap[mi] = sg.a + arow[mi] * sg.lda + 32 * g4;
+      ap[mi] = sg.a + arow[mi] * sg.lda + 16 * g4;
       asp[mi] = reinterpret_cast<const uint32_t*>(sg.as + arow[mi] * lds);
     }
     const uint8_t* bp[NW][NB];
@@ -141,8 +220,9 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
       for (int h = 0; h < NB; ++h) {
         const uint8_t* bb = h == 0 ? sg.b : sg.b2;
         const uint8_t* bbs = h == 0 ? sg.bs : sg.b2s;
-        bp[ni][h] = bb + (int64_t)g * sg.b_gstride + (int64_t)bcol[ni] * (K >> 1) + 16 * g4;
-        bsp[ni][h] = reinterpret_cast<const uint32_t*>(bbs + (int64_t)g * sg.bs_gstride + (int64_t)bcol[ni] * (K >> 5));
+        bp[ni][h] = bb + (int64_t)t.g * sg.b_gstride + (int64_t)bcol[ni] * (K >> 1) + 16 * g4;
+        bsp[ni][h] =
+            reinterpret_cast<const uint32_t*>(bbs + (int64_t)t.g * sg.bs_gstride + (int64_t)bcol[ni] * (K >> 5));
       }
     }
 
@@ -153,9 +233,9 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
     auto load = [&](int ks) {
 #pragma unroll
       for (int mi = 0; mi < MW; ++mi) {
-        const uint4* q = reinterpret_cast<const uint4*>(ap[mi] + 128 * ks);
-        fa[mi].lo = q[0];
-        fa[mi].hi = q[1];
+        const uint8_t* q = ap[mi] + 128 * ks;  // K [16g, +16) and [64+16g, +16) of this K-step
+        fa[mi].lo = *reinterpret_cast<const uint4*>(q);
+        fa[mi].hi = *reinterpret_cast<const uint4*>(q + 64);
         sa[mi] = asp[mi][ks] >> (8 * g4);
       }
 #pragma unroll
@@ -191,56 +271,86 @@ __global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
       }
     }
   }
+  epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
+}
 
-  // ---------------------------------------------------------------- epilogue
-  const bool dense = p.offsets == nullptr;
+// Dense bf16 GEMM on exactly decoded MX operands (v_mfma_f32_16x16x32_bf16):
+// A = bf16 [M][K], B = bf16 [N][K] (seg.a / seg.b, lda = K).  Every product of
+// an E4M3 and an E2M1 value (with power-of-two scales) is exact in bf16 x bf16
+// -> fp32, and this instruction accumulates at fp32 precision, unlike the
+// block-scaled MFMA, which sums each 32-element block in a window of about 14
+// bits below the block's largest product.  The latent down-projection feeds
+// the router, whose top-k must be decided on an fp32-accurate latent, so it
+// runs here.  A lane loads 64 contiguous bytes (32 K values) of its row per
+// 128-wide K-step and issues four MFMAs, slice u taking K [32g + 8u, +8); A and
+// B use the same slicing, so the pairing of K indices is consistent.
+template <int MW, int NW, int EPI>
+__global__ void __launch_bounds__(256) bf16_gemm_kernel(const GemmArgs p) {
+  constexpr int MT = 16 * MW;
+  constexpr int NT = 4 * 16 * NW;
+  static_assert(EPI == EPI_F32 || NW % 2 == 0, "quantising epilogues need whole 32-column blocks per wave");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  Tile t;
+  if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;
+  const GemmSeg& sg = p.seg[0];
+  const int K = sg.K;
+  const int ksteps = K >> 7;
+  const uint16_t* ap[MW];
 #pragma unroll
   for (int mi = 0; mi < MW; ++mi) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * mi + 4 * g4 + i;
-      const bool rok = row < rows;
-      const int64_t orow = dense ? row : (int64_t)row_base + row;
-      if (EPI == EPI_F32 || EPI == EPI_F32_QUANT) {
-        float* crow = p.c + (dense ? (int64_t)g * p.c_gstride : 0) + orow * p.ldc;
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni) {
-          const int col = n0 + 16 * ni + r16;
-          if (rok && col < p.N) crow[col] = acc[mi][ni][0][i];
-        }
-      }
-      if (EPI == EPI_F32_QUANT || EPI == EPI_SWIGLU_QUANT) {
-        uint8_t* qrow = p.q + (dense ? (int64_t)g * p.q_gstride : 0) + orow * p.N;
-        uint8_t* qsrow = p.qs + (dense ? (int64_t)g * p.qs_gstride : 0) + orow * (p.N >> 5);
-#pragma unroll
-        for (int b = 0; b < NW / 2; ++b) {
-          float v0, v1;
-          if (SWI) {
-            v0 = silu(acc[mi][2 * b][0][i]) * acc[mi][2 * b][1][i];
-            v1 = silu(acc[mi][2 * b + 1][0][i]) * acc[mi][2 * b + 1][1][i];
-            if (p.c != nullptr && rok && n0 + 32 * b < p.N) {  // optional fp32 copy of h (tracing)
-              float* crow = p.c + (dense ? (int64_t)g * p.c_gstride : 0) + orow * p.ldc;
-              crow[n0 + 32 * b + r16] = v0;
-              crow[n0 + 32 * b + 16 + r16] = v1;
-            }
-          } else {
-            v0 = acc[mi][2 * b][0][i];
-            v1 = acc[mi][2 * b + 1][0][i];
-          }
-          uint32_t m = max(__float_as_uint(v0) & 0x7fffffffu, __float_as_uint(v1) & 0x7fffffffu);
-          m = group_max_u32<16>(m);
-          const int sc = mx_scale_code<8>(m);
-          const int e = sc - 127;
-          const int cb = n0 + 32 * b;
-          if (rok && cb < p.N) {
-            qrow[cb + r16] = (uint8_t)enc_e4m3(v0, e);
-            qrow[cb + 16 + r16] = (uint8_t)enc_e4m3(v1, e);
-            if (r16 == 0) qsrow[cb >> 5] = (uint8_t)sc;
-          }
-        }
-      }
-    }
+    int r = t.m0 + 16 * mi + r16;
+    r = r < t.rows ? r : t.rows - 1;
+    ap[mi] = reinterpret_cast<const uint16_t*>(sg.a) + (int64_t)r * K + 32 * g4;
   }
+  const uint16_t* bp[NW];
+#pragma unroll
+  for (int ni = 0; ni < NW; ++ni) {
+    int c = t.n0 + 16 * ni + r16;
+    c = c < p.N ? c : p.N - 1;
+    bp[ni] = reinterpret_cast<const uint16_t*>(sg.b) + (int64_t)c * K + 32 * g4;
+  }
+  v4f acc[MW][NW][1];
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni) acc[mi][ni][0] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  uint4 fa[MW][4], fb[NW][4];
+  auto load = [&](int ks) {
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fa[mi][u] = reinterpret_cast<const uint4*>(ap[mi] + 128 * ks)[u];
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fb[ni][u] = reinterpret_cast<const uint4*>(bp[ni] + 128 * ks)[u];
+  };
+  load(0);
+  for (int ks = 0; ks < ksteps; ++ks) {
+    uint4 ca[MW][4], cb[NW][4];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ca[mi][u] = fa[mi][u];
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) cb[ni][u] = fb[ni][u];
+    if (ks + 1 < ksteps) load(ks + 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[mi][u]), as_bf16x8(cb[ni][u]),
+                                                                   acc[mi][ni][0], 0, 0, 0);
+  }
+  epilogue<MW, NW, 1, EPI>(p, t, acc, r16, g4);
 }
 
 template <int MW, int NW, int EPI>
@@ -255,6 +365,21 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 }
 
 int gemm_mtile(bool small_m) { return small_m ? 16 : 64; }
+
+template <int MW, int NW, int EPI>
+static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
+  constexpr int NT = 4 * 16 * NW;
+  const int n_ntiles = (a.N + NT - 1) / NT;
+  const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  bf16_gemm_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_gemm_quant(const GemmArgs& a, bool small_m, hipStream_t s) {
+  return small_m ? launch_bf16_cfg<1, 2, EPI_F32_QUANT>(a, s) : launch_bf16_cfg<4, 2, EPI_F32_QUANT>(a, s);
+}
 
 hipError_t launch_mx_gemm(const GemmArgs& a, int epi, bool small_m, hipStream_t s) {
   if (small_m) {

@@ -8,15 +8,33 @@
 // neighbouring lanes hold one 32-element block and agree on its maximum with
 // three xor shuffles.  Reads and writes are fully coalesced; the kernel is
 // HBM-bound (4 B read, 1.03 B (E4M3) or 0.53 B (E2M1) written per element).
+// For E4M3 it can also write the exact dequantised values as bf16 (the
+// operand of the bf16 latent down-projection).
 #include "kernels.hpp"
 #include "mx_device.hpp"
 
 namespace moe {
 
+// Exact value of an E4M3 / E2M1 code under block exponent e, as fp32
+// (exact whenever the result is a normal fp32 number).
+__device__ __forceinline__ float dec_e4m3(uint32_t c, int e) {
+  const int E = (c >> 3) & 15, m = c & 7;
+  const float v = ldexpf((float)(E ? 8 + m : m), (E ? E - 10 : -9) + e);
+  return (c & 0x80) ? -v : v;
+}
+__device__ __forceinline__ float dec_e2m1(uint32_t c, int e) {
+  const int E = (c >> 1) & 3, m = c & 1;
+  const float v = ldexpf((float)(E ? 2 + m : m), (E ? E - 2 : -1) + e);
+  return (c & 0x8) ? -v : v;
+}
+// bf16 bit pattern of a float with at most 8 significant bits (exact).
+__device__ __forceinline__ uint32_t bf16_bits(float v) { return __float_as_uint(v) >> 16; }
+
 template <int FMT>
 __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict__ in, int64_t n4,
                                                        uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales,
+                                                       uint2* __restrict__ deq) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     // n4 is a multiple of 8 and i starts 8-aligned per group of 8 lanes, so
@@ -32,6 +50,12 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
                    (enc_e4m3(v.w, e) << 24);
       reinterpret_cast<uint32_t*>(codes)[i] = w;
       if ((i & 7) == 0) scales[i >> 3] = (uint8_t)sc;
+      if (deq) {  // bf16 copy of the dequantised values (exact), for the bf16 matrix cores
+        uint2 o;
+        o.x = bf16_bits(dec_e4m3(w & 0xff, e)) | (bf16_bits(dec_e4m3((w >> 8) & 0xff, e)) << 16);
+        o.y = bf16_bits(dec_e4m3((w >> 16) & 0xff, e)) | (bf16_bits(dec_e4m3(w >> 24, e)) << 16);
+        deq[i] = o;
+      }
     } else {
       int sc = mx_scale_code<2>(m);
       int e = sc - 127;
@@ -43,18 +67,53 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
   }
 }
 
+// E2M1 (packed) + E8M0 -> bf16, one thread per 32-element block.
+__global__ void __launch_bounds__(256) decode_e2m1_bf16_kernel(const uint4* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales, int64_t nblk,
+                                                              uint4* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+    const uint4 c = codes[b];
+    const int e = (int)scales[b] - 127;
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // 8 elements per dword
+      uint4 o;
+      uint32_t* op = &o.x;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t lo = (w[q] >> (8 * h)) & 0xf, hi = (w[q] >> (8 * h + 4)) & 0xf;
+        op[h] = bf16_bits(dec_e2m1(lo, e)) | (bf16_bits(dec_e2m1(hi, e)) << 16);
+      }
+      out[4 * b + q] = o;
+    }
+  }
+}
+
+hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K, uint16_t* out,
+                                   hipStream_t s) {
+  const int64_t nblk = rows * (int64_t)K / 32;
+  if (nblk == 0) return hipSuccess;
+  int64_t blocks = (nblk + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  decode_e2m1_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(reinterpret_cast<const uint4*>(codes), scales,
+                                                                        nblk, reinterpret_cast<uint4*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const float* in, int64_t rows, int K, int fmt, uint8_t* codes, uint8_t* scales,
-                           hipStream_t s) {
+                           hipStream_t s, uint16_t* deq_bf16) {
   int64_t n4 = rows * (int64_t)K / 4;
   if (n4 == 0) return hipSuccess;
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   if (fmt == 0)
     quantize_kernel<0><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(reinterpret_cast<const float4*>(in), n4,
-                                                                     codes, scales);
+                                                                     codes, scales,
+                                                                     reinterpret_cast<uint2*>(deq_bf16));
   else
     quantize_kernel<1><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(reinterpret_cast<const float4*>(in), n4,
-                                                                     codes, scales);
+                                                                     codes, scales, nullptr);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import moe, mx
+from tests import parity
 from tests.gpu_harness import say
 
 pytestmark = pytest.mark.gpu
@@ -69,7 +70,7 @@ def _gemm_case(LY, rng, M, N, K):
     torch.cuda.synchronize()
     got = c.cpu().numpy().astype(np.float64)
     ref = moe.mm(a, b)
-    bound = K * 2.0 ** -24 * (np.abs(a.deq()) @ np.abs(b.deq()).T) + 2.0 ** -24 * np.abs(ref)
+    bound = parity.mx_mfma_bound(a, b, ref)
     return got, ref, bound, a, b
 
 
