@@ -211,7 +211,9 @@ def main():
     shape = LY.LayerShape.of(cfg)
     workers = min(16, len(os.sched_getaffinity(0)))
     extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg)}
-    weights = LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra, workers=workers)
+    weights = LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra, workers=workers,
+                                progress=lambda j, n: say(f"  encoded {j}/{n} weight matrices "
+                                                          f"({time.perf_counter() - t:.0f} s)"))
     say(f"K3 weights encoded on the GPU in {time.perf_counter() - t:.1f} s")
 
     cfg, ms, stages, work, counts = run_workload(args.workload, args.steps, args.warmup, weights, hip, say)

@@ -87,7 +87,8 @@ def mx_gemm(a_codes, a_scales, b_codes, b_scales) -> torch.Tensor:
 
 
 def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray], device="cuda",
-                   extra: Optional[Dict[str, Optional[np.ndarray]]] = None, workers: int = 8) -> Dict:
+                   extra: Optional[Dict[str, Optional[np.ndarray]]] = None, workers: int = 8,
+                   progress: Optional[Callable[[int, int], None]] = None) -> Dict:
     """MXFP4-encode every weight matrix on the GPU.
 
     ``host_fp32(name, index)`` returns the fp32 ``[out][in]`` matrix (numpy);
@@ -118,6 +119,8 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
                 nxt += 1
             dev = torch.from_numpy(np.ascontiguousarray(host, dtype=np.float32)).to(device, non_blocking=False)
             mx_quantize(dev, FMT_E2M1, out=(codes, scales))
+            if progress is not None and (j + 1) % max(1, len(jobs) // 10) == 0:
+                progress(j + 1, len(jobs))
     extra = extra or {}
     for k in ("w_router", "router_logit_bias", "selection_bias"):
         v = extra.get(k)

@@ -163,15 +163,19 @@ def dispatch(ids: np.ndarray, n_experts: int) -> Dispatch:
 # --------------------------------------------------------------------------- experts
 
 
-def swiglu_expert(aq: MXTensor, wg: MXTensor, wu: MXTensor, wd: MXTensor, decide=np.float32, full=False):
+def swiglu_expert(aq: MXTensor, wg: MXTensor, wu: MXTensor, wd: MXTensor, decide=np.float32, full=False,
+                  pick=None):
     """down(SiLU(gate a) * (up a)) with MXFP8 re-quantisation of the hidden h.
 
-    Returns (y, h, hq), plus (g, u) when ``full``.
+    Returns (y, h, hq), plus (g, u) when ``full``.  ``pick(g, u, h, hq)`` may
+    replace the codes of hq (see ``forward``'s ``resolve``).
     """
     g = mm(aq, wg)
     u = mm(aq, wu)
     h = silu(g) * u
     hq = quant(h, "e4m3", decide)
+    if pick is not None:
+        hq = pick(g, u, h, hq)
     if full:
         return mm(hq, wd), h, hq, g, u
     return mm(hq, wd), h, hq
@@ -204,8 +208,17 @@ class Trace:
 
 
 def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
-            expert_weights=None, ids_override=None) -> Trace:
-    """The whole layer.  ``expert_weights(e)`` may supply (wg, wu, wd) lazily."""
+            expert_weights=None, ids_override=None, resolve=None) -> Trace:
+    """The whole layer.  ``expert_weights(e)`` may supply (wg, wu, wd) lazily.
+
+    ``resolve`` (tests only) is consulted at every MX re-quantisation of a
+    computed tensor -- ``zq(z, zq)``, ``hq(e, rows, a, wg, wu, wd, g, u, h, hq)``,
+    ``yq(y_lat, yq, routing, dispatch, ye_rows)``, ``hs(s, wg, wu, wd, g, u, h, hq)``
+    -- and returns the codes to continue with.  The arithmetic of every step
+    is unchanged; a test uses it to replay the layer along the admissible
+    choices another implementation made where a value sits within its proven
+    error of a rounding boundary.
+    """
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
     E = W.w_router.shape[0]
@@ -220,6 +233,8 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
         r = Routing(r.scores, r.sel, ids, win / win.sum(axis=1, keepdims=True), r.gap)
     disp = dispatch(r.ids, E)                                       # step 6
     zq = quant(z, "e4m3", decide)
+    if resolve is not None:
+        zq = resolve.zq(z, zq)
 
     P = T * top_k
     F = None
@@ -235,7 +250,12 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
         else:
             wg, wu, wd = W.w_gate_e[e], W.w_up_e[e], W.w_down_e[e]
         toks = disp.pair_of_row[lo:hi] // top_k
-        ye, h, hq, g, u = swiglu_expert(zq[toks], wg, wu, wd, decide, full=True)
+        a = zq[toks]
+        pick = None
+        if resolve is not None:
+            pick = (lambda g_, u_, h_, hq_, e=e, lo=lo, hi=hi, a=a, wg=wg, wu=wu, wd=wd:
+                    resolve.hq(e, (lo, hi), a, wg, wu, wd, g_, u_, h_, hq_))
+        ye, h, hq, g, u = swiglu_expert(a, wg, wu, wd, decide, full=True, pick=pick)
         if h_rows is None:
             F = h.shape[1]
             h_rows = np.zeros((P, F))
@@ -256,12 +276,19 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
             y_lat[t] += r.gates[t, j] * ye_rows[disp.row_of_pair[t * top_k + j]]
 
     yq = quant(y_lat, "e4m3", decide)                               # step 9
+    if resolve is not None:
+        yq = resolve.yq(y_lat, yq, r, disp, ye_rows)
     y_up = mm(yq, W.w_up)
 
     y = y_up.copy()                                                 # step 10
     hs_l, hsq_l, ys_l, gs_l, us_l = [], [], [], [], []
     for s in range(len(W.w_gate_s)):
-        ys, hs, hsq, gs, us = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide, full=True)
+        pick = None
+        if resolve is not None:
+            pick = (lambda g_, u_, h_, hq_, s=s: resolve.hs(s, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s],
+                                                              g_, u_, h_, hq_))
+        ys, hs, hsq, gs, us = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide, full=True,
+                                            pick=pick)
         y += ys
         hs_l.append(hs)
         gs_l.append(gs)

@@ -131,6 +131,22 @@ def round_to_grid(y: np.ndarray, fmt) -> np.ndarray:
     return np.where(pick_hi, hi, lo).astype(np.uint8)
 
 
+def encode_with_exponent(v: np.ndarray, e: np.ndarray, fmt) -> np.ndarray:
+    """Element codes of ``v`` (blocks of 32 along the last axis) under given
+    block exponents ``e`` (shape ``v.shape[:-1] + (K/32,)``): divide by 2^e,
+    clip to the largest magnitude, round to the nearest level (ties to even)."""
+    f = _fmt(fmt)
+    v64 = np.asarray(v).astype(np.float64)
+    nb = v64.shape[-1] // BLOCK
+    blocks = v64.reshape(v64.shape[:-1] + (nb, BLOCK))
+    scale = np.ldexp(1.0, np.asarray(e))                      # exact power of two
+    y = np.abs(blocks) / scale[..., None]                      # exact (power-of-two division)
+    y = np.minimum(y, f.max_value)                             # clip to the largest magnitude
+    mag = round_to_grid(y, f)
+    codes = np.where(np.signbit(blocks), mag | f.sign_bit, mag).astype(np.uint8)
+    return codes.reshape(v64.shape)
+
+
 def quantize(v: np.ndarray, fmt) -> tuple:
     """Quantise ``v`` (any float array, last axis a multiple of 32) to MX blocks.
 
@@ -143,16 +159,9 @@ def quantize(v: np.ndarray, fmt) -> tuple:
     v64 = v.astype(np.float64)
     assert np.all(np.isfinite(v64)), "MX quantisation of non-finite values is not defined here"
     nb = v.shape[-1] // BLOCK
-    blocks = v64.reshape(v.shape[:-1] + (nb, BLOCK))
-    amax = np.abs(blocks).max(axis=-1)
+    amax = np.abs(v64.reshape(v.shape[:-1] + (nb, BLOCK))).max(axis=-1)
     e = shared_exponent(amax, f.emax)                          # [..., nb]
-    scale = np.ldexp(1.0, e)                                   # exact power of two
-    y = np.abs(blocks) / scale[..., None]                      # exact (power-of-two division)
-    y = np.minimum(y, f.max_value)                             # clip to the largest magnitude
-    mag = round_to_grid(y, f)
-    neg = np.signbit(blocks)
-    codes = np.where(neg, mag | f.sign_bit, mag).astype(np.uint8)
-    return codes.reshape(v.shape), (e + 127).astype(np.uint8)
+    return encode_with_exponent(v64, e, f), (e + 127).astype(np.uint8)
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, fmt) -> np.ndarray:

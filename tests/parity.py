@@ -1,28 +1,41 @@
-"""Comparison of a GPU layer trace with the oracle's independent fp64 chain.
+"""Comparison of a GPU layer trace with the oracle (test infrastructure).
 
-Rules (all expected values come from the oracle run on the same seeded inputs):
+What is compared
+----------------
+1. MX codes of the inputs (x) and weights: bit-exact.
+2. The latent z (bf16 matrix cores on exactly decoded operands): within the
+   fp32 accumulation bound K * 2^-24 * ||a_row|| * ||b_row||.
+3. Expert ids: the same set per token unless the oracle's gap between the k-th
+   and (k+1)-th selection key is below 1e-6 (a flagged near-tie, where the GPU's
+   set must still be a valid top-k within 1e-6); gates within max(1e-6, the
+   error the z bound propagates through the fp32 router).
+4. Dispatch: counts, offsets and permutation equal the stable sort of the
+   GPU's ids, bit-exactly.
+5. Replay.  Every MXFP8 re-quantisation of a computed tensor (zq, hq, yq, hs)
+   turns any accumulation difference that straddles a rounding boundary into a
+   whole-step code change, and such changes cascade through the later stages:
+   even fp32-level noise in the oracle itself moves its own output by ~1e-3
+   (relative L2).  Where several codes are correct, the unique part is
+   compared and the rest is checked for validity: the oracle re-runs the layer
+   (same fp64 arithmetic) and, only in blocks where ITS OWN value lies within
+   the proven error bound of a boundary, continues with the GPU's block after
+   checking that block is an admissible quantisation of some value inside that
+   bound.  Against this replay every GPU code must then match bit-exactly and
+   every fp32 tensor (h, y_e, y_lat, y) must lie within its bound, and the
+   output must meet the tolerance (relative L2 <= 5e-3, max-abs <= 5e-2 rms).
+6. The unconditioned oracle output: relative L2 <= 5e-3 (its max-abs error is
+   reported).
 
-* MX codes of inputs (x) and weights: bit-exact.
-* fp32 GEMM outputs, wherever the GEMM inputs agree bit-exactly:
-  - bf16 matrix cores (latent z): the fp32 accumulation bound
-    K * 2^-24 * ||a_row|| * ||b_row|| (Cauchy-Schwarz on sum |a_i b_i|);
-  - block-scaled MX matrix cores (expert h, output y): measured on gfx950,
-    each 32-element block's products are summed in a window ending 14 bits
-    below the block's largest product (truncated), block sums then accumulate
-    in fp32.  Bound: 2^-9 * sum_b amax_a[b] * amax_b[b]  (32 products, each
-    off by less than 2^-14 of the block maximum <= amax_a * amax_b) plus
-    (K/32 + 2) * 2^-24 * sum |a_i b_i|.
-* MX codes of computed tensors (zq, hq, yq, hs): equal to the oracle's codes
-  except where a rounding boundary (element midpoint or block power of two)
-  lies between the oracle's value and the GPU's fp32 value; those are
-  counted as flagged, never as failures.
-* expert ids: the same set per token unless the oracle's gap between the k-th
-  and (k+1)-th selection key is below 1e-6 (flagged near-tie); gates of
-  unflagged tokens within max(1e-6, the error the z bound propagates through
-  the fp32 router).
-* dispatch: counts, offsets and the permutation equal the stable sort of the
-  GPU's own ids (exactly the oracle's when no token is flagged).
-* layer output: relative L2 error <= 5e-3 and max-abs error <= 5e-2 * rms(y).
+Error bounds
+------------
+* bf16 matrix cores: fp32 accumulation, K * 2^-24 * sum |a_i b_i| (bounded by
+  Cauchy-Schwarz).
+* block-scaled MX matrix cores (measured on gfx950 with single-instruction
+  probes): within one 32-element block the products are summed in a window
+  ending 14 bits below the block's largest product (truncated); block sums
+  accumulate in fp32.  Bound: 2^-9 * sum_b amax_a[b] * amax_b[b] (32 products,
+  each off by less than 2^-14 of the block's largest product) plus
+  (K/32 + 2) * 2^-24 * sum |a_i b_i|.
 """
 
 from __future__ import annotations
@@ -35,6 +48,9 @@ EPS32 = 2.0 ** -24
 NEAR_TIE = 1e-6
 REL_L2 = 5e-3
 MAXABS_FRAC = 5e-2
+
+
+# --------------------------------------------------------------------------- bounds
 
 
 def row_norms(t: moe.MXTensor) -> np.ndarray:
@@ -52,38 +68,21 @@ def block_amax(t: moe.MXTensor) -> np.ndarray:
     return v.reshape(*v.shape[:-1], -1, 32).max(-1)
 
 
-def mx_mfma_bound(a: moe.MXTensor, b: moe.MXTensor, value: np.ndarray) -> np.ndarray:
-    """Bound for the block-scaled MFMA path (see the module docstring)."""
+def mx_mfma_bound(a: moe.MXTensor, b: moe.MXTensor, value=None) -> np.ndarray:
+    """Bound for the block-scaled MFMA path (module docstring)."""
     K = a.codes.shape[-1]
+    sab = np.abs(a.deq()) @ np.abs(b.deq()).T
     win = 2.0 ** -9 * (block_amax(a) @ block_amax(b).T)
-    acc = (K // 32 + 2) * EPS32 * (np.abs(a.deq()) @ np.abs(b.deq()).T)
-    return win + acc + EPS32 * np.abs(value)
+    out = win + (K // 32 + 2) * EPS32 * sab
+    return out + EPS32 * (sab if value is None else np.abs(value))
 
 
-def straddled(ref: np.ndarray, got: np.ndarray, fmt="e4m3") -> np.ndarray:
-    """Elements whose code may legitimately differ: a boundary between ref and got."""
-    ref32 = np.asarray(ref, np.float64).astype(np.float32).astype(np.float64)   # the value the oracle quantised
-    got = np.asarray(got, np.float64)
-    dev = np.abs(got - ref32) * (1 + 1e-6) + 1e-300
-    return moe.ambiguous_codes(ref32, dev, fmt)
-
-
-def code_report(gpu_codes, gpu_scales, ref: moe.MXTensor, ref_vals, gpu_vals, fmt="e4m3", say=None):
-    """(unflagged mismatches, flagged mismatches) of an E4M3 code tensor."""
-    sc_g = np.repeat(gpu_scales, 32, axis=-1).reshape(gpu_codes.shape)
-    sc_r = np.repeat(ref.scales, 32, axis=-1).reshape(ref.codes.shape)
-    mism = (gpu_codes != ref.codes) | (sc_g != sc_r)
-    if gpu_vals is None:
-        return int(mism.sum()), 0
-    amb = straddled(ref_vals, gpu_vals, fmt)
-    bad = mism & ~amb
-    if bad.any() and say is not None:
-        for idx in list(zip(*np.nonzero(bad)))[:5]:
-            blk = idx[:-1] + (idx[-1] // 32,)
-            say("  code mismatch at", idx, "gpu code", int(gpu_codes[idx]), "ref code", int(ref.codes[idx]),
-                "gpu scale", int(gpu_scales[blk]), "ref scale", int(ref.scales[blk]),
-                "gpu val", float(np.asarray(gpu_vals)[idx]), "ref val", float(np.asarray(ref_vals)[idx]))
-    return int(bad.sum()), int((mism & amb).sum())
+def swiglu_bound(g, u, bg, bu, h):
+    """Bound on |h_gpu - h| for h = silu(G) U given |dG| <= bg, |dU| <= bu."""
+    sg = 1 / (1 + np.exp(-g))
+    dsilu = sg * (1 + g * (1 - sg))          # |silu'| <= 1.1, |silu''| <= 0.5
+    return (np.abs(dsilu) * np.abs(u) * bg + np.abs(g * sg) * bu + bg * bu + 0.5 * np.abs(u) * bg ** 2
+            + 8 * EPS32 * np.abs(h) + 1e-30)
 
 
 def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray):
@@ -93,8 +92,91 @@ def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray):
     return float(rel), float(np.abs(diff).max()), float(rms)
 
 
-def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict, say=print) -> dict:
-    """Assert the GPU trace against the oracle trace; returns a report."""
+# --------------------------------------------------------------------------- replay
+
+
+class Replay:
+    """``resolve`` hooks for ``oracle.moe.forward``: adopt the GPU's block where
+    the oracle's own value is within its bound of a rounding boundary and the
+    GPU's block is an admissible quantisation there."""
+
+    def __init__(self, tr, W, k, dgate, xq):
+        self.tr, self.W, self.k, self.dgate, self.xq = tr, W, k, dgate, xq
+        self.stats = {}
+        P = tr["hq_codes"].shape[0]
+        L = tr["y_e"].shape[1]
+        self.h_bound = np.zeros(tr["hq_codes"].shape)
+        self.ye_bound = np.zeros((P, L))
+        self.ylat_bound = None
+        self.hs_bound = []
+
+    def _adopt(self, name, v, bound, ref: moe.MXTensor, gcodes, gscales) -> moe.MXTensor:
+        v32 = np.asarray(v, np.float64).astype(np.float32).astype(np.float64)   # the value the oracle quantised
+        bound = np.asarray(bound, np.float64) + EPS32 * np.abs(v32) + 1e-300
+        shp = v32.shape
+        nb = shp[-1] // 32
+        amb_blk = moe.ambiguous_codes(v32, bound).reshape(*shp[:-1], nb, 32).any(-1)
+        mag = np.abs(v32)
+        lo = np.maximum(mag - bound, 0.0)
+        hi = mag + bound
+        e_lo = mx.shared_exponent(lo.reshape(*shp[:-1], nb, 32).max(-1), 8)
+        e_hi = mx.shared_exponent(hi.reshape(*shp[:-1], nb, 32).max(-1), 8)
+        e_g = gscales.astype(np.int64) - 127
+        ok_scale = (e_g >= e_lo) & (e_g <= e_hi)
+        c_lo = mx.encode_with_exponent(lo, e_g, "e4m3") & 0x7F
+        c_hi = mx.encode_with_exponent(hi, e_g, "e4m3") & 0x7F
+        gm = gcodes & 0x7F
+        ok_el = (gm >= c_lo) & (gm <= c_hi) & ((np.signbit(v32) == (gcodes >= 0x80)) | (mag <= bound))
+        valid = ok_scale & ok_el.reshape(*shp[:-1], nb, 32).all(-1)
+        use = amb_blk & valid
+        st = self.stats.setdefault(name, {"ambiguous_blocks": 0, "adopted_blocks": 0, "inadmissible_blocks": 0})
+        st["ambiguous_blocks"] += int(amb_blk.sum())
+        differs = (gscales != ref.scales) | (gcodes != ref.codes).reshape(*shp[:-1], nb, 32).any(-1)
+        st["adopted_blocks"] += int((use & differs).sum())
+        st["inadmissible_blocks"] += int((amb_blk & ~valid & differs).sum())
+        codes = np.where(np.repeat(use, 32, axis=-1).reshape(shp), gcodes, ref.codes).astype(np.uint8)
+        scales = np.where(use, gscales, ref.scales).astype(np.uint8)
+        return moe.MXTensor(codes, scales, "e4m3")
+
+    # hooks -----------------------------------------------------------------
+    def zq(self, z, zq):
+        bound = gemm_bound(self.xq, self.W.w_down, z)
+        return self._adopt("zq", z, bound, zq, self.tr["zq_codes"], self.tr["zq_scales"])
+
+    def hq(self, e, rows, a, wg, wu, wd, g, u, h, hq):
+        lo, hi = rows
+        bh = swiglu_bound(g, u, mx_mfma_bound(a, wg, g), mx_mfma_bound(a, wu, u), h)
+        self.h_bound[lo:hi] = bh
+        out = self._adopt("hq", h, bh, hq, self.tr["hq_codes"][lo:hi], self.tr["hq_scales"][lo:hi])
+        self.ye_bound[lo:hi] = mx_mfma_bound(out, wd)
+        return out
+
+    def yq(self, y_lat, yq, r, disp, ye_rows):
+        k = self.k
+        rows = disp.row_of_pair.reshape(-1, k)
+        g = np.abs(r.gates)
+        b = np.zeros_like(y_lat)
+        acc = np.zeros_like(y_lat)
+        for j in range(k):
+            ye = np.abs(ye_rows[rows[:, j]])
+            b += g[:, j:j + 1] * self.ye_bound[rows[:, j]] + self.dgate[:, j:j + 1] * ye
+            acc += g[:, j:j + 1] * ye
+        b += (k + 1) * EPS32 * acc
+        self.ylat_bound = b
+        return self._adopt("yq", y_lat, b, yq, self.tr["yq_codes"], self.tr["yq_scales"])
+
+    def hs(self, s, wg, wu, wd, g, u, h, hq):
+        bh = swiglu_bound(g, u, mx_mfma_bound(self.xq, wg, g), mx_mfma_bound(self.xq, wu, u), h)
+        self.hs_bound.append(bh)
+        return self._adopt(f"hs{s}", h, bh, hq, self.tr["hs_codes"][s], self.tr["hs_scales"][s])
+
+
+# --------------------------------------------------------------------------- the check
+
+
+def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict, x=None, say=print,
+                expert_weights=None) -> dict:
+    """Assert the GPU trace against the oracle (``o`` is its unconditioned run)."""
     T, k, E = y.shape[0], cfg.top_k, cfg.n_routed
     rep = {}
 
@@ -102,47 +184,43 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
     assert np.array_equal(tr["xq_codes"], o.xq.codes), "xq codes"
     assert np.array_equal(tr["xq_scales"], o.xq.scales), "xq scales"
 
-    # 2. latent down-projection
+    # 2. latent down-projection (bf16 matrix cores)
     bz = gemm_bound(o.xq, W.w_down, o.z)
     dz = np.abs(tr["z"].astype(np.float64) - o.z)
     assert np.all(dz <= bz), f"z outside the fp32 bound: worst ratio {np.max(dz / bz):.3g}"
     rep["z_err_over_bound"] = float(np.max(dz / bz))
-    bad, flag = code_report(tr["zq_codes"], tr["zq_scales"], o.zq, o.z, tr["z"], say=say)
-    assert bad == 0, f"zq: {bad} unflagged code mismatches"
-    rep["zq_flagged"] = flag
-    zq_flag_tok = np.zeros(T, bool)
-    if flag:
-        m = (tr["zq_codes"] != o.zq.codes).any(1) | (tr["zq_scales"] != o.zq.scales).any(1)
-        zq_flag_tok |= m
 
     # 3. routing
     gi, ri = tr["ids"], o.routing.ids
+    for t in range(T):
+        assert len(set(gi[t].tolist())) == k and gi[t].min() >= 0 and gi[t].max() < E
     same = np.array([set(gi[t]) == set(ri[t]) for t in range(T)])
     near = o.routing.gap < NEAR_TIE
     assert np.all(same | near), f"ids differ on tokens {np.where(~(same | near))[0][:10]} without a near-tie"
+    for t in np.where(~same)[0]:   # flagged near-ties: the GPU's choice must still be a valid top-k
+        kth = np.sort(o.routing.sel[t])[::-1][k - 1]
+        assert np.all(o.routing.sel[t, gi[t]] >= kth - NEAR_TIE), ("invalid near-tie choice", t)
     rep["near_tie_tokens"] = int(near.sum())
     rep["ids_differ_flagged"] = int((~same).sum())
-    ok = same & ~near
-    # score error from the latent's error (z bound) and the fp32 router GEMM
     Wr = np.abs(W.w_router.astype(np.float64))
-    dlog = bz @ Wr.T + W.w_router.shape[1] * EPS32 * (np.abs(o.z) @ Wr.T) + 2 * EPS32 * (1 + np.abs(o.z) @ Wr.T)
+    zw = np.abs(o.z) @ Wr.T
+    dlog = bz @ Wr.T + W.w_router.shape[1] * EPS32 * zw + 2 * EPS32 * (1 + zw)
     ds = 0.25 * dlog + 2 * EPS32
-    rep["max_score_err_bound"] = float(ds.max())
+    dgate = np.zeros((T, k))
     worst_gate = 0.0
-    for t in np.where(ok)[0]:
-        og = dict(zip(ri[t].tolist(), o.routing.gates[t].tolist()))
-        ssum = o.routing.scores[t, ri[t]].sum()
-        dsum = ds[t, ri[t]].sum()
+    for t in range(T):
+        ssum = o.routing.scores[t, gi[t]].sum()
+        gates_t = o.routing.scores[t, gi[t]] / ssum          # the oracle's gates of the GPU's set
+        dsum = ds[t, gi[t]].sum()
         for j in range(k):
             e = int(gi[t, j])
-            tol = max(1e-6, (ds[t, e] + og[e] * dsum) / ssum + 4 * EPS32)
-            err = abs(tr["gates"][t, j] - og[e])
+            tol = max(1e-6, (ds[t, e] + gates_t[j] * dsum) / ssum + 4 * EPS32)
+            dgate[t, j] = tol
+            err = abs(float(tr["gates"][t, j]) - gates_t[j])
             worst_gate = max(worst_gate, err)
             assert err <= tol, ("gate", t, j, err, tol)
     rep["max_gate_err"] = worst_gate
     assert np.all(np.abs(tr["gates"].astype(np.float64).sum(1) - 1) <= 1e-6)
-    for t in range(T):
-        assert len(set(gi[t].tolist())) == k and gi[t].min() >= 0 and gi[t].max() < E
 
     # 4. dispatch = stable sort of the GPU's ids (bit-exact)
     d = moe.dispatch(gi, E)
@@ -151,48 +229,45 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
     assert np.array_equal(tr["pair_of_row"], d.pair_of_row), "pair_of_row"
     assert np.array_equal(tr["row_of_pair"], d.row_of_pair), "row_of_pair"
 
-    # 5. expert hidden states, rows whose token agrees upstream (same ids, same zq)
-    tok_ok = same & ~zq_flag_tok
-    if np.array_equal(gi, ri) and "h" in tr:
-        rows_ok = tok_ok[o.disp.pair_of_row // k]
-        g, u = o.g_rows, o.u_rows
-        # error bounds of G and U (block-scaled MFMA), then of h = silu(G) U
-        bnd_g = np.zeros_like(g)
-        bnd_u = np.zeros_like(g)
-        for e in range(E):
-            lo, hi = o.disp.offsets[e], o.disp.offsets[e + 1]
-            if hi == lo:
-                continue
-            a = o.zq[o.disp.pair_of_row[lo:hi] // k]
-            bnd_g[lo:hi] = mx_mfma_bound(a, W.w_gate_e[e], g[lo:hi])
-            bnd_u[lo:hi] = mx_mfma_bound(a, W.w_up_e[e], u[lo:hi])
-        sg = 1 / (1 + np.exp(-g))
-        dsilu = sg * (1 + g * (1 - sg))
-        bh = np.abs(dsilu) * np.abs(u) * bnd_g + np.abs(g * sg) * bnd_u + bnd_g * bnd_u \
-            + 0.5 * np.abs(u) * bnd_g ** 2 + 8 * EPS32 * np.abs(o.h_rows)
-        dh = np.abs(tr["h"].astype(np.float64) - o.h_rows)
-        viol = (dh > bh) & rows_ok[:, None]
-        assert not viol.any(), f"h outside bound on {viol.sum()} elements"
-        bad, flag = code_report(tr["hq_codes"], tr["hq_scales"], o.hq_rows, o.h_rows, tr["h"], say=say)
-        assert bad == 0, f"hq: {bad} unflagged code mismatches"
-        rep["hq_flagged"] = flag
+    # 5. replay along the GPU's admissible choices
+    if x is not None:
+        rp = Replay(tr, W, k, dgate, o.xq)
+        c = moe.forward(x, W, k, ids_override=gi, resolve=rp, expert_weights=expert_weights)
+        for name, st in rp.stats.items():
+            assert st["inadmissible_blocks"] == 0, (name, st)
+        rep["replay"] = rp.stats
+        for name, gc, gs, ref in (("zq", tr["zq_codes"], tr["zq_scales"], c.zq),
+                                  ("hq", tr["hq_codes"], tr["hq_scales"], c.hq_rows),
+                                  ("yq", tr["yq_codes"], tr["yq_scales"], c.yq)):
+            nbad = int((gc != ref.codes).sum()) + int((gs != ref.scales).sum())
+            if nbad:
+                say(f"  {name} mismatches at {np.argwhere(gc != ref.codes)[:3].tolist()}")
+            assert nbad == 0, f"{name}: {nbad} code/scale mismatches against the replay"
+        for s in range(len(W.w_gate_s)):
+            assert np.array_equal(tr["hs_codes"][s], c.hq_shared[s].codes), f"hs{s} codes"
+            assert np.array_equal(tr["hs_scales"][s], c.hq_shared[s].scales), f"hs{s} scales"
+            dh = np.abs(tr["hs"][s].astype(np.float64) - c.h_shared[s])
+            assert np.all(dh <= rp.hs_bound[s]), f"hs{s} outside its bound"
+        dh = np.abs(tr["h"].astype(np.float64) - c.h_rows)
+        assert np.all(dh <= rp.h_bound), f"h outside its bound on {(dh > rp.h_bound).sum()} elements"
+        dye = np.abs(tr["y_e"].astype(np.float64) - c.ye_rows)
+        assert np.all(dye <= rp.ye_bound), f"y_e outside its bound on {(dye > rp.ye_bound).sum()} elements"
+        dyl = np.abs(tr["y_lat"].astype(np.float64) - c.y_lat)
+        assert np.all(dyl <= rp.ylat_bound), f"y_lat outside its bound on {(dyl > rp.ylat_bound).sum()} elements"
+        by = mx_mfma_bound(c.yq, W.w_up)
+        for s in range(len(W.w_gate_s)):
+            by = by + mx_mfma_bound(c.hq_shared[s], W.w_down_s[s])
+        by = by + (1 + len(W.w_gate_s)) * EPS32 * np.abs(c.y)
+        dy = np.abs(y.astype(np.float64) - c.y)
+        assert np.all(dy <= by), f"y outside its bound on {(dy > by).sum()} elements"
+        rel, maxabs, rms = output_errors(y, c.y)
+        rep.update(replay_rel_l2=rel, replay_max_abs_over_rms=maxabs / rms)
+        assert rel <= REL_L2, f"relative L2 vs replay {rel:.3g}"
+        assert maxabs <= MAXABS_FRAC * rms, f"max abs vs replay {maxabs:.3g} (rms {rms:.3g})"
 
-    # 6. combined latent codes
-    bad, flag = code_report(tr["yq_codes"], tr["yq_scales"], o.yq, o.y_lat, tr["y_lat"])
-    rep["yq_mismatch_unflagged"] = bad
-    rep["yq_flagged"] = flag
-
-    # 7. shared experts
-    for s in range(len(W.w_gate_s)):
-        bad, flag = code_report(tr["hs_codes"][s], tr["hs_scales"][s], o.hq_shared[s], o.h_shared[s],
-                                tr["hs"][s] if "hs" in tr else None)
-        assert bad == 0, f"shared {s}: {bad} unflagged code mismatches"
-        rep[f"hs{s}_flagged"] = flag
-
-    # 8. output
+    # 6. unconditioned oracle output
     rel, maxabs, rms = output_errors(y, o.y)
-    rep.update(rel_l2=rel, max_abs=maxabs, rms=rms)
+    rep.update(rel_l2=rel, max_abs_over_rms=maxabs / rms, rms=rms)
     say("parity report:", rep)
     assert rel <= REL_L2, f"relative L2 {rel:.3g}"
-    assert maxabs <= MAXABS_FRAC * rms, f"max abs {maxabs:.3g} vs rms {rms:.3g}"
     return rep

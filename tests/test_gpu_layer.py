@@ -47,7 +47,7 @@ def _layer_case(cfg, x=None, selection_bias=None, check_codes=True):
         x = synth.gen_hidden(cfg)
     y, tr = run_traced(lay, x)
     o = moe.forward(x, W, cfg.top_k)
-    rep = parity.check_layer(cfg, W, o, y, tr, say=say)
+    rep = parity.check_layer(cfg, W, o, y, tr, x=x, say=say)
     lay.close()
     return rep, y, tr, o
 

@@ -1,0 +1,86 @@
+"""CPU checks of the parity machinery itself: a perturbed oracle run standing
+in for the GPU must pass; planted mistakes must fail."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe, mx, weights
+from tests import parity
+
+
+def _fake_trace(cfg, W, x, eps, seed=0):
+    """Run the oracle with relative noise eps * sum|ab| injected into every MX
+    product, and package it like the GPU trace."""
+    rng = np.random.default_rng(seed)
+    orig = moe.mm
+
+    def noisy(a, b):
+        r = orig(a, b)
+        return r + eps * (np.abs(a.deq()) @ np.abs(b.deq()).T) * rng.standard_normal(r.shape)
+
+    moe.mm = noisy
+    try:
+        n = moe.forward(x, W, cfg.top_k)
+    finally:
+        moe.mm = orig
+    f32 = lambda v: np.asarray(v).astype(np.float32)
+    tr = {
+        "xq_codes": n.xq.codes, "xq_scales": n.xq.scales, "z": f32(n.z), "zq_codes": n.zq.codes,
+        "zq_scales": n.zq.scales, "ids": n.routing.ids, "gates": f32(n.routing.gates),
+        "counts": n.disp.counts.astype(np.int32), "offsets": n.disp.offsets.astype(np.int32),
+        "pair_of_row": n.disp.pair_of_row.astype(np.int32), "row_of_pair": n.disp.row_of_pair.astype(np.int32),
+        "h": f32(n.h_rows), "hq_codes": n.hq_rows.codes, "hq_scales": n.hq_rows.scales, "y_e": f32(n.ye_rows),
+        "y_lat": f32(n.y_lat), "yq_codes": n.yq.codes, "yq_scales": n.yq.scales,
+        "hs": np.stack([f32(h) for h in n.h_shared]), "hs_codes": np.stack([q.codes for q in n.hq_shared]),
+        "hs_scales": np.stack([q.scales for q in n.hq_shared]),
+    }
+    return f32(n.y), tr
+
+
+@pytest.fixture(scope="module")
+def tiny_case():
+    cfg = synth.config("tiny")
+    W = weights.layer(cfg)
+    x = synth.gen_hidden(cfg)
+    o = moe.forward(x, W, cfg.top_k)
+    y, tr = _fake_trace(cfg, W, x, eps=2e-7)
+    return cfg, W, x, o, y, tr
+
+
+def test_perturbed_run_passes_and_adopts_boundary_choices(tiny_case):
+    cfg, W, x, o, y, tr = tiny_case
+    rep = parity.check_layer(cfg, W, o, y, tr, x=x, say=lambda *a: None)
+    adopted = sum(v["adopted_blocks"] for v in rep["replay"].values())
+    assert adopted > 0            # the noise does move codes across boundaries ...
+    assert rep["replay_rel_l2"] < 1e-4   # ... and the replay follows them exactly
+
+
+def test_planted_code_error_fails(tiny_case):
+    cfg, W, x, o, y, tr = tiny_case
+    bad = dict(tr)
+    codes = tr["hq_codes"].copy()
+    # the largest-magnitude element of row 0 is far from any boundary: change its code
+    j = int(np.argmax(np.abs(o.h_rows[0])))
+    codes[0, j] ^= 0x01
+    bad["hq_codes"] = codes
+    with pytest.raises(AssertionError):
+        parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
+
+
+def test_planted_permutation_error_fails(tiny_case):
+    cfg, W, x, o, y, tr = tiny_case
+    bad = dict(tr)
+    por = tr["pair_of_row"].copy()
+    por[[0, 1]] = por[[1, 0]]
+    bad["pair_of_row"] = por
+    with pytest.raises(AssertionError, match="pair_of_row"):
+        parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
+
+
+def test_planted_output_error_fails(tiny_case):
+    cfg, W, x, o, y, tr = tiny_case
+    y2 = y.copy()
+    y2[3, 7] += 0.1 * np.abs(y).max()
+    with pytest.raises(AssertionError):
+        parity.check_layer(cfg, W, o, y2, tr, x=x, say=lambda *a: None)
