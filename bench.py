@@ -188,6 +188,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB read + 1 GiB write elementwise kernel first (calibrates HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -206,6 +208,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = _hip()
+    if args.copy_probe:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
     cfg = synth.config(args.workload)
     t = time.perf_counter()
     shape = LY.LayerShape.of(cfg)

@@ -75,15 +75,17 @@ struct GemmArgs {
   int max_mtiles;              // upper bound of M-tiles (grid size / n-tiles)
 };
 
-// M-tile height of the small-M (decode) and large-M configurations.
-int gemm_mtile(bool small_m);
+// Kernel configurations: weight streaming with 16 or 64 rows per M-tile (few
+// rows per group: decode), or the register-tiled kernel with 64-row tiles.
+enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE64 = 2 };
+int gemm_mtile(int shape);
 
 // Dense bf16 GEMM (seg[0].a = bf16 [M][K], seg[0].b = bf16 [N][K]) with the
 // fp32 + MXFP8 epilogue (EPI_F32_QUANT).
-hipError_t launch_bf16_gemm_quant(const GemmArgs& args, bool small_m, hipStream_t s);
+hipError_t launch_bf16_gemm_quant(const GemmArgs& args, int shape, hipStream_t s);
 
 // Launch the grouped/dense MX GEMM with an automatically chosen tile shape.
-hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, bool small_m, hipStream_t s);
+hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, int shape, hipStream_t s);
 
 // ---- Combine (combine.hip) --------------------------------------------------
 // y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then

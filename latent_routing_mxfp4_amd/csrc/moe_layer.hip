@@ -207,9 +207,12 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   uint8_t* hs = at<uint8_t>(ws, pl.hs);
   uint8_t* hss = at<uint8_t>(ws, pl.hss);
 
-  const bool small_dense = T <= 256;
-  const bool small_routed = P <= (int64_t)32 * E;
-  const int mt_small = moe::gemm_mtile(true), mt_big = moe::gemm_mtile(false);
+  // Kernel shapes: weight streaming when a group has few rows (decode), the
+  // register-tiled kernel otherwise.
+  const int dense_shape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_TILE64;
+  const int routed_shape = P <= (int64_t)16 * E ? moe::GEMM_STREAM16 : moe::GEMM_TILE64;
+  const int mt_dense = moe::gemm_mtile(dense_shape);
+  const int mt_small = moe::gemm_mtile(moe::GEMM_STREAM16), mt_big = moe::gemm_mtile(moe::GEMM_TILE64);
 
   hipEvent_t const* ev = tr && tr->events ? reinterpret_cast<hipEvent_t const*>(tr->events) : nullptr;
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
@@ -234,8 +237,9 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.ldc = L;
     a.q = zq;
     a.qs = zqs;
-    a.max_mtiles = (T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense);
-    MOE_HIP(moe::launch_bf16_gemm_quant(a, small_dense, s));
+    const int bshape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_TILE64;
+    a.max_mtiles = (T + moe::gemm_mtile(bshape) - 1) / moe::gemm_mtile(bshape);
+    MOE_HIP(moe::launch_bf16_gemm_quant(a, bshape, s));
   }
   MOE_HIP(mark(MOE_EV_DOWN));
 
@@ -249,8 +253,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(moe::launch_dispatch(ids, T, E, k, dscr, counts, offsets, rop, por, mt_small, ms0, mt_big, ms1, s));
   MOE_HIP(mark(MOE_EV_DISPATCH));
 
-  const int mt_r = small_routed ? mt_small : mt_big;
-  const int32_t* ms_r = small_routed ? ms0 : ms1;
+  const int mt_r = moe::gemm_mtile(routed_shape);
+  const int32_t* ms_r = routed_shape == moe::GEMM_STREAM16 ? ms0 : ms1;
   const int64_t max_mt_r = P / mt_r + (P < E ? P : E) + 1;
 
   // 6. routed GEMM1 + SwiGLU + MXFP8
@@ -278,7 +282,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.q = hq;
     a.qs = hqs;
     a.max_mtiles = (int)max_mt_r;
-    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, small_routed, s));
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, routed_shape, s));
   }
   MOE_HIP(mark(MOE_EV_EXPERT_UP));
 
@@ -295,7 +299,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.c = ye;
     a.ldc = L;
     a.max_mtiles = (int)max_mt_r;
-    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, small_routed, s));
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, routed_shape, s));
   }
   MOE_HIP(mark(MOE_EV_EXPERT_DOWN));
 
@@ -327,8 +331,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.qs = hss;
     a.q_gstride = (int64_t)T * Fs;
     a.qs_gstride = (int64_t)T * Fs / 32;
-    a.max_mtiles = S * ((T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense));
-    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, small_dense, s));
+    a.max_mtiles = S * ((T + mt_dense - 1) / mt_dense);
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, dense_shape, s));
   }
   MOE_HIP(mark(MOE_EV_SHARED_UP));
 
@@ -353,8 +357,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.N = d;
     a.c = y;
     a.ldc = d;
-    a.max_mtiles = (T + moe::gemm_mtile(small_dense) - 1) / moe::gemm_mtile(small_dense);
-    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, small_dense, s));
+    a.max_mtiles = (T + mt_dense - 1) / mt_dense;
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, dense_shape, s));
   }
   MOE_HIP(mark(MOE_EV_OUT));
 
@@ -410,7 +414,7 @@ int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* 
   if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MOE_ERR_INVALID_ARG;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
     return MOE_ERR_INVALID_ARG;
-  const bool small = M <= 256;
+  const int shape = M <= 16 ? moe::GEMM_STREAM16 : M <= 256 ? moe::GEMM_STREAM64 : moe::GEMM_TILE64;
   moe::GemmArgs a = {};
   a.nseg = 1;
   a.seg[0] = {a_codes, a_scales, K, b_codes, b_scales, nullptr, nullptr, 0, 0, K};
@@ -419,8 +423,8 @@ int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* 
   a.N = N;
   a.c = c;
   a.ldc = N;
-  a.max_mtiles = (M + moe::gemm_mtile(small) - 1) / moe::gemm_mtile(small);
-  if (moe::launch_mx_gemm(a, moe::EPI_F32, small, static_cast<hipStream_t>(stream)) != hipSuccess)
+  a.max_mtiles = (M + moe::gemm_mtile(shape) - 1) / moe::gemm_mtile(shape);
+  if (moe::launch_mx_gemm(a, moe::EPI_F32, shape, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }

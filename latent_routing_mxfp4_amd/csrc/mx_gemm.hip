@@ -56,6 +56,9 @@ __device__ __forceinline__ v8i as_v8i(const uint4& f) {
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 to_uint4(const u32x4& v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& f) {
   union {
@@ -353,6 +356,181 @@ __global__ void __launch_bounds__(256) bf16_gemm_kernel(const GemmArgs p) {
   epilogue<MW, NW, 1, EPI>(p, t, acc, r16, g4);
 }
 
+// Weight-streaming variant for few rows per group (decode).  The weights are
+// read exactly once, so the kernel is HBM-bound and its loads are shaped for
+// that:
+//  * codes: per 256-wide K super-step each lane reads 32 contiguous bytes of its
+//    weight row, and the four lane groups of a wave together read the row's
+//    whole 128-byte line in one pass (a half-line read and its other half
+//    issued one step later get evicted in between and fetched twice);
+//  * scales: the workgroup copies its tile's E8M0 rows (contiguous in memory)
+//    into LDS once per K segment, instead of touching each 128-byte scale line
+//    once per K-step.
+// The two 32-element blocks a lane loads per super-step feed two MFMAs (u = 0,
+// 1); in MFMA u lane group g holds physical block 8s + 2g + u, and the E4M3
+// operand gathers the matching K values in its split-half layout.  A K tail of
+// 128 uses the plain one-step layout.
+template <int MW, int NW, int EPI>
+__global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
+  extern __shared__ uint8_t bscale_lds[];  // [NB][NT rows][K/32]
+  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
+  constexpr int NB = SWI ? 2 : 1;
+  constexpr int MT = 16 * MW;
+  constexpr int NT = 4 * 16 * NW;
+  static_assert(EPI == EPI_F32 || NW % 2 == 0, "quantising epilogues need whole 32-column blocks per wave");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
+  Tile t;
+  if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;  // uniform across the workgroup
+  const int tile_n0 = t.n0 - wave * 16 * NW;
+
+  int64_t arow[MW];
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi) {
+    int r = t.m0 + 16 * mi + r16;
+    r = r < t.rows ? r : t.rows - 1;
+    int sr = t.row_base + r;
+    if (p.offsets) arow[mi] = p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr;
+    else arow[mi] = r;
+  }
+  int bcol[NW];
+#pragma unroll
+  for (int ni = 0; ni < NW; ++ni) {
+    int c = t.n0 + 16 * ni + r16;
+    bcol[ni] = c < p.N ? c : p.N - 1;
+  }
+  const int nrows = min(NT, p.N - tile_n0);
+
+  v4f acc[MW][NW][NB];
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) acc[mi][ni][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSeg& sg = p.seg[s];
+    const int K = sg.K;
+    const int kb = K >> 5;  // scale bytes per row (multiple of 4)
+    // ---- stage this tile's B scales in LDS
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>((h == 0 ? sg.bs : sg.b2s) +
+                                                              (int64_t)t.g * sg.bs_gstride + (int64_t)tile_n0 * kb);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(bscale_lds + h * NT * kb);
+      const int nw = nrows * kb / 4;
+      for (int i = tid; i < nw; i += 256) dst[i] = src[i];
+    }
+    __syncthreads();
+
+    const uint8_t* ap[MW];
+    const uint8_t* asp[MW];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi) {
+      ap[mi] = sg.a + arow[mi] * sg.lda;
+      asp[mi] = sg.as + arow[mi] * kb;
+    }
+    const uint8_t* bp[NW][NB];
+    const uint8_t* bsl[NW][NB];
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) {
+        bp[ni][h] = (h == 0 ? sg.b : sg.b2) + (int64_t)t.g * sg.b_gstride + (int64_t)bcol[ni] * (K >> 1);
+        const int lr = min(wave * 16 * NW + 16 * ni + r16, nrows - 1);
+        bsl[ni][h] = bscale_lds + h * NT * kb + lr * kb;
+      }
+
+    const int nsup = K >> 8;
+    const int a_off = 32 * (2 * (g4 >> 1)) + 16 * (g4 & 1);   // + 32u, second half at +128
+    uint4 fb[NW][NB][2];
+    auto load_b = [&](int ss) {
+#pragma unroll
+      for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+        for (int h = 0; h < NB; ++h) {
+          const u32x4* q = reinterpret_cast<const u32x4*>(bp[ni][h] + 128 * ss + 32 * g4);
+          fb[ni][h][0] = to_uint4(__builtin_nontemporal_load(q));
+          fb[ni][h][1] = to_uint4(__builtin_nontemporal_load(q + 1));
+        }
+    };
+    if (nsup > 0) load_b(0);
+    for (int ss = 0; ss < nsup; ++ss) {
+      uint4 cb[NW][NB][2];
+#pragma unroll
+      for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+        for (int h = 0; h < NB; ++h) { cb[ni][h][0] = fb[ni][h][0]; cb[ni][h][1] = fb[ni][h][1]; }
+      if (ss + 1 < nsup) load_b(ss + 1);
+      uint32_t sbw[NW][NB];
+#pragma unroll
+      for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+        for (int h = 0; h < NB; ++h) sbw[ni][h] = *reinterpret_cast<const uint16_t*>(bsl[ni][h] + 8 * ss + 2 * g4);
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi) {
+        const uint32_t saw = *reinterpret_cast<const uint16_t*>(asp[mi] + 8 * ss + 2 * g4);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint8_t* q = ap[mi] + 256 * ss + a_off + 32 * u;
+          Frag8 fa;
+          fa.lo = *reinterpret_cast<const uint4*>(q);
+          fa.hi = *reinterpret_cast<const uint4*>(q + 128);
+          const v8i av = as_v8i(fa);
+          const int sa = (int)(saw >> (8 * u));
+#pragma unroll
+          for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+            for (int h = 0; h < NB; ++h)
+              acc[mi][ni][h] = mfma_f8f4(av, as_v8i(cb[ni][h][u]), acc[mi][ni][h], sa, (int)(sbw[ni][h] >> (8 * u)));
+        }
+      }
+    }
+    if (K & 255) {  // one 128-wide K-step left: plain layout
+      const int kl = (K >> 7) - 1;
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi) {
+        const uint8_t* q = ap[mi] + 128 * kl + 16 * g4;
+        Frag8 fa;
+        fa.lo = *reinterpret_cast<const uint4*>(q);
+        fa.hi = *reinterpret_cast<const uint4*>(q + 64);
+        const v8i av = as_v8i(fa);
+        const int sa = asp[mi][4 * kl + g4];
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+          for (int h = 0; h < NB; ++h) {
+            const uint4 fbt = *reinterpret_cast<const uint4*>(bp[ni][h] + 64 * kl + 16 * g4);
+            acc[mi][ni][h] = mfma_f8f4(av, as_v8i(fbt), acc[mi][ni][h], sa, (int)bsl[ni][h][4 * kl + g4]);
+          }
+      }
+    }
+  }
+  epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
+}
+
+template <int MW, int NW, int EPI>
+static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
+  constexpr int NT = 4 * 16 * NW;
+  constexpr int NB = EPI == EPI_SWIGLU_QUANT ? 2 : 1;
+  const int n_ntiles = (a.N + NT - 1) / NT;
+  const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  int kb = 0;
+  for (int i = 0; i < a.nseg; ++i) kb = max(kb, a.seg[i].K >> 5);
+  const size_t smem = (size_t)NB * NT * kb;
+  if (smem > 65536) return hipErrorInvalidValue;
+  mx_gemm_stream_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), smem, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int MW, int NW, int EPI>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int NT = 4 * 16 * NW;
@@ -364,7 +542,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int gemm_mtile(bool small_m) { return small_m ? 16 : 64; }
+int gemm_mtile(int shape) { return shape == GEMM_STREAM16 ? 16 : 64; }
 
 template <int MW, int NW, int EPI>
 static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
@@ -377,16 +555,24 @@ static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bf16_gemm_quant(const GemmArgs& a, bool small_m, hipStream_t s) {
-  return small_m ? launch_bf16_cfg<1, 2, EPI_F32_QUANT>(a, s) : launch_bf16_cfg<4, 2, EPI_F32_QUANT>(a, s);
+hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
+  return shape == GEMM_STREAM16 ? launch_bf16_cfg<1, 2, EPI_F32_QUANT>(a, s)
+                                : launch_bf16_cfg<4, 2, EPI_F32_QUANT>(a, s);
 }
 
-hipError_t launch_mx_gemm(const GemmArgs& a, int epi, bool small_m, hipStream_t s) {
-  if (small_m) {
+hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) {
+  if (shape == GEMM_STREAM16) {
     switch (epi) {
-      case EPI_F32: return launch_cfg<1, 2, EPI_F32>(a, s);
-      case EPI_F32_QUANT: return launch_cfg<1, 2, EPI_F32_QUANT>(a, s);
-      default: return launch_cfg<1, 2, EPI_SWIGLU_QUANT>(a, s);
+      case EPI_F32: return launch_stream_cfg<1, 2, EPI_F32>(a, s);
+      case EPI_F32_QUANT: return launch_stream_cfg<1, 2, EPI_F32_QUANT>(a, s);
+      default: return launch_stream_cfg<1, 2, EPI_SWIGLU_QUANT>(a, s);
+    }
+  }
+  if (shape == GEMM_STREAM64) {
+    switch (epi) {
+      case EPI_F32: return launch_stream_cfg<4, 2, EPI_F32>(a, s);
+      case EPI_F32_QUANT: return launch_stream_cfg<4, 2, EPI_F32_QUANT>(a, s);
+      default: return launch_stream_cfg<4, 2, EPI_SWIGLU_QUANT>(a, s);
     }
   }
   switch (epi) {
