@@ -76,8 +76,9 @@ struct GemmArgs {
 };
 
 // Kernel configurations: weight streaming with 16 or 64 rows per M-tile (few
-// rows per group: decode), or the register-tiled kernel with 64-row tiles.
-enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE64 = 2 };
+// rows per group: decode), the register-tiled kernel with 64-row tiles, or the
+// LDS-staged kernel with 128 x 128 tiles (many rows per group: prefill).
+enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE64 = 2, GEMM_TILE128 = 3 };
 int gemm_mtile(int shape);
 
 // Dense bf16 GEMM (seg[0].a = bf16 [M][K], seg[0].b = bf16 [N][K]) with the

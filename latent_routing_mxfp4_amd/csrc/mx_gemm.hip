@@ -515,6 +515,242 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
+// LDS-staged tiled variant (many rows per group: prefill).  A workgroup owns
+// a 128-row x 128-weight-row tile (for SwiGLU: 64 gate + the matching 64 up
+// rows, i.e. 64 output columns); its 4 waves form a 2 x 2 grid, each computing
+// 64 rows x 64 weight rows with 16 MFMAs per 128-wide K-step.
+//
+// Operands move global -> LDS with gfx950's direct loads (global_load_lds,
+// 16 bytes per lane, no staging registers) through a 3-buffer ring: while the
+// MFMAs consume K-step k, the loads of k+1 and k+2 are in flight.  A wave
+// issues 7 loads per K-step (4 for A, 2 for B, 1 for the scales), so
+// "vmcnt <= 7" means step k has landed.  A lane's LDS slot is fixed by the
+// hardware (base + 16 * lane), so each lane fetches whichever global chunk
+// belongs in that slot; the LDS rows are XOR-swizzled by 16-byte chunk so the
+// 16 rows a fragment read touches fall on distinct banks.  The routed gate/up
+// GEMM gathers its A rows through the permutation in these loads.
+//
+// Tile order: the flat tile list is cut into 8 contiguous chunks, one per XCD
+// (workgroup i runs on XCD i % 8), so an expert's tiles share one L2; inside
+// an expert the M-tiles of one weight column-tile are consecutive, so each
+// weight tile is fetched from HBM once and reused from L2.
+constexpr int LT_M = 128;   // rows per tile
+constexpr int LT_B = 128;   // weight rows per tile
+constexpr int LT_OFF_B = LT_M * 128;
+constexpr int LT_OFF_AS = LT_OFF_B + LT_B * 64;
+constexpr int LT_OFF_BS = LT_OFF_AS + 4 * LT_M;
+constexpr int LT_STAGE = LT_OFF_BS + 4 * LT_B;   // bytes per LDS buffer (25600)
+constexpr int LT_NBUF = 3;
+constexpr int LT_LOADS = 7;                       // direct loads per wave per K-step
+
+// Direct global -> LDS loads (16 or 4 bytes per lane; lane l lands at
+// m0 + size * l) and their waits are issued as inline assembly: the compiler's
+// wait-count pass would otherwise treat every in-flight LDS load as aliasing
+// every LDS read and drain the whole pipeline (vmcnt(0)) before each fragment
+// read.  Ordering is kept by hand: wait_vmcnt<N>() after issue, then a barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void gl_lds16(const void* g, const uint8_t* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory");
+}
+__device__ __forceinline__ void gl_lds4(const void* g, const uint8_t* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that waits only for this wave's LDS operations: the
+// direct loads in flight are governed by wait_vmcnt, so the barrier must not
+// drain them (__syncthreads would wait for vmcnt(0)).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int EPI>
+__global__ void __launch_bounds__(256) mx_gemm_lds_kernel(const GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
+  constexpr int NB = SWI ? 2 : 1;
+  constexpr int NCOL = SWI ? LT_B / 2 : LT_B;       // output columns per tile
+  constexpr int NW = SWI ? 2 : 4;                     // 16-col fragments per wave (per matrix)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- tile decode (XCD-chunked, M-fastest inside an expert)
+  const int n_nt = (p.N + NCOL - 1) / NCOL;
+  const bool routed = p.offsets != nullptr;
+  const int mpg = routed ? 0 : (p.M + LT_M - 1) / LT_M;
+  const int total = routed ? p.mtile_start[p.G] * n_nt : p.G * mpg * n_nt;
+  const int per = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per) return;
+  const int lin = (blockIdx.x & 7) * per + slot;
+  if (lin >= total) return;
+  int g, mt, nt, rows, row_base;
+  if (routed) {
+    int lo = 0, hi = p.G;  // mtile_start[lo]*n_nt <= lin < mtile_start[hi]*n_nt
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.mtile_start[mid] * n_nt <= lin) lo = mid; else hi = mid;
+    }
+    g = lo;
+    const int mte = p.mtile_start[g + 1] - p.mtile_start[g];
+    const int local = lin - p.mtile_start[g] * n_nt;
+    nt = local / mte;
+    mt = local - nt * mte;
+    row_base = p.offsets[g];
+    rows = p.offsets[g + 1] - row_base;
+  } else {
+    g = lin / (mpg * n_nt);
+    const int local = lin - g * mpg * n_nt;
+    nt = local / mpg;
+    mt = local - nt * mpg;
+    row_base = 0;
+    rows = p.M;
+  }
+  const int m0 = mt * LT_M;
+  const int col0 = nt * NCOL;
+
+  // ---- what this lane loads.  A: load i (0..3) fills LDS bytes [1024*(4*wave+i), +1024):
+  // tile row 32*wave + 8*i + lane/8, physical chunk lane%8.  B: load i (0..1) fills
+  // [OFF_B + 1024*(2*wave+i), +1024): tile row 32*wave + 16*i + lane/4, physical
+  // chunk lane%4.  Scales: wave w fills dwords [64w, 64w+64) of the A|B scale columns.
+  auto a_src_row = [&](int trow) -> int64_t {
+    int r = m0 + trow;
+    r = r < rows ? r : rows - 1;
+    const int sr = row_base + r;
+    return routed ? (p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr) : (int64_t)r;
+  };
+  auto b_col = [&](int trow, int& h) {
+    int c;
+    if (SWI) { h = trow >= NCOL; c = col0 + (trow - h * NCOL); }
+    else { h = 0; c = col0 + trow; }
+    return c < p.N ? c : p.N - 1;
+  };
+  int64_t a_row[4];
+  int a_chunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    a_row[i] = a_src_row(r);
+    a_chunk[i] = (lane & 7) ^ (r & 7);
+  }
+  int b_trow[2], b_chunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 32 * wave + 16 * i + (lane >> 2);
+    b_trow[i] = r;
+    b_chunk[i] = (lane & 3) ^ ((r >> 1) & 3);
+  }
+  const int s_trow = 64 * (wave & 1) + lane;        // tile row of this lane's scale dword
+  const int64_t s_arow = wave < 2 ? a_src_row(s_trow) : 0;
+
+  v4f acc[4][NW][NB];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) acc[mi][ni][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int sgi = 0; sgi < p.nseg; ++sgi) {
+    const GemmSeg& sg = p.seg[sgi];
+    const int K = sg.K;
+    const int ksteps = K >> 7;
+    const int kb = K >> 5;
+    const uint8_t* ga[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ga[i] = sg.a + a_row[i] * sg.lda + 16 * a_chunk[i];
+    const uint8_t* gb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int h;
+      const int c = b_col(b_trow[i], h);
+      gb[i] = (h ? sg.b2 : sg.b) + (int64_t)g * sg.b_gstride + (int64_t)c * (K >> 1) + 16 * b_chunk[i];
+    }
+    const uint8_t* gs;
+    if (wave < 2) {
+      gs = sg.as + s_arow * kb;
+    } else {
+      int h;
+      const int c = b_col(s_trow, h);
+      gs = (h ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + (int64_t)c * kb;
+    }
+    auto issue = [&](int ks) {
+      uint8_t* buf = lds + (ks % LT_NBUF) * LT_STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (4 * wave + i));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) gl_lds16(gb[i] + 64 * ks, buf + LT_OFF_B + 1024 * (2 * wave + i));
+      gl_lds4(gs + 4 * ks, buf + LT_OFF_AS + 256 * wave);
+    };
+
+    __syncthreads();  // the previous segment's buffers are no longer read
+    issue(0);
+    if (ksteps > 1) issue(1);
+    for (int ks = 0; ks < ksteps; ++ks) {
+      if (ks + 1 < ksteps) wait_vmcnt<LT_LOADS>(); else wait_vmcnt<0>();
+      barrier_lds();
+      if (ks + 2 < ksteps) issue(ks + 2);
+      const uint8_t* buf = lds + (ks % LT_NBUF) * LT_STAGE;
+      v8i bf[NW][NB];
+      int bsc[NW][NB];
+#pragma unroll
+      for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+        for (int h = 0; h < NB; ++h) {
+          const int trow = SWI ? (h * NCOL + wn * 32 + 16 * ni + r16) : (wn * 64 + 16 * ni + r16);
+          bf[ni][h] = as_v8i(*reinterpret_cast<const uint4*>(buf + LT_OFF_B + trow * 64 + ((g4 ^ ((trow >> 1) & 3)) << 4)));
+          bsc[ni][h] = (int)(reinterpret_cast<const uint32_t*>(buf + LT_OFF_BS)[trow] >> (8 * g4));
+        }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = wm * 64 + 16 * mi + r16;
+        Frag8 fa;
+        fa.lo = *reinterpret_cast<const uint4*>(buf + r * 128 + ((g4 ^ (r & 7)) << 4));
+        fa.hi = *reinterpret_cast<const uint4*>(buf + r * 128 + (((4 + g4) ^ (r & 7)) << 4));
+        const v8i av = as_v8i(fa);
+        const int sa = (int)(reinterpret_cast<const uint32_t*>(buf + LT_OFF_AS)[r] >> (8 * g4));
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+          for (int h = 0; h < NB; ++h) acc[mi][ni][h] = mfma_f8f4(av, bf[ni][h], acc[mi][ni][h], sa, bsc[ni][h]);
+      }
+    }
+  }
+
+  Tile t;
+  t.g = g;
+  t.m0 = m0 + wm * 64;
+  t.rows = rows;
+  t.row_base = row_base;
+  t.n0 = col0 + wn * 16 * NW;
+  epilogue<4, NW, NB, EPI>(p, t, acc, r16, g4);
+}
+
+template <int EPI>
+static hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t s) {
+  constexpr int NCOL = EPI == EPI_SWIGLU_QUANT ? LT_B / 2 : LT_B;
+  const int n_nt = (a.N + NCOL - 1) / NCOL;
+  int64_t tiles = (int64_t)a.max_mtiles * n_nt;
+  tiles = (tiles + 7) / 8 * 8;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  constexpr size_t smem = (size_t)LT_NBUF * LT_STAGE;
+  static bool attr_set = false;  // per-process, set before the first launch
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mx_gemm_lds_kernel<EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  mx_gemm_lds_kernel<EPI><<<dim3((unsigned)tiles), dim3(256), smem, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int MW, int NW, int EPI>
 static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int NT = 4 * 16 * NW;
@@ -542,7 +778,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int gemm_mtile(int shape) { return shape == GEMM_STREAM16 ? 16 : 64; }
+int gemm_mtile(int shape) { return shape == GEMM_STREAM16 ? 16 : shape == GEMM_TILE128 ? LT_M : 64; }
 
 template <int MW, int NW, int EPI>
 static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
@@ -573,6 +809,13 @@ hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) 
       case EPI_F32: return launch_stream_cfg<4, 2, EPI_F32>(a, s);
       case EPI_F32_QUANT: return launch_stream_cfg<4, 2, EPI_F32_QUANT>(a, s);
       default: return launch_stream_cfg<4, 2, EPI_SWIGLU_QUANT>(a, s);
+    }
+  }
+  if (shape == GEMM_TILE128) {
+    switch (epi) {
+      case EPI_F32: return launch_lds_cfg<EPI_F32>(a, s);
+      case EPI_F32_QUANT: return launch_lds_cfg<EPI_F32_QUANT>(a, s);
+      default: return launch_lds_cfg<EPI_SWIGLU_QUANT>(a, s);
     }
   }
   switch (epi) {
