@@ -76,9 +76,10 @@ struct GemmArgs {
 };
 
 // Kernel configurations: weight streaming with 16 or 64 rows per M-tile (few
-// rows per group: decode), the register-tiled kernel with 64-row tiles, or the
-// LDS-staged kernel with 128 x 128 tiles (many rows per group: prefill).
-enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE64 = 2, GEMM_TILE128 = 3 };
+// rows per group: decode), the register-tiled kernel with 64-row tiles, the
+// LDS-staged kernel with 128 x 128 tiles, or the 512-thread kernel with
+// 128 x 512 tiles (many rows per group: prefill).
+enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE64 = 2, GEMM_TILE128 = 3, GEMM_WIDE = 4 };
 int gemm_mtile(int shape);
 
 // Dense bf16 GEMM (seg[0].a = bf16 [M][K], seg[0].b = bf16 [N][K]) with the
@@ -87,6 +88,11 @@ hipError_t launch_bf16_gemm_quant(const GemmArgs& args, int shape, hipStream_t s
 
 // Launch the grouped/dense MX GEMM with an automatically chosen tile shape.
 hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, int shape, hipStream_t s);
+
+// The 512-thread, 128 x 512 tile kernel for many rows per group (prefill);
+// routed M-tiles are gemm_wide_mtile() rows.  Every K must be a multiple of 128.
+int gemm_wide_mtile();
+hipError_t launch_mx_gemm_wide(const GemmArgs& args, int epilogue, hipStream_t s);
 
 // ---- Combine (combine.hip) --------------------------------------------------
 // y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then

@@ -209,10 +209,10 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
 
   // Kernel shapes: weight streaming when a group has few rows (decode), the
   // register-tiled kernel otherwise.
-  const int dense_shape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_TILE128;
-  const int routed_shape = P <= (int64_t)16 * E ? moe::GEMM_STREAM16 : moe::GEMM_TILE128;
+  const int dense_shape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_WIDE;
+  const int routed_shape = P <= (int64_t)16 * E ? moe::GEMM_STREAM16 : moe::GEMM_WIDE;
   const int mt_dense = moe::gemm_mtile(dense_shape);
-  const int mt_small = moe::gemm_mtile(moe::GEMM_STREAM16), mt_big = moe::gemm_mtile(moe::GEMM_TILE128);
+  const int mt_small = moe::gemm_mtile(moe::GEMM_STREAM16), mt_big = moe::gemm_mtile(moe::GEMM_WIDE);
 
   hipEvent_t const* ev = tr && tr->events ? reinterpret_cast<hipEvent_t const*>(tr->events) : nullptr;
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
@@ -414,7 +414,7 @@ int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* 
   if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MOE_ERR_INVALID_ARG;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))
     return MOE_ERR_INVALID_ARG;
-  const int shape = M <= 16 ? moe::GEMM_STREAM16 : M <= 256 ? moe::GEMM_STREAM64 : moe::GEMM_TILE128;
+  const int shape = M <= 16 ? moe::GEMM_STREAM16 : M <= 256 ? moe::GEMM_STREAM64 : moe::GEMM_WIDE;
   moe::GemmArgs a = {};
   a.nseg = 1;
   a.seg[0] = {a_codes, a_scales, K, b_codes, b_scales, nullptr, nullptr, 0, 0, K};

@@ -30,6 +30,8 @@
 // lanes), so its maximum is a 16-lane xor reduction.
 #include "kernels.hpp"
 #include "mx_device.hpp"
+#include "lds_pipe.hpp"
+#include "gemm_epilogue.hpp"
 
 namespace moe {
 
@@ -53,7 +55,6 @@ __device__ __forceinline__ v8i as_v8i(const uint4& f) {
   return r;
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -70,10 +71,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& f) {
 }
 
 }  // namespace
-
-struct Tile {
-  int g, m0, rows, row_base, n0;
-};
 
 // Map a workgroup to (group, M-tile, N-tile).  Returns false for workgroups
 // past the last M-tile (the grid is sized for the worst case).
@@ -104,63 +101,6 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int wave, int NWC
   }
   t.n0 = nt * NT + wave * NWC;
   return true;
-}
-
-// Write one wave's MW x NW accumulator tiles (16x16 each; NB accumulators per
-// tile for SwiGLU) in the epilogue's form.  Lane (r16, g4) holds column
-// n0 + 16*ni + r16 of rows m0 + 16*mi + 4*g4 + i.
-template <int MW, int NW, int NB, int EPI>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const v4f (&acc)[MW][NW][NB], int r16,
-                                         int g4) {
-  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
-  const bool dense = p.offsets == nullptr;
-#pragma unroll
-  for (int mi = 0; mi < MW; ++mi) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = t.m0 + 16 * mi + 4 * g4 + i;
-      const bool rok = row < t.rows;
-      const int64_t orow = dense ? row : (int64_t)t.row_base + row;
-      if (EPI == EPI_F32 || EPI == EPI_F32_QUANT) {
-        float* crow = p.c + (dense ? (int64_t)t.g * p.c_gstride : 0) + orow * p.ldc;
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni) {
-          const int col = t.n0 + 16 * ni + r16;
-          if (rok && col < p.N) crow[col] = acc[mi][ni][0][i];
-        }
-      }
-      if (EPI == EPI_F32_QUANT || EPI == EPI_SWIGLU_QUANT) {
-        uint8_t* qrow = p.q + (dense ? (int64_t)t.g * p.q_gstride : 0) + orow * p.N;
-        uint8_t* qsrow = p.qs + (dense ? (int64_t)t.g * p.qs_gstride : 0) + orow * (p.N >> 5);
-#pragma unroll
-        for (int b = 0; b < NW / 2; ++b) {
-          float v0, v1;
-          if (SWI) {
-            v0 = silu(acc[mi][2 * b][0][i]) * acc[mi][2 * b][NB - 1][i];
-            v1 = silu(acc[mi][2 * b + 1][0][i]) * acc[mi][2 * b + 1][NB - 1][i];
-            if (p.c != nullptr && rok && t.n0 + 32 * b < p.N) {  // optional fp32 copy of h (tracing)
-              float* crow = p.c + (dense ? (int64_t)t.g * p.c_gstride : 0) + orow * p.ldc;
-              crow[t.n0 + 32 * b + r16] = v0;
-              crow[t.n0 + 32 * b + 16 + r16] = v1;
-            }
-          } else {
-            v0 = acc[mi][2 * b][0][i];
-            v1 = acc[mi][2 * b + 1][0][i];
-          }
-          uint32_t m = max(__float_as_uint(v0) & 0x7fffffffu, __float_as_uint(v1) & 0x7fffffffu);
-          m = group_max_u32<16>(m);
-          const int sc = mx_scale_code<8>(m);
-          const int e = sc - 127;
-          const int cb = t.n0 + 32 * b;
-          if (rok && cb < p.N) {
-            qrow[cb + r16] = (uint8_t)enc_e4m3(v0, e);
-            qrow[cb + 16 + r16] = (uint8_t)enc_e4m3(v1, e);
-            if (r16 == 0) qsrow[cb >> 5] = (uint8_t)sc;
-          }
-        }
-      }
-    }
-  }
 }
 
 template <int MW, int NW, int EPI>
@@ -543,67 +483,6 @@ constexpr int LT_STAGE = LT_OFF_BS + 4 * LT_B;   // bytes per LDS buffer (25600)
 constexpr int LT_NBUF = 3;
 constexpr int LT_LOADS = 7;                       // direct loads per wave per K-step
 
-// Direct global -> LDS loads (16 or 4 bytes per lane; lane l lands at
-// m0 + size * l) and their waits are issued as inline assembly: the compiler's
-// wait-count pass would otherwise treat every in-flight LDS load as aliasing
-// every LDS read and drain the whole pipeline (vmcnt(0)) before each fragment
-// read.  Ordering is kept by hand: wait_vmcnt<N>() after issue, then a barrier.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void gl_lds16(const void* g, const uint8_t* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory");
-}
-__device__ __forceinline__ void gl_lds4(const void* g, const uint8_t* lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr(lds)), "v"(g) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Workgroup barrier that waits only for this wave's LDS operations: the
-// direct loads in flight are governed by wait_vmcnt, so the barrier must not
-// drain them (__syncthreads would wait for vmcnt(0)).
-__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Tile decode shared by the LDS-staged kernels: the flat tile list (group,
-// weight column-tile, M-tile; M fastest) is cut into 8 contiguous chunks, one
-// per XCD (workgroup i runs on XCD i % 8).  False for workgroups past the end.
-__device__ __forceinline__ bool decode_lds_tile(const GemmArgs& p, int ncol, int& g, int& mt, int& nt, int& rows,
-                                                int& row_base) {
-  const int n_nt = (p.N + ncol - 1) / ncol;
-  const bool routed = p.offsets != nullptr;
-  const int mpg = routed ? 0 : (p.M + LT_M - 1) / LT_M;
-  const int total = routed ? p.mtile_start[p.G] * n_nt : p.G * mpg * n_nt;
-  const int per = (total + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
-  if (slot >= per) return false;
-  const int lin = (blockIdx.x & 7) * per + slot;
-  if (lin >= total) return false;
-  if (routed) {
-    int lo = 0, hi = p.G;  // mtile_start[lo]*n_nt <= lin < mtile_start[hi]*n_nt
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.mtile_start[mid] * n_nt <= lin) lo = mid; else hi = mid;
-    }
-    g = lo;
-    const int mte = p.mtile_start[g + 1] - p.mtile_start[g];
-    const int local = lin - p.mtile_start[g] * n_nt;
-    nt = local / mte;
-    mt = local - nt * mte;
-    row_base = p.offsets[g];
-    rows = p.offsets[g + 1] - row_base;
-  } else {
-    g = lin / (mpg * n_nt);
-    const int local = lin - g * mpg * n_nt;
-    nt = local / mpg;
-    mt = local - nt * mpg;
-    row_base = 0;
-    rows = p.M;
-  }
-  return true;
-}
-
 template <int EPI>
 __global__ void __launch_bounds__(256) mx_gemm_lds_kernel(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -620,7 +499,7 @@ __global__ void __launch_bounds__(256) mx_gemm_lds_kernel(const GemmArgs p) {
   // ---- tile decode (XCD-chunked, M-fastest inside an expert)
   const bool routed = p.offsets != nullptr;
   int g, mt, nt, rows, row_base;
-  if (!decode_lds_tile(p, NCOL, g, mt, nt, rows, row_base)) return;
+  if (!decode_lds_tile<LT_M>(p, NCOL, g, mt, nt, rows, row_base)) return;
   const int m0 = mt * LT_M;
   const int col0 = nt * NCOL;
 
@@ -763,7 +642,7 @@ __global__ void __launch_bounds__(256) bf16_gemm_lds_kernel(const GemmArgs p) {
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   int g, mt, nt, rows, row_base;
-  if (!decode_lds_tile(p, LT_B, g, mt, nt, rows, row_base)) return;
+  if (!decode_lds_tile<LT_M>(p, LT_B, g, mt, nt, rows, row_base)) return;
   const int m0 = mt * LT_M;
   const int col0 = nt * LT_B;
   const GemmSeg& sg = p.seg[0];
@@ -897,7 +776,9 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int gemm_mtile(int shape) { return shape == GEMM_STREAM16 ? 16 : shape == GEMM_TILE128 ? LT_M : 64; }
+int gemm_mtile(int shape) {
+  return shape == GEMM_STREAM16 ? 16 : shape == GEMM_TILE128 ? LT_M : shape == GEMM_WIDE ? gemm_wide_mtile() : 64;
+}
 
 template <int MW, int NW, int EPI>
 static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
@@ -917,6 +798,7 @@ hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
 }
 
 hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) {
+  if (shape == GEMM_WIDE) return launch_mx_gemm_wide(a, epi, s);
   if (shape == GEMM_STREAM16) {
     switch (epi) {
       case EPI_F32: return launch_stream_cfg<1, 2, EPI_F32>(a, s);

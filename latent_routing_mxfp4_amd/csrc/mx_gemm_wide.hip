@@ -1,0 +1,244 @@
+// mx_gemm_wide.hip -- grouped / dense MX GEMM for many rows per group
+// (prefill): one 512-thread workgroup per CU owns a 128-row x 512-weight-row
+// tile and streams both operands through a three-stage LDS ring.
+//
+// Why this shape on gfx950.  The expert weights are read from HBM once per
+// (expert, N-tile) and the activations of an expert stay in L2 while its
+// tiles run, so what bounds the loop is the number of bytes each CU keeps in
+// flight (LDS capacity: 160 KB) against the latency of weight misses, and the
+// L2 -> LDS traffic per MFMA.  A 128 x 512 tile moves 48 KB of codes per
+// 128-deep K-step for 16.8 MFLOP -- half the bytes per flop of a 128 x 128
+// tile -- and a 3 x 50.5 KB ring keeps two K-steps (64 KB of weights) in
+// flight per CU.  Eight waves (two per SIMD) compute 64 x 128 each, so one
+// wave's LDS reads and barrier wait overlap the other's MFMAs; every wave
+// reads 16 KB of LDS per 32 MFMAs (about 63 B/clk/CU at the MFMA rate, plus
+// 25 B/clk of staging writes, inside the ~117 B/clk LDS read rate).
+//
+// Loads are direct global -> LDS (inline assembly, waits placed by hand; see
+// lds_pipe.hpp): per K-step each wave issues 2 A-code, 4 B-code, one A-scale
+// (16 lanes) and one B-scale load, and the stage for step ks+2 is issued
+// right after the barrier of step ks.
+//
+// Scale layouts in LDS are permuted so that a lane reads the scale dwords of
+// its four A fragments with one 16-byte read and of its eight B fragments
+// with two; the MFMA takes the scale from bits [7:0], so each dword is
+// shifted right by 8 * (lane / 16).
+//
+// Column mapping.  SwiGLU: the tile's 512 weight rows are 256 gate rows and
+// the 256 matching up rows (h columns col0 .. col0+255); wave (wm, wn) owns h
+// columns col0 + 64 wn .. +63 (fragments 0..3 gate, 4..7 up).  Otherwise the
+// tile is 512 output columns and wave wn owns col0 + 128 wn .. +127.
+#include "gemm_epilogue.hpp"
+#include "kernels.hpp"
+#include "lds_pipe.hpp"
+#include "mx_device.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int WD_M = 128;                        // rows per M-tile
+constexpr int WD_B = 512;                        // weight rows per tile
+constexpr int WD_OFF_B = WD_M * 128;             // A codes: 128 rows x 128 bytes
+constexpr int WD_OFF_AS = WD_OFF_B + WD_B * 64;  // B codes: 512 rows x 64 bytes
+constexpr int WD_OFF_BS = WD_OFF_AS + 4 * WD_M;  // A scales: 128 dwords
+constexpr int WD_STAGE = WD_OFF_BS + 4 * WD_B;   // B scales: 512 dwords -> 51712 bytes
+constexpr int WD_NBUF = 3;
+constexpr int WD_LOADS = 8;  // direct loads per wave per K-step
+
+template <int EPI>
+__global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
+  constexpr int NB = SWI ? 2 : 1;              // accumulators per fragment (gate, up)
+  constexpr int NW = SWI ? 4 : 8;              // output fragments per wave
+  constexpr int NCOL = SWI ? WD_B / 2 : WD_B;  // output columns per tile
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int wm = wave >> 2, wn = wave & 3;
+
+  const bool routed = p.offsets != nullptr;
+  int g, mt, nt, rows, row_base;
+  if (!decode_lds_tile<WD_M>(p, NCOL, g, mt, nt, rows, row_base)) return;
+  const int m0 = mt * WD_M;
+  const int col0 = nt * NCOL;
+
+  auto a_src_row = [&](int trow) -> int64_t {
+    int r = m0 + trow;
+    r = r < rows ? r : rows - 1;
+    const int sr = row_base + r;
+    return routed ? (p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr) : (int64_t)r;
+  };
+  // Tile B row -> (matrix, output column), clamped into [0, N).
+  auto b_col = [&](int brow, int& up) -> int {
+    int c;
+    if (SWI) {
+      up = brow >= NCOL;
+      c = col0 + (brow & (NCOL - 1));
+    } else {
+      up = 0;
+      c = col0 + brow;
+    }
+    return c < p.N ? c : p.N - 1;
+  };
+  // Tile B row of fragment ni (0..7) of wave column wc, lane row r.
+  auto b_row = [&](int wc, int ni, int r) -> int {
+    if (SWI) return (ni < 4 ? 0 : NCOL) + 64 * wc + 16 * (ni & 3) + r;
+    return 128 * wc + 16 * ni + r;
+  };
+
+  // A codes: load i (0..1) of wave w fills LDS [1024*(2w+i), +1024): tile row
+  // 8*(2w+i) + lane/8, physical chunk lane%8 (logical chunk XOR row%8).
+  int64_t a_row[2];
+  int a_chunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (2 * wave + i) + (lane >> 3);
+    a_row[i] = a_src_row(r);
+    a_chunk[i] = (lane & 7) ^ (r & 7);
+  }
+  // B codes: load i (0..3) of wave w fills [OFF_B + 1024*(4w+i), +1024): tile
+  // B row 16*(4w+i) + lane/4, physical chunk lane%4 (logical XOR (row/2)%4).
+  int b_brow[4], b_chunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * (4 * wave + i) + (lane >> 2);
+    b_brow[i] = r;
+    b_chunk[i] = (lane & 3) ^ ((r >> 1) & 3);
+  }
+  // A scales (lanes 0..15 of each wave): dword d = 16w + lane holds tile row
+  // 64*(d/64) + 16*(d%4) + (d/4)%16, so lane (r16, g4) of M-half wm finds its
+  // rows 64wm + 16mi + r16 (mi = 0..3) at dwords 64wm + 4r16 .. +3.
+  const int as_d = 16 * wave + (lane & 15);
+  const int64_t as_row = a_src_row(64 * (as_d >> 6) + 16 * (as_d & 3) + ((as_d >> 2) & 15));
+  // B scales: dword d = 64w + lane holds the B row of fragment d%8, lane row
+  // (d/8)%16 of wave column d/128, so lane (r16, g4) of wave column wn finds
+  // its eight at dwords 128wn + 8r16 .. +7.
+  const int bs_d = 64 * wave + lane;
+  const int bs_brow = b_row(bs_d >> 7, bs_d & 7, (bs_d >> 3) & 15);
+
+  v4f acc[4][NW][NB];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) acc[mi][ni][h] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int sgi = 0; sgi < p.nseg; ++sgi) {
+    const GemmSeg& sg = p.seg[sgi];
+    const int K = sg.K;
+    const int ksteps = K >> 7;
+    const int kb = K >> 5;
+    const uint8_t* ga[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ga[i] = sg.a + a_row[i] * sg.lda + 16 * a_chunk[i];
+    const uint8_t* gb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int up;
+      const int c = b_col(b_brow[i], up);
+      gb[i] = (up ? sg.b2 : sg.b) + (int64_t)g * sg.b_gstride + (int64_t)c * (K >> 1) + 16 * b_chunk[i];
+    }
+    const uint8_t* gas = sg.as + as_row * (sg.lda >> 5);
+    const uint8_t* gbs;
+    {
+      int up;
+      const int c = b_col(bs_brow, up);
+      gbs = (up ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + (int64_t)c * kb;
+    }
+    auto issue = [&](int ks) {
+      uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (2 * wave + i));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 64 * ks, buf + WD_OFF_B + 1024 * (4 * wave + i));
+      if (lane < 16) gl_lds4(gas + 4 * ks, buf + WD_OFF_AS + 64 * wave);
+      gl_lds4(gbs + 4 * ks, buf + WD_OFF_BS + 256 * wave);
+    };
+
+    __syncthreads();  // the previous segment's stages are no longer read
+    issue(0);
+    if (ksteps > 1) issue(1);
+    for (int ks = 0; ks < ksteps; ++ks) {
+      if (ks + 1 < ksteps) wait_vmcnt<WD_LOADS>(); else wait_vmcnt<0>();
+      barrier_lds();
+      if (ks + 2 < ksteps) issue(ks + 2);
+      const uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
+      const int sh = 8 * g4;
+      const uint4 bsd0 = *reinterpret_cast<const uint4*>(buf + WD_OFF_BS + 512 * wn + 32 * r16);
+      const uint4 bsd1 = *reinterpret_cast<const uint4*>(buf + WD_OFF_BS + 512 * wn + 32 * r16 + 16);
+      const uint4 asd = *reinterpret_cast<const uint4*>(buf + WD_OFF_AS + 256 * wm + 16 * r16);
+      const uint32_t bs_all[8] = {bsd0.x, bsd0.y, bsd0.z, bsd0.w, bsd1.x, bsd1.y, bsd1.z, bsd1.w};
+      const uint32_t as_all[4] = {asd.x, asd.y, asd.z, asd.w};
+      v8i bf[8];
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) {
+        const int tr = b_row(wn, ni, r16);
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + WD_OFF_B + tr * 64 + ((g4 ^ ((tr >> 1) & 3)) << 4));
+        bf[ni][0] = (int)v.x; bf[ni][1] = (int)v.y; bf[ni][2] = (int)v.z; bf[ni][3] = (int)v.w;
+        bf[ni][4] = 0; bf[ni][5] = 0; bf[ni][6] = 0; bf[ni][7] = 0;
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = 64 * wm + 16 * mi + r16;
+        const uint4 lo = *reinterpret_cast<const uint4*>(buf + r * 128 + ((g4 ^ (r & 7)) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(buf + r * 128 + (((4 + g4) ^ (r & 7)) << 4));
+        v8i av;
+        av[0] = (int)lo.x; av[1] = (int)lo.y; av[2] = (int)lo.z; av[3] = (int)lo.w;
+        av[4] = (int)hi.x; av[5] = (int)hi.y; av[6] = (int)hi.z; av[7] = (int)hi.w;
+        const int sa = (int)(as_all[mi] >> sh);
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) {
+          const int sb = (int)(bs_all[ni] >> sh);
+          if (SWI) acc[mi][ni & 3][ni >> 2] = mfma_f8f4(av, bf[ni], acc[mi][ni & 3][ni >> 2], sa, sb);
+          else acc[mi][ni][0] = mfma_f8f4(av, bf[ni], acc[mi][ni][0], sa, sb);
+        }
+      }
+    }
+  }
+
+  Tile t;
+  t.g = g;
+  t.m0 = m0 + 64 * wm;
+  t.rows = rows;
+  t.row_base = row_base;
+  t.n0 = SWI ? col0 + 64 * wn : col0 + 128 * wn;
+  epilogue<4, NW, NB, EPI>(p, t, acc, r16, g4);
+}
+
+template <int EPI>
+hipError_t launch_wide_cfg(const GemmArgs& a, hipStream_t s) {
+  constexpr int NCOL = EPI == EPI_SWIGLU_QUANT ? WD_B / 2 : WD_B;
+  const int n_nt = (a.N + NCOL - 1) / NCOL;
+  int64_t tiles = (int64_t)a.max_mtiles * n_nt;
+  tiles = (tiles + 7) / 8 * 8;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  constexpr size_t smem = (size_t)WD_NBUF * WD_STAGE;
+  static bool attr_set = false;  // per process, before the first launch
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mx_gemm_wide_kernel<EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  mx_gemm_wide_kernel<EPI><<<dim3((unsigned)tiles), dim3(512), smem, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_wide_mtile() { return WD_M; }
+
+hipError_t launch_mx_gemm_wide(const GemmArgs& a, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_F32: return launch_wide_cfg<EPI_F32>(a, s);
+    case EPI_F32_QUANT: return launch_wide_cfg<EPI_F32_QUANT>(a, s);
+    default: return launch_wide_cfg<EPI_SWIGLU_QUANT>(a, s);
+  }
+}
+
+}  // namespace moe
