@@ -23,11 +23,25 @@
  * (E4M3, OCP "FN" variant), 32 elements per block sharing one E8M0 scale.
  * The router weight is fp32 and is not quantised.
  *
- * Storage of an MX tensor [rows][K] (blocks run along K, the contraction dim):
+ * Row-major storage of an MX tensor [rows][K] (blocks run along K, the
+ * contraction dim):
  *   E2M1 codes: [rows][K/2] bytes, element 2i in the low nibble of byte i;
  *   E4M3 codes: [rows][K] bytes;
  *   scales:     [rows][K/32] bytes, E8M0 (value 2^(c-127)).
- * Weight matrices are stored [out][in] (nn.Linear orientation).
+ * Weight matrices are [out][in] (nn.Linear orientation).  The weights the MX
+ * GEMMs read are stored in FRAGMENT ORDER instead, which keeps the same bytes
+ * per matrix but puts each operand of one 16x16x128 block-scaled MFMA in one
+ * contiguous 1 KB block (the kernels' hot loops then load whole cache lines
+ * and need no shuffling).  For G matrices [N][K], N % 16 == 0, K % 128 == 0:
+ *   codes:  matrix g starts at g*N*K/2; block (nb, kb) = rows 16nb..16nb+15,
+ *           elements 128kb..128kb+127 sits at (nb*(K/128) + kb)*1024; inside
+ *           it, bytes 16l..16l+15 (l = r + 16q, r < 16, q < 4) are the E2M1
+ *           codes of row 16nb + r, elements 128kb + 32q .. +31 (two per byte,
+ *           even element in the low nibble);
+ *   scales: matrix g starts at g*N*K/32; then [K/128][N] groups of 4 bytes:
+ *           group (kb, n) holds the E8M0 scales of blocks 4kb..4kb+3 of row n.
+ * moe_mx_quantize_weights writes this order; moe_mx_pack_weights converts
+ * row-major E2M1 into it.
  *
  * All tensor pointers are DEVICE pointers unless stated otherwise.  Every
  * call is asynchronous on the given HIP stream (a hipStream_t passed as
@@ -80,9 +94,10 @@ typedef struct {
 
 /* Layer weights.  Non-owning: every buffer must outlive the handle and must
  * not change while a forward that reads it is in flight.  Expert tensors are
- * the E (or S) matrices stored back to back. */
+ * the E (or S) matrices stored back to back.  w_down is row-major; every other
+ * MX tensor is in fragment order (see the top of this file). */
 typedef struct {
-  moe_mx_tensor w_down;            /* [L][d]      latent down-projection        */
+  moe_mx_tensor w_down;            /* [L][d]      latent down-projection (row-major) */
   moe_mx_tensor w_up;              /* [d][L]      latent up-projection          */
   const float* w_router;           /* [E][L] fp32 router                        */
   const float* router_logit_bias;  /* [E] added to the logits, or NULL (zeros)  */
@@ -176,10 +191,26 @@ int moe_layer_destroy(moe_layer_t layer);
 int moe_mx_quantize(const float* in, int64_t rows, int32_t K, int32_t fmt,
                     uint8_t* codes, uint8_t* scales, void* stream);
 
-/* Dense MX GEMM c[M][N] = deq(a) deq(b)^T in fp32, a = E4M3 [M][K],
- * b = E2M1 [N][K] (layout as above), K a positive multiple of 128.  This is the
- * block-scaled matrix-core kernel the layer's projections run on, exposed for
- * stage-level checks. */
+/* MX E2M1 quantisation of G weight matrices in[G*N][K] (fp32, row-major),
+ * written in fragment order (codes G*N*K/2 bytes, scales G*N*K/32 bytes): the
+ * same codes and scales as moe_mx_quantize with fmt 1, permuted.  N must be a
+ * positive multiple of 16 and K of 128; G >= 0.
+ * Errors: MOE_ERR_INVALID_ARG (sizes, null or misaligned pointers: in 16-byte,
+ * codes 2-byte aligned), MOE_ERR_HIP. */
+int moe_mx_quantize_weights(const float* in, int64_t G, int32_t N, int32_t K,
+                            uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Convert G row-major E2M1 matrices (codes [G*N][K/2], scales [G*N][K/32])
+ * into fragment order (out_codes, out_scales; same sizes, must not overlap the
+ * inputs).  N % 16 == 0, K % 128 == 0.  Codes buffers 16-byte aligned, scale
+ * buffers 4-byte aligned.  Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
+int moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t G, int32_t N, int32_t K,
+                        uint8_t* out_codes, uint8_t* out_scales, void* stream);
+
+/* Dense MX GEMM c[M][N] = deq(a) deq(b)^T in fp32, a = E4M3 [M][K] (row-major),
+ * b = E2M1 [N][K] in fragment order, N a positive multiple of 16, K of 128.
+ * This is the block-scaled matrix-core kernel the layer's projections run on,
+ * exposed for stage-level checks. */
 int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                 const uint8_t* b_scales, int32_t M, int32_t N, int32_t K, float* c, void* stream);
 

@@ -27,6 +27,8 @@ EXPORTED = (
     "moe_layer_forward",
     "moe_layer_destroy",
     "moe_mx_quantize",
+    "moe_mx_quantize_weights",
+    "moe_mx_pack_weights",
     "moe_mx_gemm",
 )
 
@@ -103,6 +105,10 @@ def load() -> ctypes.CDLL:
     lib.moe_layer_destroy.argtypes = [vp]
     lib.moe_mx_quantize.restype = ctypes.c_int
     lib.moe_mx_quantize.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.moe_mx_quantize_weights.restype = ctypes.c_int
+    lib.moe_mx_quantize_weights.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.moe_mx_pack_weights.restype = ctypes.c_int
+    lib.moe_mx_pack_weights.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
     lib.moe_mx_gemm.restype = ctypes.c_int
     lib.moe_mx_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     _lib = lib
@@ -142,6 +148,17 @@ def moe_layer_destroy(handle: int) -> None:
 
 def moe_mx_quantize(src: int, rows: int, K: int, fmt: int, codes: int, scales: int, stream: int = 0) -> None:
     _check(load().moe_mx_quantize(src, int(rows), int(K), int(fmt), codes, scales, stream), "moe_mx_quantize")
+
+
+def moe_mx_quantize_weights(src: int, G: int, N: int, K: int, codes: int, scales: int, stream: int = 0) -> None:
+    _check(load().moe_mx_quantize_weights(src, int(G), int(N), int(K), codes, scales, stream),
+           "moe_mx_quantize_weights")
+
+
+def moe_mx_pack_weights(codes: int, scales: int, G: int, N: int, K: int, out_codes: int, out_scales: int,
+                        stream: int = 0) -> None:
+    _check(load().moe_mx_pack_weights(codes, scales, int(G), int(N), int(K), out_codes, out_scales, stream),
+           "moe_mx_pack_weights")
 
 
 def moe_mx_gemm(a_codes: int, a_scales: int, b_codes: int, b_scales: int, M: int, N: int, K: int, c: int,

@@ -7,10 +7,24 @@
 namespace moe {
 
 // ---- MX quantisation (mx_quant.hip) -----------------------------------------
-// fmt 0: E4M3 codes [rows][K]; fmt 1: E2M1 packed codes [rows][K/2].
+// fmt 0: E4M3 codes [rows][K]; fmt 1: E2M1 packed codes [rows][K/2] (row-major),
+// or, with frag_rows = N > 0, in fragment order for rows/N matrices of N rows.
 // deq_bf16 (E4M3 only, may be null): bf16 [rows][K] of the dequantised values.
+//
+// Fragment order (every weight matrix the MX GEMMs read), for G matrices
+// [N][K] with N % 16 == 0 and K % 128 == 0:
+//   codes:  per matrix, 1024-byte blocks (nb, kb) at (nb * K/128 + kb) * 1024,
+//           nb = row / 16, kb = k / 128; inside, lane l = r + 16 q holds 16
+//           bytes at 16 l: row 16 nb + r, elements 128 kb + 32 q .. +31, two per
+//           byte, even element low -- the B operand of one 16x16x128 MFMA.
+//   scales: per matrix, [K/128][N] dwords: the four E8M0 scales of row n for
+//           K-step kb (byte j = block 4 kb + j).
+// A matrix's codes and scales are N*K/2 and N*K/32 bytes, as in row-major.
 hipError_t launch_quantize(const float* in, int64_t rows, int K, int fmt, uint8_t* codes,
-                           uint8_t* scales, hipStream_t s, uint16_t* deq_bf16 = nullptr);
+                           uint8_t* scales, hipStream_t s, uint16_t* deq_bf16 = nullptr, int frag_rows = 0);
+// Row-major E2M1 codes [G*N][K/2] + scales [G*N][K/32] -> fragment order.
+hipError_t launch_pack_e2m1(const uint8_t* codes, const uint8_t* scales, int64_t G, int N, int K,
+                            uint8_t* out_codes, uint8_t* out_scales, hipStream_t s);
 // E2M1 packed [rows][K/2] + scales [rows][K/32] -> exact bf16 [rows][K].
 hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
                                    uint16_t* out, hipStream_t s);
@@ -76,10 +90,10 @@ struct GemmArgs {
 };
 
 // Kernel configurations: weight streaming with 16 or 64 rows per M-tile (few
-// rows per group: decode), the register-tiled kernel with 64-row tiles, the
-// LDS-staged kernel with 128 x 128 tiles, or the 512-thread kernel with
-// 128 x 512 tiles (many rows per group: prefill).
-enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE64 = 2, GEMM_TILE128 = 3, GEMM_WIDE = 4 };
+// rows per group: decode), the 512-thread kernel with 128 x 512 tiles (many
+// rows per group: prefill), and the 128 x 128 LDS-staged bf16 kernel of the
+// latent down-projection (GEMM_TILE128, bf16 only).
+enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE128 = 3, GEMM_WIDE = 4 };
 int gemm_mtile(int shape);
 
 // Dense bf16 GEMM (seg[0].a = bf16 [M][K], seg[0].b = bf16 [N][K]) with the

@@ -407,9 +407,35 @@ int moe_mx_quantize(const float* in, int64_t rows, int32_t K, int32_t fmt, uint8
   return MOE_OK;
 }
 
+int moe_mx_quantize_weights(const float* in, int64_t G, int32_t N, int32_t K, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+  if (G < 0 || N <= 0 || N % 16 || K <= 0 || K % 128) return MOE_ERR_INVALID_ARG;
+  if (G == 0) return MOE_OK;
+  if (!in || !codes || !scales || !aligned(in, 16) || !aligned(codes, 2)) return MOE_ERR_INVALID_ARG;
+  if (G > ((int64_t)1 << 40) / ((int64_t)N * K)) return MOE_ERR_INVALID_ARG;
+  if (moe::launch_quantize(in, G * N, K, 1, codes, scales, static_cast<hipStream_t>(stream), nullptr, N) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t G, int32_t N, int32_t K,
+                        uint8_t* out_codes, uint8_t* out_scales, void* stream) {
+  if (G < 0 || N <= 0 || N % 16 || K <= 0 || K % 128) return MOE_ERR_INVALID_ARG;
+  if (G == 0) return MOE_OK;
+  if (!codes || !scales || !out_codes || !out_scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned(codes, 16) || !aligned(out_codes, 16) || !aligned(scales, 4) || !aligned(out_scales, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (G > ((int64_t)1 << 40) / ((int64_t)N * K)) return MOE_ERR_INVALID_ARG;
+  if (moe::launch_pack_e2m1(codes, scales, G, N, K, out_codes, out_scales, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
                 int32_t M, int32_t N, int32_t K, float* c, void* stream) {
-  if (M < 0 || N < 0 || K <= 0 || K % 128) return MOE_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || N % 16 || K <= 0 || K % 128) return MOE_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return MOE_OK;
   if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return MOE_ERR_INVALID_ARG;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4))

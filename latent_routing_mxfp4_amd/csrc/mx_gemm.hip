@@ -6,7 +6,7 @@
 // as stored, never expanded to a wider copy (Kimi K3 open-weights serving,
 // section "Native MXFP4": kernels should consume that representation).
 //
-// The same kernel runs
+// The MX kernels run
 //   * the routed experts as one grouped GEMM over ragged, runtime-sized
 //     segments (Four Bits at a Time, "What has to change in the serving
 //     stacks": up to 896 runtime-sized groups per layer) -- the group of an
@@ -14,20 +14,11 @@
 //     nothing is read back to the host;
 //   * the dense projections (latent down/up) and the shared experts.
 //
-// Work decomposition: a workgroup of 4 waves owns an (MT x NT) output tile;
-// the waves split the N columns, each wave computes MT x (16*NW) with
-// MW x NW 16x16 MFMA tiles (two accumulators per tile for SwiGLU: gate and
-// up).  Operands go straight from global memory into the MFMA register
-// layout, one 16-byte load per lane per E2M1 fragment, two per E4M3 fragment
-// (the two K halves the E4M3 operand layout interleaves),
-// one dword of 4 block scales per row per K-step.  The K loop is software
-// pipelined one K-step deep.
-//
-// Epilogues: fp32 store; fp32 store plus MXFP8 quantisation along N; or
-// h = SiLU(gate) * up quantised to MXFP8 (the expert hidden state; h itself is
-// also stored in fp32 when an output pointer is given, for tracing), where the
-// 32-column block of a row sits in one wave (two adjacent 16-column tiles x 16
-// lanes), so its maximum is a 16-lane xor reduction.
+// Kernels here: the weight-streaming MX GEMM for few rows per group (decode),
+// and the bf16 GEMMs (register-tiled and LDS-staged) of the dense latent
+// down-projection.  The prefill-shaped MX GEMM is in mx_gemm_wide.hip and the
+// epilogues shared by all of them in gemm_epilogue.hpp.  MX weights are read
+// in fragment order (kernels.hpp).
 #include "kernels.hpp"
 #include "mx_device.hpp"
 #include "lds_pipe.hpp"
@@ -101,120 +92,6 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int wave, int NWC
   }
   t.n0 = nt * NT + wave * NWC;
   return true;
-}
-
-template <int MW, int NW, int EPI>
-__global__ void __launch_bounds__(256) mx_gemm_kernel(const GemmArgs p) {
-  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
-  constexpr int NB = SWI ? 2 : 1;
-  constexpr int MT = 16 * MW;
-  constexpr int NT = 4 * 16 * NW;
-  static_assert(EPI == EPI_F32 || NW % 2 == 0, "quantising epilogues need whole 32-column blocks per wave");
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
-  Tile t;
-  if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;
-
-  // Rows of A this lane feeds (clamped into the group; results of clamped rows are dropped).
-  int64_t arow[MW];
-#pragma unroll
-  for (int mi = 0; mi < MW; ++mi) {
-    int r = t.m0 + 16 * mi + r16;
-    r = r < t.rows ? r : t.rows - 1;
-    int sr = t.row_base + r;
-    if (p.offsets) arow[mi] = p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr;
-    else arow[mi] = r;
-  }
-  int bcol[NW];
-#pragma unroll
-  for (int ni = 0; ni < NW; ++ni) {
-    int c = t.n0 + 16 * ni + r16;
-    bcol[ni] = c < p.N ? c : p.N - 1;
-  }
-
-  v4f acc[MW][NW][NB];
-#pragma unroll
-  for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-      for (int h = 0; h < NB; ++h) acc[mi][ni][h] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int s = 0; s < p.nseg; ++s) {
-    const GemmSeg& sg = p.seg[s];
-    const int K = sg.K;
-    const int ksteps = K >> 7;
-    const int64_t lds = sg.lda >> 5;
-    const uint8_t* ap[MW];
-    const uint32_t* asp[MW];
-#pragma unroll
-    for (int mi = 0; mi < MW; ++mi) {
-      ap[mi] = sg.a + arow[mi] * sg.lda + 16 * g4;
-      asp[mi] = reinterpret_cast<const uint32_t*>(sg.as + arow[mi] * lds);
-    }
-    const uint8_t* bp[NW][NB];
-    const uint32_t* bsp[NW][NB];
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni) {
-#pragma unroll
-      for (int h = 0; h < NB; ++h) {
-        const uint8_t* bb = h == 0 ? sg.b : sg.b2;
-        const uint8_t* bbs = h == 0 ? sg.bs : sg.b2s;
-        bp[ni][h] = bb + (int64_t)t.g * sg.b_gstride + (int64_t)bcol[ni] * (K >> 1) + 16 * g4;
-        bsp[ni][h] =
-            reinterpret_cast<const uint32_t*>(bbs + (int64_t)t.g * sg.bs_gstride + (int64_t)bcol[ni] * (K >> 5));
-      }
-    }
-
-    Frag8 fa[MW];
-    uint32_t sa[MW];
-    uint4 fb[NW][NB];
-    uint32_t sb[NW][NB];
-    auto load = [&](int ks) {
-#pragma unroll
-      for (int mi = 0; mi < MW; ++mi) {
-        const uint8_t* q = ap[mi] + 128 * ks;  // K [16g, +16) and [64+16g, +16) of this K-step
-        fa[mi].lo = *reinterpret_cast<const uint4*>(q);
-        fa[mi].hi = *reinterpret_cast<const uint4*>(q + 64);
-        sa[mi] = asp[mi][ks] >> (8 * g4);
-      }
-#pragma unroll
-      for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-        for (int h = 0; h < NB; ++h) {
-          fb[ni][h] = *reinterpret_cast<const uint4*>(bp[ni][h] + 64 * ks);
-          sb[ni][h] = bsp[ni][h][ks] >> (8 * g4);
-        }
-    };
-
-    load(0);
-    for (int ks = 0; ks < ksteps; ++ks) {
-      Frag8 ca[MW];
-      uint32_t csa[MW];
-      uint4 cb[NW][NB];
-      uint32_t csb[NW][NB];
-#pragma unroll
-      for (int mi = 0; mi < MW; ++mi) { ca[mi] = fa[mi]; csa[mi] = sa[mi]; }
-#pragma unroll
-      for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-        for (int h = 0; h < NB; ++h) { cb[ni][h] = fb[ni][h]; csb[ni][h] = sb[ni][h]; }
-      if (ks + 1 < ksteps) load(ks + 1);
-#pragma unroll
-      for (int mi = 0; mi < MW; ++mi) {
-        const v8i av = as_v8i(ca[mi]);
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-          for (int h = 0; h < NB; ++h)
-            acc[mi][ni][h] = mfma_f8f4(av, as_v8i(cb[ni][h]), acc[mi][ni][h], (int)csa[mi], (int)csb[ni][h]);
-      }
-    }
-  }
-  epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
 // Dense bf16 GEMM on exactly decoded MX operands (v_mfma_f32_16x16x32_bf16):
@@ -297,22 +174,15 @@ __global__ void __launch_bounds__(256) bf16_gemm_kernel(const GemmArgs p) {
 }
 
 // Weight-streaming variant for few rows per group (decode).  The weights are
-// read exactly once, so the kernel is HBM-bound and its loads are shaped for
-// that:
-//  * codes: per 256-wide K super-step each lane reads 32 contiguous bytes of its
-//    weight row, and the four lane groups of a wave together read the row's
-//    whole 128-byte line in one pass (a half-line read and its other half
-//    issued one step later get evicted in between and fetched twice);
-//  * scales: the workgroup copies its tile's E8M0 rows (contiguous in memory)
-//    into LDS once per K segment, instead of touching each 128-byte scale line
-//    once per K-step.
-// The two 32-element blocks a lane loads per super-step feed two MFMAs (u = 0,
-// 1); in MFMA u lane group g holds physical block 8s + 2g + u, and the E4M3
-// operand gathers the matching K values in its split-half layout.  A K tail of
-// 128 uses the plain one-step layout.
+// read exactly once, so the kernel is HBM-bound.  A workgroup of 4 waves owns
+// MT x NT outputs (each wave 16*NW weight rows); per 128-deep K-step a wave
+// loads, for each of its weight fragments, the fragment-order block of codes
+// (1 KB contiguous; lane l takes its 16-byte MFMA operand at 16 l, read
+// non-temporally) and the 64 contiguous scale bytes of the block's 16 rows,
+// one K-step ahead of the MFMAs.  The few activation rows (L2-resident) are
+// read in the E4M3 operand layout straight from global memory.
 template <int MW, int NW, int EPI>
 __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
-  extern __shared__ uint8_t bscale_lds[];  // [NB][NT rows][K/32]
   constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
   constexpr int NB = SWI ? 2 : 1;
   constexpr int MT = 16 * MW;
@@ -326,7 +196,6 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   const int g4 = lane >> 4;
   Tile t;
   if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;  // uniform across the workgroup
-  const int tile_n0 = t.n0 - wave * 16 * NW;
 
   int64_t arow[MW];
 #pragma unroll
@@ -337,13 +206,14 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
     if (p.offsets) arow[mi] = p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr;
     else arow[mi] = r;
   }
-  int bcol[NW];
+  // First weight row of fragment ni, clamped so that its 16-row block lies in
+  // [0, N) (N % 16 == 0); rows past N are computed on repeated data, never stored.
+  int fcol[NW];
 #pragma unroll
   for (int ni = 0; ni < NW; ++ni) {
-    int c = t.n0 + 16 * ni + r16;
-    bcol[ni] = c < p.N ? c : p.N - 1;
+    const int c = t.n0 + 16 * ni;
+    fcol[ni] = c < p.N - 16 ? c : p.N - 16;
   }
-  const int nrows = min(NT, p.N - tile_n0);
 
   v4f acc[MW][NW][NB];
 #pragma unroll
@@ -356,277 +226,81 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   for (int s = 0; s < p.nseg; ++s) {
     const GemmSeg& sg = p.seg[s];
     const int K = sg.K;
-    const int kb = K >> 5;  // scale bytes per row (multiple of 4)
-    // ---- stage this tile's B scales in LDS
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < NB; ++h) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>((h == 0 ? sg.bs : sg.b2s) +
-                                                              (int64_t)t.g * sg.bs_gstride + (int64_t)tile_n0 * kb);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(bscale_lds + h * NT * kb);
-      const int nw = nrows * kb / 4;
-      for (int i = tid; i < nw; i += 256) dst[i] = src[i];
-    }
-    __syncthreads();
-
+    const int nks = K >> 7;
+    const int kb = K >> 5;
     const uint8_t* ap[MW];
     const uint8_t* asp[MW];
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi) {
-      ap[mi] = sg.a + arow[mi] * sg.lda;
-      asp[mi] = sg.as + arow[mi] * kb;
+      ap[mi] = sg.a + arow[mi] * sg.lda + 16 * g4;
+      asp[mi] = sg.as + arow[mi] * kb + g4;
     }
     const uint8_t* bp[NW][NB];
-    const uint8_t* bsl[NW][NB];
+    const uint8_t* bsp[NW][NB];
 #pragma unroll
     for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
       for (int h = 0; h < NB; ++h) {
-        bp[ni][h] = (h == 0 ? sg.b : sg.b2) + (int64_t)t.g * sg.b_gstride + (int64_t)bcol[ni] * (K >> 1);
-        const int lr = min(wave * 16 * NW + 16 * ni + r16, nrows - 1);
-        bsl[ni][h] = bscale_lds + h * NT * kb + lr * kb;
+        bp[ni][h] = (h == 0 ? sg.b : sg.b2) + (int64_t)t.g * sg.b_gstride + (int64_t)(fcol[ni] >> 4) * nks * 1024 +
+                    16 * lane;
+        bsp[ni][h] = (h == 0 ? sg.bs : sg.b2s) + (int64_t)t.g * sg.bs_gstride + 4 * (int64_t)(fcol[ni] + r16) + g4;
       }
+    const int64_t bs_k = 4 * (int64_t)p.N;  // bytes between K-steps of the scales
 
-    const int nsup = K >> 8;
-    const int a_off = 32 * (2 * (g4 >> 1)) + 16 * (g4 & 1);   // + 32u, second half at +128
-    uint4 fb[NW][NB][2];
-    auto load_b = [&](int ss) {
+    uint4 fb[NW][NB];
+    int fs[NW][NB];
+    auto load_b = [&](int ks) {
 #pragma unroll
       for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
         for (int h = 0; h < NB; ++h) {
-          const u32x4* q = reinterpret_cast<const u32x4*>(bp[ni][h] + 128 * ss + 32 * g4);
-          fb[ni][h][0] = to_uint4(__builtin_nontemporal_load(q));
-          fb[ni][h][1] = to_uint4(__builtin_nontemporal_load(q + 1));
+          fb[ni][h] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni][h] + 1024 * ks)));
+          fs[ni][h] = bsp[ni][h][bs_k * ks];
         }
     };
-    if (nsup > 0) load_b(0);
-    for (int ss = 0; ss < nsup; ++ss) {
-      uint4 cb[NW][NB][2];
+    load_b(0);
+    for (int ks = 0; ks < nks; ++ks) {
+      uint4 cb[NW][NB];
+      int cs[NW][NB];
 #pragma unroll
       for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
-        for (int h = 0; h < NB; ++h) { cb[ni][h][0] = fb[ni][h][0]; cb[ni][h][1] = fb[ni][h][1]; }
-      if (ss + 1 < nsup) load_b(ss + 1);
-      uint32_t sbw[NW][NB];
-#pragma unroll
-      for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-        for (int h = 0; h < NB; ++h) sbw[ni][h] = *reinterpret_cast<const uint16_t*>(bsl[ni][h] + 8 * ss + 2 * g4);
-#pragma unroll
-      for (int mi = 0; mi < MW; ++mi) {
-        const uint32_t saw = *reinterpret_cast<const uint16_t*>(asp[mi] + 8 * ss + 2 * g4);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint8_t* q = ap[mi] + 256 * ss + a_off + 32 * u;
-          Frag8 fa;
-          fa.lo = *reinterpret_cast<const uint4*>(q);
-          fa.hi = *reinterpret_cast<const uint4*>(q + 128);
-          const v8i av = as_v8i(fa);
-          const int sa = (int)(saw >> (8 * u));
-#pragma unroll
-          for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-            for (int h = 0; h < NB; ++h)
-              acc[mi][ni][h] = mfma_f8f4(av, as_v8i(cb[ni][h][u]), acc[mi][ni][h], sa, (int)(sbw[ni][h] >> (8 * u)));
+        for (int h = 0; h < NB; ++h) {
+          cb[ni][h] = fb[ni][h];
+          cs[ni][h] = fs[ni][h];
         }
-      }
-    }
-    if (K & 255) {  // one 128-wide K-step left: plain layout
-      const int kl = (K >> 7) - 1;
+      if (ks + 1 < nks) load_b(ks + 1);
 #pragma unroll
       for (int mi = 0; mi < MW; ++mi) {
-        const uint8_t* q = ap[mi] + 128 * kl + 16 * g4;
+        const uint8_t* q = ap[mi] + 128 * ks;
         Frag8 fa;
         fa.lo = *reinterpret_cast<const uint4*>(q);
         fa.hi = *reinterpret_cast<const uint4*>(q + 64);
         const v8i av = as_v8i(fa);
-        const int sa = asp[mi][4 * kl + g4];
+        const int sa = asp[mi][4 * ks];
 #pragma unroll
         for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
-          for (int h = 0; h < NB; ++h) {
-            const uint4 fbt = *reinterpret_cast<const uint4*>(bp[ni][h] + 64 * kl + 16 * g4);
-            acc[mi][ni][h] = mfma_f8f4(av, as_v8i(fbt), acc[mi][ni][h], sa, (int)bsl[ni][h][4 * kl + g4]);
-          }
+          for (int h = 0; h < NB; ++h) acc[mi][ni][h] = mfma_f8f4(av, as_v8i(cb[ni][h]), acc[mi][ni][h], sa, cs[ni][h]);
       }
     }
   }
   epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
-// LDS-staged tiled variant (many rows per group: prefill).  A workgroup owns
-// a 128-row x 128-weight-row tile (for SwiGLU: 64 gate + the matching 64 up
-// rows, i.e. 64 output columns); its 4 waves form a 2 x 2 grid, each computing
-// 64 rows x 64 weight rows with 16 MFMAs per 128-wide K-step.
-//
-// Operands move global -> LDS with gfx950's direct loads (global_load_lds,
-// 16 bytes per lane, no staging registers) through a 3-buffer ring: while the
-// MFMAs consume K-step k, the loads of k+1 and k+2 are in flight.  A wave
-// issues 7 loads per K-step (4 for A, 2 for B, 1 for the scales), so
-// "vmcnt <= 7" means step k has landed.  A lane's LDS slot is fixed by the
-// hardware (base + 16 * lane), so each lane fetches whichever global chunk
-// belongs in that slot; the LDS rows are XOR-swizzled by 16-byte chunk so the
-// 16 rows a fragment read touches fall on distinct banks.  The routed gate/up
-// GEMM gathers its A rows through the permutation in these loads.
-//
-// Tile order: the flat tile list is cut into 8 contiguous chunks, one per XCD
-// (workgroup i runs on XCD i % 8), so an expert's tiles share one L2; inside
-// an expert the M-tiles of one weight column-tile are consecutive, so each
-// weight tile is fetched from HBM once and reused from L2.
-constexpr int LT_M = 128;   // rows per tile
-constexpr int LT_B = 128;   // weight rows per tile
-constexpr int LT_OFF_B = LT_M * 128;
-constexpr int LT_OFF_AS = LT_OFF_B + LT_B * 64;
-constexpr int LT_OFF_BS = LT_OFF_AS + 4 * LT_M;
-constexpr int LT_STAGE = LT_OFF_BS + 4 * LT_B;   // bytes per LDS buffer (25600)
-constexpr int LT_NBUF = 3;
-constexpr int LT_LOADS = 7;                       // direct loads per wave per K-step
-
-template <int EPI>
-__global__ void __launch_bounds__(256) mx_gemm_lds_kernel(const GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
-  constexpr int NB = SWI ? 2 : 1;
-  constexpr int NCOL = SWI ? LT_B / 2 : LT_B;       // output columns per tile
-  constexpr int NW = SWI ? 2 : 4;                     // 16-col fragments per wave (per matrix)
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // ---- tile decode (XCD-chunked, M-fastest inside an expert)
-  const bool routed = p.offsets != nullptr;
-  int g, mt, nt, rows, row_base;
-  if (!decode_lds_tile<LT_M>(p, NCOL, g, mt, nt, rows, row_base)) return;
-  const int m0 = mt * LT_M;
-  const int col0 = nt * NCOL;
-
-  // ---- what this lane loads.  A: load i (0..3) fills LDS bytes [1024*(4*wave+i), +1024):
-  // tile row 32*wave + 8*i + lane/8, physical chunk lane%8.  B: load i (0..1) fills
-  // [OFF_B + 1024*(2*wave+i), +1024): tile row 32*wave + 16*i + lane/4, physical
-  // chunk lane%4.  Scales: wave w fills dwords [64w, 64w+64) of the A|B scale columns.
-  auto a_src_row = [&](int trow) -> int64_t {
-    int r = m0 + trow;
-    r = r < rows ? r : rows - 1;
-    const int sr = row_base + r;
-    return routed ? (p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr) : (int64_t)r;
-  };
-  auto b_col = [&](int trow, int& h) {
-    int c;
-    if (SWI) { h = trow >= NCOL; c = col0 + (trow - h * NCOL); }
-    else { h = 0; c = col0 + trow; }
-    return c < p.N ? c : p.N - 1;
-  };
-  int64_t a_row[4];
-  int a_chunk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 32 * wave + 8 * i + (lane >> 3);
-    a_row[i] = a_src_row(r);
-    a_chunk[i] = (lane & 7) ^ (r & 7);
-  }
-  int b_trow[2], b_chunk[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 32 * wave + 16 * i + (lane >> 2);
-    b_trow[i] = r;
-    b_chunk[i] = (lane & 3) ^ ((r >> 1) & 3);
-  }
-  const int s_trow = 64 * (wave & 1) + lane;        // tile row of this lane's scale dword
-  const int64_t s_arow = wave < 2 ? a_src_row(s_trow) : 0;
-
-  v4f acc[4][NW][NB];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-      for (int h = 0; h < NB; ++h) acc[mi][ni][h] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int sgi = 0; sgi < p.nseg; ++sgi) {
-    const GemmSeg& sg = p.seg[sgi];
-    const int K = sg.K;
-    const int ksteps = K >> 7;
-    const int kb = K >> 5;
-    const uint8_t* ga[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ga[i] = sg.a + a_row[i] * sg.lda + 16 * a_chunk[i];
-    const uint8_t* gb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int h;
-      const int c = b_col(b_trow[i], h);
-      gb[i] = (h ? sg.b2 : sg.b) + (int64_t)g * sg.b_gstride + (int64_t)c * (K >> 1) + 16 * b_chunk[i];
-    }
-    const uint8_t* gs;
-    if (wave < 2) {
-      gs = sg.as + s_arow * kb;
-    } else {
-      int h;
-      const int c = b_col(s_trow, h);
-      gs = (h ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + (int64_t)c * kb;
-    }
-    auto issue = [&](int ks) {
-      uint8_t* buf = lds + (ks % LT_NBUF) * LT_STAGE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (4 * wave + i));
-#pragma unroll
-      for (int i = 0; i < 2; ++i) gl_lds16(gb[i] + 64 * ks, buf + LT_OFF_B + 1024 * (2 * wave + i));
-      gl_lds4(gs + 4 * ks, buf + LT_OFF_AS + 256 * wave);
-    };
-
-    __syncthreads();  // the previous segment's buffers are no longer read
-    issue(0);
-    if (ksteps > 1) issue(1);
-    for (int ks = 0; ks < ksteps; ++ks) {
-      if (ks + 1 < ksteps) wait_vmcnt<LT_LOADS>(); else wait_vmcnt<0>();
-      barrier_lds();
-      if (ks + 2 < ksteps) issue(ks + 2);
-      const uint8_t* buf = lds + (ks % LT_NBUF) * LT_STAGE;
-      v8i bf[NW][NB];
-      int bsc[NW][NB];
-#pragma unroll
-      for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-        for (int h = 0; h < NB; ++h) {
-          const int trow = SWI ? (h * NCOL + wn * 32 + 16 * ni + r16) : (wn * 64 + 16 * ni + r16);
-          bf[ni][h] = as_v8i(*reinterpret_cast<const uint4*>(buf + LT_OFF_B + trow * 64 + ((g4 ^ ((trow >> 1) & 3)) << 4)));
-          bsc[ni][h] = (int)(reinterpret_cast<const uint32_t*>(buf + LT_OFF_BS)[trow] >> (8 * g4));
-        }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int r = wm * 64 + 16 * mi + r16;
-        Frag8 fa;
-        fa.lo = *reinterpret_cast<const uint4*>(buf + r * 128 + ((g4 ^ (r & 7)) << 4));
-        fa.hi = *reinterpret_cast<const uint4*>(buf + r * 128 + (((4 + g4) ^ (r & 7)) << 4));
-        const v8i av = as_v8i(fa);
-        const int sa = (int)(reinterpret_cast<const uint32_t*>(buf + LT_OFF_AS)[r] >> (8 * g4));
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-          for (int h = 0; h < NB; ++h) acc[mi][ni][h] = mfma_f8f4(av, bf[ni][h], acc[mi][ni][h], sa, bsc[ni][h]);
-      }
-    }
-  }
-
-  Tile t;
-  t.g = g;
-  t.m0 = m0 + wm * 64;
-  t.rows = rows;
-  t.row_base = row_base;
-  t.n0 = col0 + wn * 16 * NW;
-  epilogue<4, NW, NB, EPI>(p, t, acc, r16, g4);
-}
-
-// bf16 twin of the LDS-staged kernel for the dense latent down-projection
-// (A = bf16 [M][K], B = bf16 [N][K], exact images of the MX operands).  Same
-// 128 x 128 tile and 2 x 2 waves; a K-step is 64 elements (128 bytes per row
-// for both operands), consumed as two 16x16x32 bf16 MFMAs per fragment pair
-// (slice u takes chunk 4u + g of the row for lane group g, identically in A
-// and B).  bf16 does half the MACs per staged byte of the MX path, so the ring
-// has four 32 KB buffers (three K-steps in flight).
+// LDS-staged bf16 GEMM for the dense latent down-projection (A = bf16 [M][K],
+// B = bf16 [N][K], exact images of the MX operands).  A workgroup owns a
+// 128 x 128 tile; its 4 waves form a 2 x 2 grid of 64 x 64.  Operands move
+// global -> LDS with gfx950's direct loads (16 bytes per lane, no staging
+// registers) through a ring of four 32 KB buffers (three K-steps in flight);
+// a lane's LDS slot is fixed by the hardware (base + 16 * lane), so each lane
+// fetches whichever global chunk belongs there, and rows are XOR-swizzled by
+// 16-byte chunk so a fragment read hits distinct banks.  A K-step is 64
+// elements (128 bytes per row for both operands), consumed as two 16x16x32
+// bf16 MFMAs per fragment pair (slice u takes chunk 4u + g of the row for lane
+// group g, identically in A and B).  Tiles are ordered XCD-aware (lds_pipe.hpp).
+constexpr int LT_M = 128;  // rows per tile
+constexpr int LT_B = 128;  // weight rows per tile
 constexpr int LB_STAGE = LT_M * 128 + LT_B * 128;
 constexpr int LB_NBUF = 4;
 constexpr int LB_LOADS = 8;
@@ -729,55 +403,20 @@ static hipError_t launch_bf16_lds_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI>
-static hipError_t launch_lds_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int NCOL = EPI == EPI_SWIGLU_QUANT ? LT_B / 2 : LT_B;
-  const int n_nt = (a.N + NCOL - 1) / NCOL;
-  int64_t tiles = (int64_t)a.max_mtiles * n_nt;
-  tiles = (tiles + 7) / 8 * 8;
-  if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  constexpr size_t smem = (size_t)LT_NBUF * LT_STAGE;
-  static bool attr_set = false;  // per-process, set before the first launch
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mx_gemm_lds_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  mx_gemm_lds_kernel<EPI><<<dim3((unsigned)tiles), dim3(256), smem, s>>>(a);
-  return hipGetLastError();
-}
-
 template <int MW, int NW, int EPI>
 static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int NT = 4 * 16 * NW;
-  constexpr int NB = EPI == EPI_SWIGLU_QUANT ? 2 : 1;
+  if (a.N % 16 != 0) return hipErrorInvalidValue;  // fragment-order weights
   const int n_ntiles = (a.N + NT - 1) / NT;
   const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  int kb = 0;
-  for (int i = 0; i < a.nseg; ++i) kb = max(kb, a.seg[i].K >> 5);
-  const size_t smem = (size_t)NB * NT * kb;
-  if (smem > 65536) return hipErrorInvalidValue;
-  mx_gemm_stream_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), smem, s>>>(a);
-  return hipGetLastError();
-}
-
-template <int MW, int NW, int EPI>
-static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int NT = 4 * 16 * NW;
-  const int n_ntiles = (a.N + NT - 1) / NT;
-  const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  mx_gemm_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  mx_gemm_stream_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
 int gemm_mtile(int shape) {
-  return shape == GEMM_STREAM16 ? 16 : shape == GEMM_TILE128 ? LT_M : shape == GEMM_WIDE ? gemm_wide_mtile() : 64;
+  return shape == GEMM_STREAM16 ? 16 : shape == GEMM_STREAM64 ? 64 : shape == GEMM_WIDE ? gemm_wide_mtile() : LT_M;
 }
 
 template <int MW, int NW, int EPI>
@@ -813,18 +452,7 @@ hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) 
       default: return launch_stream_cfg<4, 2, EPI_SWIGLU_QUANT>(a, s);
     }
   }
-  if (shape == GEMM_TILE128) {
-    switch (epi) {
-      case EPI_F32: return launch_lds_cfg<EPI_F32>(a, s);
-      case EPI_F32_QUANT: return launch_lds_cfg<EPI_F32_QUANT>(a, s);
-      default: return launch_lds_cfg<EPI_SWIGLU_QUANT>(a, s);
-    }
-  }
-  switch (epi) {
-    case EPI_F32: return launch_cfg<4, 2, EPI_F32>(a, s);
-    case EPI_F32_QUANT: return launch_cfg<4, 2, EPI_F32_QUANT>(a, s);
-    default: return launch_cfg<4, 2, EPI_SWIGLU_QUANT>(a, s);
-  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -19,10 +19,16 @@
 // (16 lanes) and one B-scale load, and the stage for step ks+2 is issued
 // right after the barrier of step ks.
 //
-// Scale layouts in LDS are permuted so that a lane reads the scale dwords of
-// its four A fragments with one 16-byte read and of its eight B fragments
-// with two; the MFMA takes the scale from bits [7:0], so each dword is
-// shifted right by 8 * (lane / 16).
+// The weights are stored in fragment order (kernels.hpp): one 16 x 128 block
+// of codes is 1 KB contiguous in MFMA lane order, so each B load instruction
+// moves one whole block (eight full cache lines) and a lane later reads its
+// operand at 16 * lane, with no bank conflicts and no swizzle; a K-step's
+// scale dwords of consecutive weight rows are contiguous too.  The A tile is
+// gathered by row (activations), 128 bytes per row and K-step, with its
+// 16-byte chunks XOR-swizzled by row in LDS.  The A scales are permuted so
+// that a lane reads its four A fragments' scale dwords with one 16-byte read.
+// The MFMA takes the scale from bits [7:0], so each dword is shifted right by
+// 8 * (lane / 16).
 //
 // Column mapping.  SwiGLU: the tile's 512 weight rows are 256 gate rows and
 // the 256 matching up rows (h columns col0 .. col0+255); wave (wm, wn) owns h
@@ -71,8 +77,9 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
     const int sr = row_base + r;
     return routed ? (p.gather ? (int64_t)(p.gather[sr] / p.gather_div) : (int64_t)sr) : (int64_t)r;
   };
-  // Tile B row -> (matrix, output column), clamped into [0, N).
-  auto b_col = [&](int brow, int& up) -> int {
+  // Tile B row -> (matrix, output column), clamped into [0, N); for the first
+  // row of a 16-row block the clamp keeps the whole block inside (N % 16 == 0).
+  auto b_col = [&](int brow, int& up, int last) -> int {
     int c;
     if (SWI) {
       up = brow >= NCOL;
@@ -81,7 +88,7 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
       up = 0;
       c = col0 + brow;
     }
-    return c < p.N ? c : p.N - 1;
+    return c < last ? c : last;
   };
   // Tile B row of fragment ni (0..7) of wave column wc, lane row r.
   auto b_row = [&](int wc, int ni, int r) -> int {
@@ -99,25 +106,15 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
     a_row[i] = a_src_row(r);
     a_chunk[i] = (lane & 7) ^ (r & 7);
   }
-  // B codes: load i (0..3) of wave w fills [OFF_B + 1024*(4w+i), +1024): tile
-  // B row 16*(4w+i) + lane/4, physical chunk lane%4 (logical XOR (row/2)%4).
-  int b_brow[4], b_chunk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * (4 * wave + i) + (lane >> 2);
-    b_brow[i] = r;
-    b_chunk[i] = (lane & 3) ^ ((r >> 1) & 3);
-  }
+  // B codes: load i (0..3) of wave w copies the fragment-order block of tile
+  // B rows 16*(4w+i) .. +15 into [OFF_B + 1024*(4w+i), +1024).
   // A scales (lanes 0..15 of each wave): dword d = 16w + lane holds tile row
   // 64*(d/64) + 16*(d%4) + (d/4)%16, so lane (r16, g4) of M-half wm finds its
   // rows 64wm + 16mi + r16 (mi = 0..3) at dwords 64wm + 4r16 .. +3.
   const int as_d = 16 * wave + (lane & 15);
   const int64_t as_row = a_src_row(64 * (as_d >> 6) + 16 * (as_d & 3) + ((as_d >> 2) & 15));
-  // B scales: dword d = 64w + lane holds the B row of fragment d%8, lane row
-  // (d/8)%16 of wave column d/128, so lane (r16, g4) of wave column wn finds
-  // its eight at dwords 128wn + 8r16 .. +7.
-  const int bs_d = 64 * wave + lane;
-  const int bs_brow = b_row(bs_d >> 7, bs_d & 7, (bs_d >> 3) & 15);
+  // B scales: dword tr of the stage holds tile B row tr; wave w loads rows
+  // 64w .. 64w+63 (contiguous in memory for one K-step).
 
   v4f acc[4][NW][NB];
 #pragma unroll
@@ -139,24 +136,25 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int up;
-      const int c = b_col(b_brow[i], up);
-      gb[i] = (up ? sg.b2 : sg.b) + (int64_t)g * sg.b_gstride + (int64_t)c * (K >> 1) + 16 * b_chunk[i];
+      const int c = b_col(16 * (4 * wave + i), up, p.N - 16);  // first row of the block
+      gb[i] = (up ? sg.b2 : sg.b) + (int64_t)g * sg.b_gstride + (int64_t)(c >> 4) * ksteps * 1024 + 16 * lane;
     }
     const uint8_t* gas = sg.as + as_row * (sg.lda >> 5);
     const uint8_t* gbs;
     {
       int up;
-      const int c = b_col(bs_brow, up);
-      gbs = (up ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + (int64_t)c * kb;
+      const int c = b_col(64 * wave + lane, up, p.N - 1);
+      gbs = (up ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + 4 * (int64_t)c;
     }
+    const int64_t bs_kstride = 4 * (int64_t)p.N;  // bytes between K-steps of the B scales
     auto issue = [&](int ks) {
       uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
 #pragma unroll
       for (int i = 0; i < 2; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (2 * wave + i));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 64 * ks, buf + WD_OFF_B + 1024 * (4 * wave + i));
+      for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 1024 * ks, buf + WD_OFF_B + 1024 * (4 * wave + i));
       if (lane < 16) gl_lds4(gas + 4 * ks, buf + WD_OFF_AS + 64 * wave);
-      gl_lds4(gbs + 4 * ks, buf + WD_OFF_BS + 256 * wave);
+      gl_lds4(gbs + bs_kstride * ks, buf + WD_OFF_BS + 256 * wave);
     };
 
     __syncthreads();  // the previous segment's stages are no longer read
@@ -168,16 +166,17 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
       if (ks + 2 < ksteps) issue(ks + 2);
       const uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
       const int sh = 8 * g4;
-      const uint4 bsd0 = *reinterpret_cast<const uint4*>(buf + WD_OFF_BS + 512 * wn + 32 * r16);
-      const uint4 bsd1 = *reinterpret_cast<const uint4*>(buf + WD_OFF_BS + 512 * wn + 32 * r16 + 16);
       const uint4 asd = *reinterpret_cast<const uint4*>(buf + WD_OFF_AS + 256 * wm + 16 * r16);
-      const uint32_t bs_all[8] = {bsd0.x, bsd0.y, bsd0.z, bsd0.w, bsd1.x, bsd1.y, bsd1.z, bsd1.w};
       const uint32_t as_all[4] = {asd.x, asd.y, asd.z, asd.w};
+      uint32_t bs_all[8];
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni)
+        bs_all[ni] = *reinterpret_cast<const uint32_t*>(buf + WD_OFF_BS + 4 * b_row(wn, ni, r16));
       v8i bf[8];
 #pragma unroll
       for (int ni = 0; ni < 8; ++ni) {
-        const int tr = b_row(wn, ni, r16);
-        const uint4 v = *reinterpret_cast<const uint4*>(buf + WD_OFF_B + tr * 64 + ((g4 ^ ((tr >> 1) & 3)) << 4));
+        const int blk = b_row(wn, ni, 0) >> 4;
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + WD_OFF_B + 1024 * blk + 16 * lane);
         bf[ni][0] = (int)v.x; bf[ni][1] = (int)v.y; bf[ni][2] = (int)v.z; bf[ni][3] = (int)v.w;
         bf[ni][4] = 0; bf[ni][5] = 0; bf[ni][6] = 0; bf[ni][7] = 0;
       }
@@ -212,6 +211,7 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
 template <int EPI>
 hipError_t launch_wide_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int NCOL = EPI == EPI_SWIGLU_QUANT ? WD_B / 2 : WD_B;
+  if (a.N % 16 != 0) return hipErrorInvalidValue;  // fragment-order weights
   const int n_nt = (a.N + NCOL - 1) / NCOL;
   int64_t tiles = (int64_t)a.max_mtiles * n_nt;
   tiles = (tiles + 7) / 8 * 8;

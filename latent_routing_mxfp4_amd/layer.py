@@ -76,8 +76,34 @@ def mx_quantize(x: torch.Tensor, fmt: int, out: Optional[Tuple[torch.Tensor, tor
     return codes, scales
 
 
+def mx_quantize_weights(x: torch.Tensor, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """MXFP4-encode fp32 weight matrices ``x`` ([N][K] or [G][N][K], CUDA) in
+    fragment order; returns (codes, scales) shaped like the row-major result
+    ([..., N, K/2] and [..., N, K/32]) but holding the permuted bytes."""
+    assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.dim() in (2, 3)
+    N, K = x.shape[-2], x.shape[-1]
+    G = x.shape[0] if x.dim() == 3 else 1
+    if out is None:
+        codes = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8, device=x.device)
+    else:
+        codes, scales = out
+    _lib.moe_mx_quantize_weights(x.data_ptr(), G, N, K, codes.data_ptr(), scales.data_ptr(), _stream())
+    return codes, scales
+
+
+def mx_pack_weights(codes: torch.Tensor, scales: torch.Tensor):
+    """Row-major E2M1 ([..., N, K/2] codes, [..., N, K/32] scales) -> fragment order."""
+    N, K = codes.shape[-2], codes.shape[-1] * 2
+    G = codes.numel() // (N * K // 2)
+    oc, os_ = torch.empty_like(codes), torch.empty_like(scales)
+    _lib.moe_mx_pack_weights(codes.data_ptr(), scales.data_ptr(), G, N, K, oc.data_ptr(), os_.data_ptr(), _stream())
+    return oc, os_
+
+
 def mx_gemm(a_codes, a_scales, b_codes, b_scales) -> torch.Tensor:
-    """fp32 deq(a) @ deq(b)^T with a E4M3 [M][K], b packed E2M1 [N][K/2]."""
+    """fp32 deq(a) @ deq(b)^T with a E4M3 [M][K] (row-major) and b E2M1 [N][K]
+    in fragment order (as from ``mx_quantize_weights``)."""
     M, K = a_codes.shape
     N = b_codes.shape[0]
     c = torch.empty(M, N, dtype=torch.float32, device=a_codes.device)
@@ -93,7 +119,9 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
 
     ``host_fp32(name, index)`` returns the fp32 ``[out][in]`` matrix (numpy);
     matrices are produced by a thread pool, copied to the device one at a
-    time through a staging buffer and encoded with ``moe_mx_quantize``.
+    time and encoded there: ``w_down`` row-major (``moe_mx_quantize``, it feeds
+    the bf16 latent projection), every other matrix in fragment order
+    (``moe_mx_quantize_weights``, read by the MX GEMMs).
     ``extra`` carries the fp32 router (``w_router``) and the optional biases.
     """
     out: Dict = {}
@@ -118,7 +146,10 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
                 futs.append(ex.submit(host_fp32, jobs[nxt][0], jobs[nxt][1]))
                 nxt += 1
             dev = torch.from_numpy(np.ascontiguousarray(host, dtype=np.float32)).to(device, non_blocking=False)
-            mx_quantize(dev, FMT_E2M1, out=(codes, scales))
+            if name == "w_down":
+                mx_quantize(dev, FMT_E2M1, out=(codes, scales))
+            else:
+                mx_quantize_weights(dev, out=(codes, scales))
             if progress is not None and (j + 1) % max(1, len(jobs) // 10) == 0:
                 progress(j + 1, len(jobs))
     extra = extra or {}

@@ -121,7 +121,17 @@ def test_quantize_and_gemm_argument_errors():
     assert lib.moe_mx_quantize(FAKE, 4, 64, 2, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_mx_quantize(None, 4, 64, 0, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_mx_quantize(FAKE, 0, 64, 0, FAKE, FAKE, None) == _lib.MOE_OK
-    assert lib.moe_mx_gemm(FAKE, FAKE, FAKE, FAKE, 4, 4, 96, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.moe_mx_gemm(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, FAKE, None) == _lib.MOE_OK
-    assert lib.moe_mx_gemm(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_gemm(FAKE, FAKE, FAKE, FAKE, 4, 16, 96, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_gemm(FAKE, FAKE, FAKE, FAKE, 4, 8, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG  # N % 16
+    assert lib.moe_mx_gemm(FAKE, FAKE, FAKE, FAKE, 0, 16, 128, FAKE, None) == _lib.MOE_OK
+    assert lib.moe_mx_gemm(FAKE + 4, FAKE, FAKE, FAKE, 4, 16, 128, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    # fragment-order weights: N % 16, K % 128, pointers
+    assert lib.moe_mx_quantize_weights(FAKE, 1, 8, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_quantize_weights(FAKE, 1, 16, 96, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_quantize_weights(None, 1, 16, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_quantize_weights(FAKE, 0, 16, 128, FAKE, FAKE, None) == _lib.MOE_OK
+    assert lib.moe_mx_pack_weights(FAKE, FAKE, 1, 24, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_pack_weights(FAKE, FAKE, 1, 16, 64, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_pack_weights(FAKE + 4, FAKE, 1, 16, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_mx_pack_weights(FAKE, FAKE, 0, 16, 128, FAKE, FAKE, None) == _lib.MOE_OK
     assert _lib.moe_status_string(-3).startswith("workspace")

@@ -8,6 +8,7 @@ import pytest
 
 from oracle import moe, mx
 from tests import parity
+from tests.frag_layout import to_fragment_order
 from tests.gpu_harness import say
 
 pytestmark = pytest.mark.gpu
@@ -55,6 +56,34 @@ def test_quantize_bit_exact(LY, fmt):
         assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+def test_quantize_weights_fragment_order(LY):
+    """Fragment-order E2M1 encoding = the oracle's codes, permuted as defined."""
+    rng = np.random.default_rng(43)
+    for G, N, K in ((3, 48, 384), (1, 16, 128), (2, 64, 1024)):
+        say(f"quantize_weights G={G} N={N} K={K}")
+        v = _special_values(rng, G * N, K).reshape(G, N, K)
+        codes, scales = LY.mx_quantize_weights(torch.from_numpy(v).cuda())
+        torch.cuda.synchronize()
+        rc, rs = mx.quantize(v, "e2m1")
+        fc, fs = to_fragment_order(mx.pack_e2m1(rc), rs)
+        assert np.array_equal(scales.cpu().numpy(), fs)
+        assert np.array_equal(codes.cpu().numpy(), fc)
+
+
+def test_pack_weights_matches_fragment_quantiser(LY):
+    rng = np.random.default_rng(44)
+    G, N, K = 4, 32, 512
+    say(f"pack_weights G={G} N={N} K={K}")
+    v = torch.from_numpy(rng.standard_normal((G, N, K)).astype(np.float32)).cuda()
+    rc, rs = LY.mx_quantize(v, 1)
+    pc, ps = LY.mx_pack_weights(rc, rs)
+    qc, qs = LY.mx_quantize_weights(v)
+    torch.cuda.synchronize()
+    assert torch.equal(pc, qc) and torch.equal(ps, qs)
+    fc, fs = to_fragment_order(rc.cpu().numpy(), rs.cpu().numpy())
+    assert np.array_equal(pc.cpu().numpy(), fc) and np.array_equal(ps.cpu().numpy(), fs)
+
+
 def _rand_mx(rng, rows, K, fmt, spread=4.0):
     v = (rng.standard_normal((rows, K)) * np.exp(rng.uniform(-spread, spread, (rows, K // 32)).repeat(32, 1)))
     q = moe.quant(v.astype(np.float32), fmt)
@@ -65,8 +94,9 @@ def _gemm_case(LY, rng, M, N, K):
     say(f"mx_gemm M={M} N={N} K={K}")
     a = _rand_mx(rng, M, K, "e4m3")
     b = _rand_mx(rng, N, K, "e2m1")
+    bc, bs = to_fragment_order(mx.pack_e2m1(b.codes), b.scales)
     c = LY.mx_gemm(torch.from_numpy(a.codes).cuda(), torch.from_numpy(a.scales).cuda(),
-                   torch.from_numpy(mx.pack_e2m1(b.codes)).cuda(), torch.from_numpy(b.scales).cuda())
+                   torch.from_numpy(bc).cuda(), torch.from_numpy(bs).cuda())
     torch.cuda.synchronize()
     got = c.cpu().numpy().astype(np.float64)
     ref = moe.mm(a, b)

@@ -6,6 +6,7 @@ import pytest
 import synth
 from oracle import moe, weights
 from tests import parity
+from tests.frag_layout import from_fragment_order
 from tests.gpu_harness import gpu_layer, gpu_weights, run_traced, say
 
 pytestmark = pytest.mark.gpu
@@ -20,18 +21,23 @@ def _need_gpu():
 
 
 def _check_weight_codes(cfg, gw, W):
+    """The GPU-encoded weights equal the oracle's codes: w_down row-major, the
+    rest in fragment order (read back through the layout's numpy statement)."""
     from oracle import mx
     for name in ("w_down", "w_up"):
         c, s = gw[name]
+        c, s = c.cpu().numpy(), s.cpu().numpy()
+        if name != "w_down":
+            c, s = from_fragment_order(c, s)
         ref = getattr(W, name)
-        assert np.array_equal(s.cpu().numpy(), ref.scales), name
-        assert np.array_equal(c.cpu().numpy(), mx.pack_e2m1(ref.codes)), name
+        assert np.array_equal(s, ref.scales), name
+        assert np.array_equal(c, mx.pack_e2m1(ref.codes)), name
     for name in ("w_gate_e", "w_up_e", "w_down_e", "w_gate_s", "w_up_s", "w_down_s"):
         lst = getattr(W, name)
         if not lst:
             continue
         c, s = gw[name]
-        c, s = c.cpu().numpy(), s.cpu().numpy()
+        c, s = from_fragment_order(c.cpu().numpy(), s.cpu().numpy())
         for i, ref in enumerate(lst):
             assert np.array_equal(s[i], ref.scales), (name, i)
             assert np.array_equal(c[i], mx.pack_e2m1(ref.codes)), (name, i)
