@@ -17,21 +17,21 @@ constexpr int kWave = 64;
 // integer work on the fp32 bit pattern, so the result does not depend on the
 // rounding mode of any float operation.
 
-// floor(log2(|a|)) of a nonzero fp32 bit pattern (sign ignored).
+// floor(log2(|a|)) of a nonzero fp32 bit pattern (sign ignored); selects, no
+// branches, so that many of these can be interleaved.
 __device__ __forceinline__ int floor_log2_bits(uint32_t mag) {
-  uint32_t ex = mag >> 23;
-  if (ex) return (int)ex - 127;
-  return -149 + (31 - __clz(mag));  // subnormal: mag * 2^-149
+  const int ex = (int)(mag >> 23);
+  const int sub = -118 - (int)__clz(mag);  // subnormal: mag * 2^-149 -> (31 - clz) - 149
+  return ex ? ex - 127 : sub;
 }
 
 // E8M0 code of a block with maximum magnitude amax (fp32 bits, sign cleared).
 // EMAX = 8 for E4M3, 2 for E2M1.  amax == 0 gives code 0 (the clamp floor).
 template <int EMAX>
 __device__ __forceinline__ int mx_scale_code(uint32_t amax_bits) {
-  if (amax_bits == 0) return 0;
   int e = floor_log2_bits(amax_bits) - EMAX;
   e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  return e + 127;
+  return amax_bits == 0 ? 0 : e + 127;
 }
 
 // Element code of fp32 v under block exponent e = scale_code - 127.
