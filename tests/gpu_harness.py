@@ -43,3 +43,34 @@ def run_traced(layer, x_np: np.ndarray):
 
 def to_np(t):
     return t.detach().cpu().numpy()
+
+
+PER_TOKEN = ("xq_codes", "xq_scales", "z", "zq_codes", "zq_scales", "logits", "ids", "gates", "y_lat",
+             "yq_codes", "yq_scales")
+PER_ROW = ("h", "hq_codes", "hq_scales", "y_e")
+
+
+def run_traced_tokens(layer, x_np: np.ndarray, tokens):
+    """Run the whole batch with a full trace, but bring back only what the
+    sampled ``tokens`` need: their per-token rows, the per-row (sorted) trace
+    rows of their k pairs in (token, slot) order, and the batch-wide routing
+    and dispatch arrays.  Returns (y[tokens], sub, full)."""
+    T = x_np.shape[0]
+    x = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).cuda()
+    tr = layer.trace_buffers(T)
+    y = layer.forward(x, trace=tr)
+    torch.cuda.synchronize()
+    tok = torch.as_tensor(np.asarray(tokens, np.int64), device="cuda")
+    k = tr["ids"].shape[1]
+    pairs = (tok[:, None] * k + torch.arange(k, device="cuda")[None, :]).reshape(-1)
+    rows = tr["row_of_pair"].long()[pairs]
+    sub = {n: to_np(tr[n][tok]) for n in PER_TOKEN}
+    sub.update({n: to_np(tr[n][rows]) for n in PER_ROW})
+    for n in ("hs", "hs_codes", "hs_scales"):
+        if n in tr:
+            sub[n] = to_np(tr[n][:, tok])
+    full = {n: to_np(tr[n]) for n in ("ids", "gates", "counts", "offsets", "pair_of_row", "row_of_pair")}
+    ysub = to_np(y[tok])
+    del tr, y, x
+    torch.cuda.empty_cache()
+    return ysub, sub, full

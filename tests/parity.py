@@ -274,3 +274,51 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
     say("parity report:", rep)
     assert rel <= REL_L2, f"relative L2 {rel:.3g}"
     return rep
+
+
+# --------------------------------------------------------------------------- sampled tokens
+
+
+def check_full_dispatch(full: dict, E: int, k: int):
+    """Batch-wide properties that are unique and cheap: every token routes to k
+    distinct valid experts, gates sum to one, and the GPU's dispatch is exactly
+    the stable expert-sorted permutation of its own ids."""
+    ids = full["ids"]
+    T = ids.shape[0]
+    assert ids.min() >= 0 and ids.max() < E, "expert id out of range"
+    srt = np.sort(ids, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1]), "repeated expert in a token's top-k"
+    assert np.all(np.abs(full["gates"].astype(np.float64).sum(1) - 1) <= 1e-6), "gates do not sum to 1"
+    d = moe.dispatch(ids, E)
+    assert np.array_equal(full["counts"], d.counts), "counts"
+    assert np.array_equal(full["offsets"], d.offsets), "offsets"
+    assert np.array_equal(full["pair_of_row"], d.pair_of_row), "pair_of_row"
+    assert np.array_equal(full["row_of_pair"], d.row_of_pair), "row_of_pair"
+    return {"tokens": int(T), "pairs": int(T * k), "touched_experts": int((d.counts > 0).sum()),
+            "max_expert_rows": int(d.counts.max())}
+
+
+def subset_trace(sub: dict, E: int, k: int) -> dict:
+    """A trace of the sampled tokens alone, laid out as the layer would lay out
+    a batch of just those tokens: per-row arrays reordered into the subset's
+    own stable expert-sorted dispatch (the GPU rows of a pair do not depend on
+    the other tokens)."""
+    tr = dict(sub)
+    d = moe.dispatch(sub["ids"], E)
+    for n in ("h", "hq_codes", "hq_scales", "y_e"):
+        v = sub[n]                      # rows in (token, slot) order
+        out = np.empty_like(v)
+        out[d.row_of_pair] = v
+        tr[n] = out
+    tr.update(counts=d.counts, offsets=d.offsets, pair_of_row=d.pair_of_row, row_of_pair=d.row_of_pair)
+    return tr
+
+
+def check_tokens(cfg, W, x_sub, y_sub, sub, expert_weights, say=print) -> dict:
+    """The sampled tokens' full path against the oracle, with the same checks
+    as check_layer (replay included) on the subset's trace."""
+    import dataclasses as _dc
+    tr = subset_trace(sub, cfg.n_routed, cfg.top_k)
+    csub = _dc.replace(cfg, T=x_sub.shape[0])
+    o = moe.forward(x_sub, W, cfg.top_k, expert_weights=expert_weights)
+    return check_layer(csub, W, o, y_sub, tr, x=x_sub, say=say, expert_weights=expert_weights)
