@@ -177,7 +177,126 @@ def cpu_baseline(name, n_tokens, say):
                       f"{dt:.1f} s wall"}
 
 
+# --------------------------------------------------------------------------- rocprofv3 summaries
+
+PROFILE_MD = os.path.join(ROOT, "profiles", "k3_layer_kernels_and_hbm_traffic.md")
+PROFILE_CMD = ("python3 /root/repo/bench.py --steps 3 --warmup 1 --decode-steps 5 --no-cpu-baseline "
+               "--copy-probe")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources: a traffic figure is only reported for the
+    exact kernels its counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "latent_routing_mxfp4_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _csv(path):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*.csv"), recursive=True)
+    return files
+
+
+def _grid(r):
+    if "Grid_Size" in r:
+        return int(r["Grid_Size"])
+    return int(r.get("Grid_Size_X", 1)) * int(r.get("Grid_Size_Y", 1)) * int(r.get("Grid_Size_Z", 1))
+
+
+def summarize_profiles(stats_dir, fetch_dir, write_dir) -> str:
+    """Markdown summary of three rocprofv3 runs of PROFILE_CMD: per (kernel,
+    grid) the dispatch count, mean duration, FETCH_SIZE and WRITE_SIZE per
+    dispatch, and HBM bytes per launch scaled by the same counters on the
+    1 GiB copy kernel (--copy-probe); plus the machine-readable traffic lines
+    the benchmark reads."""
+    import csv
+    import collections
+    import re
+
+    def one(d, suffix):
+        f = [x for x in _csv(d) if x.endswith(suffix)]
+        assert f, (d, suffix)
+        return list(csv.DictReader(open(f[0])))
+
+    trace = one(stats_dir, "kernel_trace.csv")
+    dur = collections.defaultdict(list)
+    for r in trace:
+        dur[(r["Kernel_Name"], _grid(r))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    cnt = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        agg = collections.defaultdict(list)
+        for r in one(d, "counter_collection.csv"):
+            if r["Counter_Name"] == name:
+                agg[(r["Kernel_Name"], _grid(r))].append(float(r["Counter_Value"]))
+        cnt[name] = {k: sum(v) / len(v) for k, v in agg.items()}
+    # calibration: torch.mul over 2^28 floats reads 1 GiB and writes 1 GiB
+    probe = [k for k in cnt["FETCH_SIZE"] if "MulFunctor" in k[0]]   # the only torch.mul of the run
+    assert probe, "no copy-probe dispatch in the counter runs"
+    f_fac = (1 << 20) / cnt["FETCH_SIZE"][probe[0]]        # KiB actually read / KiB counted
+    w_fac = (1 << 20) / cnt["WRITE_SIZE"][probe[0]]
+
+    def short(n):
+        n = re.sub(r"\(.*", "", n.replace("void ", "").replace("(anonymous namespace)::", ""))
+        return n
+
+    rows = []
+    for key, ds in dur.items():
+        fk, wk = cnt["FETCH_SIZE"].get(key), cnt["WRITE_SIZE"].get(key)
+        hbm = None if fk is None or wk is None else (fk * f_fac + wk * w_fac) * 1024
+        rows.append((sum(ds), short(key[0]), key[1], len(ds), sum(ds) / len(ds), fk, wk, hbm))
+    rows.sort(reverse=True)
+    out = ["# K3 LatentMoE layer on MI355X: kernel times and HBM traffic", "",
+           "Commands (run from /tmp with TMPDIR=/tmp; the benchmark runs the 16384-token prefill batch, "
+           "then the 64-token decode batch, both at K3 width):", "",
+           "    rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/p_stats -o run -- " + PROFILE_CMD,
+           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/p_fetch -o run -- " + PROFILE_CMD,
+           "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/p_write -o run -- " + PROFILE_CMD,
+           "    python3 /root/repo/bench.py --summarize /tmp/p_stats /tmp/p_fetch /tmp/p_write", "",
+           f"Counter calibration (1 GiB read + 1 GiB write elementwise kernel): FETCH_SIZE x {f_fac:.3f}, "
+           f"WRITE_SIZE x {w_fac:.3f} (KiB per dispatch -> KiB moved).", "",
+           "| kernel | grid (threads) | dispatches | mean ms | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB/launch |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for tot, name, grid, n, mean, fk, wk, hbm in rows[:24]:
+        out.append(f"| {name} | {grid} | {n} | {mean:.4f} | {fk if fk is None else round(fk)} | "
+                   f"{wk if wk is None else round(wk)} | {'-' if hbm is None else f'{hbm / 1e6:.1f}'} |")
+    # the dominant kernels: expert_up = largest-grid dispatch of the prefill / decode gate-up kernels
+    out += ["", "Dominant kernels (expert_up: routed gate/up GEMM + SwiGLU + MXFP8), machine-readable:", ""]
+    dig = source_digest()
+    for wl, pat in (("k3_prefill", "mx_gemm_wide_kernel<2>"), ("k3_decode", "mx_gemm_stream_kernel<1, 2, 2>")):
+        cand = [r for r in rows if r[1].endswith(pat)]
+        if not cand:
+            continue
+        r = max(cand, key=lambda r: r[2])
+        out.append(f"    traffic {wl} expert_up mean_ms={r[4]:.4f} hbm_bytes={0 if r[7] is None else int(r[7])} "
+                   f"sources={dig}")
+    return "\n".join(out) + "\n"
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of expert_up from the committed counter summary,
+    or None when the kernels changed since the counters were taken."""
+    try:
+        text = open(PROFILE_MD).read()
+    except OSError:
+        return None
+    import re
+    m = re.search(rf"traffic {workload} expert_up mean_ms=([0-9.]+) hbm_bytes=([0-9]+) sources=([0-9a-f]+)", text)
+    if not m or m.group(3) != source_digest():
+        return None
+    return {"bytes": int(m.group(2)), "profiled_ms": float(m.group(1))}
+
+
 def main():
+    if len(sys.argv) == 5 and sys.argv[1] == "--summarize":
+        sys.stdout.write(summarize_profiles(*sys.argv[2:5]))
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -227,9 +346,11 @@ def main():
     cfg, ms, stages, work, counts = run_workload(args.workload, args.steps, args.warmup, weights, hip, say)
     value = cfg.T / (ms / 1e3)
     dom_ms = stages["expert_up"]
+    tp = profiled_traffic(cfg.name)
     roof = {"bound": "mfma", "achieved": work["expert_up_flops"] / (dom_ms / 1e3) / 1e12, "peak": PEAK_MX_TFLOPS,
             "unit": "TFLOP/s", "kernel": "expert_up (routed gate/up grouped GEMM + SwiGLU + MXFP8)",
-            "traffic": None}
+            "traffic": None if tp is None else tp["bytes"],
+            "algorithmic_bytes": work["expert_up_bytes"]}
     roof["frac"] = roof["achieved"] / roof["peak"]
     out = {
         "metric": "LatentMoE layer tokens/s (K3 width); HBM GB/s decode, MFMA % prefill vs peak",
@@ -257,8 +378,10 @@ def main():
     if not args.no_decode and args.workload != "k3_decode":
         dcfg, dms, dst, dwork, dcounts = run_workload("k3_decode", args.decode_steps, args.warmup, weights, hip, say)
         dom = dst["expert_up"]
+        dtp = profiled_traffic(dcfg.name)
         droof = {"bound": "hbm", "achieved": dwork["expert_up_bytes"] / (dom / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
-                 "unit": "GB/s", "kernel": "expert_up", "traffic": None}
+                 "unit": "GB/s", "kernel": "expert_up (routed gate/up weight-streaming GEMM + SwiGLU + MXFP8)",
+                 "traffic": None if dtp is None else dtp["bytes"], "algorithmic_bytes": dwork["expert_up_bytes"]}
         droof["frac"] = droof["achieved"] / droof["peak"]
         out["decode"] = {"workload": f"{dcfg.name}: T={dcfg.T}", "value": dcfg.T / (dms / 1e3), "unit": "tokens/s",
                          "ms_per_step": dms, "roofline": droof,
