@@ -38,8 +38,8 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t xq, xqs, xdq, wdn16, z, zq, zqs, logits, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye, ylat,
-      yq, yqs, hs, hss, total;
+  size_t xq, xqs, xdq, wdn16, z, zq, zqs, logits, rpart, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye,
+      ylat, yq, yqs, hs, hss, total;
 };
 
 Plan make_plan(const moe_layer_config& c, int64_t T) {
@@ -61,6 +61,10 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   p.zq = take(T * L);
   p.zqs = take(T * L / 32);
   p.logits = take(T * E * 4);
+  {
+    const int split = T > 0 ? moe::router_split((int)T, (int)E, (int)L) : 1;
+    p.rpart = take(split > 1 ? (size_t)split * T * E * 4 : 0);  // router K-slice partial sums
+  }
   p.ids = take(P * 4);
   p.gates = take(P * 4);
   p.dscr = take(moe::dispatch_scratch_ints((int)T, (int)E) * 4);
@@ -244,7 +248,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(mark(MOE_EV_DOWN));
 
   // 3-4. router
-  MOE_HIP(moe::launch_router_logits(z, w.w_router, w.router_logit_bias, T, E, L, logits, s));
+  MOE_HIP(moe::launch_router_logits(z, w.w_router, w.router_logit_bias, T, E, L, logits,
+                                    at<float>(ws, pl.rpart), s));
   MOE_HIP(mark(MOE_EV_LOGITS));
   MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, ids, gates, s));
   MOE_HIP(mark(MOE_EV_TOPK));

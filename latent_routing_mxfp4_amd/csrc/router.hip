@@ -9,7 +9,8 @@
 // Two kernels:
 //   router_logits: logits[T][E] = z[T][L] W[E][L]^T (+ logit bias), fp32 in
 //     and out, on the fp32 matrix cores (v_mfma_f32_16x16x4f32) with 64x64
-//     tiles staged through LDS.
+//     tiles staged through LDS; for few tiles (decode) the K range is split
+//     over extra workgroups and the slices summed in a fixed order.
 //   topk: one wave per token; the E selection keys sit in LDS, each lane keeps
 //     the best key of its strided slice, and k rounds of a 64-lane
 //     (key desc, id asc) reduction pick the winners in slot order; only the
@@ -29,17 +30,25 @@ constexpr int RK = 32;   // K chunk
 constexpr int RPAD = 4;  // LDS row padding (floats)
 }  // namespace
 
+// One 64 x 64 tile of z W^T over the K range [kbeg, kend).  With split > 1
+// (few tiles: small T) the K range is cut into `split` slices, one per
+// blockIdx.z, and each slice writes its partial sums to out + z*T*E; a second
+// kernel adds the slices in a fixed order (deterministic), plus the bias.
 __global__ void __launch_bounds__(256) router_logits_kernel(const float* __restrict__ z,
                                                            const float* __restrict__ w,
                                                            const float* __restrict__ bias, int T, int E,
-                                                           int L, float* __restrict__ logits) {
-  __shared__ float zs[RT][RK + RPAD];
-  __shared__ float ws[RE][RK + RPAD];
+                                                           int L, int kslice, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) float zs[RT][RK + RPAD];
+  __shared__ __attribute__((aligned(16))) float ws[RE][RK + RPAD];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int t0 = blockIdx.y * RT, e0 = blockIdx.x * RE;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;  // wave's 32x32 sub-tile
+  const int kbeg = blockIdx.z * kslice;
+  const int kend = min(L, kbeg + kslice);
+  float* const dst = out + (int64_t)blockIdx.z * T * E;
+  const float* const bvec = gridDim.z == 1 ? bias : nullptr;  // the reduction adds it otherwise
 
   v4f_t acc[2][2];
 #pragma unroll
@@ -47,7 +56,7 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float* __restr
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = v4f_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < L; k0 += RK) {
+  for (int k0 = kbeg; k0 < kend; k0 += RK) {
     // 64 rows x 32 floats = 512 float4 per operand; 2 per thread.
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -56,8 +65,8 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float* __restr
       float4 vz = make_float4(0.f, 0.f, 0.f, 0.f), vw = make_float4(0.f, 0.f, 0.f, 0.f);
       if (t0 + r < T) vz = *reinterpret_cast<const float4*>(z + (int64_t)(t0 + r) * L + k0 + c4);
       if (e0 + r < E) vw = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + r) * L + k0 + c4);
-      zs[r][c4 + 0] = vz.x; zs[r][c4 + 1] = vz.y; zs[r][c4 + 2] = vz.z; zs[r][c4 + 3] = vz.w;
-      ws[r][c4 + 0] = vw.x; ws[r][c4 + 1] = vw.y; ws[r][c4 + 2] = vw.z; ws[r][c4 + 3] = vw.w;
+      *reinterpret_cast<float4*>(&zs[r][c4]) = vz;
+      *reinterpret_cast<float4*>(&ws[r][c4]) = vw;
     }
     __syncthreads();
 #pragma unroll
@@ -77,20 +86,52 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float* __restr
     for (int b = 0; b < 2; ++b) {
       const int e = e0 + wn + 16 * b + r16;
       if (e >= E) continue;
-      const float bb = bias ? bias[e] : 0.f;
+      const float bb = bvec ? bvec[e] : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + wm + 16 * a + 4 * g4 + i;
-        if (t < T) logits[(int64_t)t * E + e] = acc[a][b][i] + bb;
+        if (t < T) dst[(int64_t)t * E + e] = acc[a][b][i] + bb;
       }
     }
 }
 
+// logits = sum over slices s = 0 .. split-1, in that order, + bias.
+__global__ void __launch_bounds__(256) router_reduce_kernel(const float* __restrict__ part, const float* __restrict__ bias,
+                                                           int64_t n, int E, int split, float* __restrict__ logits) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float v = part[i];
+    for (int s = 1; s < split; ++s) v += part[(int64_t)s * n + i];
+    logits[i] = v + (bias ? bias[i % E] : 0.f);
+  }
+}
+
+int router_split(int T, int E, int L) {
+  const int tiles = ((E + RE - 1) / RE) * ((T + RT - 1) / RT);
+  if (tiles >= 256) return 1;
+  int split = (512 + tiles - 1) / tiles;
+  const int chunks = L / RK;
+  return split > chunks ? chunks : split;
+}
+
 hipError_t launch_router_logits(const float* z, const float* w, const float* bias, int T, int E, int L,
-                                float* logits, hipStream_t s) {
+                                float* logits, float* partial, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT);
-  router_logits_kernel<<<grid, dim3(256), 0, s>>>(z, w, bias, T, E, L, logits);
+  const int split = router_split(T, E, L);
+  const int kslice = ((L / RK + split - 1) / split) * RK;
+  const int nz = (L + kslice - 1) / kslice;
+  dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT, nz);
+  if (nz == 1) {
+    router_logits_kernel<<<grid, dim3(256), 0, s>>>(z, w, bias, T, E, L, kslice, logits);
+    return hipGetLastError();
+  }
+  router_logits_kernel<<<grid, dim3(256), 0, s>>>(z, w, bias, T, E, L, kslice, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)T * E;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  router_reduce_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(partial, bias, n, E, nz, logits);
   return hipGetLastError();
 }
 
