@@ -7,20 +7,33 @@
 // then projected back to model width, so it is quantised here to MXFP8, the
 // input format of that projection.
 //
-// One workgroup per token; each thread owns 4 consecutive latent features
-// (one 16-byte load per expert row), sums the k rows in slot order in fp32
-// (deterministic, no atomics), and 8 neighbouring lanes agree on the block
-// maximum of their 32 features.  HBM-bound: k*L*4 bytes read per token.
+// One workgroup per token with one thread per 4 consecutive latent features
+// (L/4 threads, 896 at K3 width), so a thread issues its k 16-byte expert-row
+// loads back to back; the k rows are summed in slot order in fp32
+// (deterministic, no atomics).  The MXFP8 block maximum of 32 features is a
+// reduction over 8 neighbouring lanes by DPP lane swaps, and the codes come
+// from the hardware fp32 -> E4M3 conversion of the clamped, power-of-two
+// scaled values (identical to the integer encoder).  HBM-bound: k*L*4 bytes
+// read per token.
+#include "gemm_epilogue.hpp"
 #include "kernels.hpp"
 #include "mx_device.hpp"
 
 namespace moe {
 
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y_e,
-                                                     const float* __restrict__ gates,
-                                                     const int32_t* __restrict__ row_of_pair, int k, int L,
-                                                     float* __restrict__ y_lat, uint8_t* __restrict__ yq,
-                                                     uint8_t* __restrict__ yqs) {
+// Maximum over each group of 8 neighbouring lanes (pairs, quads, half-rows).
+__device__ __forceinline__ uint32_t lane8_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return v;
+}
+
+__global__ void __launch_bounds__(1024) combine_kernel(const float* __restrict__ y_e,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ row_of_pair, int k, int L,
+                                                      float* __restrict__ y_lat, uint8_t* __restrict__ yq,
+                                                      uint8_t* __restrict__ yqs) {
   __shared__ int32_t rows[64];
   __shared__ float gs[64];
   const int t = blockIdx.x;
@@ -29,25 +42,31 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     gs[threadIdx.x] = gates[(int64_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  const int n4 = L >> 2;  // multiple of 8
-  for (int f = threadIdx.x; f < n4; f += 256) {
+  const int n4 = L >> 2;  // a multiple of 8: the 8 lanes of a block are active together
+  for (int f = threadIdx.x; f < n4; f += blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float4 v = reinterpret_cast<const float4*>(y_e + (int64_t)rows[j] * L)[f];
-      const float g = gs[j];
-      acc.x = fmaf(g, v.x, acc.x);
-      acc.y = fmaf(g, v.y, acc.y);
-      acc.z = fmaf(g, v.z, acc.z);
-      acc.w = fmaf(g, v.w, acc.w);
+    for (int j0 = 0; j0 < k; j0 += 8) {  // 8 row loads in flight, then the sums in slot order
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) v[u] = reinterpret_cast<const float4*>(y_e + (int64_t)rows[j0 + u] * L)[f];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < k) {
+          const float g = gs[j0 + u];
+          acc.x = fmaf(g, v[u].x, acc.x);
+          acc.y = fmaf(g, v[u].y, acc.y);
+          acc.z = fmaf(g, v[u].z, acc.z);
+          acc.w = fmaf(g, v[u].w, acc.w);
+        }
     }
-    if (y_lat) reinterpret_cast<float4*>(y_lat + (int64_t)t * L)[f] = acc;
     uint32_t m = max(max(__float_as_uint(acc.x) & 0x7fffffffu, __float_as_uint(acc.y) & 0x7fffffffu),
                      max(__float_as_uint(acc.z) & 0x7fffffffu, __float_as_uint(acc.w) & 0x7fffffffu));
-    m = group_max_u32<8>(m);
+    m = lane8_max_u32(m);  // non-negative floats order like their bit patterns
     const int sc = mx_scale_code<8>(m);
     const int e = sc - 127;
-    const uint32_t w = enc_e4m3(acc.x, e) | (enc_e4m3(acc.y, e) << 8) | (enc_e4m3(acc.z, e) << 16) |
-                       (enc_e4m3(acc.w, e) << 24);
+    const uint32_t w = e4m3x2(acc.x, acc.y, e) | (e4m3x2(acc.z, acc.w, e) << 16);
+    if (y_lat) reinterpret_cast<float4*>(y_lat + (int64_t)t * L)[f] = acc;
     reinterpret_cast<uint32_t*>(yq + (int64_t)t * L)[f] = w;
     if ((f & 7) == 0) yqs[(int64_t)t * (L >> 5) + (f >> 3)] = (uint8_t)sc;
   }
@@ -56,7 +75,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* y_e, const float* gates, const int32_t* row_of_pair, int T, int k, int L,
                           float* y_lat, uint8_t* yq, uint8_t* yqs, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  combine_kernel<<<dim3(T), dim3(256), 0, s>>>(y_e, gates, row_of_pair, k, L, y_lat, yq, yqs);
+  int threads = ((L / 4 + 63) / 64) * 64;
+  threads = threads > 1024 ? 1024 : threads;
+  combine_kernel<<<dim3(T), dim3(threads), 0, s>>>(y_e, gates, row_of_pair, k, L, y_lat, yq, yqs);
   return hipGetLastError();
 }
 
