@@ -93,15 +93,16 @@ struct GemmArgs {
 };
 
 // Kernel configurations: weight streaming with 16 or 64 rows per M-tile (few
-// rows per group: decode), the 512-thread kernel with 128 x 512 tiles (many
-// rows per group: prefill), and the 128 x 128 LDS-staged bf16 kernel of the
-// latent down-projection (GEMM_TILE128, bf16 only).
-enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_TILE128 = 3, GEMM_WIDE = 4 };
+// rows per group: decode) and the 512-thread kernels with 128-row tiles (many
+// rows per group: prefill; 128 x 512 for MX, 128 x 256 for bf16).
+enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_WIDE = 4 };
 int gemm_mtile(int shape);
 
 // Dense bf16 GEMM (seg[0].a = bf16 [M][K], seg[0].b = bf16 [N][K]) with the
-// fp32 + MXFP8 epilogue (EPI_F32_QUANT).
+// fp32 + MXFP8 epilogue (EPI_F32_QUANT); shape GEMM_WIDE = the 512-thread
+// 128 x 256 kernel (mx_gemm_wide.hip), K a multiple of 64.
 hipError_t launch_bf16_gemm_quant(const GemmArgs& args, int shape, hipStream_t s);
+hipError_t launch_bf16_gemm_wide(const GemmArgs& args, hipStream_t s);
 
 // Launch the grouped/dense MX GEMM with an automatically chosen tile shape.
 hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, int shape, hipStream_t s);

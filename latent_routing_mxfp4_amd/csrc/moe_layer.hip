@@ -241,7 +241,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.ldc = L;
     a.q = zq;
     a.qs = zqs;
-    const int bshape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_TILE128;
+    const int bshape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_WIDE;
     a.max_mtiles = (T + moe::gemm_mtile(bshape) - 1) / moe::gemm_mtile(bshape);
     MOE_HIP(moe::launch_bf16_gemm_quant(a, bshape, s));
   }

@@ -15,8 +15,8 @@
 //   * the dense projections (latent down/up) and the shared experts.
 //
 // Kernels here: the weight-streaming MX GEMM for few rows per group (decode),
-// and the bf16 GEMMs (register-tiled and LDS-staged) of the dense latent
-// down-projection.  The prefill-shaped MX GEMM is in mx_gemm_wide.hip and the
+// and the register-tiled bf16 GEMM of the dense latent down-projection for
+// few rows (its prefill twin is in mx_gemm_wide.hip).  The prefill-shaped MX GEMM is in mx_gemm_wide.hip and the
 // epilogues shared by all of them in gemm_epilogue.hpp.  MX weights are read
 // in fragment order (kernels.hpp).
 #include "kernels.hpp"
@@ -288,121 +288,6 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
-// LDS-staged bf16 GEMM for the dense latent down-projection (A = bf16 [M][K],
-// B = bf16 [N][K], exact images of the MX operands).  A workgroup owns a
-// 128 x 128 tile; its 4 waves form a 2 x 2 grid of 64 x 64.  Operands move
-// global -> LDS with gfx950's direct loads (16 bytes per lane, no staging
-// registers) through a ring of four 32 KB buffers (three K-steps in flight);
-// a lane's LDS slot is fixed by the hardware (base + 16 * lane), so each lane
-// fetches whichever global chunk belongs there, and rows are XOR-swizzled by
-// 16-byte chunk so a fragment read hits distinct banks.  A K-step is 64
-// elements (128 bytes per row for both operands), consumed as two 16x16x32
-// bf16 MFMAs per fragment pair (slice u takes chunk 4u + g of the row for lane
-// group g, identically in A and B).  Tiles are ordered XCD-aware (lds_pipe.hpp).
-constexpr int LT_M = 128;  // rows per tile
-constexpr int LT_B = 128;  // weight rows per tile
-constexpr int LB_STAGE = LT_M * 128 + LT_B * 128;
-constexpr int LB_NBUF = 4;
-constexpr int LB_LOADS = 8;
-
-template <int EPI>
-__global__ void __launch_bounds__(256) bf16_gemm_lds_kernel(const GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int NW = 4;
-  static_assert(EPI != EPI_SWIGLU_QUANT, "dense projection only");
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  int g, mt, nt, rows, row_base;
-  if (!decode_lds_tile<LT_M>(p, LT_B, g, mt, nt, rows, row_base)) return;
-  const int m0 = mt * LT_M;
-  const int col0 = nt * LT_B;
-  const GemmSeg& sg = p.seg[0];
-  const int K = sg.K;
-  const int ksteps = K >> 6;
-  // load i (0..3) of this wave fills tile row 32*wave + 8*i + lane/8, physical chunk lane%8
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 32 * wave + 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    int ar = m0 + r;
-    ar = ar < rows ? ar : rows - 1;
-    int bc = col0 + r;
-    bc = bc < p.N ? bc : p.N - 1;
-    ga[i] = sg.a + ((int64_t)ar * K) * 2 + 16 * c;
-    gb[i] = sg.b + (int64_t)g * sg.b_gstride + ((int64_t)bc * K) * 2 + 16 * c;
-  }
-  auto issue = [&](int ks) {
-    uint8_t* buf = lds + (ks % LB_NBUF) * LB_STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (4 * wave + i));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 128 * ks, buf + LT_M * 128 + 1024 * (4 * wave + i));
-  };
-  v4f acc[4][NW][1];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni) acc[mi][ni][0] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int j = 0; j < LB_NBUF - 1 && j < ksteps; ++j) issue(j);
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int ahead = min(LB_NBUF - 2, ksteps - 1 - ks);  // K-steps still in flight after this one
-    if (ahead >= 2) wait_vmcnt<2 * LB_LOADS>(); else if (ahead == 1) wait_vmcnt<LB_LOADS>(); else wait_vmcnt<0>();
-    barrier_lds();
-    if (ks + LB_NBUF - 1 < ksteps) issue(ks + LB_NBUF - 1);
-    const uint8_t* buf = lds + (ks % LB_NBUF) * LB_STAGE;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x8 bfr[NW];
-#pragma unroll
-      for (int ni = 0; ni < NW; ++ni) {
-        const int trow = wn * 64 + 16 * ni + r16;
-        bfr[ni] = as_bf16x8(*reinterpret_cast<const uint4*>(buf + LT_M * 128 + trow * 128 +
-                                                            (((4 * u + g4) ^ (trow & 7)) << 4)));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int r = wm * 64 + 16 * mi + r16;
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(buf + r * 128 + (((4 * u + g4) ^ (r & 7)) << 4)));
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni)
-          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bfr[ni], acc[mi][ni][0], 0, 0, 0);
-      }
-    }
-  }
-  Tile t;
-  t.g = g;
-  t.m0 = m0 + wm * 64;
-  t.rows = rows;
-  t.row_base = row_base;
-  t.n0 = col0 + wn * 64;
-  epilogue<4, NW, 1, EPI>(p, t, acc, r16, g4);
-}
-
-template <int EPI>
-static hipError_t launch_bf16_lds_cfg(const GemmArgs& a, hipStream_t s) {
-  const int n_nt = (a.N + LT_B - 1) / LT_B;
-  int64_t tiles = (int64_t)a.max_mtiles * n_nt;
-  tiles = (tiles + 7) / 8 * 8;
-  if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  constexpr size_t smem = (size_t)LB_NBUF * LB_STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bf16_gemm_lds_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  bf16_gemm_lds_kernel<EPI><<<dim3((unsigned)tiles), dim3(256), smem, s>>>(a);
-  return hipGetLastError();
-}
-
 template <int MW, int NW, int EPI>
 static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int NT = 4 * 16 * NW;
@@ -416,7 +301,7 @@ static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
 }
 
 int gemm_mtile(int shape) {
-  return shape == GEMM_STREAM16 ? 16 : shape == GEMM_STREAM64 ? 64 : shape == GEMM_WIDE ? gemm_wide_mtile() : LT_M;
+  return shape == GEMM_STREAM16 ? 16 : shape == GEMM_STREAM64 ? 64 : gemm_wide_mtile();
 }
 
 template <int MW, int NW, int EPI>
@@ -431,7 +316,7 @@ static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
-  if (shape == GEMM_TILE128) return launch_bf16_lds_cfg<EPI_F32_QUANT>(a, s);
+  if (shape == GEMM_WIDE) return launch_bf16_gemm_wide(a, s);
   return shape == GEMM_STREAM16 ? launch_bf16_cfg<1, 2, EPI_F32_QUANT>(a, s)
                                 : launch_bf16_cfg<4, 2, EPI_F32_QUANT>(a, s);
 }
