@@ -325,7 +325,7 @@ hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) 
   if (shape == GEMM_WIDE) return launch_mx_gemm_wide(a, epi, s);
   if (shape == GEMM_STREAM16) {
     switch (epi) {
-      case EPI_F32: return launch_stream_cfg<1, 2, EPI_F32>(a, s);
+      case EPI_F32: return launch_stream_cfg<1, 4, EPI_F32>(a, s);  // 64 columns per wave: more bytes in flight
       case EPI_F32_QUANT: return launch_stream_cfg<1, 2, EPI_F32_QUANT>(a, s);
       default: return launch_stream_cfg<1, 2, EPI_SWIGLU_QUANT>(a, s);
     }
