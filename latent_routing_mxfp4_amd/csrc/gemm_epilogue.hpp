@@ -16,30 +16,17 @@ struct Tile {
   int g, m0, rows, row_base, n0;
 };
 
-// exp(-a) for a >= 0: 2^(-a log2 e) with the exponent split into hi + lo
-// (the product's rounding error recovered with an fma, plus log2 e's own
-// low part), the hardware 2^x applied to hi and a first-order correction
-// e * (1 + lo ln 2) for |lo| < 2^-17.  About 3 units of fp32 rounding.
-__device__ __forceinline__ float exp_neg(float a) {
-  constexpr float kLog2e = 1.44269502162933349609375f;        // log2(e) rounded to fp32
-  constexpr float kLog2eLo = 1.925963033500011079e-8f;        // log2(e) - kLog2e
-  constexpr float kLn2 = 0.693147180559945309f;
-  const float hi = -a * kLog2e;
-  const float lo = fmaf(-a, kLog2eLo, fmaf(-a, kLog2e, -hi));
-  const float e = __builtin_amdgcn_exp2f(hi);
-  return fmaf(e, lo * kLn2, e);
-}
-
-// SiLU(x) = x * sigmoid(x), with sigmoid formed from t = exp(-|x|) in (0, 1]:
-// 1 / (1 + t) for x >= 0 and t / (1 + t) for x < 0, so nothing overflows for
-// any x.  The reciprocal is the hardware estimate refined by one Newton step;
-// the result is within about 9 units of fp32 rounding of x * sigmoid(x).
-__device__ __forceinline__ float silu(float x) {
-  const float t = exp_neg(fabsf(x));
-  const float d = 1.0f + t;
-  float r = __builtin_amdgcn_rcpf(d);
-  r = fmaf(fmaf(-d, r, 1.0f), r, r);
-  return x * (x >= 0.0f ? r : t * r);
+// SiLU(g) * u = g * u / (1 + e^-g), with e^-g = 2^(-g log2 e) from the
+// hardware exp2 and 1 / (1 + t) from the hardware reciprocal.  For g < -88.7
+// t is +inf and the result a signed zero (the exact value is below 1e-36).
+// Relative error, in units of 2^-24: the rounded exponent -g log2 e carries
+// 2|g| units into t, exp2 two more; t / (1 + t) of that reaches the quotient,
+// plus 1 + t (one), the reciprocal (two) and the two products (one each) --
+// at most 7 units for g >= 0 and 2|g| + 7 for g < 0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  constexpr float kLog2e = 1.44269502162933349609375f;  // log2(e) rounded to fp32
+  const float t = __builtin_amdgcn_exp2f(-g * kLog2e);
+  return g * __builtin_amdgcn_rcpf(1.0f + t) * u;
 }
 
 // Two E4M3 codes (bits 0-7 and 8-15) of v0, v1 under block exponent e: the
@@ -67,10 +54,19 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
 // MXFP8 block (32 columns: this lane's v0 at column c, v1 at c + 16, over the
 // 16 lanes of its row) -> two codes and the block's scale code.
 __device__ __forceinline__ uint32_t quant_pair(float v0, float v1, int& sc) {
-  uint32_t m = max(__float_as_uint(v0) & 0x7fffffffu, __float_as_uint(v1) & 0x7fffffffu);
+  uint32_t m = __float_as_uint(fmaxf(fabsf(v0), fabsf(v1)));
   m = row16_max_u32(m);  // non-negative floats order like their bit patterns
   sc = mx_scale_code<8>(m);
   return e4m3x2(v0, v1, sc - 127);
+}
+
+// Byte offset from a wave-uniform base: the address is the base (scalar
+// registers) plus a zero-extended 32-bit lane offset, so no 64-bit vector
+// arithmetic is spent per store.  A wave's rows of any output span less than
+// 4 GB (the launchers bound N and ldc).
+template <class T>
+__device__ __forceinline__ T* at_byte(T* base, uint32_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<uint8_t*>(base) + off);
 }
 
 // Write one wave's MW x NW accumulator tiles (16x16 each; NB accumulators per
@@ -83,13 +79,18 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
   constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
   constexpr bool QNT = EPI != EPI_F32;
   const bool dense = p.offsets == nullptr;
-  // Kernel arguments read once (stores through these pointers cannot alias them).
+  // Kernel arguments read once (stores through these pointers cannot alias
+  // them); bases at the wave's first output row and column.
   const int N = p.N;
-  const int64_t ldc = p.ldc;
-  float* const cbase = p.c ? p.c + (dense ? (int64_t)t.g * p.c_gstride : 0) + t.n0 + r16 : nullptr;
-  uint8_t* const qbase = QNT ? p.q + (dense ? (int64_t)t.g * p.q_gstride : 0) + t.n0 + r16 : nullptr;
-  uint8_t* const sbase = QNT ? p.qs + (dense ? (int64_t)t.g * p.qs_gstride : 0) + (t.n0 >> 5) : nullptr;
-  const int64_t row0 = dense ? 0 : (int64_t)t.row_base;
+  const uint32_t ldc = (uint32_t)p.ldc;
+  const int64_t orow0 = (dense ? 0 : (int64_t)t.row_base) + t.m0;
+  float* const cb = p.c ? p.c + (dense ? (int64_t)t.g * p.c_gstride : 0) + orow0 * (int64_t)ldc + t.n0 : nullptr;
+  uint8_t* const qb = QNT ? p.q + (dense ? (int64_t)t.g * p.q_gstride : 0) + orow0 * N + t.n0 : nullptr;
+  uint8_t* const sb = QNT ? p.qs + (dense ? (int64_t)t.g * p.qs_gstride : 0) + orow0 * (N >> 5) + (t.n0 >> 5)
+                          : nullptr;
+  const uint32_t c_lane = 4u * ((uint32_t)(4 * g4) * ldc + (uint32_t)r16);
+  const uint32_t q_lane = (uint32_t)(4 * g4) * (uint32_t)N + (uint32_t)r16;
+  const uint32_t s_lane = (uint32_t)(4 * g4) * (uint32_t)(N >> 5);
 #pragma unroll
   for (int mi = 0; mi < MW; ++mi) {
     // Values, block maxima and codes of the fragment's four rows first, with
@@ -104,8 +105,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
 #pragma unroll
         for (int b = 0; b < NQ; ++b) {
           if (SWI) {
-            hv[i][b][0] = silu(acc[mi][2 * b][0][i]) * acc[mi][2 * b][NB - 1][i];
-            hv[i][b][1] = silu(acc[mi][2 * b + 1][0][i]) * acc[mi][2 * b + 1][NB - 1][i];
+            hv[i][b][0] = swiglu(acc[mi][2 * b][0][i], acc[mi][2 * b][NB - 1][i]);
+            hv[i][b][1] = swiglu(acc[mi][2 * b + 1][0][i], acc[mi][2 * b + 1][NB - 1][i]);
           } else {
             hv[i][b][0] = acc[mi][2 * b][0][i];
             hv[i][b][1] = acc[mi][2 * b + 1][0][i];
@@ -117,26 +118,26 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
     for (int i = 0; i < 4; ++i) {
       const int row = t.m0 + 16 * mi + 4 * g4 + i;
       if (row >= t.rows) continue;  // uniform over the 16 lanes of the row
-      const int64_t orow = row0 + row;
-      if (!SWI && cbase != nullptr) {
-        float* crow = cbase + orow * ldc;
+      const uint32_t rr = (uint32_t)(16 * mi + i);  // row within the wave's rows, less 4*g4
+      if (!SWI && cb != nullptr) {
+        const uint32_t o = c_lane + 4u * rr * ldc;
 #pragma unroll
         for (int ni = 0; ni < NW; ++ni)
-          if (t.n0 + 16 * ni < N) crow[16 * ni] = acc[mi][ni][0][i];
+          if (t.n0 + 16 * ni < N) *at_byte(cb, o + 64u * ni) = acc[mi][ni][0][i];
       }
       if (QNT) {
-        uint8_t* qrow = qbase + orow * N;
-        uint8_t* srow = sbase + orow * (N >> 5);
+        const uint32_t oq = q_lane + rr * (uint32_t)N;
+        const uint32_t os = s_lane + rr * (uint32_t)(N >> 5);
 #pragma unroll
         for (int b = 0; b < NQ; ++b) {
           if (t.n0 + 32 * b < N) {
-            qrow[32 * b] = (uint8_t)(q2[i][b] & 0xFF);
-            qrow[32 * b + 16] = (uint8_t)(q2[i][b] >> 8);
-            if (r16 == 0) srow[b] = (uint8_t)sc[i][b];
-            if (SWI && cbase != nullptr) {  // optional fp32 copy of h (tracing)
-              float* crow = cbase + orow * ldc;
-              crow[32 * b] = hv[i][b][0];
-              crow[32 * b + 16] = hv[i][b][1];
+            qb[oq + 32u * b] = (uint8_t)(q2[i][b] & 0xFF);
+            qb[oq + 32u * b + 16u] = (uint8_t)(q2[i][b] >> 8);
+            if (r16 == 0) sb[os + b] = (uint8_t)sc[i][b];
+            if (SWI && cb != nullptr) {  // optional fp32 copy of h (tracing)
+              const uint32_t o = c_lane + 4u * rr * ldc + 128u * b;
+              *at_byte(cb, o) = hv[i][b][0];
+              *at_byte(cb, o + 64u) = hv[i][b][1];
             }
           }
         }

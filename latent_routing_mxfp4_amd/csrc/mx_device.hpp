@@ -17,21 +17,16 @@ constexpr int kWave = 64;
 // integer work on the fp32 bit pattern, so the result does not depend on the
 // rounding mode of any float operation.
 
-// floor(log2(|a|)) of a nonzero fp32 bit pattern (sign ignored); selects, no
-// branches, so that many of these can be interleaved.
-__device__ __forceinline__ int floor_log2_bits(uint32_t mag) {
-  const int ex = (int)(mag >> 23);
-  const int sub = -118 - (int)__clz(mag);  // subnormal: mag * 2^-149 -> (31 - clz) - 149
-  return ex ? ex - 127 : sub;
-}
-
-// E8M0 code of a block with maximum magnitude amax (fp32 bits, sign cleared).
-// EMAX = 8 for E4M3, 2 for E2M1.  amax == 0 gives code 0 (the clamp floor).
+// E8M0 code of a block with maximum magnitude amax (fp32 bits, sign cleared):
+// clamp(floor(log2 amax) - EMAX, -127, 127) + 127, with EMAX = 8 for E4M3
+// and 2 for E2M1.  For a normal amax floor(log2 amax) is the exponent field
+// minus 127, so the code is the field minus EMAX; the lower clamp (code 0)
+// takes exactly the fields <= EMAX, which include every subnormal amax and
+// amax == 0; the upper clamp is never reached (field <= 255).
 template <int EMAX>
 __device__ __forceinline__ int mx_scale_code(uint32_t amax_bits) {
-  int e = floor_log2_bits(amax_bits) - EMAX;
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  return amax_bits == 0 ? 0 : e + 127;
+  const int c = (int)(amax_bits >> 23) - EMAX;
+  return c > 0 ? c : 0;
 }
 
 // Element code of fp32 v under block exponent e = scale_code - 127.

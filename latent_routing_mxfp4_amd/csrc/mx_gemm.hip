@@ -315,13 +315,22 @@ static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The epilogue addresses a wave's output rows with 32-bit offsets from a
+// wave-uniform base (gemm_epilogue.hpp): N and ldc below 2^22 keep 128 rows
+// of fp32 output under 4 GB.
+static bool epilogue_dims_ok(const GemmArgs& a) {
+  return a.N > 0 && a.N < (1 << 22) && a.ldc >= 0 && a.ldc < (1 << 22);
+}
+
 hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
+  if (!epilogue_dims_ok(a)) return hipErrorInvalidValue;
   if (shape == GEMM_WIDE) return launch_bf16_gemm_wide(a, s);
   return shape == GEMM_STREAM16 ? launch_bf16_cfg<1, 2, EPI_F32_QUANT>(a, s)
                                 : launch_bf16_cfg<4, 2, EPI_F32_QUANT>(a, s);
 }
 
 hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) {
+  if (!epilogue_dims_ok(a)) return hipErrorInvalidValue;
   if (shape == GEMM_WIDE) return launch_mx_gemm_wide(a, epi, s);
   if (shape == GEMM_STREAM16) {
     switch (epi) {

@@ -34,6 +34,8 @@
 // the 256 matching up rows (h columns col0 .. col0+255); wave (wm, wn) owns h
 // columns col0 + 64 wn .. +63 (fragments 0..3 gate, 4..7 up).  Otherwise the
 // tile is 512 output columns and wave wn owns col0 + 128 wn .. +127.
+#include <type_traits>
+
 #include "gemm_epilogue.hpp"
 #include "kernels.hpp"
 #include "lds_pipe.hpp"
@@ -47,8 +49,8 @@ constexpr int WD_M = 128;                        // rows per M-tile
 constexpr int WD_B = 512;                        // weight rows per tile
 constexpr int WD_OFF_B = WD_M * 128;             // A codes: 128 rows x 128 bytes
 constexpr int WD_OFF_AS = WD_OFF_B + WD_B * 64;  // B codes: 512 rows x 64 bytes
-constexpr int WD_OFF_BS = WD_OFF_AS + 4 * WD_M;  // A scales: 128 dwords
-constexpr int WD_STAGE = WD_OFF_BS + 4 * WD_B;   // B scales: 512 dwords -> 51712 bytes
+constexpr int WD_OFF_BS = WD_OFF_AS + 4 * 512;   // A scales: 128 dwords in 512 slots
+constexpr int WD_STAGE = WD_OFF_BS + 4 * WD_B;   // B scales: 512 dwords -> 53248 bytes
 constexpr int WD_NBUF = 3;
 constexpr int WD_LOADS = 8;  // direct loads per wave per K-step
 
@@ -108,9 +110,11 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
   }
   // B codes: load i (0..3) of wave w copies the fragment-order block of tile
   // B rows 16*(4w+i) .. +15 into [OFF_B + 1024*(4w+i), +1024).
-  // A scales (lanes 0..15 of each wave): dword d = 16w + lane holds tile row
-  // 64*(d/64) + 16*(d%4) + (d/4)%16, so lane (r16, g4) of M-half wm finds its
-  // rows 64wm + 16mi + r16 (mi = 0..3) at dwords 64wm + 4r16 .. +3.
+  // A scales: value d (0..127) = tile row 64*(d/64) + 16*(d%4) + (d/4)%16 is
+  // loaded by lane d%16 of wave d/16 into slot 64*(d/16) + d%16 (lanes 16..63
+  // load copies into the other slots, so the load needs no lane mask), and
+  // lane (r16, g4) of M-half wm finds its rows 64wm + 16mi + r16 (mi = 0..3),
+  // values 64wm + 4r16 .. +3, in four consecutive slots.
   const int as_d = 16 * wave + (lane & 15);
   const int64_t as_row = a_src_row(64 * (as_d >> 6) + 16 * (as_d & 3) + ((as_d >> 2) & 15));
   // B scales: dword tr of the stage holds tile B row tr; wave w loads rows
@@ -147,26 +151,50 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
       gbs = (up ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + 4 * (int64_t)c;
     }
     const int64_t bs_kstride = 4 * (int64_t)p.N;  // bytes between K-steps of the B scales
-    auto issue = [&](int ks) {
+    // Stage loads in four parts (2 A-code; 2 B-code; 2 B-code; A-scale and
+    // B-scale), issued between the MFMA groups of the step before, so that
+    // the direct loads queue behind MFMAs instead of stalling the waves in
+    // one burst after the barrier.
+    auto issue_part = [&](int ks, int part) {
       uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
+      if (part == 0) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (2 * wave + i));
+        for (int i = 0; i < 2; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (2 * wave + i));
+      } else if (part < 3) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 1024 * ks, buf + WD_OFF_B + 1024 * (4 * wave + i));
-      if (lane < 16) gl_lds4(gas + 4 * ks, buf + WD_OFF_AS + 64 * wave);
-      gl_lds4(gbs + bs_kstride * ks, buf + WD_OFF_BS + 256 * wave);
+        for (int j = 0; j < 2; ++j) {
+          const int i = 2 * (part - 1) + j;
+          gl_lds16(gb[i] + 1024 * ks, buf + WD_OFF_B + 1024 * (4 * wave + i));
+        }
+      } else {
+        gl_lds4(gas + 4 * ks, buf + WD_OFF_AS + 256 * wave);
+        gl_lds4(gbs + bs_kstride * ks, buf + WD_OFF_BS + 256 * wave);
+      }
+    };
+    auto issue = [&](int ks) {
+#pragma unroll
+      for (int part = 0; part < 4; ++part) issue_part(ks, part);
+    };
+    auto rd_a = [&](const uint8_t* buf, int mi) -> v8i {
+      const int r = 64 * wm + 16 * mi + r16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(buf + r * 128 + ((g4 ^ (r & 7)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(buf + r * 128 + (((4 + g4) ^ (r & 7)) << 4));
+      v8i av;
+      av[0] = (int)lo.x; av[1] = (int)lo.y; av[2] = (int)lo.z; av[3] = (int)lo.w;
+      av[4] = (int)hi.x; av[5] = (int)hi.y; av[6] = (int)hi.z; av[7] = (int)hi.w;
+      return av;
     };
 
-    __syncthreads();  // the previous segment's stages are no longer read
-    issue(0);
-    if (ksteps > 1) issue(1);
-    for (int ks = 0; ks < ksteps; ++ks) {
+    // One K-step; with_issue (a compile-time tag) also issues the stage two
+    // steps ahead, so the steady-state loop has no branch between its MFMA
+    // groups and its loads.
+    auto step = [&](int ks, auto with_issue) {
       if (ks + 1 < ksteps) wait_vmcnt<WD_LOADS>(); else wait_vmcnt<0>();
       barrier_lds();
-      if (ks + 2 < ksteps) issue(ks + 2);
       const uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
       const int sh = 8 * g4;
-      const uint4 asd = *reinterpret_cast<const uint4*>(buf + WD_OFF_AS + 256 * wm + 16 * r16);
+      const uint4 asd =
+          *reinterpret_cast<const uint4*>(buf + WD_OFF_AS + 1024 * wm + 256 * (r16 >> 2) + 16 * (r16 & 3));
       const uint32_t as_all[4] = {asd.x, asd.y, asd.z, asd.w};
       uint32_t bs_all[8];
 #pragma unroll
@@ -180,14 +208,11 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
         bf[ni][0] = (int)v.x; bf[ni][1] = (int)v.y; bf[ni][2] = (int)v.z; bf[ni][3] = (int)v.w;
         bf[ni][4] = 0; bf[ni][5] = 0; bf[ni][6] = 0; bf[ni][7] = 0;
       }
+      v8i av = rd_a(buf, 0);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        const int r = 64 * wm + 16 * mi + r16;
-        const uint4 lo = *reinterpret_cast<const uint4*>(buf + r * 128 + ((g4 ^ (r & 7)) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(buf + r * 128 + (((4 + g4) ^ (r & 7)) << 4));
-        v8i av;
-        av[0] = (int)lo.x; av[1] = (int)lo.y; av[2] = (int)lo.z; av[3] = (int)lo.w;
-        av[4] = (int)hi.x; av[5] = (int)hi.y; av[6] = (int)hi.z; av[7] = (int)hi.w;
+        v8i an;
+        if (mi < 3) an = rd_a(buf, mi + 1);  // next fragment's read overlaps these MFMAs
         const int sa = (int)(as_all[mi] >> sh);
 #pragma unroll
         for (int ni = 0; ni < 8; ++ni) {
@@ -195,8 +220,21 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
           if (SWI) acc[mi][ni & 3][ni >> 2] = mfma_f8f4(av, bf[ni], acc[mi][ni & 3][ni >> 2], sa, sb);
           else acc[mi][ni][0] = mfma_f8f4(av, bf[ni], acc[mi][ni][0], sa, sb);
         }
+        if constexpr (decltype(with_issue)::value) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_part(ks + 2, mi);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (mi < 3) av = an;
       }
-    }
+    };
+
+    __syncthreads();  // the previous segment's stages are no longer read
+    issue(0);
+    if (ksteps > 1) issue(1);
+    int ks = 0;
+    for (; ks + 2 < ksteps; ++ks) step(ks, std::true_type{});
+    for (; ks < ksteps; ++ks) step(ks, std::false_type{});
   }
 
   Tile t;

@@ -81,11 +81,14 @@ def swiglu_bound(g, u, bg, bu, h):
     """Bound on |h_gpu - h| for h = silu(G) U given |dG| <= bg, |dU| <= bu."""
     sg = 1 / (1 + np.exp(-g))
     dsilu = sg * (1 + g * (1 - sg))          # |silu'| <= 1.1, |silu''| <= 0.5
-    # The last term is the kernel's own fp32 evaluation of SiLU(G) * U: exp
-    # (<= 2 units of 2^-24), 1 + t, a Newton-refined reciprocal (<= 1.5), t * r,
-    # x * sigmoid and the product with U -- at most about 8.5 units; 12 leaves margin.
-    return (np.abs(dsilu) * np.abs(u) * bg + np.abs(g * sg) * bu + bg * bu + 0.5 * np.abs(u) * bg ** 2
-            + 12 * EPS32 * np.abs(h) + 1e-30)
+    # The last term is the kernel's own fp32 evaluation G * U / (1 + 2^(-G log2 e)):
+    # the rounded exponent puts 2|G| units of 2^-24 into t, exp2 two more, and
+    # t / (1 + t) of that reaches the quotient; 1 + t, the reciprocal (two units)
+    # and the two products add five -- at most 7 units for G >= 0 and 2|G| + 7
+    # below; 9 + 2|G| leaves margin.
+    # Both are taken at the kernel's own operands, |G| + bg and |h| + prop.
+    prop = np.abs(dsilu) * np.abs(u) * bg + np.abs(g * sg) * bu + bg * bu + 0.5 * np.abs(u) * bg ** 2
+    return prop + (9 + 2 * (np.abs(g) + bg)) * EPS32 * (np.abs(h) + prop) + 1e-30
 
 
 def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray):
