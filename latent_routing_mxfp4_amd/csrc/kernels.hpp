@@ -104,6 +104,14 @@ int gemm_mtile(int shape);
 hipError_t launch_bf16_gemm_quant(const GemmArgs& args, int shape, hipStream_t s);
 hipError_t launch_bf16_gemm_wide(const GemmArgs& args, hipStream_t s);
 
+// Few-row dense GEMM from row-major MXFP4 weights (seg[0].b codes [N][K/2],
+// seg[0].bs scales [N][K/32]) decoded to bf16 in registers, A = bf16 [M][K]:
+// K split into S slices whose fp32 partial sums go to part[S][M][N], then
+// z = their sum in slice order and, when zq is given, its MXFP8 codes along N.
+int bf16_mx_splitk_slices(int M, int N, int K);
+hipError_t launch_bf16_mx_splitk(const GemmArgs& args, float* part, int S, float* z, uint8_t* zq, uint8_t* zqs,
+                                 hipStream_t s);
+
 // Launch the grouped/dense MX GEMM with an automatically chosen tile shape.
 hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, int shape, hipStream_t s);
 

@@ -34,11 +34,12 @@ struct moe_layer {
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kFewRows = 256;  // decode-shaped batches: weight-streaming kernels
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t xq, xqs, xdq, wdn16, z, zq, zqs, logits, rpart, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye,
+  size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye,
       ylat, yq, yqs, hs, hss, total;
 };
 
@@ -56,7 +57,11 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   p.xq = take(T * d);
   p.xqs = take(T * d / 32);
   p.xdq = take(T * d * 2);
-  p.wdn16 = take(L * d * 2);
+  // Latent down-projection: at most kFewRows tokens stream the MXFP4 weights
+  // (K-slice partial sums), more tokens use a bf16 image of W_down.
+  const bool few = T <= kFewRows;
+  p.wdn16 = take(few ? 0 : L * d * 2);
+  p.zpart = take(few && T > 0 ? (size_t)moe::bf16_mx_splitk_slices((int)T, (int)L, (int)d) * T * L * 4 : 0);
   p.z = take(T * L * 4);
   p.zq = take(T * L);
   p.zqs = take(T * L / 32);
@@ -189,6 +194,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   uint8_t* xqs = at<uint8_t>(ws, pl.xqs);
   uint16_t* xdq = at<uint16_t>(ws, pl.xdq);
   uint16_t* wdn16 = at<uint16_t>(ws, pl.wdn16);
+  float* zpart = at<float>(ws, pl.zpart);
   float* z = at<float>(ws, pl.z);
   uint8_t* zq = at<uint8_t>(ws, pl.zq);
   uint8_t* zqs = at<uint8_t>(ws, pl.zqs);
@@ -212,8 +218,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   uint8_t* hss = at<uint8_t>(ws, pl.hss);
 
   // Kernel shapes: weight streaming when a group has few rows (decode), the
-  // register-tiled kernel otherwise.
-  const int dense_shape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_WIDE;
+  // LDS-staged 512-thread kernels otherwise.
+  const int dense_shape = T <= kFewRows ? moe::GEMM_STREAM16 : moe::GEMM_WIDE;
   const int routed_shape = P <= (int64_t)16 * E ? moe::GEMM_STREAM16 : moe::GEMM_WIDE;
   const int mt_dense = moe::gemm_mtile(dense_shape);
   const int mt_small = moe::gemm_mtile(moe::GEMM_STREAM16), mt_big = moe::gemm_mtile(moe::GEMM_WIDE);
@@ -227,8 +233,20 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(mark(MOE_EV_QUANT_X));
 
   // 2. z, zq: bf16 matrix cores on the exactly decoded MX operands, so that the
-  //    latent the router ranks is accurate to fp32 accumulation.
-  {
+  //    latent the router ranks is accurate to fp32 accumulation.  Few tokens:
+  //    W_down is decoded in registers while it streams (K-slice partials, then
+  //    their sum and MXFP8); many tokens: one bf16 image, then the LDS kernel.
+  if (T <= kFewRows) {
+    moe::GemmArgs a = {};
+    a.nseg = 1;
+    a.seg[0] = {reinterpret_cast<const uint8_t*>(xdq), nullptr, d, w.w_down.codes, w.w_down.scales,
+                nullptr, nullptr, 0, 0, d};
+    a.G = 1;
+    a.M = T;
+    a.N = L;
+    a.ldc = L;
+    MOE_HIP(moe::launch_bf16_mx_splitk(a, zpart, moe::bf16_mx_splitk_slices(T, L, d), z, zq, zqs, s));
+  } else {
     MOE_HIP(moe::launch_decode_e2m1_bf16(w.w_down.codes, w.w_down.scales, L, d, wdn16, s));
     moe::GemmArgs a = {};
     a.nseg = 1;
@@ -241,9 +259,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     a.ldc = L;
     a.q = zq;
     a.qs = zqs;
-    const int bshape = T <= 256 ? moe::GEMM_STREAM16 : moe::GEMM_WIDE;
-    a.max_mtiles = (T + moe::gemm_mtile(bshape) - 1) / moe::gemm_mtile(bshape);
-    MOE_HIP(moe::launch_bf16_gemm_quant(a, bshape, s));
+    a.max_mtiles = (T + moe::gemm_mtile(moe::GEMM_WIDE) - 1) / moe::gemm_mtile(moe::GEMM_WIDE);
+    MOE_HIP(moe::launch_bf16_gemm_quant(a, moe::GEMM_WIDE, s));
   }
   MOE_HIP(mark(MOE_EV_DOWN));
 

@@ -15,10 +15,11 @@
 //   * the dense projections (latent down/up) and the shared experts.
 //
 // Kernels here: the weight-streaming MX GEMM for few rows per group (decode),
-// and the register-tiled bf16 GEMM of the dense latent down-projection for
-// few rows (its prefill twin is in mx_gemm_wide.hip).  The prefill-shaped MX GEMM is in mx_gemm_wide.hip and the
-// epilogues shared by all of them in gemm_epilogue.hpp.  MX weights are read
-// in fragment order (kernels.hpp).
+// and the few-row latent down-projection, a bf16 GEMM that decodes the MXFP4
+// weights in registers (its prefill twin is in mx_gemm_wide.hip).  The
+// prefill-shaped MX GEMM is in mx_gemm_wide.hip and the epilogues shared by
+// all of them in gemm_epilogue.hpp.  MX weights are read in fragment order
+// (kernels.hpp), except W_down, which the bf16 paths read row-major.
 #include "kernels.hpp"
 #include "mx_device.hpp"
 #include "lds_pipe.hpp"
@@ -94,21 +95,60 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int wave, int NWC
   return true;
 }
 
-// Dense bf16 GEMM on exactly decoded MX operands (v_mfma_f32_16x16x32_bf16):
-// A = bf16 [M][K], B = bf16 [N][K] (seg.a / seg.b, lda = K).  Every product of
-// an E4M3 and an E2M1 value (with power-of-two scales) is exact in bf16 x bf16
-// -> fp32, and this instruction accumulates at fp32 precision, unlike the
-// block-scaled MFMA, which sums each 32-element block in a window of about 14
-// bits below the block's largest product.  The latent down-projection feeds
-// the router, whose top-k must be decided on an fp32-accurate latent, so it
-// runs here.  A lane loads 64 contiguous bytes (32 K values) of its row per
-// 128-wide K-step and issues four MFMAs, slice u taking K [32g + 8u, +8); A and
-// B use the same slicing, so the pairing of K indices is consistent.
-template <int MW, int NW, int EPI>
-__global__ void __launch_bounds__(256) bf16_gemm_kernel(const GemmArgs p) {
+// Exact bf16 image of one MX E2M1 block (32 elements, 16 bytes, scale code
+// sc): dword h of output u holds elements 8u + 2h (low half) and 8u + 2h + 1
+// (high half), element 2i being the low nibble of byte i.  For scale codes
+// 2..252 the bf16 of magnitude code m in 1..7 is (sc << 7) + 64 (m - 2), less
+// another 64 for m = 1 (0.5 has no mantissa bit); other scale codes (subnormal
+// or overflowing results, never produced by the weight encoder for finite
+// weights of useful size) take the general path through fp32.
+__device__ __forceinline__ uint32_t e2m1_bf16_fast(uint32_t c, int sc) {
+  const uint32_t m = c & 7u;
+  uint32_t v = (uint32_t)(sc << 7) + 64u * m - 128u - (m == 1u ? 64u : 0u);
+  v = m == 0u ? 0u : v;
+  return v | ((c & 8u) << 12);
+}
+__device__ __forceinline__ uint32_t e2m1_bf16_slow(uint32_t c, int sc) {
+  const int E = (c >> 1) & 3, m = c & 1;
+  const float v = ldexpf((float)(E ? 2 + m : m), (E ? E - 2 : -1) + sc - 127);
+  return __float_as_uint((c & 0x8) ? -v : v) >> 16;
+}
+__device__ __forceinline__ void e2m1_block_bf16(const uint4& codes, int sc, uint4 (&out)[4]) {
+  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+  const bool fast = sc >= 2 && sc <= 252;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    uint32_t* o = &out[u].x;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t lo = (w[u] >> (8 * h)) & 0xf, hi = (w[u] >> (8 * h + 4)) & 0xf;
+      o[h] = fast ? (e2m1_bf16_fast(lo, sc) | (e2m1_bf16_fast(hi, sc) << 16))
+                  : (e2m1_bf16_slow(lo, sc) | (e2m1_bf16_slow(hi, sc) << 16));
+    }
+  }
+}
+
+// Few-row dense bf16 GEMM straight from MXFP4 weights (the latent
+// down-projection at decode): A = exact bf16 image of the MXFP8 activations
+// [M][K] (seg.a), B = row-major MXFP4 [N][K] (seg.b codes, seg.bs scales [N][K/32]),
+// decoded to its exact bf16 image in registers, so the weights are read once
+// at 17/32 bytes per element and no bf16 copy is written.  Why bf16: every
+// product of an E4M3 and an E2M1 value (power-of-two scales) is exact in
+// bf16 x bf16 -> fp32 and v_mfma_f32_16x16x32_bf16 accumulates at fp32
+// precision, unlike the block-scaled MFMA, which sums each 32-element block in
+// a window of about 14 bits below its largest product; the router's top-k is
+// decided on this latent.  A lane loads 64 contiguous bytes (32 K values) of
+// its activation row and one MX block (16 code bytes) of its weight row per
+// 128-wide K-step and issues four MFMAs, slice u taking K [32g + 8u, +8) of
+// both operands, so the pairing of K indices is consistent.  The K range is
+// split over gridDim.y slices of kper K-steps, each writing its fp32 partial
+// sums to part[slice][M][N]; splitk_reduce_kernel adds them in slice order.
+// Weight blocks and scales are read D K-steps ahead in a register ring.
+template <int MW, int NW>
+__global__ void __launch_bounds__(256) bf16_mx_splitk_kernel(const GemmArgs p, float* __restrict__ part, int kper) {
   constexpr int MT = 16 * MW;
   constexpr int NT = 4 * 16 * NW;
-  static_assert(EPI == EPI_F32 || NW % 2 == 0, "quantising epilogues need whole 32-column blocks per wave");
+  constexpr int D = MW == 1 ? 4 : 2;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -117,20 +157,25 @@ __global__ void __launch_bounds__(256) bf16_gemm_kernel(const GemmArgs p) {
   if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;
   const GemmSeg& sg = p.seg[0];
   const int K = sg.K;
-  const int ksteps = K >> 7;
+  const int ks0 = blockIdx.y * kper;
+  int nks = (K >> 7) - ks0;
+  nks = nks < kper ? nks : kper;
+  if (nks <= 0) return;
   const uint16_t* ap[MW];
 #pragma unroll
   for (int mi = 0; mi < MW; ++mi) {
     int r = t.m0 + 16 * mi + r16;
     r = r < t.rows ? r : t.rows - 1;
-    ap[mi] = reinterpret_cast<const uint16_t*>(sg.a) + (int64_t)r * K + 32 * g4;
+    ap[mi] = reinterpret_cast<const uint16_t*>(sg.a) + (int64_t)r * K + 128 * ks0 + 32 * g4;
   }
-  const uint16_t* bp[NW];
+  const uint8_t* bp[NW];
+  const uint8_t* bsp[NW];
 #pragma unroll
   for (int ni = 0; ni < NW; ++ni) {
     int c = t.n0 + 16 * ni + r16;
     c = c < p.N ? c : p.N - 1;
-    bp[ni] = reinterpret_cast<const uint16_t*>(sg.b) + (int64_t)c * K + 32 * g4;
+    bp[ni] = sg.b + (int64_t)c * (K >> 1) + 64 * ks0 + 16 * g4;
+    bsp[ni] = sg.bs + (int64_t)c * (K >> 5) + 4 * ks0 + g4;
   }
   v4f acc[MW][NW][1];
 #pragma unroll
@@ -138,39 +183,95 @@ __global__ void __launch_bounds__(256) bf16_gemm_kernel(const GemmArgs p) {
 #pragma unroll
     for (int ni = 0; ni < NW; ++ni) acc[mi][ni][0] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 fa[MW][4], fb[NW][4];
-  auto load = [&](int ks) {
-#pragma unroll
-    for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) fa[mi][u] = reinterpret_cast<const uint4*>(ap[mi] + 128 * ks)[u];
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) fb[ni][u] = reinterpret_cast<const uint4*>(bp[ni] + 128 * ks)[u];
+  struct Slot {
+    uint4 a[MW][4];
+    uint4 b[NW];
+    int bs[NW];
   };
-  load(0);
-  for (int ks = 0; ks < ksteps; ++ks) {
-    uint4 ca[MW][4], cb[NW][4];
+  Slot sl[D];
+  auto load = [&](int ks, Slot& q) {
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni) {
+      q.b[ni] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni] + 64 * ks)));
+      q.bs[ni] = bsp[ni][4 * ks];
+    }
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ca[mi][u] = fa[mi][u];
+      for (int u = 0; u < 4; ++u) q.a[mi][u] = reinterpret_cast<const uint4*>(ap[mi] + 128 * ks)[u];
+  };
+  auto compute = [&](const Slot& q) {
+    uint4 bf[NW][4];
 #pragma unroll
-    for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) cb[ni][u] = fb[ni][u];
-    if (ks + 1 < ksteps) load(ks + 1);
+    for (int ni = 0; ni < NW; ++ni) e2m1_block_bf16(q.b[ni], q.bs[ni], bf[ni]);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NW; ++ni)
-          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[mi][u]), as_bf16x8(cb[ni][u]),
+          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a[mi][u]), as_bf16x8(bf[ni][u]),
                                                                    acc[mi][ni][0], 0, 0, 0);
+  };
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nks) load(j, sl[j]);
+  int ks = 0;
+  for (; ks + 2 * D <= nks; ks += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      compute(sl[j]);
+      load(ks + j + D, sl[j]);
+    }
   }
-  epilogue<MW, NW, 1, EPI>(p, t, acc, r16, g4);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (ks + j < nks) {
+      compute(sl[j]);
+      if (ks + j + D < nks) load(ks + j + D, sl[j]);
+    }
+  ks += D;
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (ks + j < nks) compute(sl[j]);
+
+  GemmArgs q = p;  // the slice's partial sums, fp32 [M][N]
+  q.c = part + (int64_t)blockIdx.y * p.M * p.N;
+  q.ldc = p.N;
+  q.q = nullptr;
+  epilogue<MW, NW, 1, EPI_F32>(q, t, acc, r16, g4);
+}
+
+// c = sum over slices of part[s][M][N] (slice order), and with QNT its MXFP8
+// codes along N.  One thread per (row, 32-column block, r): columns 32b + r
+// and 32b + 16 + r, so the 16 lanes of a block form one DPP row (quant_pair).
+template <bool QNT>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                            float* __restrict__ c, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ qs) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nb = N >> 5;
+  const int r = (int)(i & 15);
+  const int64_t blk = i >> 4;  // row * nb + b; the 16 lanes of a DPP row share it
+  if (blk >= (int64_t)M * nb) return;
+  const int64_t row = blk / nb;
+  const int b = (int)(blk - row * nb);
+  const int64_t o = row * N + 32 * b + r;
+  const int64_t MN = (int64_t)M * N;
+  float v0 = 0.f, v1 = 0.f;
+  for (int sl = 0; sl < S; ++sl) {
+    v0 += part[sl * MN + o];
+    v1 += part[sl * MN + o + 16];
+  }
+  c[o] = v0;
+  c[o + 16] = v1;
+  if (QNT) {
+    int sc;
+    const uint32_t w = quant_pair(v0, v1, sc);
+    q[o] = (uint8_t)(w & 0xFF);
+    q[o + 16] = (uint8_t)(w >> 8);
+    if (r == 0) qs[row * nb + b] = (uint8_t)sc;
+  }
 }
 
 // Weight-streaming variant for few rows per group (decode).  The weights are
@@ -179,10 +280,12 @@ __global__ void __launch_bounds__(256) bf16_gemm_kernel(const GemmArgs p) {
 // loads, for each of its weight fragments, the fragment-order block of codes
 // (1 KB contiguous; lane l takes its 16-byte MFMA operand at 16 l, read
 // non-temporally) and the 64 contiguous scale bytes of the block's 16 rows,
-// one K-step ahead of the MFMAs.  The few activation rows (L2-resident) are
-// read in the E4M3 operand layout straight from global memory.
+// D K-steps ahead of the MFMAs, together with the few activation rows
+// (L2-resident), read in the E4M3 operand layout straight from global memory.
 template <int MW, int NW, int EPI>
 __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
+  // K-steps in flight per wave: as many as keep two waves per SIMD.
+  constexpr int D = MW == 1 ? (NW <= 2 ? 4 : 2) : 1;
   constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
   constexpr int NB = SWI ? 2 : 1;
   constexpr int MT = 16 * MW;
@@ -247,43 +350,65 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
       }
     const int64_t bs_k = 4 * (int64_t)p.N;  // bytes between K-steps of the scales
 
-    uint4 fb[NW][NB];
-    int fs[NW][NB];
-    auto load_b = [&](int ks) {
-#pragma unroll
-      for (int ni = 0; ni < NW; ++ni)
-#pragma unroll
-        for (int h = 0; h < NB; ++h) {
-          fb[ni][h] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni][h] + 1024 * ks)));
-          fs[ni][h] = bsp[ni][h][bs_k * ks];
-        }
+    // Register ring of D K-steps: slot j holds the operands of step ks + j
+    // (weight block and scale per fragment, activation fragment and scale per
+    // M-fragment).  Each slot is refilled right after its MFMAs, so D steps
+    // of loads stay in flight and a step's MFMAs wait only for its own slot.
+    struct Slot {
+      uint4 b[NW][NB];
+      int bs[NW][NB];
+      Frag8 a[MW];
+      int as[MW];
     };
-    load_b(0);
-    for (int ks = 0; ks < nks; ++ks) {
-      uint4 cb[NW][NB];
-      int cs[NW][NB];
+    Slot sl[D];
+    auto load = [&](int ks, Slot& q) {
 #pragma unroll
       for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
         for (int h = 0; h < NB; ++h) {
-          cb[ni][h] = fb[ni][h];
-          cs[ni][h] = fs[ni][h];
+          q.b[ni][h] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni][h] + 1024 * ks)));
+          q.bs[ni][h] = bsp[ni][h][bs_k * ks];
         }
-      if (ks + 1 < nks) load_b(ks + 1);
 #pragma unroll
       for (int mi = 0; mi < MW; ++mi) {
-        const uint8_t* q = ap[mi] + 128 * ks;
-        Frag8 fa;
-        fa.lo = *reinterpret_cast<const uint4*>(q);
-        fa.hi = *reinterpret_cast<const uint4*>(q + 64);
-        const v8i av = as_v8i(fa);
-        const int sa = asp[mi][4 * ks];
+        const uint8_t* g = ap[mi] + 128 * ks;
+        q.a[mi].lo = *reinterpret_cast<const uint4*>(g);
+        q.a[mi].hi = *reinterpret_cast<const uint4*>(g + 64);
+        q.as[mi] = asp[mi][4 * ks];
+      }
+    };
+    auto compute = [&](const Slot& q) {
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi) {
+        const v8i av = as_v8i(q.a[mi]);
 #pragma unroll
         for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
-          for (int h = 0; h < NB; ++h) acc[mi][ni][h] = mfma_f8f4(av, as_v8i(cb[ni][h]), acc[mi][ni][h], sa, cs[ni][h]);
+          for (int h = 0; h < NB; ++h)
+            acc[mi][ni][h] = mfma_f8f4(av, as_v8i(q.b[ni][h]), acc[mi][ni][h], q.as[mi], q.bs[ni][h]);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < nks) load(j, sl[j]);
+    int ks = 0;
+    for (; ks + 2 * D <= nks; ks += D) {  // steady state: every refill is in range
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        compute(sl[j]);
+        load(ks + j + D, sl[j]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < D; ++j)  // last refills
+      if (ks + j < nks) {
+        compute(sl[j]);
+        if (ks + j + D < nks) load(ks + j + D, sl[j]);
+      }
+    ks += D;
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (ks + j < nks) compute(sl[j]);
   }
   epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
 }
@@ -304,17 +429,6 @@ int gemm_mtile(int shape) {
   return shape == GEMM_STREAM16 ? 16 : shape == GEMM_STREAM64 ? 64 : gemm_wide_mtile();
 }
 
-template <int MW, int NW, int EPI>
-static hipError_t launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int NT = 4 * 16 * NW;
-  const int n_ntiles = (a.N + NT - 1) / NT;
-  const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  bf16_gemm_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
-}
-
 // The epilogue addresses a wave's output rows with 32-bit offsets from a
 // wave-uniform base (gemm_epilogue.hpp): N and ldc below 2^22 keep 128 rows
 // of fp32 output under 4 GB.
@@ -323,10 +437,45 @@ static bool epilogue_dims_ok(const GemmArgs& a) {
 }
 
 hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
+  if (!epilogue_dims_ok(a) || shape != GEMM_WIDE) return hipErrorInvalidValue;
+  return launch_bf16_gemm_wide(a, s);
+}
+
+int bf16_mx_splitk_slices(int M, int N, int K) {
+  const int n_ntiles = (N + 127) / 128, mtiles = (M + 63) / 64;
+  const int tiles = n_ntiles * mtiles;
+  int S = (1024 + 4 * tiles - 1) / (4 * tiles);  // about 1024 waves
+  const int ksteps = K / 128;
+  S = S < 8 ? S : 8;                            // partials stay small next to the weights
+  S = S < ksteps ? S : ksteps;
+  return S > 0 ? S : 1;
+}
+
+hipError_t launch_bf16_mx_splitk(const GemmArgs& a, float* part, int S, float* z, uint8_t* zq, uint8_t* zqs,
+                                 hipStream_t s) {
+  if (a.nseg != 1 || a.offsets != nullptr || a.G != 1 || a.seg[0].K % 128 != 0 || a.N % 32 != 0 || a.M <= 0 ||
+      S <= 0)
+    return hipErrorInvalidValue;
   if (!epilogue_dims_ok(a)) return hipErrorInvalidValue;
-  if (shape == GEMM_WIDE) return launch_bf16_gemm_wide(a, s);
-  return shape == GEMM_STREAM16 ? launch_bf16_cfg<1, 2, EPI_F32_QUANT>(a, s)
-                                : launch_bf16_cfg<4, 2, EPI_F32_QUANT>(a, s);
+  const int ksteps = a.seg[0].K / 128;
+  const int kper = (ksteps + S - 1) / S;
+  const int Sx = (ksteps + kper - 1) / kper;  // slices actually used
+  const bool small = a.M <= 16;
+  const int MT = small ? 16 : 64;
+  const int n_ntiles = (a.N + 127) / 128;
+  const int64_t grid = (int64_t)((a.M + MT - 1) / MT) * n_ntiles;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (small)
+    bf16_mx_splitk_kernel<1, 2><<<dim3((unsigned)grid, (unsigned)Sx), dim3(256), 0, s>>>(a, part, kper);
+  else
+    bf16_mx_splitk_kernel<4, 2><<<dim3((unsigned)grid, (unsigned)Sx), dim3(256), 0, s>>>(a, part, kper);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)a.M * (a.N / 32) * 16;
+  const int64_t blocks = (threads + 255) / 256;
+  if (zq) splitk_reduce_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(part, Sx, a.M, a.N, z, zq, zqs);
+  else splitk_reduce_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(part, Sx, a.M, a.N, z, nullptr, nullptr);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) {

@@ -11,10 +11,11 @@
 //     and out, on the fp32 matrix cores (v_mfma_f32_16x16x4f32) with 64x64
 //     tiles staged through LDS; for few tiles (decode) the K range is split
 //     over extra workgroups and the slices summed in a fixed order.
-//   topk: one wave per token; the E selection keys sit in LDS, each lane keeps
-//     the best key of its strided slice, and k rounds of a 64-lane
-//     (key desc, id asc) reduction pick the winners in slot order; only the
-//     winning lane rescans its slice.  k <= 64 (slot j is held by lane j).
+//   topk: one wave per token; the E selection keys and raw scores sit in LDS,
+//     each lane keeps the best key of its strided slice, and k rounds of a
+//     64-lane (key desc, id asc) reduction (DPP within rows, readlane across)
+//     pick the winners in slot order; only the winning lane rescans its
+//     slice.  k <= 64 (slot j is held by lane j).
 #include <float.h>
 
 #include "kernels.hpp"
@@ -144,6 +145,32 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 }
 }  // namespace
 
+// Best (key, id) over the wave, in every lane: DPP swaps within rows of 16
+// lanes (pairs, pairs of pairs, half-row mirror, row mirror), then the four
+// row winners compared through readlane (uniform result, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& wk, int& wi) {
+  const float ok = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(wk), CTRL, 0xF, 0xF, true));
+  const int oi = __builtin_amdgcn_mov_dpp(wi, CTRL, 0xF, 0xF, true);
+  if (better(ok, oi, wk, wi)) { wk = ok; wi = oi; }
+}
+__device__ __forceinline__ void wave_best(float& wk, int& wi) {
+  best_step<0xB1>(wk, wi);   // quad_perm 1,0,3,2
+  best_step<0x4E>(wk, wi);   // quad_perm 2,3,0,1
+  best_step<0x141>(wk, wi);  // row_half_mirror
+  best_step<0x140>(wk, wi);  // row_mirror
+  float bk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), 0));
+  int bi = __builtin_amdgcn_readlane(wi, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float k2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), 16 * r));
+    const int i2 = __builtin_amdgcn_readlane(wi, 16 * r);
+    if (better(k2, i2, bk, bi)) { bk = k2; bi = i2; }
+  }
+  wk = bk;
+  wi = bi;
+}
+
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
                                                   const float* __restrict__ sel_bias, int T, int E, int k,
                                                   int32_t* __restrict__ ids, float* __restrict__ gates) {
@@ -151,16 +178,19 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;  // no block-level barrier below
-  float* keys = keys_smem + (int64_t)wave * E;
+  float* keys = keys_smem + (int64_t)wave * 2 * E;  // selection keys, then raw scores
+  float* scores = keys + E;
   const float* lrow = logits + (int64_t)t * E;
 
   float bk = -INFINITY;
   int bi = 0x7fffffff;
   for (int e = lane; e < E; e += 64) {
-    float key = sigmoidf(lrow[e]);
+    const float sc = sigmoidf(lrow[e]);
+    float key = sc;
     if (sel_bias) key += sel_bias[e];
     key = fmaxf(key, -FLT_MAX);  // NaN / -inf inputs rank last but stay above "taken" (-inf)
     keys[e] = key;
+    scores[e] = sc;
     if (better(key, e, bk, bi)) { bk = key; bi = e; }
   }
   float ssum = 0.f;
@@ -169,13 +199,8 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   for (int r = 0; r < k; ++r) {
     float wk = bk;
     int wi = bi;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      float ok = __shfl_xor(wk, o, 64);
-      int oi = __shfl_xor(wi, o, 64);
-      if (better(ok, oi, wk, wi)) { wk = ok; wi = oi; }
-    }
-    const float sw = sigmoidf(lrow[wi]);
+    wave_best(wk, wi);
+    const float sw = scores[wi];
     ssum += sw;  // every lane adds the same values in the same (slot) order
     if (lane == r) { mys = sw; myid = wi; }
     if ((wi & 63) == lane) {  // owner marks it taken and rescans its slice
@@ -194,10 +219,82 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   }
 }
 
+// Same selection with each lane's keys and raw scores in registers (expert
+// e = lane + 64 j in slot j, E <= 64 * KPL): the winner's lane marks it taken
+// and rescans its KPL keys without touching memory, and the winner's score is
+// broadcast by readlane.  Same keys, same order of comparisons and sums as
+// topk_kernel, so the same ids and gates.
+template <int KPL>
+__global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__ logits,
+                                                      const float* __restrict__ sel_bias, int T, int E, int k,
+                                                      int32_t* __restrict__ ids, float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* lrow = logits + (int64_t)t * E;
+  float key[KPL], scr[KPL];
+  float bk = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = -INFINITY;  // past E: never selected (k <= E finite keys exist)
+    scr[j] = 0.f;
+    if (e < E) {
+      const float sc = sigmoidf(lrow[e]);
+      float kk = sc;
+      if (sel_bias) kk += sel_bias[e];
+      kk = fmaxf(kk, -FLT_MAX);
+      key[j] = kk;
+      scr[j] = sc;
+      if (better(kk, e, bk, bi)) { bk = kk; bi = e; }
+    }
+  }
+  float ssum = 0.f;
+  float mys = 0.f;
+  int myid = 0;
+  for (int r = 0; r < k; ++r) {
+    float wk = bk;
+    int wi = bi;
+    wave_best(wk, wi);
+    const int wj = wi >> 6;  // uniform
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) mine = j == wj ? scr[j] : mine;
+    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), wi & 63));
+    ssum += sw;
+    if (lane == r) { mys = sw; myid = wi; }
+    if ((wi & 63) == lane) {
+      bk = -INFINITY;
+      bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        key[j] = j == wj ? -INFINITY : key[j];
+        if (better(key[j], lane + 64 * j, bk, bi)) { bk = key[j]; bi = lane + 64 * j; }
+      }
+    }
+  }
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = myid;
+    gates[(int64_t)t * k + lane] = mys / ssum;
+  }
+}
+
 hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
                        float* gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const size_t smem = (size_t)4 * E * sizeof(float);
+  if (E <= 64 * 16) {
+    topk_reg_kernel<16><<<dim3((T + 3) / 4), dim3(256), 0, s>>>(logits, sel_bias, T, E, k, ids, gates);
+    return hipGetLastError();
+  }
+  const size_t smem = (size_t)4 * 2 * E * sizeof(float);  // 4 waves x (keys + scores): 128 KB at E = 4096
+  static bool attr_set = false;                          // per process, before the first launch
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 2 * 4096 * (int)sizeof(float));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   topk_kernel<<<dim3((T + 3) / 4), dim3(256), smem, s>>>(logits, sel_bias, T, E, k, ids, gates);
   return hipGetLastError();
 }

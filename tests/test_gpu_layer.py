@@ -97,3 +97,11 @@ def test_determinism_two_forwards_bitwise_equal():
 
 def test_mid_layer_parity():
     _layer_case(synth.config("mid"))
+
+
+def test_tiny_many_experts_lds_topk():
+    """More than 1024 routed experts: top-k keeps its keys in LDS instead of
+    registers (the K3 router has 896)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("tiny", T=40), n_routed=1280, top_k=6)
+    _layer_case(cfg, check_codes=False)
