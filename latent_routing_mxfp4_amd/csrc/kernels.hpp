@@ -30,12 +30,16 @@ hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, 
                                    uint16_t* out, hipStream_t s);
 
 // ---- Router (router.hip) ----------------------------------------------------
-// logits[T][E] = z[T][L] w[E][L]^T (+ bias[E]) in fp32 on the fp32 matrix cores.
-// `partial` (router_split(T, E, L) * T * E floats, or null when that is 1)
-// holds the K-slice sums when the tile grid is small.
+// logits[T][E] = z[T][L] w[E][L]^T (+ bias[E]) at fp32 accuracy.  Many tokens
+// (router_bf16x3 true): three exact bf16 pieces per operand on the bf16 matrix
+// cores, with w's pieces written to `wplanes` (3 * E * L bf16) first.  Few
+// tokens: the fp32 matrix cores; `partial` (router_split(T, E, L) * T * E
+// floats, or null when that is 1) holds the K-slice sums when the tile grid is
+// small.
 int router_split(int T, int E, int L);
+bool router_bf16x3(int T, int E, int L);
 hipError_t launch_router_logits(const float* z, const float* w, const float* logit_bias, int T, int E,
-                                int L, float* logits, float* partial, hipStream_t s);
+                                int L, float* logits, float* partial, uint16_t* wplanes, hipStream_t s);
 // Per token: s = sigmoid(logit), key = s + sel_bias, top-k by (key desc, id asc),
 // gates = s / sum(s over the k winners).
 hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,

@@ -39,7 +39,7 @@ constexpr int64_t kFewRows = 256;  // decode-shaped batches: weight-streaming ke
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye,
+  size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, wrpl, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye,
       ylat, yq, yqs, hs, hss, total;
 };
 
@@ -69,6 +69,8 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   {
     const int split = T > 0 ? moe::router_split((int)T, (int)E, (int)L) : 1;
     p.rpart = take(split > 1 ? (size_t)split * T * E * 4 : 0);  // router K-slice partial sums
+    // bf16 pieces of the router weight (many-token router)
+    p.wrpl = take(T > 0 && moe::router_bf16x3((int)T, (int)E, (int)L) ? (size_t)3 * E * L * 2 : 0);
   }
   p.ids = take(P * 4);
   p.gates = take(P * 4);
@@ -266,7 +268,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
 
   // 3-4. router
   MOE_HIP(moe::launch_router_logits(z, w.w_router, w.router_logit_bias, T, E, L, logits,
-                                    at<float>(ws, pl.rpart), s));
+                                    at<float>(ws, pl.rpart), at<uint16_t>(ws, pl.wrpl), s));
   MOE_HIP(mark(MOE_EV_LOGITS));
   MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, ids, gates, s));
   MOE_HIP(mark(MOE_EV_TOPK));

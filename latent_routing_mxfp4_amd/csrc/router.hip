@@ -96,6 +96,197 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float* __restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// Many tokens: the same fp32 product on the bf16 matrix cores.  Every fp32
+// value is split exactly into three bf16 pieces by truncation (x0 = the top 8
+// significant bits, x1 = the next 8 of x - x0, x2 = x - x0 - x1, each exact),
+// and z w ~ z0 w0 + z0 w1 + z1 w0 + z0 w2 + z1 w1 + z2 w0: every term is an
+// exact product accumulated in fp32; the three dropped terms are below
+// 2^-23 |z w| together, the size of one fp32 rounding of the product.  Six
+// v_mfma_f32_32x32x16_bf16 run at about 2.2 PFLOP/s against 157 TFLOP/s for
+// the fp32 instruction.  The router weight is split once per forward
+// (split3_kernel); the latent is split while it is staged into LDS.
+//
+// Tile 128 tokens x 128 experts, 4 waves of 64 x 64 (2 x 2 MFMA tiles of
+// 32 x 32), K chunks of 32 staged as three bf16 planes per operand with an
+// 80-byte row stride (eight consecutive rows hit distinct banks); the next
+// chunk's global loads are issued before the current chunk's MFMAs.
+// v_mfma_f32_32x32x16_bf16 operands (probed on gfx950): lane l holds row
+// (A) / column (B) l % 32, K [8 (l / 32), +8); D register i of lane l is
+// column l % 32, row 8 (i / 4) + 4 (l / 32) + i % 4.
+namespace {
+constexpr int BT = 128, BE = 128, BK = 32;
+constexpr int BROW = 80;                // bytes per LDS row (32 bf16 + 16 padding)
+constexpr int BPLANE = 128 * BROW;      // one plane of one operand
+constexpr int BOP = 3 * BPLANE;         // three planes
+typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
+typedef float f16v_r __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t hi16_pair(uint32_t lo_elem, uint32_t hi_elem) {
+  return (lo_elem >> 16) | (hi_elem & 0xFFFF0000u);
+}
+// Three bf16 pieces of four fp32 values, packed two per dword per plane.
+__device__ __forceinline__ void split3x4(const float4& v, uint2 (&pl)[3]) {
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b0 = __float_as_uint(x[i]) & 0xFFFF0000u;
+    const float r = x[i] - __uint_as_float(b0);
+    const uint32_t b1 = __float_as_uint(r) & 0xFFFF0000u;
+    const float r2 = r - __uint_as_float(b1);
+    p0[i] = b0;
+    p1[i] = b1;
+    p2[i] = __float_as_uint(r2);
+  }
+  pl[0] = make_uint2(hi16_pair(p0[0], p0[1]), hi16_pair(p0[2], p0[3]));
+  pl[1] = make_uint2(hi16_pair(p1[0], p1[1]), hi16_pair(p1[2], p1[3]));
+  pl[2] = make_uint2(hi16_pair(p2[0], p2[1]), hi16_pair(p2[2], p2[3]));
+}
+}  // namespace
+
+// planes[p][i] = piece p of w[i] (bf16 bits), i < n (n % 4 == 0).
+__global__ void __launch_bounds__(256) split3_kernel(const float4* __restrict__ w, int64_t n4,
+                                                     uint2* __restrict__ planes) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    uint2 pl[3];
+    split3x4(w[i], pl);
+    planes[i] = pl[0];
+    planes[n4 + i] = pl[1];
+    planes[2 * n4 + i] = pl[2];
+  }
+}
+
+__global__ void __launch_bounds__(256) router_logits_bf16x3_kernel(const float* __restrict__ z,
+                                                                  const uint16_t* __restrict__ wpl,
+                                                                  const float* __restrict__ bias, int T, int E,
+                                                                  int L, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t rl_lds[];
+  uint8_t* const As = rl_lds;        // 3 planes x 128 token rows
+  uint8_t* const Bs = rl_lds + BOP;  // 3 planes x 128 expert rows
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int t0 = blockIdx.y * BT, e0 = blockIdx.x * BE;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int64_t plane = (int64_t)E * L;  // elements per weight plane
+
+  // Staging: A, thread handles float4 f = tid + 256 it (it < 4): row f / 8,
+  // K 4 (f % 8); B, uint4 g = tid + 256 it (it < 6): plane g / 512, row
+  // (g % 512) / 4, K 8 (g % 4).  Rows past T or E repeat the last one.
+  // Source pointers are fixed per thread; a chunk adds k0.
+  const float* za[4];
+  const uint16_t* wb[6];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int f = tid + 256 * it;
+    int r = t0 + (f >> 3);
+    r = r < T ? r : T - 1;
+    za[it] = z + (int64_t)r * L + 4 * (f & 7);
+  }
+#pragma unroll
+  for (int it = 0; it < 6; ++it) {
+    const int g = tid + 256 * it;
+    const int p = g >> 9, q = g & 511;
+    int r = e0 + (q >> 2);
+    r = r < E ? r : E - 1;
+    wb[it] = wpl + p * plane + (int64_t)r * L + 8 * (q & 3);
+  }
+  float4 ra0, ra1, ra2, ra3;
+  uint4 rb0, rb1, rb2, rb3, rb4, rb5;
+#define RL_GLOAD(k0)                                                     \
+  do {                                                                   \
+    ra0 = *reinterpret_cast<const float4*>(za[0] + (k0));                \
+    ra1 = *reinterpret_cast<const float4*>(za[1] + (k0));                \
+    ra2 = *reinterpret_cast<const float4*>(za[2] + (k0));                \
+    ra3 = *reinterpret_cast<const float4*>(za[3] + (k0));                \
+    rb0 = *reinterpret_cast<const uint4*>(wb[0] + (k0));                 \
+    rb1 = *reinterpret_cast<const uint4*>(wb[1] + (k0));                 \
+    rb2 = *reinterpret_cast<const uint4*>(wb[2] + (k0));                 \
+    rb3 = *reinterpret_cast<const uint4*>(wb[3] + (k0));                 \
+    rb4 = *reinterpret_cast<const uint4*>(wb[4] + (k0));                 \
+    rb5 = *reinterpret_cast<const uint4*>(wb[5] + (k0));                 \
+  } while (0)
+  auto store_a = [&](int it, const float4& v) {
+    const int f = tid + 256 * it;
+    uint2 pl[3];
+    split3x4(v, pl);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      *reinterpret_cast<uint2*>(As + p * BPLANE + (f >> 3) * BROW + 8 * (f & 7)) = pl[p];
+  };
+  auto store_b = [&](int it, const uint4& v) {
+    const int g = tid + 256 * it;
+    const int p = g >> 9, q = g & 511;
+    *reinterpret_cast<uint4*>(Bs + p * BPLANE + (q >> 2) * BROW + 16 * (q & 3)) = v;
+  };
+
+  f16v_r acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  RL_GLOAD(0);
+  for (int k0 = 0; k0 < L; k0 += BK) {
+    __syncthreads();  // previous chunk's fragments are read
+    store_a(0, ra0);
+    store_a(1, ra1);
+    store_a(2, ra2);
+    store_a(3, ra3);
+    store_b(0, rb0);
+    store_b(1, rb1);
+    store_b(2, rb2);
+    store_b(3, rb3);
+    store_b(4, rb4);
+    store_b(5, rb5);
+    __syncthreads();
+    if (k0 + BK < L) RL_GLOAD(k0 + BK);  // lands during this chunk's MFMAs
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int koff = 2 * (16 * kk + 8 * lh);
+      bf16x8_r af[2][3], bf[2][3];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          af[t][p] = *reinterpret_cast<const bf16x8_r*>(As + p * BPLANE + (wm + 32 * t + l32) * BROW + koff);
+          bf[t][p] = *reinterpret_cast<const bf16x8_r*>(Bs + p * BPLANE + (wn + 32 * t + l32) * BROW + koff);
+        }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          f16v_r c = acc[a][b];
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][0], bf[b][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][0], bf[b][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][1], bf[b][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][0], bf[b][2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][1], bf[b][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a][2], bf[b][0], c, 0, 0, 0);
+          acc[a][b] = c;
+        }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int e = e0 + wn + 32 * b + l32;
+    if (e >= E) continue;
+    const float bb = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + wm + 32 * a + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (t < T) out[(int64_t)t * E + e] = acc[a][b][i] + bb;
+      }
+  }
+#undef RL_GLOAD
+}
+
 // logits = sum over slices s = 0 .. split-1, in that order, + bias.
 __global__ void __launch_bounds__(256) router_reduce_kernel(const float* __restrict__ part, const float* __restrict__ bias,
                                                            int64_t n, int E, int split, float* __restrict__ logits) {
@@ -115,9 +306,33 @@ int router_split(int T, int E, int L) {
   return split > chunks ? chunks : split;
 }
 
+bool router_bf16x3(int T, int E, int L) {
+  return L % BK == 0 && (int64_t)((T + BT - 1) / BT) * ((E + BE - 1) / BE) >= 128;
+}
+
 hipError_t launch_router_logits(const float* z, const float* w, const float* bias, int T, int E, int L,
-                                float* logits, float* partial, hipStream_t s) {
+                                float* logits, float* partial, uint16_t* wplanes, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (router_bf16x3(T, E, L) && wplanes != nullptr) {
+    const int64_t n4 = (int64_t)E * L / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    split3_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(reinterpret_cast<const float4*>(w), n4,
+                                                               reinterpret_cast<uint2*>(wplanes));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr size_t smem = 2 * BOP;
+    static bool attr_set = false;  // per process, before the first launch
+    if (!attr_set) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_bf16x3_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    dim3 grid((E + BE - 1) / BE, (T + BT - 1) / BT);
+    router_logits_bf16x3_kernel<<<grid, dim3(256), smem, s>>>(z, wplanes, bias, T, E, L, logits);
+    return hipGetLastError();
+  }
   const int split = router_split(T, E, L);
   const int kslice = ((L / RK + split - 1) / split) * RK;
   const int nz = (L + kslice - 1) / kslice;

@@ -105,3 +105,11 @@ def test_tiny_many_experts_lds_topk():
     import dataclasses
     cfg = dataclasses.replace(synth.config("tiny", T=40), n_routed=1280, top_k=6)
     _layer_case(cfg, check_codes=False)
+
+
+def test_tiny_many_tokens_split_bf16_router():
+    """Enough (token, expert) tiles for the router to run as three-piece bf16
+    products (2048 tokens x 1024 experts = 128 tiles of 128 x 128)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("tiny", T=2048), n_routed=1024, top_k=8)
+    _layer_case(cfg, check_codes=False)
