@@ -90,7 +90,7 @@ def algorithmic_work(cfg, counts):
     return work
 
 
-def run_workload(name, steps, warmup, weights, hip, say):
+def run_workload(name, steps, warmup, weights, hip, say, logit_bias=None):
     import numpy as np
     import torch
 
@@ -100,6 +100,9 @@ def run_workload(name, steps, warmup, weights, hip, say):
 
     cfg = synth.config(name)
     shape = LY.LayerShape.of(cfg)
+    if logit_bias is not None:   # same weights, another router logit bias (the skewed batch)
+        weights = dict(weights)
+        weights["router_logit_bias"] = torch.from_numpy(logit_bias).cuda()
     lay = LY.LatentMoE(shape, weights, cfg.T)
     x = torch.from_numpy(synth.gen_hidden(cfg)).cuda()
     y = torch.empty_like(x)
@@ -128,6 +131,10 @@ def run_workload(name, steps, warmup, weights, hip, say):
     stage_ms = {}
     for si, sname in enumerate(_lib.STAGES):
         stage_ms[sname] = statistics.mean(evs.elapsed(i, si, si + 1) for i in range(steps))
+    # per-step forward time between the first and the last stage event
+    per_step = sorted(evs.elapsed(i, 0, len(_lib.STAGES)) for i in range(steps))
+    pick = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
+    step_stats = {"median": statistics.median(per_step), "p10": pick(0.1), "p90": pick(0.9)}
     evs.close()
 
     # routing statistics of this batch (outside the timed region)
@@ -136,6 +143,7 @@ def run_workload(name, steps, warmup, weights, hip, say):
     torch.cuda.synchronize()
     counts = tb["counts"].cpu().numpy()
     work = algorithmic_work(cfg, counts)
+    work["step_events_ms"] = step_stats
     lay.close()
     say(f"{name}: {ms_per_step:.3f} ms/step; stages (ms): " +
         ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
@@ -303,12 +311,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="k3_prefill", choices=["k3_prefill", "k3_decode", "k3_skew"])
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--skew-steps", type=int, default=5,
+                    help="steps of the 8192-token Zipf-skewed batch reported under 'skew' (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="run one 1 GiB read + 1 GiB write elementwise kernel first (calibrates HBM counters)")
+                    help="kept for the profile command: the copy probe now always runs first")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -327,12 +337,18 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     hip = _hip()
-    if args.copy_probe:
-        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        torch.mul(a, 1.0, out=b)
-        torch.cuda.synchronize()
-        del a, b
+    # STREAM-style probe on this GPU: 1 GiB read + 1 GiB write (also the
+    # calibration dispatch of the HBM counters in the committed profile).
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.mul(a, 1.0, out=b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.mul(a, 1.0, out=b)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
     cfg = synth.config(args.workload)
     t = time.perf_counter()
     shape = LY.LayerShape.of(cfg)
@@ -369,6 +385,7 @@ def main():
                                f"E={cfg.n_routed} top-{cfg.top_k}, {cfg.n_shared} shared, "
                                f"d_ff={cfg.d_ff_routed}", "tokens": cfg.T, "parallelism": "single GPU"},
         "roofline": roof,
+        "step_events_ms": work["step_events_ms"],
         "layer": {"mx_tflops": work["mx_flops"] / (ms / 1e3) / 1e12,
                   "mx_frac": work["mx_flops"] / (ms / 1e3) / 1e12 / PEAK_MX_TFLOPS,
                   "stage_ms": stages, "touched_experts": work["touched_experts"],
@@ -387,11 +404,28 @@ def main():
                          "ms_per_step": dms, "roofline": droof,
                          "layer_gbs": dwork["layer_bytes"] / (dms / 1e3) / 1e9,
                          "layer_hbm_frac": dwork["layer_bytes"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS,
-                         "stage_ms": dst, "touched_experts": dwork["touched_experts"]}
+                         "stage_ms": dst, "step_events_ms": dwork["step_events_ms"],
+                         "touched_experts": dwork["touched_experts"]}
+    if args.skew_steps > 0 and args.workload == "k3_prefill":
+        scfg = synth.config("k3_skew")
+        kcfg, kms, kst, kwork, kcounts = run_workload("k3_skew", args.skew_steps, args.warmup, weights, hip, say,
+                                                      logit_bias=synth.gen_logit_bias(scfg))
+        out["skew"] = {"workload": f"{kcfg.name}: T={kcfg.T}, Zipf(1.1) router logit bias", "value": kcfg.T / (kms / 1e3),
+                       "unit": "tokens/s", "ms_per_step": kms,
+                       "mx_frac": kwork["mx_flops"] / (kms / 1e3) / 1e12 / PEAK_MX_TFLOPS,
+                       "expert_up_tflops": kwork["expert_up_flops"] / (kst["expert_up"] / 1e3) / 1e12,
+                       "max_expert_load": int(kcounts.max()), "mean_expert_load": float(kcounts.mean()),
+                       "empty_experts": int((kcounts == 0).sum()), "stage_ms": kst,
+                       "step_events_ms": kwork["step_events_ms"]}
+    out["hbm_copy_probe_gbs"] = copy_gbs
     if args.workload == "k3_decode":
         dom = stages["expert_up"]
+        tp = profiled_traffic(cfg.name)
         out["roofline"] = {"bound": "hbm", "achieved": work["expert_up_bytes"] / (dom / 1e3) / 1e9,
-                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "kernel": "expert_up", "traffic": None}
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "kernel": "expert_up (routed gate/up weight-streaming GEMM + SwiGLU + MXFP8)",
+                           "traffic": None if tp is None else tp["bytes"],
+                           "algorithmic_bytes": work["expert_up_bytes"]}
         out["roofline"]["frac"] = out["roofline"]["achieved"] / PEAK_HBM_GBS
 
     del weights

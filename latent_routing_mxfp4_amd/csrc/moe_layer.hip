@@ -328,7 +328,9 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(mark(MOE_EV_EXPERT_DOWN));
 
   // 8. combine
-  MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, ylat, yq, yqs, s));
+  // The fp32 combined latent is only kept for a trace; yq is what the
+  // up-projection reads.
+  MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, tr && tr->y_lat ? ylat : nullptr, yq, yqs, s));
   MOE_HIP(mark(MOE_EV_COMBINE));
 
   // 9. shared experts, first half
