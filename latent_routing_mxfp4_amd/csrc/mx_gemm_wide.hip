@@ -72,6 +72,10 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
   if (!decode_lds_tile<WD_M>(p, NCOL, g, mt, nt, rows, row_base)) return;
   const int m0 = mt * WD_M;
   const int col0 = nt * NCOL;
+  // 16-row fragments of this wave that hold at least one row of the group
+  // (the last M-tile of a group is usually partly past its rows).
+  int mvalid = (rows - m0 - 64 * wm + 15) >> 4;
+  mvalid = __builtin_amdgcn_readfirstlane(mvalid < 0 ? 0 : (mvalid > 4 ? 4 : mvalid));
 
   auto a_src_row = [&](int trow) -> int64_t {
     int r = m0 + trow;
@@ -201,24 +205,33 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
       for (int ni = 0; ni < 8; ++ni)
         bs_all[ni] = *reinterpret_cast<const uint32_t*>(buf + WD_OFF_BS + 4 * b_row(wn, ni, r16));
       v8i bf[8];
-#pragma unroll
-      for (int ni = 0; ni < 8; ++ni) {
+      auto rd_b = [&](int ni) {
         const int blk = b_row(wn, ni, 0) >> 4;
         const uint4 v = *reinterpret_cast<const uint4*>(buf + WD_OFF_B + 1024 * blk + 16 * lane);
         bf[ni][0] = (int)v.x; bf[ni][1] = (int)v.y; bf[ni][2] = (int)v.z; bf[ni][3] = (int)v.w;
         bf[ni][4] = 0; bf[ni][5] = 0; bf[ni][6] = 0; bf[ni][7] = 0;
-      }
+      };
+      // The first MFMAs wait only for half of the B fragments and A fragment
+      // 0: all eight waves read right after the barrier, so a smaller first
+      // batch shortens the time the matrix cores wait for LDS.
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) rd_b(ni);
       v8i av = rd_a(buf, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ni = 4; ni < 8; ++ni) rd_b(ni);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         v8i an;
         if (mi < 3) an = rd_a(buf, mi + 1);  // next fragment's read overlaps these MFMAs
         const int sa = (int)(as_all[mi] >> sh);
+        if (mi < mvalid) {  // fragments wholly past the group's last row are skipped
 #pragma unroll
-        for (int ni = 0; ni < 8; ++ni) {
-          const int sb = (int)(bs_all[ni] >> sh);
-          if (SWI) acc[mi][ni & 3][ni >> 2] = mfma_f8f4(av, bf[ni], acc[mi][ni & 3][ni >> 2], sa, sb);
-          else acc[mi][ni][0] = mfma_f8f4(av, bf[ni], acc[mi][ni][0], sa, sb);
+          for (int ni = 0; ni < 8; ++ni) {
+            const int sb = (int)(bs_all[ni] >> sh);
+            if (SWI) acc[mi][ni & 3][ni >> 2] = mfma_f8f4(av, bf[ni], acc[mi][ni & 3][ni >> 2], sa, sb);
+            else acc[mi][ni][0] = mfma_f8f4(av, bf[ni], acc[mi][ni][0], sa, sb);
+          }
         }
         if constexpr (decltype(with_issue)::value) {
           __builtin_amdgcn_sched_barrier(0);
