@@ -30,6 +30,14 @@ The steps follow the pages in their order:
 10. Shared experts at full width on ``xq``, summed with the routed branch
     (Moat page, "How the router picks 16 of 896": both branches are summed).
 
+A non-latent layer (``W.w_down is None``; the second workload, a K2-shaped
+MoE) skips steps 2 and 9: the router reads the fp32 input, the experts read
+``xq`` at model width, and the combined routed output is summed with the
+shared experts as is.  With ``W.gating == "softmax"`` the selection key is the
+logit (plus the selection bias) and the gates are the softmax over the k
+winners' logits, the gate of the MoE data-path toy (Four Bits at a Time,
+"What it takes to serve it").
+
 Decision precision.  Where a float decides an integer (an MX code, the top-k
 order), the oracle first rounds its fp64 value to fp32, the precision the GPU
 path decides in (``decide=np.float32``); ``decide=None`` keeps pure fp64.
@@ -85,8 +93,8 @@ def silu(v):
 @dataclasses.dataclass
 class LayerWeights:
     """MX weights of one layer (oracle-side codes), fp32 router and biases."""
-    w_down: MXTensor                  # [L][d]
-    w_up: MXTensor                    # [d][L]
+    w_down: Optional[MXTensor]        # [L][d]; None: no latent (L = d)
+    w_up: Optional[MXTensor]          # [d][L]; None with w_down
     w_router: np.ndarray              # fp32 [E][L]
     w_gate_e: list                    # E x MXTensor [F][L]   (entries may be filled lazily)
     w_up_e: list                      # E x MXTensor [F][L]
@@ -96,6 +104,7 @@ class LayerWeights:
     w_down_s: list                    # S x MXTensor [d][Fs]
     logit_bias: Optional[np.ndarray] = None       # fp32 [E] or None
     selection_bias: Optional[np.ndarray] = None   # fp32 [E] or None
+    gating: str = "sigmoid"                       # or "softmax" (over the winners' logits)
 
 
 # --------------------------------------------------------------------------- routing
@@ -103,16 +112,30 @@ class LayerWeights:
 
 @dataclasses.dataclass
 class Routing:
-    scores: np.ndarray     # [T][E] sigmoid scores (fp64)
+    scores: np.ndarray     # [T][E] sigmoid scores (fp64); the logits with softmax gating
     sel: np.ndarray        # [T][E] selection keys
     ids: np.ndarray        # [T][k] int32, slot order = descending key, ties -> lower id
     gates: np.ndarray      # [T][k] fp64, sums to 1 per token
     gap: np.ndarray        # [T] key(k-th) - key(k+1-th); +inf when k == E
 
 
+def winner_gates(scores: np.ndarray, ids: np.ndarray, gating: str = "sigmoid") -> np.ndarray:
+    """Gates of the selected experts: sigmoid scores over their sum (Moat page,
+    Fig. 2), or the softmax over the winners' logits (the MoE data-path toy)."""
+    win = np.take_along_axis(scores, ids, axis=1)
+    if gating == "softmax":
+        e = np.exp(win - win.max(axis=1, keepdims=True))
+        return e / e.sum(axis=1, keepdims=True)
+    if gating != "sigmoid":
+        raise ValueError(gating)
+    return win / win.sum(axis=1, keepdims=True)
+
+
 def route(z: np.ndarray, w_router: np.ndarray, k: int, logit_bias=None, selection_bias=None,
-          decide=np.float32) -> Routing:
-    """Sigmoid router on the latent and top-k selection (Moat page, Fig. 2)."""
+          decide=np.float32, gating: str = "sigmoid") -> Routing:
+    """Sigmoid router on the latent and top-k selection (Moat page, Fig. 2).
+    With ``gating="softmax"`` the keys are the logits themselves (a monotone
+    change of the sigmoid's order) and the gates the softmax of the winners'."""
     z = np.asarray(z, dtype=np.float64)
     if decide is not None:
         z = z.astype(decide).astype(np.float64)   # the router reads the fp32 latent
@@ -121,7 +144,7 @@ def route(z: np.ndarray, w_router: np.ndarray, k: int, logit_bias=None, selectio
         logits = logits + np.asarray(logit_bias, dtype=np.float64)[None, :]
     if decide is not None:
         logits = logits.astype(decide).astype(np.float64)
-    s = sigmoid(logits)
+    s = sigmoid(logits) if gating == "sigmoid" else logits
     if decide is not None:
         s = s.astype(decide).astype(np.float64)
     sel = s if selection_bias is None else s + np.asarray(selection_bias, dtype=np.float64)[None, :]
@@ -136,8 +159,7 @@ def route(z: np.ndarray, w_router: np.ndarray, k: int, logit_bias=None, selectio
         ids[t] = order[:k]
         if k < E:
             gap[t] = sel[t, order[k - 1]] - sel[t, order[k]]
-    win = np.take_along_axis(s, ids, axis=1)
-    gates = win / win.sum(axis=1, keepdims=True)
+    gates = winner_gates(s, ids, gating)
     return Routing(scores=s, sel=sel, ids=ids, gates=gates, gap=gap)
 
 
@@ -224,17 +246,20 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
     E = W.w_router.shape[0]
     L = W.w_router.shape[1]
 
+    latent = W.w_down is not None
     xq = quant(x, "e4m3", decide)                                   # step 1
-    z = mm(xq, W.w_down)                                            # step 2
-    r = route(z, W.w_router, top_k, W.logit_bias, W.selection_bias, decide)   # steps 3-5
+    z = mm(xq, W.w_down) if latent else x.astype(np.float64)        # step 2 (latent only)
+    r = route(z, W.w_router, top_k, W.logit_bias, W.selection_bias, decide, W.gating)   # steps 3-5
     if ids_override is not None:
         ids = np.asarray(ids_override, dtype=np.int32)
-        win = np.take_along_axis(r.scores, ids, axis=1)
-        r = Routing(r.scores, r.sel, ids, win / win.sum(axis=1, keepdims=True), r.gap)
+        r = Routing(r.scores, r.sel, ids, winner_gates(r.scores, ids, W.gating), r.gap)
     disp = dispatch(r.ids, E)                                       # step 6
-    zq = quant(z, "e4m3", decide)
-    if resolve is not None:
-        zq = resolve.zq(z, zq)
+    if latent:
+        zq = quant(z, "e4m3", decide)
+        if resolve is not None:
+            zq = resolve.zq(z, zq)
+    else:
+        zq = xq                                                     # the experts read xq
 
     P = T * top_k
     F = None
@@ -275,10 +300,13 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
         for j in range(top_k):
             y_lat[t] += r.gates[t, j] * ye_rows[disp.row_of_pair[t * top_k + j]]
 
-    yq = quant(y_lat, "e4m3", decide)                               # step 9
-    if resolve is not None:
-        yq = resolve.yq(y_lat, yq, r, disp, ye_rows)
-    y_up = mm(yq, W.w_up)
+    if latent:                                                      # step 9
+        yq = quant(y_lat, "e4m3", decide)
+        if resolve is not None:
+            yq = resolve.yq(y_lat, yq, r, disp, ye_rows)
+        y_up = mm(yq, W.w_up)
+    else:
+        yq, y_up = None, y_lat.copy()
 
     y = y_up.copy()                                                 # step 10
     hs_l, hsq_l, ys_l, gs_l, us_l = [], [], [], [], []
@@ -308,18 +336,18 @@ def forward_dense_mask(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.flo
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
     E = W.w_router.shape[0]
+    latent = W.w_down is not None
     xq = quant(x, "e4m3", decide)
-    z = mm(xq, W.w_down)
-    r = route(z, W.w_router, top_k, W.logit_bias, W.selection_bias, decide)
+    z = mm(xq, W.w_down) if latent else x.astype(np.float64)
+    r = route(z, W.w_router, top_k, W.logit_bias, W.selection_bias, decide, W.gating)
     dense_gate = np.zeros((T, E))
     np.put_along_axis(dense_gate, r.ids, r.gates, axis=1)
-    zq = quant(z, "e4m3", decide)
+    zq = quant(z, "e4m3", decide) if latent else xq
     y_lat = np.zeros_like(z)
     for e in range(E):
         ye, _, _ = swiglu_expert(zq, W.w_gate_e[e], W.w_up_e[e], W.w_down_e[e], decide)
         y_lat += dense_gate[:, e:e + 1] * ye
-    yq = quant(y_lat, "e4m3", decide)
-    y = mm(yq, W.w_up)
+    y = mm(quant(y_lat, "e4m3", decide), W.w_up) if latent else y_lat.copy()
     for s in range(len(W.w_gate_s)):
         ys, _, _ = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide)
         y = y + ys

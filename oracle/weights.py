@@ -55,8 +55,8 @@ def layer(cfg, experts: str = "all", selection_bias=None) -> moe.LayerWeights:
     else:
         ge, ue, de = [], [], []
     return moe.LayerWeights(
-        w_down=dense(cfg, "w_down"),
-        w_up=dense(cfg, "w_up"),
+        w_down=dense(cfg, "w_down") if cfg.latent else None,
+        w_up=dense(cfg, "w_up") if cfg.latent else None,
         w_router=synth.gen_router(cfg),
         w_gate_e=ge, w_up_e=ue, w_down_e=de,
         w_gate_s=[dense(cfg, "w_gate_s", s) for s in range(S)],
@@ -64,4 +64,5 @@ def layer(cfg, experts: str = "all", selection_bias=None) -> moe.LayerWeights:
         w_down_s=[dense(cfg, "w_down_s", s) for s in range(S)],
         logit_bias=synth.gen_logit_bias(cfg),
         selection_bias=selection_bias,
+        gating=cfg.gating,
     )

@@ -43,6 +43,9 @@ class LayerConfig:
     logit_bias: str      # "none" or "zipf" (per-expert popularity bias on the router logits)
     seed_x: int          # seed of the hidden states
     seed_w: int          # seed of every weight tensor
+    latent: bool = True          # False: no latent projections (routed width = model width)
+    gating: str = "sigmoid"      # "sigmoid": winners' sigmoid scores / their sum;
+                                 # "softmax": softmax over the winners' logits
 
     def with_tokens(self, T: int) -> "LayerConfig":
         return dataclasses.replace(self, T=int(T))
@@ -90,6 +93,15 @@ CONFIGS = {
     "k3_skew": LayerConfig("k3_skew", T=8192, d_model=7168, d_latent=3584, n_routed=896,
                            top_k=16, n_shared=2, d_ff_shared=3072, d_ff_routed=3072,
                            router_init="normal", logit_bias="zipf", seed_x=1005, seed_w=1003),
+    # Non-latent MoE at K2-like width (384 experts, top-8, one shared expert):
+    # the experts read the model-width activations, the router the fp32 input,
+    # and the gates are the softmax over the winners' logits.
+    "k2_tiny": LayerConfig("k2_tiny", T=64, d_model=256, d_latent=256, n_routed=48, top_k=4,
+                           n_shared=1, d_ff_shared=256, d_ff_routed=128, router_init="normal",
+                           logit_bias="none", seed_x=1006, seed_w=1006, latent=False, gating="softmax"),
+    "k2_prefill": LayerConfig("k2_prefill", T=8192, d_model=7168, d_latent=7168, n_routed=384, top_k=8,
+                              n_shared=1, d_ff_shared=2048, d_ff_routed=2048, router_init="normal",
+                              logit_bias="none", seed_x=1007, seed_w=1007, latent=False, gating="softmax"),
 }
 
 
@@ -123,7 +135,7 @@ def n_matrices(cfg: LayerConfig, name: str) -> int:
         return cfg.n_routed
     if name.endswith("_s"):
         return cfg.n_shared
-    return 1
+    return 1 if cfg.latent else 0   # the latent projections exist only with a latent
 
 
 def gen_weight(cfg: LayerConfig, name: str, expert: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
