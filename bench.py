@@ -69,6 +69,7 @@ def algorithmic_work(cfg, counts):
     T, d, L, E, k, S, F, Fs = (cfg.T, cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k, cfg.n_shared,
                                cfg.d_ff_routed, cfg.d_ff_shared)
     P = T * k
+    lat = int(getattr(cfg, "latent", True))   # 0: no latent projections (L = d)
     mxb = lambda n: n * 17 // 32          # E2M1 codes + E8M0 scales
     f8b = lambda n: n * 33 // 32          # E4M3 codes + E8M0 scales
     touched = int((counts > 0).sum())
@@ -82,9 +83,9 @@ def algorithmic_work(cfg, counts):
         "expert_down_flops": 2.0 * P * F * L,
         "expert_down_bytes": touched * mxb(w_dn_e) + P * f8b(F) + P * L * 4,
     }
-    mx_flops = (2.0 * T * d * L + work["expert_up_flops"] + work["expert_down_flops"] + 2.0 * T * L * d
+    mx_flops = (lat * 4.0 * T * d * L + work["expert_up_flops"] + work["expert_down_flops"]
                 + S * (2.0 * T * d * 2 * Fs + 2.0 * T * Fs * d))
-    weight_bytes = (mxb(2 * d * L) + touched * (mxb(w_up_e) + mxb(w_dn_e)) + S * mxb(3 * d * Fs) + E * L * 4)
+    weight_bytes = (lat * mxb(2 * d * L) + touched * (mxb(w_up_e) + mxb(w_dn_e)) + S * mxb(3 * d * Fs) + E * L * 4)
     work.update(mx_flops=mx_flops, router_flops=2.0 * T * L * E, weight_bytes=weight_bytes,
                 layer_bytes=weight_bytes + T * d * 8 + P * (f8b(L) + f8b(F) * 2 + 8 * L))
     return work
@@ -148,6 +149,35 @@ def run_workload(name, steps, warmup, weights, hip, say, logit_bias=None):
     say(f"{name}: {ms_per_step:.3f} ms/step; stages (ms): " +
         ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
     return cfg, ms_per_step, stage_ms, work, counts
+
+
+def k2_report(steps, warmup, hip, say):
+    """The non-latent K2-like layer (its own weights, encoded after the K3
+    weights are freed): throughput, MX matrix-core share and the expert GEMM's
+    rate.  A report line beside the headline, not the headline."""
+    import torch
+
+    import synth
+    from latent_routing_mxfp4_amd import layer as LY
+
+    cfg = synth.config("k2_prefill")
+    t = time.perf_counter()
+    shape = LY.LayerShape.of(cfg)
+    extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg)}
+    weights = LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra,
+                                workers=min(16, len(os.sched_getaffinity(0))))
+    say(f"K2 weights encoded on the GPU in {time.perf_counter() - t:.1f} s")
+    kcfg, kms, kst, kwork, kcounts = run_workload("k2_prefill", steps, warmup, weights, hip, say)
+    del weights
+    torch.cuda.empty_cache()
+    return {"workload": f"{kcfg.name}: T={kcfg.T}, d={kcfg.d_model}, no latent, E={kcfg.n_routed} "
+                        f"top-{kcfg.top_k} softmax gates, {kcfg.n_shared} shared, d_ff={kcfg.d_ff_routed}",
+            "value": kcfg.T / (kms / 1e3), "unit": "tokens/s", "ms_per_step": kms,
+            "mx_frac": kwork["mx_flops"] / (kms / 1e3) / 1e12 / PEAK_MX_TFLOPS,
+            "expert_up_tflops": kwork["expert_up_flops"] / (kst["expert_up"] / 1e3) / 1e12,
+            "expert_up_frac": kwork["expert_up_flops"] / (kst["expert_up"] / 1e3) / 1e12 / PEAK_MX_TFLOPS,
+            "touched_experts": kwork["touched_experts"], "max_expert_load": int(kcounts.max()),
+            "stage_ms": kst, "step_events_ms": kwork["step_events_ms"]}
 
 
 def cpu_baseline(name, n_tokens, say):
@@ -313,6 +343,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--skew-steps", type=int, default=5,
                     help="steps of the 8192-token Zipf-skewed batch reported under 'skew' (0: skip)")
+    ap.add_argument("--k2-steps", type=int, default=5,
+                    help="steps of the non-latent K2-like 8192-token layer reported under 'k2' (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2)
@@ -430,6 +462,8 @@ def main():
 
     del weights
     torch.cuda.empty_cache()
+    if args.k2_steps > 0 and args.workload == "k3_prefill":
+        out["k2"] = k2_report(args.k2_steps, args.warmup, hip, say)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_tokens, say)
     print(json.dumps(out), flush=True)

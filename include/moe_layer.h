@@ -84,6 +84,16 @@ typedef struct {
   int32_t d_ff_routed; /* F:  routed-expert intermediate width   */
   int32_t d_ff_shared; /* Fs: shared-expert intermediate width   */
   int32_t max_tokens;  /* largest T a forward call may pass      */
+  /* Second workload (zero = the LatentMoE above).  identity_latent != 0: no
+   * latent projections (d_latent must equal d_model; w_down and w_up may be
+   * NULL): the router reads x itself, the experts read xq, and
+   *     y = y_lat + shared experts       (y_lat at model width, fp32).
+   * softmax_gates != 0: selection keys are logit + selection_bias and the
+   * gates are the softmax over the k winners' logits (the gate of the MoE
+   * data-path toy, Kimi K3: 2.8 Trillion Parameters, Four Bits at a Time,
+   * section "What it takes to serve it"). */
+  int32_t identity_latent;
+  int32_t softmax_gates;
 } moe_layer_config;
 
 /* One MXFP4 (E2M1) tensor: packed codes and E8M0 scales, device memory. */

@@ -41,7 +41,8 @@ class MoEError(RuntimeError):
 
 class MoeLayerConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "d_model", "d_latent", "n_routed", "top_k", "n_shared", "d_ff_routed", "d_ff_shared", "max_tokens")]
+        "d_model", "d_latent", "n_routed", "top_k", "n_shared", "d_ff_routed", "d_ff_shared", "max_tokens",
+        "identity_latent", "softmax_gates")]
 
 
 class MoeMxTensor(ctypes.Structure):

@@ -60,15 +60,17 @@ __global__ void __launch_bounds__(1024) combine_kernel(const float* __restrict__
           acc.w = fmaf(g, v[u].w, acc.w);
         }
     }
-    uint32_t m = max(max(__float_as_uint(acc.x) & 0x7fffffffu, __float_as_uint(acc.y) & 0x7fffffffu),
-                     max(__float_as_uint(acc.z) & 0x7fffffffu, __float_as_uint(acc.w) & 0x7fffffffu));
-    m = lane8_max_u32(m);  // non-negative floats order like their bit patterns
-    const int sc = mx_scale_code<8>(m);
-    const int e = sc - 127;
-    const uint32_t w = e4m3x2(acc.x, acc.y, e) | (e4m3x2(acc.z, acc.w, e) << 16);
     if (y_lat) reinterpret_cast<float4*>(y_lat + (int64_t)t * L)[f] = acc;
-    reinterpret_cast<uint32_t*>(yq + (int64_t)t * L)[f] = w;
-    if ((f & 7) == 0) yqs[(int64_t)t * (L >> 5) + (f >> 3)] = (uint8_t)sc;
+    if (yq) {  // uniform over the launch
+      uint32_t m = max(max(__float_as_uint(acc.x) & 0x7fffffffu, __float_as_uint(acc.y) & 0x7fffffffu),
+                       max(__float_as_uint(acc.z) & 0x7fffffffu, __float_as_uint(acc.w) & 0x7fffffffu));
+      m = lane8_max_u32(m);  // non-negative floats order like their bit patterns
+      const int sc = mx_scale_code<8>(m);
+      const int e = sc - 127;
+      const uint32_t w = e4m3x2(acc.x, acc.y, e) | (e4m3x2(acc.z, acc.w, e) << 16);
+      reinterpret_cast<uint32_t*>(yq + (int64_t)t * L)[f] = w;
+      if ((f & 7) == 0) yqs[(int64_t)t * (L >> 5) + (f >> 3)] = (uint8_t)sc;
+    }
   }
 }
 

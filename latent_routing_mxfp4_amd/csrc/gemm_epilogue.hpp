@@ -123,7 +123,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
         const uint32_t o = c_lane + 4u * rr * ldc;
 #pragma unroll
         for (int ni = 0; ni < NW; ++ni)
-          if (t.n0 + 16 * ni < N) *at_byte(cb, o + 64u * ni) = acc[mi][ni][0][i];
+          if (t.n0 + 16 * ni < N) {
+            float* dst = at_byte(cb, o + 64u * ni);
+            *dst = p.c_accumulate ? *dst + acc[mi][ni][0][i] : acc[mi][ni][0][i];
+          }
       }
       if (QNT) {
         const uint32_t oq = q_lane + rr * (uint32_t)N;

@@ -41,9 +41,10 @@ bool router_bf16x3(int T, int E, int L);
 hipError_t launch_router_logits(const float* z, const float* w, const float* logit_bias, int T, int E,
                                 int L, float* logits, float* partial, uint16_t* wplanes, hipStream_t s);
 // Per token: s = sigmoid(logit), key = s + sel_bias, top-k by (key desc, id asc),
-// gates = s / sum(s over the k winners).
-hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
-                       float* gates, hipStream_t s);
+// gates = s / sum(s over the k winners).  softmax_gates: key = logit + sel_bias,
+// gates = softmax over the k winners' logits.
+hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, bool softmax_gates,
+                       int32_t* ids, float* gates, hipStream_t s);
 
 // ---- Dispatch (permute.hip) -------------------------------------------------
 size_t dispatch_scratch_ints(int T, int E);
@@ -89,6 +90,7 @@ struct GemmArgs {
   float* c;
   int64_t ldc;
   int64_t c_gstride;           // elements between dense groups' outputs
+  int c_accumulate;            // fp32 output (EPI_F32): c += acc instead of c = acc
   uint8_t* q;                  // E4M3 codes [rows][N]
   uint8_t* qs;                 // scales [rows][N/32]
   int64_t q_gstride;           // bytes between dense groups' code outputs
@@ -126,7 +128,8 @@ hipError_t launch_mx_gemm_wide(const GemmArgs& args, int epilogue, hipStream_t s
 
 // ---- Combine (combine.hip) --------------------------------------------------
 // y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then
-// yq = MXFP8(y_lat) per row; y_lat_out may be null.
+// yq = MXFP8(y_lat) per row; y_lat_out may be null, and so may yq/yqs (no
+// quantisation).
 hipError_t launch_combine(const float* y_e, const float* gates, const int32_t* row_of_pair, int T, int k,
                           int L, float* y_lat_out, uint8_t* yq, uint8_t* yqs, hipStream_t s);
 

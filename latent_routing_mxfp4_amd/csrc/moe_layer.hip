@@ -54,17 +54,21 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
     o = align_up(o + bytes);
     return at;
   };
+  // Without a latent (second workload) nothing of the latent path exists:
+  // the router reads x, the experts read xq and the combine writes y.
+  const int64_t lat = c.identity_latent ? 0 : 1;
   p.xq = take(T * d);
   p.xqs = take(T * d / 32);
-  p.xdq = take(T * d * 2);
+  p.xdq = take(lat * T * d * 2);
   // Latent down-projection: at most kFewRows tokens stream the MXFP4 weights
   // (K-slice partial sums), more tokens use a bf16 image of W_down.
   const bool few = T <= kFewRows;
-  p.wdn16 = take(few ? 0 : L * d * 2);
-  p.zpart = take(few && T > 0 ? (size_t)moe::bf16_mx_splitk_slices((int)T, (int)L, (int)d) * T * L * 4 : 0);
-  p.z = take(T * L * 4);
-  p.zq = take(T * L);
-  p.zqs = take(T * L / 32);
+  p.wdn16 = take(few ? 0 : lat * L * d * 2);
+  p.zpart =
+      take(few && T > 0 ? (size_t)lat * moe::bf16_mx_splitk_slices((int)T, (int)L, (int)d) * T * L * 4 : 0);
+  p.z = take(lat * T * L * 4);
+  p.zq = take(lat * T * L);
+  p.zqs = take(lat * T * L / 32);
   p.logits = take(T * E * 4);
   {
     const int split = T > 0 ? moe::router_split((int)T, (int)E, (int)L) : 1;
@@ -84,9 +88,9 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   p.hq = take(P * F);
   p.hqs = take(P * F / 32);
   p.ye = take(P * L * 4);
-  p.ylat = take(T * L * 4);
-  p.yq = take(T * L);
-  p.yqs = take(T * L / 32);
+  p.ylat = take(lat * T * L * 4);
+  p.yq = take(lat * T * L);
+  p.yqs = take(lat * T * L / 32);
   p.hs = take(S * T * Fs);
   p.hss = take(S * T * Fs / 32);
   p.total = o;
@@ -100,6 +104,7 @@ int check_config(const moe_layer_config* c) {
     return MOE_ERR_INVALID_ARG;
   if (c->top_k > c->n_routed || c->n_shared > 8 || c->max_tokens > (1 << 20)) return MOE_ERR_INVALID_ARG;
   if (c->n_shared > 0 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->identity_latent && c->d_latent != c->d_model) return MOE_ERR_INVALID_ARG;
   if (c->n_routed > 4096 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
   if (c->d_model % 128 || c->d_latent % 128 || c->d_ff_routed % 128) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && c->d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
@@ -139,13 +144,14 @@ int moe_layer_create(const moe_layer_config* cfg, const moe_layer_weights* w, mo
   if (!cfg || !w || !out) return MOE_ERR_INVALID_ARG;
   int st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (!mx_ok(w->w_down) || !mx_ok(w->w_up) || !w->w_router || !mx_ok(w->w_gate_e) || !mx_ok(w->w_up_e) ||
-      !mx_ok(w->w_down_e))
+  const bool latent = !cfg->identity_latent;
+  if ((latent && (!mx_ok(w->w_down) || !mx_ok(w->w_up))) || !w->w_router || !mx_ok(w->w_gate_e) ||
+      !mx_ok(w->w_up_e) || !mx_ok(w->w_down_e))
     return MOE_ERR_INVALID_ARG;
   if (cfg->n_shared > 0 && (!mx_ok(w->w_gate_s) || !mx_ok(w->w_up_s) || !mx_ok(w->w_down_s)))
     return MOE_ERR_INVALID_ARG;
-  if (!mx_aligned(w->w_down) || !mx_aligned(w->w_up) || !mx_aligned(w->w_gate_e) || !mx_aligned(w->w_up_e) ||
-      !mx_aligned(w->w_down_e) || !aligned(w->w_router, 16))
+  if ((latent && (!mx_aligned(w->w_down) || !mx_aligned(w->w_up))) || !mx_aligned(w->w_gate_e) ||
+      !mx_aligned(w->w_up_e) || !mx_aligned(w->w_down_e) || !aligned(w->w_router, 16))
     return MOE_ERR_INVALID_ARG;
   if (cfg->n_shared > 0 && (!mx_aligned(w->w_gate_s) || !mx_aligned(w->w_up_s) || !mx_aligned(w->w_down_s)))
     return MOE_ERR_INVALID_ARG;
@@ -231,14 +237,21 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(mark(MOE_EV_START));
 
   // 1. xq (and its exact bf16 image for the latent down-projection)
-  MOE_HIP(moe::launch_quantize(x, T, d, 0, xq, xqs, s, xdq));
+  const bool latent = !c.identity_latent;
+  MOE_HIP(moe::launch_quantize(x, T, d, 0, xq, xqs, s, latent ? xdq : nullptr));
   MOE_HIP(mark(MOE_EV_QUANT_X));
+  // What the router and the routed experts read: the latent, or x itself.
+  const float* zr = latent ? z : x;
+  const uint8_t* zqa = latent ? zq : xq;
+  const uint8_t* zqsa = latent ? zqs : xqs;
 
   // 2. z, zq: bf16 matrix cores on the exactly decoded MX operands, so that the
   //    latent the router ranks is accurate to fp32 accumulation.  Few tokens:
   //    W_down is decoded in registers while it streams (K-slice partials, then
   //    their sum and MXFP8); many tokens: one bf16 image, then the LDS kernel.
-  if (T <= kFewRows) {
+  if (!latent) {
+    // no latent projection
+  } else if (T <= kFewRows) {
     moe::GemmArgs a = {};
     a.nseg = 1;
     a.seg[0] = {reinterpret_cast<const uint8_t*>(xdq), nullptr, d, w.w_down.codes, w.w_down.scales,
@@ -267,10 +280,10 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(mark(MOE_EV_DOWN));
 
   // 3-4. router
-  MOE_HIP(moe::launch_router_logits(z, w.w_router, w.router_logit_bias, T, E, L, logits,
+  MOE_HIP(moe::launch_router_logits(zr, w.w_router, w.router_logit_bias, T, E, L, logits,
                                     at<float>(ws, pl.rpart), at<uint16_t>(ws, pl.wrpl), s));
   MOE_HIP(mark(MOE_EV_LOGITS));
-  MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, ids, gates, s));
+  MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, c.softmax_gates != 0, ids, gates, s));
   MOE_HIP(mark(MOE_EV_TOPK));
 
   // 5. dispatch
@@ -285,8 +298,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   {
     moe::GemmArgs a = {};
     a.nseg = 1;
-    a.seg[0] = {zq,
-                zqs,
+    a.seg[0] = {zqa,
+                zqsa,
                 L,
                 w.w_gate_e.codes,
                 w.w_gate_e.scales,
@@ -330,7 +343,12 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   // 8. combine
   // The fp32 combined latent is only kept for a trace; yq is what the
   // up-projection reads.
-  MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, tr && tr->y_lat ? ylat : nullptr, yq, yqs, s));
+  if (latent) {
+    MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, tr && tr->y_lat ? ylat : nullptr, yq, yqs, s));
+  } else {  // the routed output at model width goes straight to y
+    MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, y, nullptr, nullptr, s));
+    if (tr && tr->y_lat) MOE_HIP(hipMemcpyAsync(tr->y_lat, y, (size_t)T * L * 4, hipMemcpyDeviceToDevice, s));
+  }
   MOE_HIP(mark(MOE_EV_COMBINE));
 
   // 9. shared experts, first half
@@ -362,13 +380,16 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   }
   MOE_HIP(mark(MOE_EV_SHARED_UP));
 
-  // 10. y = up-projection + shared down-projections (one K-concatenated GEMM)
-  {
+  // 10. y = up-projection + shared down-projections (one K-concatenated
+  //     GEMM); without a latent, y (the routed output) += the shared ones.
+  if (latent || S > 0) {
     moe::GemmArgs a = {};
-    a.nseg = 1 + S;
-    a.seg[0] = {yq, yqs, L, w.w_up.codes, w.w_up.scales, nullptr, nullptr, 0, 0, L};
+    const int s0 = latent ? 1 : 0;
+    a.nseg = s0 + S;
+    if (latent) a.seg[0] = {yq, yqs, L, w.w_up.codes, w.w_up.scales, nullptr, nullptr, 0, 0, L};
+    a.c_accumulate = latent ? 0 : 1;
     for (int i = 0; i < S; ++i)
-      a.seg[1 + i] = {hs + (int64_t)i * T * Fs,
+      a.seg[s0 + i] = {hs + (int64_t)i * T * Fs,
                       hss + (int64_t)i * T * Fs / 32,
                       Fs,
                       w.w_down_s.codes + (int64_t)i * d * Fs / 2,
@@ -397,9 +418,9 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     const size_t Ts = (size_t)T, Ps = (size_t)P;
     MOE_HIP(cp(tr->xq_codes, xq, Ts * d));
     MOE_HIP(cp(tr->xq_scales, xqs, Ts * d / 32));
-    MOE_HIP(cp(tr->z, z, Ts * L * 4));
-    MOE_HIP(cp(tr->zq_codes, zq, Ts * L));
-    MOE_HIP(cp(tr->zq_scales, zqs, Ts * L / 32));
+    MOE_HIP(cp(tr->z, zr, Ts * L * 4));
+    MOE_HIP(cp(tr->zq_codes, zqa, Ts * L));
+    MOE_HIP(cp(tr->zq_scales, zqsa, Ts * L / 32));
     MOE_HIP(cp(tr->logits, logits, Ts * E * 4));
     MOE_HIP(cp(tr->ids, ids, Ps * 4));
     MOE_HIP(cp(tr->gates, gates, Ps * 4));
@@ -410,9 +431,11 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     MOE_HIP(cp(tr->hq_codes, hq, Ps * F));
     MOE_HIP(cp(tr->hq_scales, hqs, Ps * F / 32));
     MOE_HIP(cp(tr->y_e, ye, Ps * L * 4));
-    MOE_HIP(cp(tr->y_lat, ylat, Ts * L * 4));
-    MOE_HIP(cp(tr->yq_codes, yq, Ts * L));
-    MOE_HIP(cp(tr->yq_scales, yqs, Ts * L / 32));
+    if (latent) {  // (without a latent, y_lat was copied before the shared experts were added)
+      MOE_HIP(cp(tr->y_lat, ylat, Ts * L * 4));
+      MOE_HIP(cp(tr->yq_codes, yq, Ts * L));
+      MOE_HIP(cp(tr->yq_scales, yqs, Ts * L / 32));
+    }
     if (S > 0) {
       MOE_HIP(cp(tr->hs_codes, hs, (size_t)S * Ts * Fs));
       MOE_HIP(cp(tr->hs_scales, hss, (size_t)S * Ts * Fs / 32));

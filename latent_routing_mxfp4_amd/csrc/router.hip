@@ -11,7 +11,8 @@
 //     and out, on the fp32 matrix cores (v_mfma_f32_16x16x4f32) with 64x64
 //     tiles staged through LDS; for few tiles (decode) the K range is split
 //     over extra workgroups and the slices summed in a fixed order.
-//   topk: one wave per token; the E selection keys and raw scores sit in LDS,
+//   topk: one wave per token (sigmoid scores, or the logits themselves with
+//     softmax gates); the E selection keys and raw scores sit in LDS,
 //     each lane keeps the best key of its strided slice, and k rounds of a
 //     64-lane (key desc, id asc) reduction (DPP within rows, readlane across)
 //     pick the winners in slot order; only the winning lane rescans its
@@ -386,9 +387,25 @@ __device__ __forceinline__ void wave_best(float& wk, int& wi) {
   wi = bi;
 }
 
+// Gates of the k winners held by lanes 0..k-1 (raw score `mys` of slot
+// `lane`): sigmoid scores over their slot-order sum `ssum`, or with softmax
+// gates (raw score = the logit) the softmax over the winners, its sum taken in
+// slot order so that every lane and every run divides by the same value.
+__device__ __forceinline__ float winner_gate(bool softmax, int k, int lane, float mys, float ssum) {
+  if (!softmax) return mys / ssum;
+  float mx = lane < k ? mys : -INFINITY;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float ev = lane < k ? expf(mys - mx) : 0.f;
+  float esum = 0.f;
+  for (int j = 0; j < k; ++j) esum += __shfl(ev, j, 64);
+  return ev / esum;
+}
+
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
                                                   const float* __restrict__ sel_bias, int T, int E, int k,
-                                                  int32_t* __restrict__ ids, float* __restrict__ gates) {
+                                                  bool softmax, int32_t* __restrict__ ids,
+                                                  float* __restrict__ gates) {
   extern __shared__ float keys_smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -400,7 +417,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   float bk = -INFINITY;
   int bi = 0x7fffffff;
   for (int e = lane; e < E; e += 64) {
-    const float sc = sigmoidf(lrow[e]);
+    const float sc = softmax ? lrow[e] : sigmoidf(lrow[e]);
     float key = sc;
     if (sel_bias) key += sel_bias[e];
     key = fmaxf(key, -FLT_MAX);  // NaN / -inf inputs rank last but stay above "taken" (-inf)
@@ -428,9 +445,10 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
       }
     }
   }
+  const float gt = winner_gate(softmax, k, lane, mys, ssum);
   if (lane < k) {
     ids[(int64_t)t * k + lane] = myid;
-    gates[(int64_t)t * k + lane] = mys / ssum;
+    gates[(int64_t)t * k + lane] = gt;
   }
 }
 
@@ -442,7 +460,8 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 template <int KPL>
 __global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__ logits,
                                                       const float* __restrict__ sel_bias, int T, int E, int k,
-                                                      int32_t* __restrict__ ids, float* __restrict__ gates) {
+                                                      bool softmax, int32_t* __restrict__ ids,
+                                                      float* __restrict__ gates) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -456,7 +475,7 @@ __global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__
     key[j] = -INFINITY;  // past E: never selected (k <= E finite keys exist)
     scr[j] = 0.f;
     if (e < E) {
-      const float sc = sigmoidf(lrow[e]);
+      const float sc = softmax ? lrow[e] : sigmoidf(lrow[e]);
       float kk = sc;
       if (sel_bias) kk += sel_bias[e];
       kk = fmaxf(kk, -FLT_MAX);
@@ -489,17 +508,19 @@ __global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__
       }
     }
   }
+  const float gt = winner_gate(softmax, k, lane, mys, ssum);
   if (lane < k) {
     ids[(int64_t)t * k + lane] = myid;
-    gates[(int64_t)t * k + lane] = mys / ssum;
+    gates[(int64_t)t * k + lane] = gt;
   }
 }
 
-hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
-                       float* gates, hipStream_t s) {
+hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, bool softmax_gates,
+                       int32_t* ids, float* gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (E <= 64 * 16) {
-    topk_reg_kernel<16><<<dim3((T + 3) / 4), dim3(256), 0, s>>>(logits, sel_bias, T, E, k, ids, gates);
+    topk_reg_kernel<16><<<dim3((T + 3) / 4), dim3(256), 0, s>>>(logits, sel_bias, T, E, k, softmax_gates, ids,
+                                                                gates);
     return hipGetLastError();
   }
   const size_t smem = (size_t)4 * 2 * E * sizeof(float);  // 4 waves x (keys + scores): 128 KB at E = 4096
@@ -510,7 +531,7 @@ hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E,
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  topk_kernel<<<dim3((T + 3) / 4), dim3(256), smem, s>>>(logits, sel_bias, T, E, k, ids, gates);
+  topk_kernel<<<dim3((T + 3) / 4), dim3(256), smem, s>>>(logits, sel_bias, T, E, k, softmax_gates, ids, gates);
   return hipGetLastError();
 }
 

@@ -40,11 +40,13 @@ class LayerShape:
     n_shared: int
     d_ff_routed: int
     d_ff_shared: int
+    latent: bool = True          # False: no latent projections (d_latent == d_model)
+    softmax_gates: bool = False  # gates = softmax over the winners' logits
 
     @classmethod
     def of(cls, cfg) -> "LayerShape":
         return cls(cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k, cfg.n_shared, cfg.d_ff_routed,
-                   cfg.d_ff_shared)
+                   cfg.d_ff_shared, bool(getattr(cfg, "latent", True)), getattr(cfg, "gating", "sigmoid") == "softmax")
 
     def matrix_shape(self, name: str) -> Tuple[int, int]:
         d, L, F, Fs = self.d_model, self.d_latent, self.d_ff_routed, self.d_ff_shared
@@ -52,11 +54,12 @@ class LayerShape:
                 "w_gate_s": (Fs, d), "w_up_s": (Fs, d), "w_down_s": (d, Fs)}[name]
 
     def count(self, name: str) -> int:
-        return self.n_routed if name in ROUTED else self.n_shared if name in SHARED else 1
+        return self.n_routed if name in ROUTED else self.n_shared if name in SHARED else int(self.latent)
 
     def c_config(self, max_tokens: int) -> _lib.MoeLayerConfig:
         return _lib.MoeLayerConfig(self.d_model, self.d_latent, self.n_routed, self.top_k, self.n_shared,
-                                   self.d_ff_routed, self.d_ff_shared, int(max_tokens))
+                                   self.d_ff_routed, self.d_ff_shared, int(max_tokens), int(not self.latent),
+                                   int(self.softmax_gates))
 
 
 # --------------------------------------------------------------------------- MX helpers
@@ -212,6 +215,8 @@ class LatentMoE:
             "hq_scales": ((P, F // 32), u8), "y_e": ((P, L), f32), "y_lat": ((T, L), f32),
             "yq_codes": ((T, L), u8), "yq_scales": ((T, L // 32), u8),
         }
+        if not s.latent:  # no MXFP8 of the combined output: it is y's routed part
+            del shapes["yq_codes"], shapes["yq_scales"]
         if S > 0:
             shapes["hs"] = ((S, T, Fs), f32)
             shapes["hs_codes"] = ((S, T, Fs), u8)

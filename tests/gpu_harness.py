@@ -64,7 +64,7 @@ def run_traced_tokens(layer, x_np: np.ndarray, tokens):
     k = tr["ids"].shape[1]
     pairs = (tok[:, None] * k + torch.arange(k, device="cuda")[None, :]).reshape(-1)
     rows = tr["row_of_pair"].long()[pairs]
-    sub = {n: to_np(tr[n][tok]) for n in PER_TOKEN}
+    sub = {n: to_np(tr[n][tok]) for n in PER_TOKEN if n in tr}
     sub.update({n: to_np(tr[n][rows]) for n in PER_ROW})
     for n in ("hs", "hs_codes", "hs_scales"):
         if n in tr:

@@ -157,18 +157,24 @@ class Replay:
         self.ye_bound[lo:hi] = mx_mfma_bound(out, wd)
         return out
 
-    def yq(self, y_lat, yq, r, disp, ye_rows):
+    def combine_bound(self, r, disp, ye_rows):
+        """Bound of the fp32 gate-weighted sum of the k expert outputs: each
+        term's own error (gate error, expert-output error) plus k + 1 roundings."""
         k = self.k
         rows = disp.row_of_pair.reshape(-1, k)
         g = np.abs(r.gates)
-        b = np.zeros_like(y_lat)
-        acc = np.zeros_like(y_lat)
+        b = np.zeros((rows.shape[0], ye_rows.shape[1]))
+        acc = np.zeros_like(b)
         for j in range(k):
             ye = np.abs(ye_rows[rows[:, j]])
             b += g[:, j:j + 1] * self.ye_bound[rows[:, j]] + self.dgate[:, j:j + 1] * ye
             acc += g[:, j:j + 1] * ye
         b += (k + 1) * EPS32 * acc
         self.ylat_bound = b
+        return b
+
+    def yq(self, y_lat, yq, r, disp, ye_rows):
+        b = self.combine_bound(r, disp, ye_rows)
         return self._adopt("yq", y_lat, b, yq, self.tr["yq_codes"], self.tr["yq_scales"])
 
     def hs(self, s, wg, wu, wd, g, u, h, hq):
@@ -190,11 +196,18 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
     assert np.array_equal(tr["xq_codes"], o.xq.codes), "xq codes"
     assert np.array_equal(tr["xq_scales"], o.xq.scales), "xq scales"
 
-    # 2. latent down-projection (bf16 matrix cores)
-    bz = gemm_bound(o.xq, W.w_down, o.z)
-    dz = np.abs(tr["z"].astype(np.float64) - o.z)
-    assert np.all(dz <= bz), f"z outside the fp32 bound: worst ratio {np.max(dz / bz):.3g}"
-    rep["z_err_over_bound"] = float(np.max(dz / bz))
+    # 2. latent down-projection (bf16 matrix cores); without a latent the
+    #    router reads x and the experts xq, unchanged
+    latent = W.w_down is not None
+    if latent:
+        bz = gemm_bound(o.xq, W.w_down, o.z)
+        dz = np.abs(tr["z"].astype(np.float64) - o.z)
+        assert np.all(dz <= bz), f"z outside the fp32 bound: worst ratio {np.max(dz / bz):.3g}"
+        rep["z_err_over_bound"] = float(np.max(dz / bz))
+    else:
+        bz = np.zeros_like(o.z)
+        assert np.array_equal(tr["z"].astype(np.float64), o.z), "router input is not x"
+        assert np.array_equal(tr["zq_codes"], o.xq.codes) and np.array_equal(tr["zq_scales"], o.xq.scales)
 
     # 3. routing
     gi, ri = tr["ids"], o.routing.ids
@@ -214,7 +227,23 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
     ds = 0.25 * dlog + 2 * EPS32
     dgate = np.zeros((T, k))
     worst_gate = 0.0
-    for t in range(T):
+    if W.gating == "softmax":
+        # softmax over the winners' logits: a logit error d_j moves gate j by a
+        # factor within exp(+-(d_j + max_i d_i)); the fp32 evaluation adds the
+        # subtraction of the maximum (EPS32 |l - m| inside exp), exp itself,
+        # the k-term sum and the division.
+        for t in range(T):
+            gates_t = moe.winner_gates(o.routing.scores[t:t + 1], gi[t:t + 1], "softmax")[0]
+            lw = o.routing.scores[t, gi[t]]
+            dl = dlog[t, gi[t]]
+            spread = float(lw.max() - lw.min())
+            for j in range(k):
+                tol = max(1e-6, gates_t[j] * (np.expm1(dl[j] + dl.max()) + (k + 6 + 2 * spread) * EPS32))
+                dgate[t, j] = tol
+                err = abs(float(tr["gates"][t, j]) - gates_t[j])
+                worst_gate = max(worst_gate, err)
+                assert err <= tol, ("gate", t, j, err, tol)
+    for t in range(T if W.gating == "sigmoid" else 0):
         ssum = o.routing.scores[t, gi[t]].sum()
         gates_t = o.routing.scores[t, gi[t]] / ssum          # the oracle's gates of the GPU's set
         dsum = ds[t, gi[t]].sum()
@@ -242,9 +271,12 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
         for name, st in rp.stats.items():
             assert st["inadmissible_blocks"] == 0, (name, st)
         rep["replay"] = rp.stats
-        for name, gc, gs, ref in (("zq", tr["zq_codes"], tr["zq_scales"], c.zq),
-                                  ("hq", tr["hq_codes"], tr["hq_scales"], c.hq_rows),
-                                  ("yq", tr["yq_codes"], tr["yq_scales"], c.yq)):
+        if not latent:
+            rp.combine_bound(c.routing, c.disp, c.ye_rows)
+        checks = [("hq", tr["hq_codes"], tr["hq_scales"], c.hq_rows)]
+        if latent:
+            checks += [("zq", tr["zq_codes"], tr["zq_scales"], c.zq), ("yq", tr["yq_codes"], tr["yq_scales"], c.yq)]
+        for name, gc, gs, ref in checks:
             nbad = int((gc != ref.codes).sum()) + int((gs != ref.scales).sum())
             if nbad:
                 say(f"  {name} mismatches at {np.argwhere(gc != ref.codes)[:3].tolist()}")
@@ -260,7 +292,7 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
         assert np.all(dye <= rp.ye_bound), f"y_e outside its bound on {(dye > rp.ye_bound).sum()} elements"
         dyl = np.abs(tr["y_lat"].astype(np.float64) - c.y_lat)
         assert np.all(dyl <= rp.ylat_bound), f"y_lat outside its bound on {(dyl > rp.ylat_bound).sum()} elements"
-        by = mx_mfma_bound(c.yq, W.w_up)
+        by = mx_mfma_bound(c.yq, W.w_up) if latent else rp.ylat_bound
         for s in range(len(W.w_gate_s)):
             by = by + mx_mfma_bound(c.hq_shared[s], W.w_down_s[s])
         by = by + (1 + len(W.w_gate_s)) * EPS32 * np.abs(c.y)

@@ -25,6 +25,9 @@ def _check_weight_codes(cfg, gw, W):
     rest in fragment order (read back through the layout's numpy statement)."""
     from oracle import mx
     for name in ("w_down", "w_up"):
+        if getattr(W, name) is None:   # no latent projections
+            assert gw[name] is None, name
+            continue
         c, s = gw[name]
         c, s = c.cpu().numpy(), s.cpu().numpy()
         if name != "w_down":
@@ -112,4 +115,46 @@ def test_tiny_many_tokens_split_bf16_router():
     products (2048 tokens x 1024 experts = 128 tiles of 128 x 128)."""
     import dataclasses
     cfg = dataclasses.replace(synth.config("tiny", T=2048), n_routed=1024, top_k=8)
+    _layer_case(cfg, check_codes=False)
+
+
+# --------------------------------------------------------------------------- no latent, softmax gates
+
+
+def test_k2_tiny_layer_parity():
+    """Non-latent layer: the router reads x, the experts read xq, the combined
+    routed output is y's routed part; gates are the softmax of the winners'
+    logits."""
+    rep, y, tr, o = _layer_case(synth.config("k2_tiny"))
+    assert "yq_codes" not in tr
+
+
+def test_k2_tiny_ragged_tokens():
+    for T in (1, 7, 130):
+        _layer_case(synth.config("k2_tiny", T=T), check_codes=False)
+
+
+def test_k2_tiny_selection_bias_and_top1():
+    """The selection bias shifts the logit keys only; with top-1 every gate is
+    exactly one."""
+    import dataclasses
+    cfg = synth.config("k2_tiny", T=48)
+    _layer_case(cfg, selection_bias=synth.gen_selection_bias(cfg, 0.5), check_codes=False)
+    _, _, tr, _ = _layer_case(dataclasses.replace(cfg, top_k=1), check_codes=False)
+    assert np.all(tr["gates"] == 1.0)
+
+
+def test_k2_tiny_no_shared_expert():
+    """Without a shared expert and without a latent, y is the combine's output
+    alone (no output GEMM runs)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("k2_tiny", T=40), n_shared=0)
+    _, y, tr, _ = _layer_case(cfg, check_codes=False)
+    assert np.array_equal(y, tr["y_lat"])
+
+
+def test_k2_many_tokens_split_bf16_router():
+    """The three-piece bf16 router on x itself (2048 tokens x 1024 experts)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("k2_tiny", T=2048), n_routed=1024, top_k=8)
     _layer_case(cfg, check_codes=False)

@@ -31,10 +31,12 @@ def _fake_trace(cfg, W, x, eps, seed=0):
         "counts": n.disp.counts.astype(np.int32), "offsets": n.disp.offsets.astype(np.int32),
         "pair_of_row": n.disp.pair_of_row.astype(np.int32), "row_of_pair": n.disp.row_of_pair.astype(np.int32),
         "h": f32(n.h_rows), "hq_codes": n.hq_rows.codes, "hq_scales": n.hq_rows.scales, "y_e": f32(n.ye_rows),
-        "y_lat": f32(n.y_lat), "yq_codes": n.yq.codes, "yq_scales": n.yq.scales,
+        "y_lat": f32(n.y_lat),
         "hs": np.stack([f32(h) for h in n.h_shared]), "hs_codes": np.stack([q.codes for q in n.hq_shared]),
         "hs_scales": np.stack([q.scales for q in n.hq_shared]),
     }
+    if n.yq is not None:
+        tr.update(yq_codes=n.yq.codes, yq_scales=n.yq.scales)
     return f32(n.y), tr
 
 
@@ -84,3 +86,55 @@ def test_planted_output_error_fails(tiny_case):
     y2[3, 7] += 0.1 * np.abs(y).max()
     with pytest.raises(AssertionError):
         parity.check_layer(cfg, W, o, y2, tr, x=x, say=lambda *a: None)
+
+
+# --------------------------------------------------------------------------- no latent, softmax gates
+
+
+@pytest.fixture(scope="module")
+def k2_case():
+    cfg = synth.config("k2_tiny")
+    W = weights.layer(cfg)
+    x = synth.gen_hidden(cfg)
+    o = moe.forward(x, W, cfg.top_k)
+    y, tr = _fake_trace(cfg, W, x, eps=2e-7, seed=1)
+    return cfg, W, x, o, y, tr
+
+
+def test_k2_perturbed_run_passes(k2_case):
+    cfg, W, x, o, y, tr = k2_case
+    assert W.w_down is None and W.gating == "softmax"
+    rep = parity.check_layer(cfg, W, o, y, tr, x=x, say=lambda *a: None)
+    assert "zq" not in rep["replay"] and "yq" not in rep["replay"]
+    assert rep["replay_rel_l2"] < 1e-4
+
+
+def test_k2_planted_gate_error_fails(k2_case):
+    cfg, W, x, o, y, tr = k2_case
+    bad = dict(tr)
+    g = tr["gates"].copy()
+    g[5, 0] += 1e-4                 # a softmax gate off by far more than its logits allow
+    g[5, 1] -= 1e-4
+    bad["gates"] = g
+    with pytest.raises(AssertionError, match="gate"):
+        parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
+
+
+def test_k2_sigmoid_gates_of_a_softmax_layer_fail(k2_case):
+    """Gates normalised as sigmoid scores (the latent layer's rule) are caught."""
+    cfg, W, x, o, y, tr = k2_case
+    bad = dict(tr)
+    s = 1 / (1 + np.exp(-o.routing.scores))
+    bad["gates"] = moe.winner_gates(s, tr["ids"], "sigmoid").astype(np.float32)
+    with pytest.raises(AssertionError, match="gate"):
+        parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
+
+
+def test_k2_router_input_must_be_x(k2_case):
+    cfg, W, x, o, y, tr = k2_case
+    bad = dict(tr)
+    z = tr["z"].copy()
+    z[0, 0] = np.nextafter(z[0, 0], np.float32(np.inf))
+    bad["z"] = z
+    with pytest.raises(AssertionError, match="router input"):
+        parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
