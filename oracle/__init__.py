@@ -24,7 +24,10 @@ Pins (what the oracle is checked against; see ``tests/test_oracle_*.py``)
 * the MXFP4 rows of that page's quantisation experiment (seed 7);
 * the tokens-per-expert list of that page's MoE data-path toy (seed 0);
 * exact-integer MX matmul, brute-force dense-mask layer, single-expert
-  reduction against an independent PyTorch fp64 MLP, and the invariants.
+  reduction against an independent PyTorch fp64 MLP, and the invariants;
+* the bfloat16 rounding against PyTorch's fp32 -> bfloat16 cast (ties of both
+  parities, overflow, subnormals), and the higher-precision map's top-1 layer
+  against a PyTorch pipeline with its own casts.
 
 Layer outputs as a whole have no printed value on the pages: beyond the pins
 above their parity is checked by construction (brute force, invariants), not

@@ -38,9 +38,19 @@ logit (plus the selection bias) and the gates are the softmax over the k
 winners' logits, the gate of the MoE data-path toy (Four Bits at a Time,
 "What it takes to serve it").
 
-Decision precision.  Where a float decides an integer (an MX code, the top-k
-order), the oracle first rounds its fp64 value to fp32, the precision the GPU
-path decides in (``decide=np.float32``); ``decide=None`` keeps pure fp64.
+Precision map.  ``W.precision == "mx"``: every weight but the fp32 router is
+MXFP4 and each MX GEMM reads MXFP8 activations (the workload's own statement).
+``"bf16"``: the Moat page's map ("Precision and deployment", Fig. 6) -- only
+the routed experts are MXFP4 x MXFP8; the latent projections and the shared
+experts keep higher-precision weights, taken as bfloat16, and their GEMMs read
+bfloat16 activations: ``xb = bf16(x)`` feeds W_down and the shared gate/up
+projections, the shared hidden state is ``bf16(h)``, and the up-projection
+reads ``bf16(y_lat)``.  Products are exact in fp64 either way.
+
+Decision precision.  Where a float decides an integer (an MX code, a
+bfloat16 rounding, the top-k order), the oracle first rounds its fp64 value to
+fp32, the precision the GPU path decides in (``decide=np.float32``);
+``decide=None`` keeps pure fp64.
 """
 
 from __future__ import annotations
@@ -69,16 +79,35 @@ class MXTensor:
         return MXTensor(self.codes[idx], self.scales[idx], self.fmt)
 
 
-def quant(v, fmt="e4m3", decide=np.float32) -> MXTensor:
+@dataclasses.dataclass
+class BF16Tensor:
+    bits: np.ndarray     # uint16 bfloat16 patterns, [..., K]
+    fmt: str = "bf16"
+
+    def deq(self) -> np.ndarray:
+        return mx.bf16_value(self.bits)
+
+    def __getitem__(self, idx) -> "BF16Tensor":
+        return BF16Tensor(self.bits[idx])
+
+
+def quant(v, fmt="e4m3", decide=np.float32):
+    """MX-encode ``v`` along its last axis, or round it to bfloat16 (``fmt="bf16"``);
+    with ``decide`` the fp64 value is first rounded to that type."""
     if decide is not None:
         v = np.asarray(v).astype(decide)
+    if fmt == "bf16":
+        return BF16Tensor(mx.bf16_bits(v))
     c, s = mx.quantize(v, fmt)
     return MXTensor(c, s, fmt)
 
 
-def mm(a: MXTensor, b: MXTensor) -> np.ndarray:
-    """deq(a) @ deq(b)^T in fp64."""
-    return mx.mx_matmul(a.codes, a.scales, a.fmt, b.codes, b.scales, b.fmt)
+def mm(a, b) -> np.ndarray:
+    """deq(a) @ deq(b)^T in fp64 (MX x MX through the MX matmul; a bfloat16
+    operand makes every product exact in fp64)."""
+    if isinstance(a, MXTensor) and isinstance(b, MXTensor):
+        return mx.mx_matmul(a.codes, a.scales, a.fmt, b.codes, b.scales, b.fmt)
+    return a.deq() @ b.deq().T
 
 
 def sigmoid(v):
@@ -105,6 +134,7 @@ class LayerWeights:
     logit_bias: Optional[np.ndarray] = None       # fp32 [E] or None
     selection_bias: Optional[np.ndarray] = None   # fp32 [E] or None
     gating: str = "sigmoid"                       # or "softmax" (over the winners' logits)
+    precision: str = "mx"                         # or "bf16": latent projections + shared experts
 
 
 # --------------------------------------------------------------------------- routing
@@ -185,9 +215,9 @@ def dispatch(ids: np.ndarray, n_experts: int) -> Dispatch:
 # --------------------------------------------------------------------------- experts
 
 
-def swiglu_expert(aq: MXTensor, wg: MXTensor, wu: MXTensor, wd: MXTensor, decide=np.float32, full=False,
-                  pick=None):
-    """down(SiLU(gate a) * (up a)) with MXFP8 re-quantisation of the hidden h.
+def swiglu_expert(aq, wg, wu, wd, decide=np.float32, full=False, pick=None, hfmt="e4m3"):
+    """down(SiLU(gate a) * (up a)) with the hidden h re-encoded in ``hfmt``
+    (MXFP8, or bfloat16 for a higher-precision expert).
 
     Returns (y, h, hq), plus (g, u) when ``full``.  ``pick(g, u, h, hq)`` may
     replace the codes of hq (see ``forward``'s ``resolve``).
@@ -195,7 +225,7 @@ def swiglu_expert(aq: MXTensor, wg: MXTensor, wu: MXTensor, wd: MXTensor, decide
     g = mm(aq, wg)
     u = mm(aq, wu)
     h = silu(g) * u
-    hq = quant(h, "e4m3", decide)
+    hq = quant(h, hfmt, decide)
     if pick is not None:
         hq = pick(g, u, h, hq)
     if full:
@@ -247,7 +277,10 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
     L = W.w_router.shape[1]
 
     latent = W.w_down is not None
-    xq = quant(x, "e4m3", decide)                                   # step 1
+    hp = W.precision == "bf16"
+    if hp and not latent:
+        raise ValueError("the bfloat16 precision map is defined for the latent layer")
+    xq = quant(x, "bf16" if hp else "e4m3", decide)                 # step 1 (xb under the bf16 map)
     z = mm(xq, W.w_down) if latent else x.astype(np.float64)        # step 2 (latent only)
     r = route(z, W.w_router, top_k, W.logit_bias, W.selection_bias, decide, W.gating)   # steps 3-5
     if ids_override is not None:
@@ -260,6 +293,7 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
             zq = resolve.zq(z, zq)
     else:
         zq = xq                                                     # the experts read xq
+    sfmt = "bf16" if hp else "e4m3"                                 # shared hidden state, up-projection input
 
     P = T * top_k
     F = None
@@ -301,7 +335,7 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
             y_lat[t] += r.gates[t, j] * ye_rows[disp.row_of_pair[t * top_k + j]]
 
     if latent:                                                      # step 9
-        yq = quant(y_lat, "e4m3", decide)
+        yq = quant(y_lat, sfmt, decide)
         if resolve is not None:
             yq = resolve.yq(y_lat, yq, r, disp, ye_rows)
         y_up = mm(yq, W.w_up)
@@ -316,7 +350,7 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
             pick = (lambda g_, u_, h_, hq_, s=s: resolve.hs(s, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s],
                                                               g_, u_, h_, hq_))
         ys, hs, hsq, gs, us = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide, full=True,
-                                            pick=pick)
+                                            pick=pick, hfmt=sfmt)
         y += ys
         hs_l.append(hs)
         gs_l.append(gs)
@@ -337,7 +371,8 @@ def forward_dense_mask(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.flo
     T = x.shape[0]
     E = W.w_router.shape[0]
     latent = W.w_down is not None
-    xq = quant(x, "e4m3", decide)
+    sfmt = "bf16" if W.precision == "bf16" else "e4m3"
+    xq = quant(x, sfmt, decide)
     z = mm(xq, W.w_down) if latent else x.astype(np.float64)
     r = route(z, W.w_router, top_k, W.logit_bias, W.selection_bias, decide, W.gating)
     dense_gate = np.zeros((T, E))
@@ -347,9 +382,9 @@ def forward_dense_mask(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.flo
     for e in range(E):
         ye, _, _ = swiglu_expert(zq, W.w_gate_e[e], W.w_up_e[e], W.w_down_e[e], decide)
         y_lat += dense_gate[:, e:e + 1] * ye
-    y = mm(quant(y_lat, "e4m3", decide), W.w_up) if latent else y_lat.copy()
+    y = mm(quant(y_lat, sfmt, decide), W.w_up) if latent else y_lat.copy()
     for s in range(len(W.w_gate_s)):
-        ys, _, _ = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide)
+        ys, _, _ = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide, hfmt=sfmt)
         y = y + ys
     return y
 

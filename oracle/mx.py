@@ -244,3 +244,38 @@ def mx_bits_per_element(fmt) -> float:
     """Storage cost per element including the shared scale: (32 * element bits + 8) / 32."""
     ebits = {"e2m1": 4, "e4m3": 8}[_fmt(fmt).name]
     return (BLOCK * ebits + 8) / BLOCK
+
+
+# --------------------------------------------------------------------------- bfloat16
+#
+# The higher-precision weights of the Moat page's precision map ("Precision
+# and deployment", Fig. 6) are taken as bfloat16: the upper half of an IEEE
+# fp32 word (1 sign, 8 exponent, 7 mantissa bits).
+
+
+def bf16_bits(v) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns, round to nearest, ties to even.
+
+    The fp32 word splits into the 16 bits kept (``lo``, a sign-magnitude
+    pattern whose magnitude bits count up with |v|) and the 16 dropped
+    (``rem``).  The nearest bfloat16 is ``lo`` when ``rem`` is below half of
+    the kept unit, ``lo`` plus one unit of magnitude above half, and the even
+    one of the two at exactly half; one unit past the largest finite value is
+    infinity, as IEEE rounding gives.  NaN inputs stay NaN (quiet bit set).
+    """
+    f = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.int64)
+    lo = u >> 16
+    rem = u & 0xFFFF
+    up = (rem > 0x8000) | ((rem == 0x8000) & ((lo & 1) == 1))
+    out = np.where(up, lo + 1, lo)
+    nan = np.isnan(f)
+    out = np.where(nan, lo | 0x0040, out)
+    return out.astype(np.uint16)
+
+
+def bf16_value(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> their values (fp64, exact)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):   # signalling-NaN patterns stay NaN
+        return b.view(np.float32).astype(np.float64)

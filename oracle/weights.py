@@ -26,6 +26,14 @@ def dense(cfg, name: str, idx: int = 0) -> moe.MXTensor:
     return _q(synth.gen_weight(cfg, name, idx))
 
 
+def high(cfg, name: str, idx: int = 0):
+    """A latent-projection or shared-expert weight: MXFP4, or bfloat16 under
+    the higher-precision map (``cfg.precision == "bf16"``)."""
+    if cfg.precision == "bf16":
+        return moe.BF16Tensor(moe.mx.bf16_bits(synth.gen_weight(cfg, name, idx)))
+    return dense(cfg, name, idx)
+
+
 class ExpertCache:
     """Lazily quantised routed experts: ``cache(e) -> (w_gate, w_up, w_down)``."""
 
@@ -55,14 +63,15 @@ def layer(cfg, experts: str = "all", selection_bias=None) -> moe.LayerWeights:
     else:
         ge, ue, de = [], [], []
     return moe.LayerWeights(
-        w_down=dense(cfg, "w_down") if cfg.latent else None,
-        w_up=dense(cfg, "w_up") if cfg.latent else None,
+        w_down=high(cfg, "w_down") if cfg.latent else None,
+        w_up=high(cfg, "w_up") if cfg.latent else None,
         w_router=synth.gen_router(cfg),
         w_gate_e=ge, w_up_e=ue, w_down_e=de,
-        w_gate_s=[dense(cfg, "w_gate_s", s) for s in range(S)],
-        w_up_s=[dense(cfg, "w_up_s", s) for s in range(S)],
-        w_down_s=[dense(cfg, "w_down_s", s) for s in range(S)],
+        w_gate_s=[high(cfg, "w_gate_s", s) for s in range(S)],
+        w_up_s=[high(cfg, "w_up_s", s) for s in range(S)],
+        w_down_s=[high(cfg, "w_down_s", s) for s in range(S)],
         logit_bias=synth.gen_logit_bias(cfg),
         selection_bias=selection_bias,
         gating=cfg.gating,
+        precision=cfg.precision,
     )

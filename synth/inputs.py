@@ -46,6 +46,8 @@ class LayerConfig:
     latent: bool = True          # False: no latent projections (routed width = model width)
     gating: str = "sigmoid"      # "sigmoid": winners' sigmoid scores / their sum;
                                  # "softmax": softmax over the winners' logits
+    precision: str = "mx"        # "mx": every weight but the router MXFP4;
+                                 # "bf16": latent projections and shared experts bfloat16
 
     def with_tokens(self, T: int) -> "LayerConfig":
         return dataclasses.replace(self, T=int(T))
@@ -99,6 +101,20 @@ CONFIGS = {
     "k2_tiny": LayerConfig("k2_tiny", T=64, d_model=256, d_latent=256, n_routed=48, top_k=4,
                            n_shared=1, d_ff_shared=256, d_ff_routed=128, router_init="normal",
                            logit_bias="none", seed_x=1006, seed_w=1006, latent=False, gating="softmax"),
+    # The Moat page's precision map on the K3 layers: bfloat16 latent
+    # projections and shared experts, MXFP4 routed experts (same seeds, so the
+    # same fp32 weights as the MX presets).
+    "tiny_bf16": LayerConfig("tiny_bf16", T=64, d_model=256, d_latent=128, n_routed=32, top_k=4,
+                             n_shared=1, d_ff_shared=256, d_ff_routed=128,
+                             router_init="normal", logit_bias="none", seed_x=1001, seed_w=1001, precision="bf16"),
+    "k3_decode_bf16": LayerConfig("k3_decode_bf16", T=64, d_model=7168, d_latent=3584, n_routed=896,
+                                  top_k=16, n_shared=2, d_ff_shared=3072, d_ff_routed=3072,
+                                  router_init="normal", logit_bias="none", seed_x=1003, seed_w=1003,
+                                  precision="bf16"),
+    "k3_prefill_bf16": LayerConfig("k3_prefill_bf16", T=16384, d_model=7168, d_latent=3584, n_routed=896,
+                                   top_k=16, n_shared=2, d_ff_shared=3072, d_ff_routed=3072,
+                                   router_init="normal", logit_bias="none", seed_x=1004, seed_w=1003,
+                                   precision="bf16"),
     "k2_prefill": LayerConfig("k2_prefill", T=8192, d_model=7168, d_latent=7168, n_routed=384, top_k=8,
                               n_shared=1, d_ff_shared=2048, d_ff_routed=2048, router_init="normal",
                               logit_bias="none", seed_x=1007, seed_w=1007, latent=False, gating="softmax"),
