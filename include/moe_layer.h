@@ -94,6 +94,18 @@ typedef struct {
    * section "What it takes to serve it"). */
   int32_t identity_latent;
   int32_t softmax_gates;
+  /* Higher-precision map (Moat page, section "Precision and deployment",
+   * Fig. 6: only the routed experts are MXFP4 x MXFP8; the latent projections
+   * and the shared experts stay at higher precision, here bfloat16).
+   * dense_bf16 != 0 (latent layers only): W_down, W_up and the shared experts
+   * are the bfloat16 tensors *_bf16 of moe_layer_weights (their MX tensors may
+   * be NULL), and
+   *     xb = bf16(x)   (round to nearest even)
+   *     z  = xb W_down^T                  (fp32 accumulation)
+   *     hs = bf16(SiLU(xb W_gate_s^T) * (xb W_up_s^T))
+   *     y  = bf16(y_lat) W_up^T + sum_s hs W_down_s^T.
+   * The router, top-k, dispatch and routed experts are unchanged. */
+  int32_t dense_bf16;
 } moe_layer_config;
 
 /* One MXFP4 (E2M1) tensor: packed codes and E8M0 scales, device memory. */
@@ -118,6 +130,13 @@ typedef struct {
   moe_mx_tensor w_gate_s;          /* [S][Fs][d]  shared gate projections       */
   moe_mx_tensor w_up_s;            /* [S][Fs][d]  shared up projections         */
   moe_mx_tensor w_down_s;          /* [S][d][Fs]  shared down projections       */
+  /* bfloat16 [out][in] row-major weights of the higher-precision map
+   * (dense_bf16 != 0; otherwise ignored and may be NULL), 16-byte aligned. */
+  const uint16_t* w_down_bf16;     /* [L][d]                                    */
+  const uint16_t* w_up_bf16;       /* [d][L]                                    */
+  const uint16_t* w_gate_s_bf16;   /* [S][Fs][d]                                */
+  const uint16_t* w_up_s_bf16;     /* [S][Fs][d]                                */
+  const uint16_t* w_down_s_bf16;   /* [S][d][Fs]                                */
 } moe_layer_weights;
 
 /* Stage boundaries at which moe_layer_forward records the optional timing
@@ -162,6 +181,11 @@ typedef struct {
   float* hs;                                 /* [S][T][Fs] shared hidden, fp32 */
   uint8_t* hs_codes;   uint8_t* hs_scales;   /* [S][T][Fs], [S][T][Fs/32]    */
   void* const* events;                       /* host array of hipEvent_t, or NULL */
+  /* Higher-precision map only (the MX copies xq, yq, hs_codes are then not
+   * written): */
+  uint16_t* xb;                              /* [T][d] bf16(x)               */
+  uint16_t* yb;                              /* [T][L] bf16(y_lat)           */
+  uint16_t* hs_bf16;                         /* [S][T][Fs] shared hidden, bf16 */
 } moe_layer_trace;
 
 typedef struct moe_layer* moe_layer_t;
@@ -216,6 +240,12 @@ int moe_mx_quantize_weights(const float* in, int64_t G, int32_t N, int32_t K,
  * buffers 4-byte aligned.  Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
 int moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t G, int32_t N, int32_t K,
                         uint8_t* out_codes, uint8_t* out_scales, void* stream);
+
+/* fp32 -> bfloat16 (round to nearest, ties to even; finite inputs), n values;
+ * n % 4 == 0, in 16-byte and out 8-byte aligned.  The forward's rounding of
+ * x under the higher-precision map; callers use it to encode bfloat16 weights.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
+int moe_round_bf16(const float* in, int64_t n, uint16_t* out, void* stream);
 
 /* Dense MX GEMM c[M][N] = deq(a) deq(b)^T in fp32, a = E4M3 [M][K] (row-major),
  * b = E2M1 [N][K] in fragment order, N a positive multiple of 16, K of 128.

@@ -27,6 +27,7 @@ EXPORTED = (
     "moe_layer_forward",
     "moe_layer_destroy",
     "moe_mx_quantize",
+    "moe_round_bf16",
     "moe_mx_quantize_weights",
     "moe_mx_pack_weights",
     "moe_mx_gemm",
@@ -42,7 +43,7 @@ class MoEError(RuntimeError):
 class MoeLayerConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "d_latent", "n_routed", "top_k", "n_shared", "d_ff_routed", "d_ff_shared", "max_tokens",
-        "identity_latent", "softmax_gates")]
+        "identity_latent", "softmax_gates", "dense_bf16")]
 
 
 class MoeMxTensor(ctypes.Structure):
@@ -62,6 +63,12 @@ class MoeLayerWeights(ctypes.Structure):
         ("w_gate_s", MoeMxTensor),
         ("w_up_s", MoeMxTensor),
         ("w_down_s", MoeMxTensor),
+        # bfloat16 weights of the higher-precision map (dense_bf16)
+        ("w_down_bf16", ctypes.c_void_p),
+        ("w_up_bf16", ctypes.c_void_p),
+        ("w_gate_s_bf16", ctypes.c_void_p),
+        ("w_up_s_bf16", ctypes.c_void_p),
+        ("w_down_s_bf16", ctypes.c_void_p),
     ]
 
 
@@ -77,8 +84,13 @@ STAGES = ("quant_x", "down", "logits", "topk", "dispatch", "expert_up", "expert_
           "out")
 
 
+# written instead of xq / yq / hs codes under the higher-precision map
+BF16_TRACE_FIELDS = ("xb", "yb", "hs_bf16")
+
+
 class MoeLayerTrace(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in TRACE_FIELDS] + [("events", ctypes.c_void_p)]
+    _fields_ = ([(n, ctypes.c_void_p) for n in TRACE_FIELDS] + [("events", ctypes.c_void_p)]
+                + [(n, ctypes.c_void_p) for n in BF16_TRACE_FIELDS])
 
 
 _lib = None
@@ -112,6 +124,8 @@ def load() -> ctypes.CDLL:
     lib.moe_mx_pack_weights.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
     lib.moe_mx_gemm.restype = ctypes.c_int
     lib.moe_mx_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.moe_round_bf16.restype = ctypes.c_int
+    lib.moe_round_bf16.argtypes = [vp, i64, vp, vp]
     _lib = lib
     return lib
 
@@ -166,3 +180,7 @@ def moe_mx_gemm(a_codes: int, a_scales: int, b_codes: int, b_scales: int, M: int
                 stream: int = 0) -> None:
     _check(load().moe_mx_gemm(a_codes, a_scales, b_codes, b_scales, int(M), int(N), int(K), c, stream),
            "moe_mx_gemm")
+
+
+def moe_round_bf16(src: int, n: int, out: int, stream: int = 0) -> None:
+    _check(load().moe_round_bf16(src, int(n), out, stream), "moe_round_bf16")

@@ -1,5 +1,6 @@
 // combine.hip -- gate-weighted combine of the expert outputs, fused with the
-// MXFP8 quantisation of the combined latent.
+// MXFP8 quantisation of the combined latent (or its bfloat16 rounding, under
+// the higher-precision map).
 //
 // Four Bits at a Time, "What it takes to serve it" (MoE data-path toy): the
 // expert outputs are unpermuted and summed per token with the gates; Kimi K3
@@ -33,7 +34,7 @@ __global__ void __launch_bounds__(1024) combine_kernel(const float* __restrict__
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ row_of_pair, int k, int L,
                                                       float* __restrict__ y_lat, uint8_t* __restrict__ yq,
-                                                      uint8_t* __restrict__ yqs) {
+                                                      uint8_t* __restrict__ yqs, uint16_t* __restrict__ yb) {
   __shared__ int32_t rows[64];
   __shared__ float gs[64];
   const int t = blockIdx.x;
@@ -61,6 +62,9 @@ __global__ void __launch_bounds__(1024) combine_kernel(const float* __restrict__
         }
     }
     if (y_lat) reinterpret_cast<float4*>(y_lat + (int64_t)t * L)[f] = acc;
+    if (yb)  // bfloat16 input of a higher-precision up-projection
+      reinterpret_cast<uint2*>(yb + (int64_t)t * L)[f] =
+          make_uint2(bf16_rne(acc.x) | (bf16_rne(acc.y) << 16), bf16_rne(acc.z) | (bf16_rne(acc.w) << 16));
     if (yq) {  // uniform over the launch
       uint32_t m = max(max(__float_as_uint(acc.x) & 0x7fffffffu, __float_as_uint(acc.y) & 0x7fffffffu),
                        max(__float_as_uint(acc.z) & 0x7fffffffu, __float_as_uint(acc.w) & 0x7fffffffu));
@@ -75,11 +79,11 @@ __global__ void __launch_bounds__(1024) combine_kernel(const float* __restrict__
 }
 
 hipError_t launch_combine(const float* y_e, const float* gates, const int32_t* row_of_pair, int T, int k, int L,
-                          float* y_lat, uint8_t* yq, uint8_t* yqs, hipStream_t s) {
+                          float* y_lat, uint8_t* yq, uint8_t* yqs, hipStream_t s, uint16_t* yb) {
   if (T == 0) return hipSuccess;
   int threads = ((L / 4 + 63) / 64) * 64;
   threads = threads > 1024 ? 1024 : threads;
-  combine_kernel<<<dim3(T), dim3(threads), 0, s>>>(y_e, gates, row_of_pair, k, L, y_lat, yq, yqs);
+  combine_kernel<<<dim3(T), dim3(threads), 0, s>>>(y_e, gates, row_of_pair, k, L, y_lat, yq, yqs, yb);
   return hipGetLastError();
 }
 

@@ -70,14 +70,17 @@ __device__ __forceinline__ T* at_byte(T* base, uint32_t off) {
 }
 
 // Write one wave's MW x NW accumulator tiles (16x16 each; NB accumulators per
-// tile for SwiGLU) in the epilogue's form.  Lane (r16, g4) holds column
+// tile for SwiGLU) in the epilogue's form (fp32, MXFP8 codes, or the bf16
+// hidden state of a higher-precision SwiGLU expert).  Lane (r16, g4) holds column
 // n0 + 16*ni + r16 of rows m0 + 16*mi + 4*g4 + i.  The 16 lanes of a row
 // share its row index, so the block reductions only combine lanes of one row.
 template <int MW, int NW, int NB, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const v4f (&acc)[MW][NW][NB], int r16,
                                          int g4) {
-  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
-  constexpr bool QNT = EPI != EPI_F32;
+  constexpr bool BFO = EPI == EPI_SWIGLU_BF16;   // bf16 hidden state, no MX codes
+  constexpr bool SWI = EPI == EPI_SWIGLU_QUANT || BFO;
+  constexpr bool QNT = EPI == EPI_F32_QUANT || EPI == EPI_SWIGLU_QUANT;
+  constexpr bool PAIRS = QNT || BFO;              // values taken 32 columns (two fragments) at a time
   const bool dense = p.offsets == nullptr;
   // Kernel arguments read once (stores through these pointers cannot alias
   // them); bases at the wave's first output row and column.
@@ -88,6 +91,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
   uint8_t* const qb = QNT ? p.q + (dense ? (int64_t)t.g * p.q_gstride : 0) + orow0 * N + t.n0 : nullptr;
   uint8_t* const sb = QNT ? p.qs + (dense ? (int64_t)t.g * p.qs_gstride : 0) + orow0 * (N >> 5) + (t.n0 >> 5)
                           : nullptr;
+  uint16_t* const ob = BFO ? p.ob + (dense ? (int64_t)t.g * p.ob_gstride : 0) + orow0 * N + t.n0 : nullptr;
   const uint32_t c_lane = 4u * ((uint32_t)(4 * g4) * ldc + (uint32_t)r16);
   const uint32_t q_lane = (uint32_t)(4 * g4) * (uint32_t)N + (uint32_t)r16;
   const uint32_t s_lane = (uint32_t)(4 * g4) * (uint32_t)(N >> 5);
@@ -95,11 +99,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
   for (int mi = 0; mi < MW; ++mi) {
     // Values, block maxima and codes of the fragment's four rows first, with
     // no branches, so the independent DPP reductions interleave; then stores.
-    constexpr int NQ = QNT ? NW / 2 : 1;
+    constexpr int NQ = PAIRS ? NW / 2 : 1;
     float hv[4][NQ][2];
     uint32_t q2[4][NQ];
     int sc[4][NQ];
-    if (QNT) {
+    if (PAIRS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -111,7 +115,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
             hv[i][b][0] = acc[mi][2 * b][0][i];
             hv[i][b][1] = acc[mi][2 * b + 1][0][i];
           }
-          q2[i][b] = quant_pair(hv[i][b][0], hv[i][b][1], sc[i][b]);
+          if (QNT) q2[i][b] = quant_pair(hv[i][b][0], hv[i][b][1], sc[i][b]);
         }
     }
 #pragma unroll
@@ -138,6 +142,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& t, const
             qb[oq + 32u * b + 16u] = (uint8_t)(q2[i][b] >> 8);
             if (r16 == 0) sb[os + b] = (uint8_t)sc[i][b];
             if (SWI && cb != nullptr) {  // optional fp32 copy of h (tracing)
+              const uint32_t o = c_lane + 4u * rr * ldc + 128u * b;
+              *at_byte(cb, o) = hv[i][b][0];
+              *at_byte(cb, o + 64u) = hv[i][b][1];
+            }
+          }
+        }
+      }
+      if (BFO) {
+        const uint32_t oq = q_lane + rr * (uint32_t)N;   // element offset, as for the codes
+#pragma unroll
+        for (int b = 0; b < NQ; ++b) {
+          if (t.n0 + 32 * b < N) {
+            ob[oq + 32u * b] = (uint16_t)bf16_rne(hv[i][b][0]);
+            ob[oq + 32u * b + 16u] = (uint16_t)bf16_rne(hv[i][b][1]);
+            if (cb != nullptr) {  // optional fp32 copy of h (tracing)
               const uint32_t o = c_lane + 4u * rr * ldc + 128u * b;
               *at_byte(cb, o) = hv[i][b][0];
               *at_byte(cb, o + 64u) = hv[i][b][1];

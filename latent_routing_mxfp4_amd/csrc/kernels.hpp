@@ -28,6 +28,9 @@ hipError_t launch_pack_e2m1(const uint8_t* codes, const uint8_t* scales, int64_t
 // E2M1 packed [rows][K/2] + scales [rows][K/32] -> exact bf16 [rows][K].
 hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
                                    uint16_t* out, hipStream_t s);
+// fp32 [n] -> bfloat16 [n], round to nearest even (n % 4 == 0, in 16-byte and
+// out 8-byte aligned).
+hipError_t launch_round_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);
 
 // ---- Router (router.hip) ----------------------------------------------------
 // logits[T][E] = z[T][L] w[E][L]^T (+ bias[E]) at fp32 accuracy.  Many tokens
@@ -56,9 +59,10 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* scr
 
 // ---- MX GEMM (mx_gemm.hip) --------------------------------------------------
 enum Epilogue : int {
-  EPI_F32 = 0,         // c = acc (fp32)
-  EPI_F32_QUANT = 1,   // c = acc and q = MXFP8(acc) along N
-  EPI_SWIGLU_QUANT = 2 // q = MXFP8(SiLU(acc_gate) * acc_up) along N
+  EPI_F32 = 0,          // c = acc (fp32)
+  EPI_F32_QUANT = 1,    // c = acc and q = MXFP8(acc) along N
+  EPI_SWIGLU_QUANT = 2, // q = MXFP8(SiLU(acc_gate) * acc_up) along N
+  EPI_SWIGLU_BF16 = 3   // ob = bf16(SiLU(acc_gate) * acc_up) (bf16 kernels only)
 };
 
 struct GemmSeg {
@@ -95,6 +99,8 @@ struct GemmArgs {
   uint8_t* qs;                 // scales [rows][N/32]
   int64_t q_gstride;           // bytes between dense groups' code outputs
   int64_t qs_gstride;
+  uint16_t* ob;                // EPI_SWIGLU_BF16: bfloat16 [rows][N]
+  int64_t ob_gstride;          // elements between dense groups' bf16 outputs
   int max_mtiles;              // upper bound of M-tiles (grid size / n-tiles)
 };
 
@@ -104,16 +110,42 @@ struct GemmArgs {
 enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_WIDE = 4 };
 int gemm_mtile(int shape);
 
-// Dense bf16 GEMM (seg[0].a = bf16 [M][K], seg[0].b = bf16 [N][K]) with the
-// fp32 + MXFP8 epilogue (EPI_F32_QUANT); shape GEMM_WIDE = the 512-thread
-// 128 x 256 kernel (mx_gemm_wide.hip), K a multiple of 64.
+// Dense bf16 GEMM on the 512-thread 128 x 256 kernel (mx_gemm_wide.hip): G
+// dense groups of M rows, A = bf16 [M][K] per K segment (seg[i].a, shared by
+// the groups), B = bf16 [N][K] row-major (seg[i].b + g * b_gstride bytes), the
+// segments' products summed in fp32; every K a multiple of 64.  Epilogues:
+// EPI_F32, EPI_F32_QUANT, and EPI_SWIGLU_BF16 with seg[i].b2 the "up" matrix
+// (128 output columns per tile instead of 256).
 hipError_t launch_bf16_gemm_quant(const GemmArgs& args, int shape, hipStream_t s);
-hipError_t launch_bf16_gemm_wide(const GemmArgs& args, hipStream_t s);
+hipError_t launch_bf16_gemm_wide(const GemmArgs& args, int epilogue, hipStream_t s);
 
-// Few-row dense GEMM from row-major MXFP4 weights (seg[0].b codes [N][K/2],
-// seg[0].bs scales [N][K/32]) decoded to bf16 in registers, A = bf16 [M][K]:
-// K split into S slices whose fp32 partial sums go to part[S][M][N], then
-// z = their sum in slice order and, when zq is given, its MXFP8 codes along N.
+// Few-row dense bf16 GEMMs with K split into slices (decode sizes).  A =
+// bf16 [M][K] per segment; B row-major, either MXFP4 (seg.b codes [N][K/2],
+// seg.bs scales [N][K/32], decoded to exact bf16 in registers) or bf16
+// [N][K].  G dense groups (B + g * b_gstride bytes); with seg.b2, columns
+// [N/2, N) read b2 (the "up" half of a SwiGLU pair).  Each K segment is cut
+// into slices of at most kper 128-wide K-steps; slice s writes its fp32
+// partial sums to part[s][g][M][N].  Every K a multiple of 128, N of 32.
+constexpr int kMaxSlices = 24;
+struct SplitPlan {
+  int n;                      // slices
+  int8_t seg[kMaxSlices];     // segment of slice s
+  int16_t ks0[kMaxSlices];    // its first K-step (128 wide) in the segment
+  int16_t nks[kMaxSlices];    // its K-steps
+};
+SplitPlan splitk_plan(const GemmArgs& args);
+hipError_t launch_bf16_splitk(const GemmArgs& args, bool bf16_b, const SplitPlan& sp, float* part, hipStream_t s);
+// c[M][N] = sum of the S partials in slice order; with q, its MXFP8 codes along N.
+hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, float* c, uint8_t* q, uint8_t* qs,
+                                hipStream_t s);
+// h = SiLU(gate) * up from S partials of G pair-groups [S][G][M][2F] (gate
+// columns [0, F), up columns [F, 2F)), written as bf16 [G][M][F] and, when
+// h32 is given, fp32.
+hipError_t launch_splitk_swiglu(const float* part, int S, int G, int M, int F, float* h32, uint16_t* hb,
+                                hipStream_t s);
+
+// The latent down-projection at decode sizes (MXFP4 weights): split-K as
+// above, then z and, when zq is given, its MXFP8 codes.
 int bf16_mx_splitk_slices(int M, int N, int K);
 hipError_t launch_bf16_mx_splitk(const GemmArgs& args, float* part, int S, float* z, uint8_t* zq, uint8_t* zqs,
                                  hipStream_t s);
@@ -128,9 +160,9 @@ hipError_t launch_mx_gemm_wide(const GemmArgs& args, int epilogue, hipStream_t s
 
 // ---- Combine (combine.hip) --------------------------------------------------
 // y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then
-// yq = MXFP8(y_lat) per row; y_lat_out may be null, and so may yq/yqs (no
-// quantisation).
+// yq = MXFP8(y_lat) per row and/or yb = bf16(y_lat); any output may be null.
 hipError_t launch_combine(const float* y_e, const float* gates, const int32_t* row_of_pair, int T, int k,
-                          int L, float* y_lat_out, uint8_t* yq, uint8_t* yqs, hipStream_t s);
+                          int L, float* y_lat_out, uint8_t* yq, uint8_t* yqs, hipStream_t s,
+                          uint16_t* yb = nullptr);
 
 }  // namespace moe

@@ -18,6 +18,11 @@
 // GEMM whose K dimension is the concatenation [L | Fs | Fs ...], so the sum of
 // the routed and shared branches (Moat page, Fig. 2) happens in the fp32
 // accumulators instead of an extra pass over y.
+//
+// Higher-precision map (dense_bf16): step 1 rounds x to bf16 (xb), and steps
+// 2, 9 and 10 are bf16 GEMMs on bfloat16 weights (LDS-staged 512-thread
+// kernel for many tokens, K-split weight streaming plus a reduce for few);
+// the combine writes bf16(y_lat) and the shared hidden state is bf16.
 #include <stdint.h>
 #include <string.h>
 
@@ -40,8 +45,43 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
   size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, wrpl, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye,
-      ylat, yq, yqs, hs, hss, total;
+      ylat, yq, yqs, hs, hss, xb, yb, hb, dpart, total;
 };
+
+// The bf16 GEMMs of the higher-precision map (operand pointers left null:
+// the shapes alone decide the K-slice plan and the partial-sum buffer).
+moe::GemmArgs hp_down_args(const moe_layer_config& c, int T) {
+  moe::GemmArgs a = {};
+  a.nseg = 1;
+  a.seg[0].K = a.seg[0].lda = c.d_model;
+  a.G = 1;
+  a.M = T;
+  a.N = c.d_latent;
+  return a;
+}
+// Shared gate/up; split-K form: N = 2 Fs partial columns (gate, then up).
+moe::GemmArgs hp_shared_args(const moe_layer_config& c, int T, bool split) {
+  moe::GemmArgs a = {};
+  a.nseg = 1;
+  a.seg[0].K = a.seg[0].lda = c.d_model;
+  a.seg[0].b_gstride = (int64_t)c.d_ff_shared * c.d_model * 2;
+  a.G = c.n_shared;
+  a.M = T;
+  a.N = split ? 2 * c.d_ff_shared : c.d_ff_shared;
+  return a;
+}
+// Up-projection and shared down-projections, K = [L | Fs | Fs ...].
+moe::GemmArgs hp_out_args(const moe_layer_config& c, int T) {
+  moe::GemmArgs a = {};
+  a.nseg = 1 + c.n_shared;
+  a.seg[0].K = a.seg[0].lda = c.d_latent;
+  for (int i = 0; i < c.n_shared; ++i) a.seg[1 + i].K = a.seg[1 + i].lda = c.d_ff_shared;
+  a.G = 1;
+  a.M = T;
+  a.N = c.d_model;
+  return a;
+}
+size_t splitk_floats(const moe::GemmArgs& a) { return (size_t)moe::splitk_plan(a).n * a.G * a.M * a.N; }
 
 Plan make_plan(const moe_layer_config& c, int64_t T) {
   const int64_t d = c.d_model, L = c.d_latent, E = c.n_routed, k = c.top_k, F = c.d_ff_routed,
@@ -57,15 +97,34 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   // Without a latent (second workload) nothing of the latent path exists:
   // the router reads x, the experts read xq and the combine writes y.
   const int64_t lat = c.identity_latent ? 0 : 1;
-  p.xq = take(T * d);
-  p.xqs = take(T * d / 32);
-  p.xdq = take(lat * T * d * 2);
+  // Higher-precision map: no MXFP8 copy of x, of y_lat or of the shared
+  // hidden state; bf16 ones instead.
+  const int64_t hp = c.dense_bf16 ? 1 : 0, mxd = 1 - hp;
+  p.xq = take(mxd * T * d);
+  p.xqs = take(mxd * T * d / 32);
+  p.xdq = take(mxd * lat * T * d * 2);
   // Latent down-projection: at most kFewRows tokens stream the MXFP4 weights
   // (K-slice partial sums), more tokens use a bf16 image of W_down.
   const bool few = T <= kFewRows;
-  p.wdn16 = take(few ? 0 : lat * L * d * 2);
+  p.wdn16 = take(few ? 0 : mxd * lat * L * d * 2);
   p.zpart =
-      take(few && T > 0 ? (size_t)lat * moe::bf16_mx_splitk_slices((int)T, (int)L, (int)d) * T * L * 4 : 0);
+      take(few && T > 0 ? (size_t)mxd * lat * moe::bf16_mx_splitk_slices((int)T, (int)L, (int)d) * T * L * 4 : 0);
+  p.xb = take(hp * T * d * 2);
+  p.yb = take(hp * T * L * 2);
+  p.hb = take(hp * S * T * Fs * 2);
+  {
+    size_t f = 0;
+    if (hp && few && T > 0) {
+      f = splitk_floats(hp_down_args(c, (int)T));
+      if (S > 0) {
+        const size_t f2 = splitk_floats(hp_shared_args(c, (int)T, true));
+        f = f2 > f ? f2 : f;
+      }
+      const size_t f3 = splitk_floats(hp_out_args(c, (int)T));
+      f = f3 > f ? f3 : f;
+    }
+    p.dpart = take(f * 4);  // K-slice partial sums of the few-row bf16 GEMMs (used one at a time)
+  }
   p.z = take(lat * T * L * 4);
   p.zq = take(lat * T * L);
   p.zqs = take(lat * T * L / 32);
@@ -89,10 +148,10 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   p.hqs = take(P * F / 32);
   p.ye = take(P * L * 4);
   p.ylat = take(lat * T * L * 4);
-  p.yq = take(lat * T * L);
-  p.yqs = take(lat * T * L / 32);
-  p.hs = take(S * T * Fs);
-  p.hss = take(S * T * Fs / 32);
+  p.yq = take(mxd * lat * T * L);
+  p.yqs = take(mxd * lat * T * L / 32);
+  p.hs = take(mxd * S * T * Fs);
+  p.hss = take(mxd * S * T * Fs / 32);
   p.total = o;
   return p;
 }
@@ -105,6 +164,7 @@ int check_config(const moe_layer_config* c) {
   if (c->top_k > c->n_routed || c->n_shared > 8 || c->max_tokens > (1 << 20)) return MOE_ERR_INVALID_ARG;
   if (c->n_shared > 0 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
   if (c->identity_latent && c->d_latent != c->d_model) return MOE_ERR_INVALID_ARG;
+  if (c->dense_bf16 && c->identity_latent) return MOE_ERR_UNSUPPORTED;  // the map is the latent layer's
   if (c->n_routed > 4096 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
   if (c->d_model % 128 || c->d_latent % 128 || c->d_ff_routed % 128) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && c->d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
@@ -145,16 +205,24 @@ int moe_layer_create(const moe_layer_config* cfg, const moe_layer_weights* w, mo
   int st = check_config(cfg);
   if (st != MOE_OK) return st;
   const bool latent = !cfg->identity_latent;
-  if ((latent && (!mx_ok(w->w_down) || !mx_ok(w->w_up))) || !w->w_router || !mx_ok(w->w_gate_e) ||
+  const bool hp = cfg->dense_bf16 != 0;
+  const bool mx_dense = latent && !hp, shared = cfg->n_shared > 0;
+  if ((mx_dense && (!mx_ok(w->w_down) || !mx_ok(w->w_up))) || !w->w_router || !mx_ok(w->w_gate_e) ||
       !mx_ok(w->w_up_e) || !mx_ok(w->w_down_e))
     return MOE_ERR_INVALID_ARG;
-  if (cfg->n_shared > 0 && (!mx_ok(w->w_gate_s) || !mx_ok(w->w_up_s) || !mx_ok(w->w_down_s)))
+  if (shared && !hp && (!mx_ok(w->w_gate_s) || !mx_ok(w->w_up_s) || !mx_ok(w->w_down_s)))
     return MOE_ERR_INVALID_ARG;
-  if ((latent && (!mx_aligned(w->w_down) || !mx_aligned(w->w_up))) || !mx_aligned(w->w_gate_e) ||
+  if ((mx_dense && (!mx_aligned(w->w_down) || !mx_aligned(w->w_up))) || !mx_aligned(w->w_gate_e) ||
       !mx_aligned(w->w_up_e) || !mx_aligned(w->w_down_e) || !aligned(w->w_router, 16))
     return MOE_ERR_INVALID_ARG;
-  if (cfg->n_shared > 0 && (!mx_aligned(w->w_gate_s) || !mx_aligned(w->w_up_s) || !mx_aligned(w->w_down_s)))
+  if (shared && !hp && (!mx_aligned(w->w_gate_s) || !mx_aligned(w->w_up_s) || !mx_aligned(w->w_down_s)))
     return MOE_ERR_INVALID_ARG;
+  if (hp) {
+    auto ok16 = [](const void* p) { return p != nullptr && aligned(p, 16); };
+    if (!ok16(w->w_down_bf16) || !ok16(w->w_up_bf16)) return MOE_ERR_INVALID_ARG;
+    if (shared && (!ok16(w->w_gate_s_bf16) || !ok16(w->w_up_s_bf16) || !ok16(w->w_down_s_bf16)))
+      return MOE_ERR_INVALID_ARG;
+  }
   moe_layer* h = new (std::nothrow) moe_layer;
   if (!h) return MOE_ERR_INVALID_ARG;
   h->cfg = *cfg;
@@ -224,6 +292,13 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   uint8_t* yqs = at<uint8_t>(ws, pl.yqs);
   uint8_t* hs = at<uint8_t>(ws, pl.hs);
   uint8_t* hss = at<uint8_t>(ws, pl.hss);
+  uint16_t* xb = at<uint16_t>(ws, pl.xb);
+  uint16_t* yb = at<uint16_t>(ws, pl.yb);
+  uint16_t* hb = at<uint16_t>(ws, pl.hb);
+  float* dpart = at<float>(ws, pl.dpart);
+  const bool hp = c.dense_bf16 != 0;
+  const bool few = T <= kFewRows;
+  auto u8 = [](const void* p) { return reinterpret_cast<const uint8_t*>(p); };
 
   // Kernel shapes: weight streaming when a group has few rows (decode), the
   // LDS-staged 512-thread kernels otherwise.
@@ -238,7 +313,8 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
 
   // 1. xq (and its exact bf16 image for the latent down-projection)
   const bool latent = !c.identity_latent;
-  MOE_HIP(moe::launch_quantize(x, T, d, 0, xq, xqs, s, latent ? xdq : nullptr));
+  if (hp) MOE_HIP(moe::launch_round_bf16(x, (int64_t)T * d, xb, s));
+  else MOE_HIP(moe::launch_quantize(x, T, d, 0, xq, xqs, s, latent ? xdq : nullptr));
   MOE_HIP(mark(MOE_EV_QUANT_X));
   // What the router and the routed experts read: the latent, or x itself.
   const float* zr = latent ? z : x;
@@ -251,6 +327,22 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   //    their sum and MXFP8); many tokens: one bf16 image, then the LDS kernel.
   if (!latent) {
     // no latent projection
+  } else if (hp) {  // bfloat16 W_down on bf16(x)
+    moe::GemmArgs a = hp_down_args(c, T);
+    a.seg[0].a = u8(xb);
+    a.seg[0].b = u8(w.w_down_bf16);
+    if (few) {
+      const moe::SplitPlan sp = moe::splitk_plan(a);
+      MOE_HIP(moe::launch_bf16_splitk(a, true, sp, dpart, s));
+      MOE_HIP(moe::launch_splitk_reduce(dpart, sp.n, T, L, z, zq, zqs, s));
+    } else {
+      a.c = z;
+      a.ldc = L;
+      a.q = zq;
+      a.qs = zqs;
+      a.max_mtiles = (T + moe::gemm_mtile(moe::GEMM_WIDE) - 1) / moe::gemm_mtile(moe::GEMM_WIDE);
+      MOE_HIP(moe::launch_bf16_gemm_wide(a, moe::EPI_F32_QUANT, s));
+    }
   } else if (T <= kFewRows) {
     moe::GemmArgs a = {};
     a.nseg = 1;
@@ -343,7 +435,9 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   // 8. combine
   // The fp32 combined latent is only kept for a trace; yq is what the
   // up-projection reads.
-  if (latent) {
+  if (hp) {
+    MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, tr && tr->y_lat ? ylat : nullptr, nullptr, nullptr, s, yb));
+  } else if (latent) {
     MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, tr && tr->y_lat ? ylat : nullptr, yq, yqs, s));
   } else {  // the routed output at model width goes straight to y
     MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, y, nullptr, nullptr, s));
@@ -352,7 +446,25 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(mark(MOE_EV_COMBINE));
 
   // 9. shared experts, first half
-  if (S > 0) {
+  if (S > 0 && hp) {  // bfloat16 gate/up on bf16(x), hidden state rounded to bf16
+    moe::GemmArgs a = hp_shared_args(c, T, few);
+    a.seg[0].a = u8(xb);
+    a.seg[0].b = u8(w.w_gate_s_bf16);
+    a.seg[0].b2 = u8(w.w_up_s_bf16);
+    if (few) {
+      const moe::SplitPlan sp = moe::splitk_plan(a);
+      MOE_HIP(moe::launch_bf16_splitk(a, true, sp, dpart, s));
+      MOE_HIP(moe::launch_splitk_swiglu(dpart, sp.n, S, T, Fs, tr ? tr->hs : nullptr, hb, s));
+    } else {
+      a.c = tr ? tr->hs : nullptr;
+      a.ldc = Fs;
+      a.c_gstride = (int64_t)T * Fs;
+      a.ob = hb;
+      a.ob_gstride = (int64_t)T * Fs;
+      a.max_mtiles = S * ((T + moe::gemm_mtile(moe::GEMM_WIDE) - 1) / moe::gemm_mtile(moe::GEMM_WIDE));
+      MOE_HIP(moe::launch_bf16_gemm_wide(a, moe::EPI_SWIGLU_BF16, s));
+    }
+  } else if (S > 0) {
     moe::GemmArgs a = {};
     a.nseg = 1;
     a.seg[0] = {xq,
@@ -382,7 +494,25 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
 
   // 10. y = up-projection + shared down-projections (one K-concatenated
   //     GEMM); without a latent, y (the routed output) += the shared ones.
-  if (latent || S > 0) {
+  if (hp) {
+    moe::GemmArgs a = hp_out_args(c, T);
+    a.seg[0].a = u8(yb);
+    a.seg[0].b = u8(w.w_up_bf16);
+    for (int i = 0; i < S; ++i) {
+      a.seg[1 + i].a = u8(hb + (int64_t)i * T * Fs);
+      a.seg[1 + i].b = u8(w.w_down_s_bf16 + (int64_t)i * d * Fs);
+    }
+    if (few) {
+      const moe::SplitPlan sp = moe::splitk_plan(a);
+      MOE_HIP(moe::launch_bf16_splitk(a, true, sp, dpart, s));
+      MOE_HIP(moe::launch_splitk_reduce(dpart, sp.n, T, d, y, nullptr, nullptr, s));
+    } else {
+      a.c = y;
+      a.ldc = d;
+      a.max_mtiles = (T + moe::gemm_mtile(moe::GEMM_WIDE) - 1) / moe::gemm_mtile(moe::GEMM_WIDE);
+      MOE_HIP(moe::launch_bf16_gemm_wide(a, moe::EPI_F32, s));
+    }
+  } else if (latent || S > 0) {
     moe::GemmArgs a = {};
     const int s0 = latent ? 1 : 0;
     a.nseg = s0 + S;
@@ -416,8 +546,12 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
       return hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s);
     };
     const size_t Ts = (size_t)T, Ps = (size_t)P;
-    MOE_HIP(cp(tr->xq_codes, xq, Ts * d));
-    MOE_HIP(cp(tr->xq_scales, xqs, Ts * d / 32));
+    if (hp) {
+      MOE_HIP(cp(tr->xb, xb, Ts * d * 2));
+    } else {
+      MOE_HIP(cp(tr->xq_codes, xq, Ts * d));
+      MOE_HIP(cp(tr->xq_scales, xqs, Ts * d / 32));
+    }
     MOE_HIP(cp(tr->z, zr, Ts * L * 4));
     MOE_HIP(cp(tr->zq_codes, zqa, Ts * L));
     MOE_HIP(cp(tr->zq_scales, zqsa, Ts * L / 32));
@@ -433,10 +567,16 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     MOE_HIP(cp(tr->y_e, ye, Ps * L * 4));
     if (latent) {  // (without a latent, y_lat was copied before the shared experts were added)
       MOE_HIP(cp(tr->y_lat, ylat, Ts * L * 4));
-      MOE_HIP(cp(tr->yq_codes, yq, Ts * L));
-      MOE_HIP(cp(tr->yq_scales, yqs, Ts * L / 32));
+      if (hp) {
+        MOE_HIP(cp(tr->yb, yb, Ts * L * 2));
+      } else {
+        MOE_HIP(cp(tr->yq_codes, yq, Ts * L));
+        MOE_HIP(cp(tr->yq_scales, yqs, Ts * L / 32));
+      }
     }
-    if (S > 0) {
+    if (S > 0 && hp) {
+      MOE_HIP(cp(tr->hs_bf16, hb, (size_t)S * Ts * Fs * 2));
+    } else if (S > 0) {
       MOE_HIP(cp(tr->hs_codes, hs, (size_t)S * Ts * Fs));
       MOE_HIP(cp(tr->hs_scales, hss, (size_t)S * Ts * Fs / 32));
     }
@@ -479,6 +619,14 @@ int moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t G, 
   if (moe::launch_pack_e2m1(codes, scales, G, N, K, out_codes, out_scales, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_round_bf16(const float* in, int64_t n, uint16_t* out, void* stream) {
+  if (n < 0 || n % 4) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!in || !out || !aligned(in, 16) || !aligned(out, 8)) return MOE_ERR_INVALID_ARG;
+  if (moe::launch_round_bf16(in, n, out, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
 

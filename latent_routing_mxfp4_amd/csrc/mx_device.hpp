@@ -29,6 +29,17 @@ __device__ __forceinline__ int mx_scale_code(uint32_t amax_bits) {
   return c > 0 ? c : 0;
 }
 
+// fp32 -> bfloat16 bit pattern, round to nearest with ties to even: the upper
+// 16 bits of the word, plus one unit of magnitude when the 16 dropped bits
+// exceed half a unit, or equal it and the kept pattern is odd (adding 0x7FFF
+// plus the kept low bit carries exactly then).  Past the largest finite value
+// the carry reaches the infinity pattern, as IEEE rounding does.  Finite
+// inputs (a NaN is not preserved).
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Element code of fp32 v under block exponent e = scale_code - 127.
 // MB mantissa bits, EMIN smallest normal exponent, MAXC largest finite
 // magnitude code, SBIT sign position.  Round to nearest, ties to even code.

@@ -128,39 +128,42 @@ __device__ __forceinline__ void e2m1_block_bf16(const uint4& codes, int sc, uint
   }
 }
 
-// Few-row dense bf16 GEMM straight from MXFP4 weights (the latent
-// down-projection at decode): A = exact bf16 image of the MXFP8 activations
-// [M][K] (seg.a), B = row-major MXFP4 [N][K] (seg.b codes, seg.bs scales [N][K/32]),
-// decoded to its exact bf16 image in registers, so the weights are read once
-// at 17/32 bytes per element and no bf16 copy is written.  Why bf16: every
-// product of an E4M3 and an E2M1 value (power-of-two scales) is exact in
+// Few-row dense bf16 GEMMs with K split into slices (decode sizes): the latent
+// down-projection straight from MXFP4 weights, and the bfloat16 projections
+// and shared experts of the higher-precision map.  A = bf16 [M][K] (seg.a);
+// B row-major [N][K], either MXFP4 (seg.b codes [N][K/2], seg.bs scales
+// [N][K/32]) decoded to its exact bf16 image in registers, so the weights are
+// read once at 17/32 bytes per element and no bf16 copy is written, or bf16
+// read as is.  Why bf16 matrix cores for the MXFP8 x MXFP4 down-projection:
+// every product of an E4M3 and an E2M1 value (power-of-two scales) is exact in
 // bf16 x bf16 -> fp32 and v_mfma_f32_16x16x32_bf16 accumulates at fp32
 // precision, unlike the block-scaled MFMA, which sums each 32-element block in
 // a window of about 14 bits below its largest product; the router's top-k is
-// decided on this latent.  A lane loads 64 contiguous bytes (32 K values) of
-// its activation row and one MX block (16 code bytes) of its weight row per
-// 128-wide K-step and issues four MFMAs, slice u taking K [32g + 8u, +8) of
-// both operands, so the pairing of K indices is consistent.  The K range is
-// split over gridDim.y slices of kper K-steps, each writing its fp32 partial
-// sums to part[slice][M][N]; splitk_reduce_kernel adds them in slice order.
-// Weight blocks and scales are read D K-steps ahead in a register ring.
-template <int MW, int NW>
-__global__ void __launch_bounds__(256) bf16_mx_splitk_kernel(const GemmArgs p, float* __restrict__ part, int kper) {
+// decided on this latent.  Per 128-wide K-step a lane loads 64 contiguous
+// bytes (32 K values) of its activation row and of its weight row (or one MX
+// block, 16 code bytes) and issues four MFMAs, slice u taking K [32g + 8u, +8)
+// of both operands, so the pairing of K indices is consistent.  Slice
+// blockIdx.y covers K-steps [ks0, ks0 + nks) of one segment and writes its
+// fp32 partial sums to part[slice][g][M][N]; the reduce kernels add the
+// slices in slice order.  Weights and activations are read D K-steps ahead in
+// a register ring.
+template <int MW, int NW, bool BF16B>
+__global__ void __launch_bounds__(256) bf16_splitk_kernel(const GemmArgs p, const SplitPlan sp,
+                                                          float* __restrict__ part) {
   constexpr int MT = 16 * MW;
   constexpr int NT = 4 * 16 * NW;
-  constexpr int D = MW == 1 ? 4 : 2;
+  constexpr int D = BF16B ? 2 : (MW == 1 ? 4 : 2);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   Tile t;
   if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;
-  const GemmSeg& sg = p.seg[0];
+  const int slice = blockIdx.y;
+  const GemmSeg& sg = p.seg[sp.seg[slice]];
   const int K = sg.K;
-  const int ks0 = blockIdx.y * kper;
-  int nks = (K >> 7) - ks0;
-  nks = nks < kper ? nks : kper;
-  if (nks <= 0) return;
+  const int ks0 = sp.ks0[slice];
+  const int nks = sp.nks[slice];
   const uint16_t* ap[MW];
 #pragma unroll
   for (int mi = 0; mi < MW; ++mi) {
@@ -168,14 +171,23 @@ __global__ void __launch_bounds__(256) bf16_mx_splitk_kernel(const GemmArgs p, f
     r = r < t.rows ? r : t.rows - 1;
     ap[mi] = reinterpret_cast<const uint16_t*>(sg.a) + (int64_t)r * K + 128 * ks0 + 32 * g4;
   }
+  const int half = p.N >> 1;  // SwiGLU pair: columns [half, N) read b2
   const uint8_t* bp[NW];
   const uint8_t* bsp[NW];
 #pragma unroll
   for (int ni = 0; ni < NW; ++ni) {
     int c = t.n0 + 16 * ni + r16;
     c = c < p.N ? c : p.N - 1;
-    bp[ni] = sg.b + (int64_t)c * (K >> 1) + 64 * ks0 + 16 * g4;
-    bsp[ni] = sg.bs + (int64_t)c * (K >> 5) + 4 * ks0 + g4;
+    const bool up = sg.b2 != nullptr && c >= half;
+    const int cc = up ? c - half : c;
+    const uint8_t* base = (up ? sg.b2 : sg.b) + (int64_t)t.g * sg.b_gstride;
+    if (BF16B) {
+      bp[ni] = base + ((int64_t)cc * K + 128 * ks0 + 32 * g4) * 2;
+      bsp[ni] = nullptr;
+    } else {
+      bp[ni] = base + (int64_t)cc * (K >> 1) + 64 * ks0 + 16 * g4;
+      bsp[ni] = (up ? sg.b2s : sg.bs) + (int64_t)t.g * sg.bs_gstride + (int64_t)cc * (K >> 5) + 4 * ks0 + g4;
+    }
   }
   v4f acc[MW][NW][1];
 #pragma unroll
@@ -183,17 +195,24 @@ __global__ void __launch_bounds__(256) bf16_mx_splitk_kernel(const GemmArgs p, f
 #pragma unroll
     for (int ni = 0; ni < NW; ++ni) acc[mi][ni][0] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  constexpr int BQ = BF16B ? 4 : 1;  // 16-byte weight loads per fragment and K-step
   struct Slot {
     uint4 a[MW][4];
-    uint4 b[NW];
+    uint4 b[NW][BQ];
     int bs[NW];
   };
   Slot sl[D];
   auto load = [&](int ks, Slot& q) {
 #pragma unroll
     for (int ni = 0; ni < NW; ++ni) {
-      q.b[ni] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni] + 64 * ks)));
-      q.bs[ni] = bsp[ni][4 * ks];
+      if (BF16B) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          q.b[ni][u] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni] + 256 * ks) + u));
+      } else {
+        q.b[ni][0] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni] + 64 * ks)));
+        q.bs[ni] = bsp[ni][4 * ks];
+      }
     }
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi)
@@ -203,7 +222,14 @@ __global__ void __launch_bounds__(256) bf16_mx_splitk_kernel(const GemmArgs p, f
   auto compute = [&](const Slot& q) {
     uint4 bf[NW][4];
 #pragma unroll
-    for (int ni = 0; ni < NW; ++ni) e2m1_block_bf16(q.b[ni], q.bs[ni], bf[ni]);
+    for (int ni = 0; ni < NW; ++ni) {
+      if (BF16B) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bf[ni][u] = q.b[ni][u];
+      } else {
+        e2m1_block_bf16(q.b[ni][0], q.bs[ni], bf[ni]);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -235,9 +261,11 @@ __global__ void __launch_bounds__(256) bf16_mx_splitk_kernel(const GemmArgs p, f
   for (int j = 0; j < D; ++j)
     if (ks + j < nks) compute(sl[j]);
 
-  GemmArgs q = p;  // the slice's partial sums, fp32 [M][N]
-  q.c = part + (int64_t)blockIdx.y * p.M * p.N;
+  GemmArgs q = p;  // the slice's partial sums, fp32 [G][M][N]
+  q.c = part + (int64_t)slice * p.G * p.M * p.N;
   q.ldc = p.N;
+  q.c_gstride = (int64_t)p.M * p.N;
+  q.c_accumulate = 0;
   q.q = nullptr;
   epilogue<MW, NW, 1, EPI_F32>(q, t, acc, r16, g4);
 }
@@ -272,6 +300,30 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     q[o + 16] = (uint8_t)(w >> 8);
     if (r == 0) qs[row * nb + b] = (uint8_t)sc;
   }
+}
+
+// h = SiLU(gate) * up from the slice partials [S][G][M][2F] (slice order),
+// as bf16 [G][M][F] and optionally fp32; one thread per output element.
+__global__ void __launch_bounds__(256) splitk_swiglu_kernel(const float* __restrict__ part, int S, int G, int M,
+                                                            int F, float* __restrict__ h32,
+                                                            uint16_t* __restrict__ hb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)M * F;
+  if (i >= (int64_t)G * per) return;
+  const int64_t g = i / per;
+  const int64_t rem = i - g * per;
+  const int64_t row = rem / F;
+  const int64_t col = rem - row * F;
+  const int64_t o = (g * M + row) * (2 * (int64_t)F) + col;
+  const int64_t stride = (int64_t)G * M * 2 * F;
+  float gv = 0.f, uv = 0.f;
+  for (int sl = 0; sl < S; ++sl) {
+    gv += part[sl * stride + o];
+    uv += part[sl * stride + o + F];
+  }
+  const float h = swiglu(gv, uv);
+  hb[i] = (uint16_t)bf16_rne(h);
+  if (h32) h32[i] = h;
 }
 
 // Weight-streaming variant for few rows per group (decode).  The weights are
@@ -438,44 +490,107 @@ static bool epilogue_dims_ok(const GemmArgs& a) {
 
 hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
   if (!epilogue_dims_ok(a) || shape != GEMM_WIDE) return hipErrorInvalidValue;
-  return launch_bf16_gemm_wide(a, s);
+  return launch_bf16_gemm_wide(a, EPI_F32_QUANT, s);
+}
+
+SplitPlan splitk_plan(const GemmArgs& a) {
+  // About 1024 waves in all, at most 8 slices' worth of K cuts (the partial
+  // sums stay small next to the weights); segments are cut separately.
+  const int MT = a.M <= 16 ? 16 : 64;
+  const int tiles = a.G * ((a.N + 127) / 128) * ((a.M + MT - 1) / MT);
+  int target = (1024 + 4 * tiles - 1) / (4 * tiles);
+  target = target < 1 ? 1 : (target > 8 ? 8 : target);
+  int total = 0;
+  for (int i = 0; i < a.nseg; ++i) total += a.seg[i].K / 128;
+  const int kper = (total + target - 1) / target;
+  SplitPlan sp = {};
+  for (int i = 0; i < a.nseg; ++i) {
+    const int ks = a.seg[i].K / 128;
+    for (int k0 = 0; k0 < ks && sp.n < kMaxSlices; k0 += kper) {
+      sp.seg[sp.n] = (int8_t)i;
+      sp.ks0[sp.n] = (int16_t)k0;
+      sp.nks[sp.n] = (int16_t)(ks - k0 < kper ? ks - k0 : kper);
+      ++sp.n;
+    }
+  }
+  return sp;
+}
+
+hipError_t launch_bf16_splitk(const GemmArgs& a, bool bf16_b, const SplitPlan& sp, float* part, hipStream_t s) {
+  if (a.offsets != nullptr || a.nseg < 1 || a.nseg > 9 || a.G < 1 || a.M <= 0 || a.N % 32 != 0 || sp.n <= 0 ||
+      sp.n > kMaxSlices || !part)
+    return hipErrorInvalidValue;
+  for (int i = 0; i < a.nseg; ++i) {
+    const GemmSeg& g = a.seg[i];
+    if (g.K <= 0 || g.K % 128 != 0 || g.K / 128 > 32767 || !g.a || !g.b || (!bf16_b && !g.bs))
+      return hipErrorInvalidValue;
+    if (g.b2 && (a.N % 2 != 0 || (!bf16_b && !g.b2s))) return hipErrorInvalidValue;
+  }
+  int covered = 0;
+  for (int j = 0; j < sp.n; ++j) {  // every slice inside its segment, every K-step once
+    if (sp.seg[j] < 0 || sp.seg[j] >= a.nseg || sp.ks0[j] < 0 || sp.nks[j] <= 0 ||
+        sp.ks0[j] + sp.nks[j] > a.seg[sp.seg[j]].K / 128)
+      return hipErrorInvalidValue;
+    covered += sp.nks[j];
+  }
+  int total = 0;
+  for (int i = 0; i < a.nseg; ++i) total += a.seg[i].K / 128;
+  if (covered != total) return hipErrorInvalidValue;
+  GemmArgs q = a;
+  q.c = part;
+  q.ldc = a.N;
+  if (!epilogue_dims_ok(q)) return hipErrorInvalidValue;
+  const bool small = a.M <= 16;
+  const int MT = small ? 16 : 64;
+  const int64_t grid = (int64_t)a.G * ((a.M + MT - 1) / MT) * ((a.N + 127) / 128);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 gd((unsigned)grid, (unsigned)sp.n);
+  if (bf16_b) {
+    if (small) bf16_splitk_kernel<1, 2, true><<<gd, dim3(256), 0, s>>>(a, sp, part);
+    else bf16_splitk_kernel<4, 2, true><<<gd, dim3(256), 0, s>>>(a, sp, part);
+  } else {
+    if (small) bf16_splitk_kernel<1, 2, false><<<gd, dim3(256), 0, s>>>(a, sp, part);
+    else bf16_splitk_kernel<4, 2, false><<<gd, dim3(256), 0, s>>>(a, sp, part);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, float* c, uint8_t* q, uint8_t* qs,
+                                hipStream_t s) {
+  if (S <= 0 || M <= 0 || N % 32 != 0 || !c) return hipErrorInvalidValue;
+  const int64_t threads = (int64_t)M * (N / 32) * 16;
+  const int64_t blocks = (threads + 255) / 256;
+  if (q) splitk_reduce_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(part, S, M, N, c, q, qs);
+  else splitk_reduce_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(part, S, M, N, c, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_swiglu(const float* part, int S, int G, int M, int F, float* h32, uint16_t* hb,
+                                hipStream_t s) {
+  if (S <= 0 || G <= 0 || M <= 0 || F <= 0 || !hb) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)G * M * F;
+  splitk_swiglu_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(part, S, G, M, F, h32, hb);
+  return hipGetLastError();
 }
 
 int bf16_mx_splitk_slices(int M, int N, int K) {
-  const int n_ntiles = (N + 127) / 128, mtiles = (M + 63) / 64;
-  const int tiles = n_ntiles * mtiles;
-  int S = (1024 + 4 * tiles - 1) / (4 * tiles);  // about 1024 waves
-  const int ksteps = K / 128;
-  S = S < 8 ? S : 8;                            // partials stay small next to the weights
-  S = S < ksteps ? S : ksteps;
-  return S > 0 ? S : 1;
+  GemmArgs a = {};
+  a.nseg = 1;
+  a.seg[0].K = K;
+  a.G = 1;
+  a.M = M;
+  a.N = N;
+  return splitk_plan(a).n;
 }
 
 hipError_t launch_bf16_mx_splitk(const GemmArgs& a, float* part, int S, float* z, uint8_t* zq, uint8_t* zqs,
                                  hipStream_t s) {
-  if (a.nseg != 1 || a.offsets != nullptr || a.G != 1 || a.seg[0].K % 128 != 0 || a.N % 32 != 0 || a.M <= 0 ||
-      S <= 0)
-    return hipErrorInvalidValue;
-  if (!epilogue_dims_ok(a)) return hipErrorInvalidValue;
-  const int ksteps = a.seg[0].K / 128;
-  const int kper = (ksteps + S - 1) / S;
-  const int Sx = (ksteps + kper - 1) / kper;  // slices actually used
-  const bool small = a.M <= 16;
-  const int MT = small ? 16 : 64;
-  const int n_ntiles = (a.N + 127) / 128;
-  const int64_t grid = (int64_t)((a.M + MT - 1) / MT) * n_ntiles;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (small)
-    bf16_mx_splitk_kernel<1, 2><<<dim3((unsigned)grid, (unsigned)Sx), dim3(256), 0, s>>>(a, part, kper);
-  else
-    bf16_mx_splitk_kernel<4, 2><<<dim3((unsigned)grid, (unsigned)Sx), dim3(256), 0, s>>>(a, part, kper);
-  hipError_t e = hipGetLastError();
+  if (a.nseg != 1 || a.G != 1) return hipErrorInvalidValue;
+  const SplitPlan sp = splitk_plan(a);
+  if (sp.n != S) return hipErrorInvalidValue;  // the partial buffer was sized for S slices
+  hipError_t e = launch_bf16_splitk(a, false, sp, part, s);
   if (e != hipSuccess) return e;
-  const int64_t threads = (int64_t)a.M * (a.N / 32) * 16;
-  const int64_t blocks = (threads + 255) / 256;
-  if (zq) splitk_reduce_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(part, Sx, a.M, a.N, z, zq, zqs);
-  else splitk_reduce_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(part, Sx, a.M, a.N, z, nullptr, nullptr);
-  return hipGetLastError();
+  return launch_splitk_reduce(part, sp.n, a.M, a.N, z, zq, zqs, s);
 }
 
 hipError_t launch_mx_gemm(const GemmArgs& a, int epi, int shape, hipStream_t s) {

@@ -259,15 +259,19 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
   epilogue<4, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
-// bf16 twin for the dense latent down-projection (A = exact bf16 image of
-// the MXFP8 activations [M][K], B = exact bf16 image of W_down [N][K]; the
-// reason it runs on bf16 matrix cores is in mx_gemm.hip).  Same 512-thread,
-// one-workgroup-per-CU structure: a 128 x 256 tile, waves 2 x 4 of 64 x 64,
-// K-steps of 64 elements (128 bytes per row of either operand) staged by
-// direct loads in a ring of three 48 KB buffers; each K-step is two
-// 16x16x32 bf16 MFMAs per fragment pair, slice u taking 16-byte chunk 4u + g
-// of a row for lane group g, identically in A and B.  Rows are XOR-swizzled
-// by chunk.  Bytes per flop are twice the 128 x 128 bf16 kernel's.
+// Dense bf16 GEMM: the latent down-projection on exact bf16 images of the MX
+// operands (the reason it runs on bf16 matrix cores is in mx_gemm.hip), and
+// the bfloat16 latent projections and shared experts of the higher-precision
+// map.  Same 512-thread, one-workgroup-per-CU structure as the MX kernel: a
+// 128 x 256 tile, waves 2 x 4 of 64 x 64, K-steps of 64 elements (128 bytes
+// per row of either operand) staged by direct loads in a ring of three 48 KB
+// buffers; each K-step is two 16x16x32 bf16 MFMAs per fragment pair, slice u
+// taking 16-byte chunk 4u + g of a row for lane group g, identically in A and
+// B.  Rows are XOR-swizzled by chunk.  K segments (e.g. the up-projection and
+// the shared down-projections) run one after the other into the same
+// accumulators.  SwiGLU: B tile row r holds column (r / 64) * 32 + r % 32 of
+// the gate (r / 32 even) or up (odd) matrix, so a wave's fragments 0-1 and 2-3
+// are the gate and up values of the same 32 columns.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int WB_M = 128, WB_N = 256;
 constexpr int WB_OFF_B = WB_M * 128;
@@ -287,75 +291,82 @@ __device__ __forceinline__ bf16x8_t as_bf16x8_w(const uint4& f) {
 template <int EPI>
 __global__ void __launch_bounds__(512) bf16_gemm_wide_kernel(const GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  static_assert(EPI != EPI_SWIGLU_QUANT, "dense projection only");
-  constexpr int NW = 4;
+  static_assert(EPI != EPI_SWIGLU_QUANT, "bf16 kernels write the SwiGLU hidden state as bf16");
+  constexpr bool SWI = EPI == EPI_SWIGLU_BF16;
+  constexpr int NCOL = SWI ? WB_N / 2 : WB_N;  // output columns per tile
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wm = wave >> 2, wn = wave & 3;
   int g, mt, nt, rows, row_base;
-  if (!decode_lds_tile<WB_M>(p, WB_N, g, mt, nt, rows, row_base)) return;
+  if (!decode_lds_tile<WB_M>(p, NCOL, g, mt, nt, rows, row_base)) return;
   const int m0 = mt * WB_M;
-  const int col0 = nt * WB_N;
-  const GemmSeg& sg = p.seg[0];
-  const int K = sg.K;
-  const int ksteps = K >> 6;
-  // A load i (0..1) of wave w: tile row 8*(2w+i) + lane/8; B load i (0..3):
-  // tile B row 8*(4w+i) + lane/8; physical chunk lane%8 (logical XOR row%8).
-  const uint8_t* ga[2];
-  const uint8_t* gb[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * (2 * wave + i) + (lane >> 3);
-    int ar = m0 + r;
-    ar = ar < rows ? ar : rows - 1;
-    ga[i] = sg.a + ((int64_t)ar * K) * 2 + 16 * ((lane & 7) ^ (r & 7));
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * (4 * wave + i) + (lane >> 3);
-    int bc = col0 + r;
-    bc = bc < p.N ? bc : p.N - 1;
-    gb[i] = sg.b + (int64_t)g * sg.b_gstride + ((int64_t)bc * K) * 2 + 16 * ((lane & 7) ^ (r & 7));
-  }
-  auto issue = [&](int ks) {
-    uint8_t* buf = lds + (ks % WB_NBUF) * WB_STAGE;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (2 * wave + i));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 128 * ks, buf + WB_OFF_B + 1024 * (4 * wave + i));
-  };
-  v4f acc[4][NW][1];
+  const int col0 = nt * NCOL;
+  v4f acc[4][4][1];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NW; ++ni) acc[mi][ni][0] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni][0] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  if (ksteps > 1) issue(1);
-  for (int ks = 0; ks < ksteps; ++ks) {
-    if (ks + 1 < ksteps) wait_vmcnt<WB_LOADS>(); else wait_vmcnt<0>();
-    barrier_lds();
-    if (ks + 2 < ksteps) issue(ks + 2);
-    const uint8_t* buf = lds + (ks % WB_NBUF) * WB_STAGE;
+  for (int si = 0; si < p.nseg; ++si) {
+    const GemmSeg& sg = p.seg[si];
+    const int K = sg.K;
+    const int ksteps = K >> 6;
+    // A load i (0..1) of wave w: tile row 8*(2w+i) + lane/8; B load i (0..3):
+    // tile B row 8*(4w+i) + lane/8; physical chunk lane%8 (logical XOR row%8).
+    const uint8_t* ga[2];
+    const uint8_t* gb[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x8_t bfr[NW];
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * (2 * wave + i) + (lane >> 3);
+      int ar = m0 + r;
+      ar = ar < rows ? ar : rows - 1;
+      ga[i] = sg.a + ((int64_t)ar * K) * 2 + 16 * ((lane & 7) ^ (r & 7));
+    }
 #pragma unroll
-      for (int ni = 0; ni < NW; ++ni) {
-        const int trow = wn * 64 + 16 * ni + r16;
-        bfr[ni] = as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + WB_OFF_B + trow * 128 +
-                                                             (((4 * u + g4) ^ (trow & 7)) << 4)));
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * (4 * wave + i) + (lane >> 3);
+      int bc = SWI ? col0 + (r >> 6) * 32 + (r & 31) : col0 + r;
+      bc = bc < p.N ? bc : p.N - 1;
+      const uint8_t* base = SWI && ((r >> 5) & 1) ? sg.b2 : sg.b;
+      gb[i] = base + (int64_t)g * sg.b_gstride + ((int64_t)bc * K) * 2 + 16 * ((lane & 7) ^ (r & 7));
+    }
+    auto issue = [&](int ks) {
+      uint8_t* buf = lds + (ks % WB_NBUF) * WB_STAGE;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int r = wm * 64 + 16 * mi + r16;
-        const bf16x8_t av =
-            as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + r * 128 + (((4 * u + g4) ^ (r & 7)) << 4)));
+      for (int i = 0; i < 2; ++i) gl_lds16(ga[i] + 128 * ks, buf + 1024 * (2 * wave + i));
 #pragma unroll
-        for (int ni = 0; ni < NW; ++ni)
-          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bfr[ni], acc[mi][ni][0], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 128 * ks, buf + WB_OFF_B + 1024 * (4 * wave + i));
+    };
+    // A new segment refills buffers the previous one's last K-steps were read
+    // from: every wave must be past those reads first.
+    if (si > 0) barrier_lds();
+    issue(0);
+    if (ksteps > 1) issue(1);
+    for (int ks = 0; ks < ksteps; ++ks) {
+      if (ks + 1 < ksteps) wait_vmcnt<WB_LOADS>(); else wait_vmcnt<0>();
+      barrier_lds();
+      if (ks + 2 < ksteps) issue(ks + 2);
+      const uint8_t* buf = lds + (ks % WB_NBUF) * WB_STAGE;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t bfr[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int trow = wn * 64 + 16 * ni + r16;
+          bfr[ni] = as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + WB_OFF_B + trow * 128 +
+                                                               (((4 * u + g4) ^ (trow & 7)) << 4)));
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const int r = wm * 64 + 16 * mi + r16;
+          const bf16x8_t av =
+              as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + r * 128 + (((4 * u + g4) ^ (r & 7)) << 4)));
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bfr[ni], acc[mi][ni][0], 0, 0, 0);
+        }
       }
     }
   }
@@ -364,8 +375,21 @@ __global__ void __launch_bounds__(512) bf16_gemm_wide_kernel(const GemmArgs p) {
   t.m0 = m0 + wm * 64;
   t.rows = rows;
   t.row_base = row_base;
-  t.n0 = col0 + wn * 64;
-  epilogue<4, NW, 1, EPI>(p, t, acc, r16, g4);
+  if (SWI) {
+    v4f pr[4][2][2];  // [mi][fragment][gate, up]
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        pr[mi][ni][0] = acc[mi][ni][0];
+        pr[mi][ni][1] = acc[mi][2 + ni][0];
+      }
+    t.n0 = col0 + wn * 32;
+    epilogue<4, 2, 2, EPI>(p, t, pr, r16, g4);
+  } else {
+    t.n0 = col0 + wn * 64;
+    epilogue<4, 4, 1, EPI>(p, t, acc, r16, g4);
+  }
 }
 
 template <int EPI>
@@ -391,8 +415,14 @@ hipError_t launch_wide_cfg(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 hipError_t launch_bf16_wide_cfg(const GemmArgs& a, hipStream_t s) {
-  if (a.nseg != 1 || a.seg[0].K % 64 != 0 || a.offsets != nullptr) return hipErrorInvalidValue;
-  const int n_nt = (a.N + WB_N - 1) / WB_N;
+  if (a.nseg < 1 || a.nseg > 9 || a.offsets != nullptr) return hipErrorInvalidValue;
+  for (int i = 0; i < a.nseg; ++i) {
+    if (a.seg[i].K <= 0 || a.seg[i].K % 64 != 0 || !a.seg[i].a || !a.seg[i].b) return hipErrorInvalidValue;
+    if (EPI == EPI_SWIGLU_BF16 && !a.seg[i].b2) return hipErrorInvalidValue;
+  }
+  if (EPI == EPI_SWIGLU_BF16 && (a.N % 32 != 0 || !a.ob)) return hipErrorInvalidValue;
+  constexpr int NCOL = EPI == EPI_SWIGLU_BF16 ? WB_N / 2 : WB_N;
+  const int n_nt = (a.N + NCOL - 1) / NCOL;
   int64_t tiles = (int64_t)a.max_mtiles * n_nt;
   tiles = (tiles + 7) / 8 * 8;
   if (tiles <= 0) return hipSuccess;
@@ -413,7 +443,14 @@ hipError_t launch_bf16_wide_cfg(const GemmArgs& a, hipStream_t s) {
 
 int gemm_wide_mtile() { return WD_M; }
 
-hipError_t launch_bf16_gemm_wide(const GemmArgs& a, hipStream_t s) { return launch_bf16_wide_cfg<EPI_F32_QUANT>(a, s); }
+hipError_t launch_bf16_gemm_wide(const GemmArgs& a, int epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_F32: return launch_bf16_wide_cfg<EPI_F32>(a, s);
+    case EPI_F32_QUANT: return launch_bf16_wide_cfg<EPI_F32_QUANT>(a, s);
+    case EPI_SWIGLU_BF16: return launch_bf16_wide_cfg<EPI_SWIGLU_BF16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_mx_gemm_wide(const GemmArgs& a, int epi, hipStream_t s) {
   switch (epi) {

@@ -115,6 +115,27 @@ __global__ void __launch_bounds__(256) decode_e2m1_bf16_kernel(const uint4* __re
   }
 }
 
+// fp32 -> bfloat16 (round to nearest even), 4 values per thread.
+__global__ void __launch_bounds__(256) round_bf16_kernel(const float4* __restrict__ in, int64_t n4,
+                                                         uint2* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 v = in[i];
+    out[i] = make_uint2(bf16_rne(v.x) | (bf16_rne(v.y) << 16), bf16_rne(v.z) | (bf16_rne(v.w) << 16));
+  }
+}
+
+hipError_t launch_round_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s) {
+  if (n % 4 != 0 || ((uintptr_t)in & 15) || ((uintptr_t)out & 7)) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  round_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(reinterpret_cast<const float4*>(in), n4,
+                                                                  reinterpret_cast<uint2*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K, uint16_t* out,
                                    hipStream_t s) {
   const int64_t nblk = rows * (int64_t)K / 32;

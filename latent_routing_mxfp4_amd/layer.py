@@ -42,11 +42,13 @@ class LayerShape:
     d_ff_shared: int
     latent: bool = True          # False: no latent projections (d_latent == d_model)
     softmax_gates: bool = False  # gates = softmax over the winners' logits
+    dense_bf16: bool = False     # latent projections and shared experts in bfloat16
 
     @classmethod
     def of(cls, cfg) -> "LayerShape":
         return cls(cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k, cfg.n_shared, cfg.d_ff_routed,
-                   cfg.d_ff_shared, bool(getattr(cfg, "latent", True)), getattr(cfg, "gating", "sigmoid") == "softmax")
+                   cfg.d_ff_shared, bool(getattr(cfg, "latent", True)), getattr(cfg, "gating", "sigmoid") == "softmax",
+                   getattr(cfg, "precision", "mx") == "bf16")
 
     def matrix_shape(self, name: str) -> Tuple[int, int]:
         d, L, F, Fs = self.d_model, self.d_latent, self.d_ff_routed, self.d_ff_shared
@@ -56,10 +58,14 @@ class LayerShape:
     def count(self, name: str) -> int:
         return self.n_routed if name in ROUTED else self.n_shared if name in SHARED else int(self.latent)
 
+    def is_bf16(self, name: str) -> bool:
+        """Stored as bfloat16 (the higher-precision map) rather than MXFP4."""
+        return self.dense_bf16 and name not in ROUTED
+
     def c_config(self, max_tokens: int) -> _lib.MoeLayerConfig:
         return _lib.MoeLayerConfig(self.d_model, self.d_latent, self.n_routed, self.top_k, self.n_shared,
                                    self.d_ff_routed, self.d_ff_shared, int(max_tokens), int(not self.latent),
-                                   int(self.softmax_gates))
+                                   int(self.softmax_gates), int(self.dense_bf16))
 
 
 # --------------------------------------------------------------------------- MX helpers
@@ -118,26 +124,40 @@ def mx_gemm(a_codes, a_scales, b_codes, b_scales) -> torch.Tensor:
 def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray], device="cuda",
                    extra: Optional[Dict[str, Optional[np.ndarray]]] = None, workers: int = 8,
                    progress: Optional[Callable[[int, int], None]] = None) -> Dict:
-    """MXFP4-encode every weight matrix on the GPU.
+    """Encode every weight matrix on the GPU.
 
     ``host_fp32(name, index)`` returns the fp32 ``[out][in]`` matrix (numpy);
     matrices are produced by a thread pool, copied to the device one at a
     time and encoded there: ``w_down`` row-major (``moe_mx_quantize``, it feeds
     the bf16 latent projection), every other matrix in fragment order
-    (``moe_mx_quantize_weights``, read by the MX GEMMs).
+    (``moe_mx_quantize_weights``, read by the MX GEMMs).  Under the
+    higher-precision map the latent projections and shared experts are
+    rounded to bfloat16 instead (``moe_round_bf16``), stored row-major under
+    ``<name>_bf16`` (their MX entries are None).
     ``extra`` carries the fp32 router (``w_router``) and the optional biases.
     """
     out: Dict = {}
     jobs = []
     for name in DENSE + ROUTED + SHARED:
         n = shape.count(name)
+        stacked = name in ROUTED + SHARED
+        if shape.is_bf16(name):
+            out[name] = None
+            if n == 0:
+                out[name + "_bf16"] = None
+                continue
+            r, c = shape.matrix_shape(name)
+            wb = torch.empty(n, r, c, dtype=torch.int16, device=device)
+            out[name + "_bf16"] = wb if stacked else wb[0]
+            jobs += [(name, i, wb[i], None) for i in range(n)]
+            continue
         if n == 0:
             out[name] = None
             continue
         r, c = shape.matrix_shape(name)
         codes = torch.empty(n, r, c // 2, dtype=torch.uint8, device=device)
         scales = torch.empty(n, r, c // 32, dtype=torch.uint8, device=device)
-        out[name] = (codes if name in ROUTED + SHARED else codes[0], scales if name in ROUTED + SHARED else scales[0])
+        out[name] = (codes if stacked else codes[0], scales if stacked else scales[0])
         jobs += [(name, i, codes[i], scales[i]) for i in range(n)]
     with ThreadPoolExecutor(max_workers=workers) as ex:
         futs = [ex.submit(host_fp32, name, i) for (name, i, _, _) in jobs[:2 * workers]]
@@ -149,7 +169,9 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
                 futs.append(ex.submit(host_fp32, jobs[nxt][0], jobs[nxt][1]))
                 nxt += 1
             dev = torch.from_numpy(np.ascontiguousarray(host, dtype=np.float32)).to(device, non_blocking=False)
-            if name == "w_down":
+            if scales is None:
+                _lib.moe_round_bf16(dev.data_ptr(), dev.numel(), codes.data_ptr(), _stream())
+            elif name == "w_down":
                 mx_quantize(dev, FMT_E2M1, out=(codes, scales))
             else:
                 mx_quantize_weights(dev, out=(codes, scales))
@@ -189,7 +211,7 @@ class LatentMoE:
         self._w = _lib.MoeLayerWeights(
             mx("w_down"), mx("w_up"), _ptr(weights["w_router"]), _ptr(weights.get("router_logit_bias")),
             _ptr(weights.get("selection_bias")), mx("w_gate_e"), mx("w_up_e"), mx("w_down_e"), mx("w_gate_s"),
-            mx("w_up_s"), mx("w_down_s"))
+            mx("w_up_s"), mx("w_down_s"), *[_ptr(weights.get(n + "_bf16")) for n in DENSE + SHARED])
         self.handle = _lib.moe_layer_create(self._cfg, self._w)
         self._ws: Optional[torch.Tensor] = None
 
@@ -217,10 +239,17 @@ class LatentMoE:
         }
         if not s.latent:  # no MXFP8 of the combined output: it is y's routed part
             del shapes["yq_codes"], shapes["yq_scales"]
+        if s.dense_bf16:  # bf16 inputs of the higher-precision GEMMs instead of MXFP8 ones
+            del shapes["xq_codes"], shapes["xq_scales"], shapes["yq_codes"], shapes["yq_scales"]
+            shapes["xb"] = ((T, d), torch.int16)
+            shapes["yb"] = ((T, L), torch.int16)
         if S > 0:
             shapes["hs"] = ((S, T, Fs), f32)
-            shapes["hs_codes"] = ((S, T, Fs), u8)
-            shapes["hs_scales"] = ((S, T, Fs // 32), u8)
+            if s.dense_bf16:
+                shapes["hs_bf16"] = ((S, T, Fs), torch.int16)
+            else:
+                shapes["hs_codes"] = ((S, T, Fs), u8)
+                shapes["hs_scales"] = ((S, T, Fs // 32), u8)
         return {n: torch.empty(sh, dtype=dt, device="cuda") for n, (sh, dt) in shapes.items()}
 
     def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, trace: Optional[Dict] = None,
@@ -232,7 +261,8 @@ class LatentMoE:
         ws = self.workspace(T)
         tr = None
         if trace is not None:
-            tr = _lib.MoeLayerTrace(*[_ptr(trace.get(n)) for n in _lib.TRACE_FIELDS])
+            tr = _lib.MoeLayerTrace(*[_ptr(trace.get(n)) for n in _lib.TRACE_FIELDS], None,
+                                    *[_ptr(trace.get(n)) for n in _lib.BF16_TRACE_FIELDS])
         _lib.moe_layer_forward(self.handle, x.data_ptr(), T, y.data_ptr(), ws.data_ptr(), ws.numel(),
                                _stream() if stream is None else stream, tr)
         return y

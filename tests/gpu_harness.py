@@ -46,7 +46,7 @@ def to_np(t):
 
 
 PER_TOKEN = ("xq_codes", "xq_scales", "z", "zq_codes", "zq_scales", "logits", "ids", "gates", "y_lat",
-             "yq_codes", "yq_scales")
+             "yq_codes", "yq_scales", "xb", "yb")
 PER_ROW = ("h", "hq_codes", "hq_scales", "y_e")
 
 
@@ -66,7 +66,7 @@ def run_traced_tokens(layer, x_np: np.ndarray, tokens):
     rows = tr["row_of_pair"].long()[pairs]
     sub = {n: to_np(tr[n][tok]) for n in PER_TOKEN if n in tr}
     sub.update({n: to_np(tr[n][rows]) for n in PER_ROW})
-    for n in ("hs", "hs_codes", "hs_scales"):
+    for n in ("hs", "hs_codes", "hs_scales", "hs_bf16"):
         if n in tr:
             sub[n] = to_np(tr[n][:, tok])
     full = {n: to_np(tr[n]) for n in ("ids", "gates", "counts", "offsets", "pair_of_row", "row_of_pair")}

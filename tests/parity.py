@@ -11,7 +11,8 @@ What is compared
    error the z bound propagates through the fp32 router).
 4. Dispatch: counts, offsets and permutation equal the stable sort of the
    GPU's ids, bit-exactly.
-5. Replay.  Every MXFP8 re-quantisation of a computed tensor (zq, hq, yq, hs)
+5. Replay.  Every MXFP8 re-quantisation of a computed tensor (zq, hq, yq, hs;
+   under the higher-precision map the bfloat16 roundings of y_lat and hs)
    turns any accumulation difference that straddles a rounding boundary into a
    whole-step code change, and such changes cascade through the later stages:
    even fp32-level noise in the oracle itself moves its own output by ~1e-3
@@ -59,8 +60,22 @@ def row_norms(t: moe.MXTensor) -> np.ndarray:
 
 def gemm_bound(a: moe.MXTensor, b: moe.MXTensor, value: np.ndarray) -> np.ndarray:
     """fp32-accumulation bound (the bf16 matrix-core path)."""
-    K = a.codes.shape[-1]
+    K = a.deq().shape[-1]
     return K * EPS32 * np.outer(row_norms(a), row_norms(b)) + EPS32 * np.abs(value)
+
+
+def concat_gemm_bound(pairs, value: np.ndarray) -> np.ndarray:
+    """fp32 bound of one bf16 GEMM whose K is the concatenation of the
+    segments ``pairs`` = [(a, b), ...]: (total K) * 2^-24 * sum |a_i b_i| over
+    every segment, plus the final rounding."""
+    K = sum(a.deq().shape[-1] for a, _ in pairs)
+    sab = sum(np.outer(row_norms(a), row_norms(b)) for a, b in pairs)
+    return K * EPS32 * sab + EPS32 * np.abs(value)
+
+
+def u16(a) -> np.ndarray:
+    """bfloat16 patterns as uint16 (the trace holds them in int16 tensors)."""
+    return np.ascontiguousarray(a).view(np.uint16)
 
 
 def block_amax(t: moe.MXTensor) -> np.ndarray:
@@ -108,6 +123,7 @@ class Replay:
 
     def __init__(self, tr, W, k, dgate, xq):
         self.tr, self.W, self.k, self.dgate, self.xq = tr, W, k, dgate, xq
+        self.hp = W.precision == "bf16"   # bfloat16 latent projections and shared experts
         self.stats = {}
         P = tr["hq_codes"].shape[0]
         L = tr["y_e"].shape[1]
@@ -144,6 +160,27 @@ class Replay:
         scales = np.where(use, gscales, ref.scales).astype(np.uint8)
         return moe.MXTensor(codes, scales, "e4m3")
 
+    def _adopt_bf16(self, name, v, bound, ref: moe.BF16Tensor, gbits) -> moe.BF16Tensor:
+        """The bfloat16 rounding of each element is fixed unless the interval
+        v +- bound reaches a rounding boundary (or zero, where the sign of a
+        zero result is open); there the GPU's value must be the rounding of
+        some value inside the interval."""
+        gbits = u16(gbits)
+        v32 = np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
+        b = np.asarray(bound, np.float64) + EPS32 * np.abs(v32) + 1e-300
+        lo = mx.bf16_value(mx.bf16_bits(v32 - b))
+        hi = mx.bf16_value(mx.bf16_bits(v32 + b))
+        amb = (lo != hi) | (np.abs(v32) <= b)
+        g = mx.bf16_value(gbits)
+        valid = (g >= lo) & (g <= hi)
+        use = amb & valid
+        differs = gbits != ref.bits
+        st = self.stats.setdefault(name, {"ambiguous_blocks": 0, "adopted_blocks": 0, "inadmissible_blocks": 0})
+        st["ambiguous_blocks"] += int(amb.sum())
+        st["adopted_blocks"] += int((use & differs).sum())
+        st["inadmissible_blocks"] += int((amb & ~valid & differs).sum())
+        return moe.BF16Tensor(np.where(use, gbits, ref.bits).astype(np.uint16))
+
     # hooks -----------------------------------------------------------------
     def zq(self, z, zq):
         bound = gemm_bound(self.xq, self.W.w_down, z)
@@ -175,9 +212,15 @@ class Replay:
 
     def yq(self, y_lat, yq, r, disp, ye_rows):
         b = self.combine_bound(r, disp, ye_rows)
+        if self.hp:
+            return self._adopt_bf16("yb", y_lat, b, yq, self.tr["yb"])
         return self._adopt("yq", y_lat, b, yq, self.tr["yq_codes"], self.tr["yq_scales"])
 
     def hs(self, s, wg, wu, wd, g, u, h, hq):
+        if self.hp:   # bf16 matrix cores: fp32 accumulation of exact products
+            bh = swiglu_bound(g, u, gemm_bound(self.xq, wg, g), gemm_bound(self.xq, wu, u), h)
+            self.hs_bound.append(bh)
+            return self._adopt_bf16(f"hs{s}", h, bh, hq, self.tr["hs_bf16"][s])
         bh = swiglu_bound(g, u, mx_mfma_bound(self.xq, wg, g), mx_mfma_bound(self.xq, wu, u), h)
         self.hs_bound.append(bh)
         return self._adopt(f"hs{s}", h, bh, hq, self.tr["hs_codes"][s], self.tr["hs_scales"][s])
@@ -192,9 +235,13 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
     T, k, E = y.shape[0], cfg.top_k, cfg.n_routed
     rep = {}
 
-    # 1. input codes: bit-exact
-    assert np.array_equal(tr["xq_codes"], o.xq.codes), "xq codes"
-    assert np.array_equal(tr["xq_scales"], o.xq.scales), "xq scales"
+    # 1. input codes (MXFP8, or bfloat16 under the higher-precision map): bit-exact
+    hp = W.precision == "bf16"
+    if hp:
+        assert np.array_equal(u16(tr["xb"]), o.xq.bits), "bf16(x)"
+    else:
+        assert np.array_equal(tr["xq_codes"], o.xq.codes), "xq codes"
+        assert np.array_equal(tr["xq_scales"], o.xq.scales), "xq scales"
 
     # 2. latent down-projection (bf16 matrix cores); without a latent the
     #    router reads x and the experts xq, unchanged
@@ -275,15 +322,23 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
             rp.combine_bound(c.routing, c.disp, c.ye_rows)
         checks = [("hq", tr["hq_codes"], tr["hq_scales"], c.hq_rows)]
         if latent:
-            checks += [("zq", tr["zq_codes"], tr["zq_scales"], c.zq), ("yq", tr["yq_codes"], tr["yq_scales"], c.yq)]
+            checks += [("zq", tr["zq_codes"], tr["zq_scales"], c.zq)]
+            if hp:
+                nbad = int((u16(tr["yb"]) != c.yq.bits).sum())
+                assert nbad == 0, f"bf16(y_lat): {nbad} mismatches against the replay"
+            else:
+                checks += [("yq", tr["yq_codes"], tr["yq_scales"], c.yq)]
         for name, gc, gs, ref in checks:
             nbad = int((gc != ref.codes).sum()) + int((gs != ref.scales).sum())
             if nbad:
                 say(f"  {name} mismatches at {np.argwhere(gc != ref.codes)[:3].tolist()}")
             assert nbad == 0, f"{name}: {nbad} code/scale mismatches against the replay"
         for s in range(len(W.w_gate_s)):
-            assert np.array_equal(tr["hs_codes"][s], c.hq_shared[s].codes), f"hs{s} codes"
-            assert np.array_equal(tr["hs_scales"][s], c.hq_shared[s].scales), f"hs{s} scales"
+            if hp:
+                assert np.array_equal(u16(tr["hs_bf16"][s]), c.hq_shared[s].bits), f"hs{s} bf16"
+            else:
+                assert np.array_equal(tr["hs_codes"][s], c.hq_shared[s].codes), f"hs{s} codes"
+                assert np.array_equal(tr["hs_scales"][s], c.hq_shared[s].scales), f"hs{s} scales"
             dh = np.abs(tr["hs"][s].astype(np.float64) - c.h_shared[s])
             assert np.all(dh <= rp.hs_bound[s]), f"hs{s} outside its bound"
         dh = np.abs(tr["h"].astype(np.float64) - c.h_rows)
@@ -292,10 +347,14 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
         assert np.all(dye <= rp.ye_bound), f"y_e outside its bound on {(dye > rp.ye_bound).sum()} elements"
         dyl = np.abs(tr["y_lat"].astype(np.float64) - c.y_lat)
         assert np.all(dyl <= rp.ylat_bound), f"y_lat outside its bound on {(dyl > rp.ylat_bound).sum()} elements"
-        by = mx_mfma_bound(c.yq, W.w_up) if latent else rp.ylat_bound
-        for s in range(len(W.w_gate_s)):
-            by = by + mx_mfma_bound(c.hq_shared[s], W.w_down_s[s])
-        by = by + (1 + len(W.w_gate_s)) * EPS32 * np.abs(c.y)
+        if hp:   # one bf16 GEMM over K = [L | Fs ...]
+            by = concat_gemm_bound([(c.yq, W.w_up)] + [(c.hq_shared[s], W.w_down_s[s])
+                                                      for s in range(len(W.w_gate_s))], c.y)
+        else:
+            by = mx_mfma_bound(c.yq, W.w_up) if latent else rp.ylat_bound
+            for s in range(len(W.w_gate_s)):
+                by = by + mx_mfma_bound(c.hq_shared[s], W.w_down_s[s])
+            by = by + (1 + len(W.w_gate_s)) * EPS32 * np.abs(c.y)
         dy = np.abs(y.astype(np.float64) - c.y)
         assert np.all(dy <= by), f"y outside its bound on {(dy > by).sum()} elements"
         rel, maxabs, rms = output_errors(y, c.y)

@@ -135,3 +135,54 @@ def test_quantize_and_gemm_argument_errors():
     assert lib.moe_mx_pack_weights(FAKE + 4, FAKE, 1, 16, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_mx_pack_weights(FAKE, FAKE, 0, 16, 128, FAKE, FAKE, None) == _lib.MOE_OK
     assert _lib.moe_status_string(-3).startswith("workspace")
+
+
+# --------------------------------------------------------------------------- higher-precision map
+
+
+def _bf16_weights(shared=True, mx_dense=False):
+    t = _lib.MoeMxTensor(FAKE, FAKE)
+    z = _lib.MoeMxTensor(None, None)
+    d = t if mx_dense else z
+    w = _lib.MoeLayerWeights(d, d, FAKE, None, None, t, t, t, d, d, d)
+    w.w_down_bf16 = w.w_up_bf16 = FAKE
+    if shared:
+        w.w_gate_s_bf16 = w.w_up_s_bf16 = w.w_down_s_bf16 = FAKE
+    return w
+
+
+def test_bf16_map_create_needs_bf16_dense_weights_only():
+    cfg = _k3()
+    cfg.dense_bf16 = 1
+    assert _create_status(cfg, _bf16_weights()) == _lib.MOE_OK   # MX dense tensors may be NULL
+    assert _create_status(cfg, _bf16_weights(shared=False)) == _lib.MOE_ERR_INVALID_ARG
+    w = _bf16_weights()
+    w.w_up_bf16 = FAKE + 2                                         # misaligned
+    assert _create_status(cfg, w) == _lib.MOE_ERR_INVALID_ARG
+    w = _bf16_weights()
+    w.w_down_bf16 = None
+    assert _create_status(cfg, w) == _lib.MOE_ERR_INVALID_ARG
+    # without the flag the bf16 pointers are ignored and the MX ones required
+    cfg.dense_bf16 = 0
+    assert _create_status(cfg, _bf16_weights()) == _lib.MOE_ERR_INVALID_ARG
+    assert _create_status(cfg, _bf16_weights(mx_dense=True)) == _lib.MOE_OK
+    # the map is defined for the latent layer
+    cfg = _lib.MoeLayerConfig(7168, 7168, 384, 8, 1, 2048, 2048, 64, 1, 1, 1)
+    assert _create_status(cfg, _bf16_weights()) == _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_bf16_map_workspace_is_monotone():
+    cfg = _k3()
+    cfg.dense_bf16 = 1
+    sizes = [_lib.moe_layer_workspace_size(cfg, T) for T in (0, 1, 64, 256, 257, 4096, 16384)]
+    assert sizes[0] <= sizes[1] <= sizes[2] <= sizes[3]
+    assert sizes[4] <= sizes[5] <= sizes[6] < 8 << 30
+
+
+def test_round_bf16_argument_errors():
+    lib = _lib.load()
+    assert lib.moe_round_bf16(FAKE, 6, FAKE, None) == _lib.MOE_ERR_INVALID_ARG     # n % 4
+    assert lib.moe_round_bf16(FAKE + 4, 8, FAKE, None) == _lib.MOE_ERR_INVALID_ARG # in alignment
+    assert lib.moe_round_bf16(FAKE, 8, FAKE + 2, None) == _lib.MOE_ERR_INVALID_ARG # out alignment
+    assert lib.moe_round_bf16(None, 8, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_round_bf16(FAKE, 0, FAKE, None) == _lib.MOE_OK

@@ -24,8 +24,17 @@ def _check_weight_codes(cfg, gw, W):
     """The GPU-encoded weights equal the oracle's codes: w_down row-major, the
     rest in fragment order (read back through the layout's numpy statement)."""
     from oracle import mx
+    if W.precision == "bf16":   # bfloat16 dense weights: the oracle's own rounding of the same fp32
+        for name in ("w_down", "w_up", "w_gate_s", "w_up_s", "w_down_s"):
+            ref = getattr(W, name)
+            got = gw[name + "_bf16"].cpu().numpy().view(np.uint16)
+            if isinstance(ref, list):
+                for i, r in enumerate(ref):
+                    assert np.array_equal(got[i], r.bits), (name, i)
+            else:
+                assert np.array_equal(got, ref.bits), name
     for name in ("w_down", "w_up"):
-        if getattr(W, name) is None:   # no latent projections
+        if getattr(W, name) is None or W.precision == "bf16":   # no MX latent projections
             assert gw[name] is None, name
             continue
         c, s = gw[name]
@@ -37,7 +46,7 @@ def _check_weight_codes(cfg, gw, W):
         assert np.array_equal(c, mx.pack_e2m1(ref.codes)), name
     for name in ("w_gate_e", "w_up_e", "w_down_e", "w_gate_s", "w_up_s", "w_down_s"):
         lst = getattr(W, name)
-        if not lst:
+        if not lst or not isinstance(lst[0], moe.MXTensor):
             continue
         c, s = gw[name]
         c, s = from_fragment_order(c.cpu().numpy(), s.cpu().numpy())
@@ -157,4 +166,37 @@ def test_k2_many_tokens_split_bf16_router():
     """The three-piece bf16 router on x itself (2048 tokens x 1024 experts)."""
     import dataclasses
     cfg = dataclasses.replace(synth.config("k2_tiny", T=2048), n_routed=1024, top_k=8)
+    _layer_case(cfg, check_codes=False)
+
+
+# --------------------------------------------------------------------------- higher-precision map
+
+
+def test_bf16_map_tiny_layer_parity():
+    """bfloat16 latent projections and shared experts (split-K weight
+    streaming at 64 tokens), MXFP4 routed experts."""
+    rep, y, tr, o = _layer_case(synth.config("tiny_bf16"))
+    assert "xq_codes" not in tr and "yb" in tr
+
+
+def test_bf16_map_ragged_tokens_both_kernels():
+    """1 and 17 tokens (16- and 64-row split-K tiles), 256 (the last few-row
+    size), 257 and 300 (the 512-thread LDS kernel, ragged M-tiles)."""
+    for T in (1, 17, 256, 257, 300):
+        _layer_case(synth.config("tiny_bf16", T=T), check_codes=(T == 257))
+
+
+def test_bf16_map_mid_layer_two_shared_experts():
+    """4096 tokens, 2 shared experts: the output GEMM runs three K segments
+    [L | Fs | Fs] on the LDS kernel; the shared gate/up two dense groups."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("mid"), name="mid_bf16", precision="bf16")
+    _layer_case(cfg, check_codes=False)
+
+
+def test_bf16_map_mid_decode_two_shared_experts():
+    """The same layer at 48 tokens: every bf16 GEMM on the split-K path, the
+    output one cutting its K slices across three segments."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("mid", T=48), name="mid_bf16", precision="bf16")
     _layer_case(cfg, check_codes=False)

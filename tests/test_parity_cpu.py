@@ -26,17 +26,21 @@ def _fake_trace(cfg, W, x, eps, seed=0):
         moe.mm = orig
     f32 = lambda v: np.asarray(v).astype(np.float32)
     tr = {
-        "xq_codes": n.xq.codes, "xq_scales": n.xq.scales, "z": f32(n.z), "zq_codes": n.zq.codes,
+        "z": f32(n.z), "zq_codes": n.zq.codes,
         "zq_scales": n.zq.scales, "ids": n.routing.ids, "gates": f32(n.routing.gates),
         "counts": n.disp.counts.astype(np.int32), "offsets": n.disp.offsets.astype(np.int32),
         "pair_of_row": n.disp.pair_of_row.astype(np.int32), "row_of_pair": n.disp.row_of_pair.astype(np.int32),
         "h": f32(n.h_rows), "hq_codes": n.hq_rows.codes, "hq_scales": n.hq_rows.scales, "y_e": f32(n.ye_rows),
-        "y_lat": f32(n.y_lat),
-        "hs": np.stack([f32(h) for h in n.h_shared]), "hs_codes": np.stack([q.codes for q in n.hq_shared]),
-        "hs_scales": np.stack([q.scales for q in n.hq_shared]),
+        "y_lat": f32(n.y_lat), "hs": np.stack([f32(h) for h in n.h_shared]),
     }
-    if n.yq is not None:
-        tr.update(yq_codes=n.yq.codes, yq_scales=n.yq.scales)
+    i16 = lambda b: np.asarray(b, np.uint16).view(np.int16)   # as the GPU trace holds bf16 patterns
+    if isinstance(n.xq, moe.BF16Tensor):
+        tr.update(xb=i16(n.xq.bits), yb=i16(n.yq.bits), hs_bf16=np.stack([i16(q.bits) for q in n.hq_shared]))
+    else:
+        tr.update(xq_codes=n.xq.codes, xq_scales=n.xq.scales, hs_codes=np.stack([q.codes for q in n.hq_shared]),
+                  hs_scales=np.stack([q.scales for q in n.hq_shared]))
+        if n.yq is not None:
+            tr.update(yq_codes=n.yq.codes, yq_scales=n.yq.scales)
     return f32(n.y), tr
 
 
@@ -137,4 +141,47 @@ def test_k2_router_input_must_be_x(k2_case):
     z[0, 0] = np.nextafter(z[0, 0], np.float32(np.inf))
     bad["z"] = z
     with pytest.raises(AssertionError, match="router input"):
+        parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
+
+
+# --------------------------------------------------------------------------- higher-precision map
+
+
+@pytest.fixture(scope="module")
+def bf16_case():
+    cfg = synth.config("tiny_bf16")
+    W = weights.layer(cfg)
+    x = synth.gen_hidden(cfg)
+    o = moe.forward(x, W, cfg.top_k)
+    y, tr = _fake_trace(cfg, W, x, eps=2e-7, seed=2)
+    return cfg, W, x, o, y, tr
+
+
+def test_bf16_map_perturbed_run_passes_and_adopts(bf16_case):
+    cfg, W, x, o, y, tr = bf16_case
+    rep = parity.check_layer(cfg, W, o, y, tr, x=x, say=lambda *a: None)
+    assert "yb" in rep["replay"] and "hs0" in rep["replay"]
+    adopted = sum(v["adopted_blocks"] for v in rep["replay"].values())
+    assert adopted > 0
+    assert rep["replay_rel_l2"] < 1e-4
+
+
+def test_bf16_map_planted_rounding_error_fails(bf16_case):
+    """A shared hidden value one bfloat16 step off, far from any boundary."""
+    cfg, W, x, o, y, tr = bf16_case
+    bad = dict(tr)
+    hb = tr["hs_bf16"].copy()
+    j = int(np.argmax(np.abs(o.h_shared[0][2])))
+    hb[0, 2, j] += 1
+    bad["hs_bf16"] = hb
+    with pytest.raises(AssertionError):
+        parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
+
+
+def test_bf16_map_truncated_input_fails(bf16_case):
+    """bf16(x) by truncation instead of round-to-nearest is caught."""
+    cfg, W, x, o, y, tr = bf16_case
+    bad = dict(tr)
+    bad["xb"] = (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16).view(np.int16)
+    with pytest.raises(AssertionError, match="bf16"):
         parity.check_layer(cfg, W, o, y, bad, x=x, say=lambda *a: None)
