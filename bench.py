@@ -151,6 +151,30 @@ def run_workload(name, steps, warmup, weights, hip, say, logit_bias=None):
     return cfg, ms_per_step, stage_ms, work, counts
 
 
+def bf16_map_report(weights, steps, decode_steps, warmup, hip, say):
+    """The higher-precision map at K3 width: the same MXFP4 routed experts,
+    bfloat16 latent projections and shared experts (encoded here); prefill
+    and decode throughput and the dense stages' times."""
+    import synth
+    from latent_routing_mxfp4_amd import layer as LY
+
+    out = {}
+    w = None
+    for name, n in (("k3_prefill_bf16", steps), ("k3_decode_bf16", decode_steps)):
+        cfg = synth.config(name)
+        if w is None:
+            t = time.perf_counter()
+            w = dict(weights)
+            w.update(LY.encode_weights(LY.LayerShape.of(cfg), lambda m, i: synth.gen_weight(cfg, m, i),
+                                       names=LY.DENSE + LY.SHARED))
+            say(f"bf16 dense weights encoded in {time.perf_counter() - t:.1f} s")
+        c, ms, st, work, counts = run_workload(name, n, warmup, w, hip, say)
+        out[name] = {"workload": f"{c.name}: T={c.T}, bf16 latent projections + shared experts",
+                     "value": c.T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms, "stage_ms": st,
+                     "step_events_ms": work["step_events_ms"]}
+    return out
+
+
 def k2_report(steps, warmup, hip, say):
     """The non-latent K2-like layer (its own weights, encoded after the K3
     weights are freed): throughput, MX matrix-core share and the expert GEMM's
@@ -345,6 +369,8 @@ def main():
                     help="steps of the 8192-token Zipf-skewed batch reported under 'skew' (0: skip)")
     ap.add_argument("--k2-steps", type=int, default=5,
                     help="steps of the non-latent K2-like 8192-token layer reported under 'k2' (0: skip)")
+    ap.add_argument("--bf16-steps", type=int, default=5,
+                    help="steps of the higher-precision map (bf16 dense weights) reported under 'bf16_map' (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2)
@@ -449,6 +475,8 @@ def main():
                        "max_expert_load": int(kcounts.max()), "mean_expert_load": float(kcounts.mean()),
                        "empty_experts": int((kcounts == 0).sum()), "stage_ms": kst,
                        "step_events_ms": kwork["step_events_ms"]}
+    if args.bf16_steps > 0 and args.workload == "k3_prefill":
+        out["bf16_map"] = bf16_map_report(weights, args.bf16_steps, args.decode_steps, args.warmup, hip, say)
     out["hbm_copy_probe_gbs"] = copy_gbs
     if args.workload == "k3_decode":
         dom = stages["expert_up"]

@@ -123,7 +123,8 @@ def mx_gemm(a_codes, a_scales, b_codes, b_scales) -> torch.Tensor:
 
 def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray], device="cuda",
                    extra: Optional[Dict[str, Optional[np.ndarray]]] = None, workers: int = 8,
-                   progress: Optional[Callable[[int, int], None]] = None) -> Dict:
+                   progress: Optional[Callable[[int, int], None]] = None,
+                   names: Optional[Tuple[str, ...]] = None) -> Dict:
     """Encode every weight matrix on the GPU.
 
     ``host_fp32(name, index)`` returns the fp32 ``[out][in]`` matrix (numpy);
@@ -134,11 +135,13 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
     higher-precision map the latent projections and shared experts are
     rounded to bfloat16 instead (``moe_round_bf16``), stored row-major under
     ``<name>_bf16`` (their MX entries are None).
-    ``extra`` carries the fp32 router (``w_router``) and the optional biases.
+    ``extra`` carries the fp32 router (``w_router``) and the optional biases;
+    ``names`` restricts the encoding to those weight names (e.g. the bfloat16
+    ones, to pair with routed experts encoded before).
     """
     out: Dict = {}
     jobs = []
-    for name in DENSE + ROUTED + SHARED:
+    for name in names if names is not None else DENSE + ROUTED + SHARED:
         n = shape.count(name)
         stacked = name in ROUTED + SHARED
         if shape.is_bf16(name):
@@ -179,6 +182,8 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
                 progress(j + 1, len(jobs))
     extra = extra or {}
     for k in ("w_router", "router_logit_bias", "selection_bias"):
+        if names is not None and k not in extra:
+            continue
         v = extra.get(k)
         out[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(device)
     torch.cuda.synchronize()

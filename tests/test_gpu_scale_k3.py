@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-SAMPLES = {"k3_decode": [0, 37], "k3_prefill": [5, 9000, 16383], "k3_skew": [1, 4097]}
+SAMPLES = {"k3_decode": [0, 37], "k3_prefill": [5, 9000, 16383], "k3_skew": [1, 4097],
+           "k3_decode_bf16": [0, 63], "k3_prefill_bf16": [7, 16383]}
 
 
 @pytest.fixture(scope="module")
@@ -42,6 +43,13 @@ def k3():
     del gw
 
 
+def _bf16_dense(LY, cfg):
+    """The higher-precision map's bfloat16 latent projections and shared
+    experts, rounded on the GPU by the library from the same fp32 weights."""
+    shape = LY.LayerShape.of(cfg)
+    return LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), names=LY.DENSE + LY.SHARED)
+
+
 def _run(k3, name):
     LY, shape, gw, W, cache = k3
     cfg = synth.config(name)
@@ -49,6 +57,10 @@ def _run(k3, name):
     say(f"K3 parity {name}: T={cfg.T}, sampled tokens {tokens}")
     w = dict(gw)
     Wc = W
+    if cfg.precision == "bf16":   # same routed experts, bfloat16 dense weights
+        shape = LY.LayerShape.of(cfg)
+        w.update(_bf16_dense(LY, cfg))
+        Wc = weights.layer(cfg, experts="lazy")
     if cfg.logit_bias != "none":   # same weights, different router logit bias
         lb = synth.gen_logit_bias(cfg)
         w["router_logit_bias"] = torch.from_numpy(lb).cuda()
@@ -77,3 +89,13 @@ def test_k3_prefill_16384_tokens(k3):
 def test_k3_skewed_routing_8192_tokens(k3):
     rep, _ = _run(k3, "k3_skew")
     assert rep["max_expert_rows"] > 2 * rep["pairs"] / 896   # the Zipf bias does concentrate the load
+
+
+def test_k3_bf16_map_decode_64_tokens(k3):
+    """The higher-precision map at K3 width, 64 tokens (split-K bf16 GEMMs)."""
+    _run(k3, "k3_decode_bf16")
+
+
+def test_k3_bf16_map_prefill_16384_tokens(k3):
+    """The higher-precision map at K3 width, 16384 tokens (LDS bf16 GEMMs)."""
+    _run(k3, "k3_prefill_bf16")
