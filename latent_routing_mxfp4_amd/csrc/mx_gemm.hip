@@ -139,176 +139,45 @@ __device__ __forceinline__ void e2m1_block_bf16(const uint4& codes, int sc, uint
 // bf16 x bf16 -> fp32 and v_mfma_f32_16x16x32_bf16 accumulates at fp32
 // precision, unlike the block-scaled MFMA, which sums each 32-element block in
 // a window of about 14 bits below its largest product; the router's top-k is
-// decided on this latent.  Per 128-wide K-step a lane loads 32 K values of
-// its activation row and of its weight row (or one MX block, 16 code bytes)
-// and issues four MFMAs, slice u of lane group g taking the same K range in
-// both operands, so the pairing of K indices is consistent: K [32g + 8u, +8)
-// with MX weights (a lane's 32 values are one MX block), K [32u + 8g, +8)
-// with bf16 weights, so that the four lane groups of one load instruction
-// read 64 contiguous bytes of a row.  Slice
-// blockIdx.y covers K-steps [ks0, ks0 + nks) of one segment and writes its
-// fp32 partial sums to part[slice][g][M][N]; the reduce kernels add the
-// slices in slice order.  Weights and activations are read D K-steps ahead in
-// a register ring.
-template <int MW, int NW, bool BF16B>
+// decided on this latent.
+//
+// Slice blockIdx.y covers K-steps [ks0, ks0 + nks) (128 K values each) of one
+// segment and writes its fp32 partial sums to part[slice][g][M][N]; the
+// reduce kernels add the slices in slice order.  A workgroup (4 waves) owns
+// MT = 16 MW rows and 4 x 16 NW columns.  The activation tile of a K-step
+// (MT x 256 bytes, shared by the 4 waves) is staged in LDS by direct loads;
+// each wave streams only its own weight rows into a D-deep register ring.
+// (Loading the activations into every wave's registers put 4 MW L2 loads per
+// K-step in the same in-order counter as the weight loads, and the waits
+// before the first MFMAs of a step left almost no weight prefetch in flight.)
+// The direct loads are inline assembly with hand-placed waits (as in the
+// LDS-staged kernels); the weight loads are ordinary loads whose waits the
+// compiler places.  They are issued unconditionally (past the slice's end
+// they re-read its last K-step) and the main loop runs whole ring cycles with
+// no per-step condition: a conditional load or step let the compiler's wait
+// model assume, at the loop head, that a ring slot was loaded last, and it
+// drained every load once per cycle.  Its model does not see the direct
+// loads, so its waits are stricter than those need; the ring is a step deeper
+// to make up for it.  K pairing (the same K range in both operands): with
+// bf16 weights slice u of lane group g is K [32u + 8g, +8), so the four lane
+// groups of a weight load read 64 contiguous bytes of a row; with MX weights
+// it is K [32g + 8u, +8) (a lane's 32 values are one MX block).  The LDS copy
+// of the activation tile keeps 16-byte chunk c of row r at chunk c ^ (r % 16)
+// (conflict-free reads).
+template <int MW, int D>
+constexpr size_t splitk_lds_bytes() {
+  return (size_t)(D + 1) * 16 * MW * 256;
+}
+
+template <int MW, int NW, int D, bool MXB>
 __global__ void __launch_bounds__(256) bf16_splitk_kernel(const GemmArgs p, const SplitPlan sp,
                                                           float* __restrict__ part) {
   constexpr int MT = 16 * MW;
   constexpr int NT = 4 * 16 * NW;
-  constexpr int D = BF16B ? 2 : (MW == 1 ? 4 : 2);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  const int g4 = lane >> 4;
-  Tile t;
-  if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;
-  const int slice = blockIdx.y;
-  const GemmSeg& sg = p.seg[sp.seg[slice]];
-  const int K = sg.K;
-  const int ks0 = sp.ks0[slice];
-  const int nks = sp.nks[slice];
-  constexpr int KG = BF16B ? 8 : 32;  // K offset of lane group g4 (elements)
-  constexpr int KU = BF16B ? 32 : 8;  // K offset of slice u
-  const uint16_t* ap[MW];
-#pragma unroll
-  for (int mi = 0; mi < MW; ++mi) {
-    int r = t.m0 + 16 * mi + r16;
-    r = r < t.rows ? r : t.rows - 1;
-    ap[mi] = reinterpret_cast<const uint16_t*>(sg.a) + (int64_t)r * K + 128 * ks0 + KG * g4;
-  }
-  const int half = p.N >> 1;  // SwiGLU pair: columns [half, N) read b2
-  const uint8_t* bp[NW];
-  const uint8_t* bsp[NW];
-#pragma unroll
-  for (int ni = 0; ni < NW; ++ni) {
-    int c = t.n0 + 16 * ni + r16;
-    c = c < p.N ? c : p.N - 1;
-    const bool up = sg.b2 != nullptr && c >= half;
-    const int cc = up ? c - half : c;
-    const uint8_t* base = (up ? sg.b2 : sg.b) + (int64_t)t.g * sg.b_gstride;
-    if (BF16B) {
-      bp[ni] = base + ((int64_t)cc * K + 128 * ks0 + KG * g4) * 2;
-      bsp[ni] = nullptr;
-    } else {
-      bp[ni] = base + (int64_t)cc * (K >> 1) + 64 * ks0 + 16 * g4;
-      bsp[ni] = (up ? sg.b2s : sg.bs) + (int64_t)t.g * sg.bs_gstride + (int64_t)cc * (K >> 5) + 4 * ks0 + g4;
-    }
-  }
-  v4f acc[MW][NW][1];
-#pragma unroll
-  for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni) acc[mi][ni][0] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int BQ = BF16B ? 4 : 1;  // 16-byte weight loads per fragment and K-step
-  struct Slot {
-    uint4 a[MW][4];
-    uint4 b[NW][BQ];
-    int bs[NW];
-  };
-  Slot sl[D];
-  auto load = [&](int ks, Slot& q) {
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni) {
-      if (BF16B) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          q.b[ni][u] =
-              to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni] + 256 * ks + 2 * KU * u)));
-      } else {
-        q.b[ni][0] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni] + 64 * ks)));
-        q.bs[ni] = bsp[ni][4 * ks];
-      }
-    }
-#pragma unroll
-    for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) q.a[mi][u] = *reinterpret_cast<const uint4*>(ap[mi] + 128 * ks + KU * u);
-  };
-  auto compute = [&](const Slot& q) {
-    uint4 bf[NW][4];
-#pragma unroll
-    for (int ni = 0; ni < NW; ++ni) {
-      if (BF16B) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) bf[ni][u] = q.b[ni][u];
-      } else {
-        e2m1_block_bf16(q.b[ni][0], q.bs[ni], bf[ni]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int mi = 0; mi < MW; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NW; ++ni)
-          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a[mi][u]), as_bf16x8(bf[ni][u]),
-                                                                   acc[mi][ni][0], 0, 0, 0);
-  };
-#pragma unroll
-  for (int j = 0; j < D; ++j)
-    if (j < nks) load(j, sl[j]);
-  int ks = 0;
-  for (; ks + 2 * D <= nks; ks += D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      compute(sl[j]);
-      load(ks + j + D, sl[j]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < D; ++j)
-    if (ks + j < nks) {
-      compute(sl[j]);
-      if (ks + j + D < nks) load(ks + j + D, sl[j]);
-    }
-  ks += D;
-#pragma unroll
-  for (int j = 0; j < D; ++j)
-    if (ks + j < nks) compute(sl[j]);
-
-  GemmArgs q = p;  // the slice's partial sums, fp32 [G][M][N]
-  q.c = part + (int64_t)slice * p.G * p.M * p.N;
-  q.ldc = p.N;
-  q.c_gstride = (int64_t)p.M * p.N;
-  q.c_accumulate = 0;
-  q.q = nullptr;
-  epilogue<MW, NW, 1, EPI_F32>(q, t, acc, r16, g4);
-}
-
-// Few-row GEMM with bf16 weights (the higher-precision map at decode sizes):
-// the same K slices, tiles and partial sums as above, but the activation tile
-// (MT rows x 128 K values per K-step, shared by the workgroup's 4 waves) is
-// staged in LDS by direct loads, and each wave streams only its own weight
-// rows into a D-deep register ring.  Loading the activations into every
-// wave's registers instead put 16 L2 loads per K-step in the same in-order
-// counter as the weight loads, and the waits before the first MFMAs of a step
-// then left almost no weight prefetch in flight.  The direct loads are inline
-// assembly with hand-placed waits (as in the LDS-staged kernels); the weight
-// loads are ordinary loads whose waits the compiler places.  The weight loads
-// are issued unconditionally (past the slice's end they re-read its last
-// K-step): a conditional load before the loop made the compiler's wait model
-// assume, at the loop head, that every ring slot was just loaded, and it
-// drained all loads once per ring cycle (likewise a conditional step inside
-// the loop, see below).  Its model does not see the direct
-// loads, so its waits are stricter than needed by those; the ring is one
-// step deeper to make up for it.  K pairing: slice
-// u of lane group g is K [32u + 8g, +8), so the four lane groups of a weight
-// load read 64 contiguous bytes of a row; the LDS copy of the activation tile
-// keeps 16-byte chunk c of row r at chunk c ^ (r % 16) (conflict-free reads).
-
-template <int MW, int D>
-constexpr size_t bf16w_lds_bytes() {
-  return (size_t)(D + 1) * 16 * MW * 256;
-}
-
-template <int MW, int NW, int D>
-__global__ void __launch_bounds__(256) bf16w_splitk_kernel(const GemmArgs p, const SplitPlan sp,
-                                                           float* __restrict__ part) {
-  constexpr int MT = 16 * MW;
-  constexpr int NT = 4 * 16 * NW;
   constexpr int NBUF = D + 1;             // the buffer refilled after step s was last read at step s - 1
   constexpr int ABYTES = MT * 256;        // activation tile of one K-step
+  constexpr int BQ = MXB ? 1 : 4;         // 16-byte weight loads per fragment and K-step
+  constexpr int BLOADS = MXB ? 2 * NW : 4 * NW;  // weight loads per lane and K-step (MX: codes + scale)
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // NBUF * ABYTES
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -335,26 +204,45 @@ __global__ void __launch_bounds__(256) bf16w_splitk_kernel(const GemmArgs p, con
   }
   const int half = p.N >> 1;  // SwiGLU pair: columns [half, N) read b2
   const uint8_t* gb[NW];
+  const uint8_t* gs[NW];
 #pragma unroll
   for (int ni = 0; ni < NW; ++ni) {
     int c = t.n0 + 16 * ni + r16;
     c = c < p.N ? c : p.N - 1;
     const bool up = sg.b2 != nullptr && c >= half;
     const int cc = up ? c - half : c;
-    gb[ni] = (up ? sg.b2 : sg.b) + (int64_t)t.g * sg.b_gstride + ((int64_t)cc * K + 128 * ks0 + 8 * g4) * 2;
+    const uint8_t* base = (up ? sg.b2 : sg.b) + (int64_t)t.g * sg.b_gstride;
+    if (MXB) {
+      gb[ni] = base + (int64_t)cc * (K >> 1) + 64 * ks0 + 16 * g4;
+      gs[ni] = (up ? sg.b2s : sg.bs) + (int64_t)t.g * sg.bs_gstride + (int64_t)cc * (K >> 5) + 4 * ks0 + g4;
+    } else {
+      gb[ni] = base + ((int64_t)cc * K + 128 * ks0 + 8 * g4) * 2;
+      gs[ni] = nullptr;
+    }
   }
-  uint4 bq[D][NW][4];
+  struct BSlot {
+    uint4 v[NW][BQ];
+    int sc[NW];
+  };
+  BSlot bq[D];
   auto issue_a = [&](int ks) {
     uint8_t* buf = lds + (ks % NBUF) * ABYTES;
 #pragma unroll
     for (int i = 0; i < MW; ++i) gl_lds16(ga[i] + 256 * ks, buf + 4096 * i + 1024 * wave);
   };
-  auto issue_b = [&](int ks, uint4 (&q)[NW][4]) {
+  auto issue_b = [&](int ks, BSlot& q) {
 #pragma unroll
-    for (int ni = 0; ni < NW; ++ni)
+    for (int ni = 0; ni < NW; ++ni) {
+      if (MXB) {
+        q.v[ni][0] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gb[ni] + 64 * ks)));
+        q.sc[ni] = gs[ni][4 * ks];
+      } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        q[ni][u] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gb[ni] + 256 * ks + 64 * u)));
+        for (int u = 0; u < BQ; ++u)
+          q.v[ni][u] =
+              to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gb[ni] + 256 * ks + 64 * u)));
+      }
+    }
   };
   v4f acc[MW][NW][1];
 #pragma unroll
@@ -369,13 +257,13 @@ __global__ void __launch_bounds__(256) bf16w_splitk_kernel(const GemmArgs p, con
     issue_b(j < nks ? j : nks - 1, bq[j]);
     if (j < nks) issue_a(j);
   }
-  auto step = [&](int ks, uint4 (&q)[NW][4]) {
+  auto step = [&](int ks, BSlot& q) {
     // Issued after this step's activation loads: the D - 1 later steps'
     // weight loads and the real ones' activation loads.  At most that many
     // may still be in flight (the weight registers' own waits are the
     // compiler's).
     const int later = nks - 1 - ks < D - 1 ? nks - 1 - ks : D - 1;
-    constexpr int WB = (D - 1) * 4 * NW;
+    constexpr int WB = (D - 1) * BLOADS;
     switch (later) {
       case 0: wait_vmcnt<WB>(); break;
       case 1: wait_vmcnt<WB + MW>(); break;
@@ -384,30 +272,38 @@ __global__ void __launch_bounds__(256) bf16w_splitk_kernel(const GemmArgs p, con
     }
     barrier_lds();  // every wave's part of this step's activation tile is in LDS
     const uint8_t* buf = lds + (ks % NBUF) * ABYTES;
+    uint4 bf[NW][4];
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni) {
+      if (MXB) {
+        e2m1_block_bf16(q.v[ni][0], q.sc[ni], bf[ni]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bf[ni][u] = q.v[ni][BQ == 4 ? u : 0];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int mi = 0; mi < MW; ++mi) {
         const int row = 16 * mi + r16;
-        const uint4 av = *reinterpret_cast<const uint4*>(buf + row * 256 + (((4 * u + g4) ^ (row & 15)) << 4));
+        const int chunk = MXB ? 4 * g4 + u : 4 * u + g4;
+        const uint4 av = *reinterpret_cast<const uint4*>(buf + row * 256 + ((chunk ^ (row & 15)) << 4));
 #pragma unroll
         for (int ni = 0; ni < NW; ++ni)
-          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(q[ni][u]),
+          acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bf[ni][u]),
                                                                    acc[mi][ni][0], 0, 0, 0);
       }
     issue_b(ks + D < nks ? ks + D : nks - 1, q);
     if (ks + D < nks) issue_a(ks + D);  // its buffer was last read at step ks - 1
   };
-  // Whole ring cycles with no per-step condition (a conditional step inside
-  // the loop would let the compiler's wait model assume, at the loop head,
-  // that slot 0 was loaded last), then the remaining steps.
   int ks = 0;
-  for (; ks + D <= nks; ks += D) {
+  for (; ks + D <= nks; ks += D) {  // whole ring cycles
 #pragma unroll
     for (int j = 0; j < D; ++j) step(ks + j, bq[j]);
   }
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j)
+  for (int j = 0; j < D - 1; ++j)   // the remaining steps
     if (ks + j < nks) step(ks + j, bq[j]);
   wait_vmcnt<0>();  // the re-reads past the slice's end
 
@@ -644,11 +540,11 @@ hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
 }
 
 SplitPlan splitk_plan(const GemmArgs& a) {
-  // About 1024 waves in all, at most 8 slices' worth of K cuts (the partial
+  // About 2048 waves in all, at most 8 slices' worth of K cuts (the partial
   // sums stay small next to the weights); segments are cut separately.
   const int MT = a.M <= 16 ? 16 : 64;
   const int tiles = a.G * ((a.N + 127) / 128) * ((a.M + MT - 1) / MT);
-  int target = (1024 + 4 * tiles - 1) / (4 * tiles);
+  int target = (2048 + 4 * tiles - 1) / (4 * tiles);
   target = target < 1 ? 1 : (target > 8 ? 8 : target);
   int total = 0;
   for (int i = 0; i < a.nseg; ++i) total += a.seg[i].K / 128;
@@ -695,20 +591,23 @@ hipError_t launch_bf16_splitk(const GemmArgs& a, bool bf16_b, const SplitPlan& s
   const int64_t grid = (int64_t)a.G * ((a.M + MT - 1) / MT) * ((a.N + 127) / 128);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 gd((unsigned)grid, (unsigned)sp.n);
-  if (bf16_b) {
-    constexpr size_t lds1 = bf16w_lds_bytes<1, 4>(), lds4 = bf16w_lds_bytes<4, 4>();
-    static bool attr_set = false;  // per process, before the first launch
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bf16w_splitk_kernel<4, 2, 4>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds4);
+  constexpr int D = 4;
+  constexpr size_t lds1 = splitk_lds_bytes<1, D>(), lds4 = splitk_lds_bytes<4, D>();
+  static bool attr_set = false;  // per process, before the first launch
+  if (!attr_set) {
+    for (const void* f : {reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, false>),
+                          reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, true>)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds4);
       if (e != hipSuccess) return e;
-      attr_set = true;
     }
-    if (small) bf16w_splitk_kernel<1, 2, 4><<<gd, dim3(256), lds1, s>>>(a, sp, part);
-    else bf16w_splitk_kernel<4, 2, 4><<<gd, dim3(256), lds4, s>>>(a, sp, part);
+    attr_set = true;
+  }
+  if (bf16_b) {
+    if (small) bf16_splitk_kernel<1, 2, D, false><<<gd, dim3(256), lds1, s>>>(a, sp, part);
+    else bf16_splitk_kernel<4, 2, D, false><<<gd, dim3(256), lds4, s>>>(a, sp, part);
   } else {
-    if (small) bf16_splitk_kernel<1, 2, false><<<gd, dim3(256), 0, s>>>(a, sp, part);
-    else bf16_splitk_kernel<4, 2, false><<<gd, dim3(256), 0, s>>>(a, sp, part);
+    if (small) bf16_splitk_kernel<1, 2, D, true><<<gd, dim3(256), lds1, s>>>(a, sp, part);
+    else bf16_splitk_kernel<4, 2, D, true><<<gd, dim3(256), lds4, s>>>(a, sp, part);
   }
   return hipGetLastError();
 }
