@@ -243,7 +243,7 @@ def cpu_baseline(name, n_tokens, say):
 
 PROFILE_MD = os.path.join(ROOT, "profiles", "k3_layer_kernels_and_hbm_traffic.md")
 PROFILE_CMD = ("python3 /root/repo/bench.py --steps 3 --warmup 1 --decode-steps 5 --no-cpu-baseline "
-               "--copy-probe")
+               "--k2-steps 0 --bf16-steps 0 --copy-probe")
 
 
 def source_digest() -> str:
