@@ -65,12 +65,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& f) {
 }  // namespace
 
 // Map a workgroup to (group, M-tile, N-tile).  Returns false for workgroups
-// past the last M-tile (the grid is sized for the worst case).
+// past the last M-tile (the grid is sized for the worst case).  The fields
+// are computed in locals and stored once, so the tile stays in registers
+// (filling them branch by branch through the reference left the tile in
+// per-lane scratch memory).
 template <int MT, int NT>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int wave, int NWC, Tile& t) {
   const int n_ntiles = (p.N + NT - 1) / NT;
   const int gm = blockIdx.x / n_ntiles;
   const int nt = blockIdx.x - gm * n_ntiles;
+  int g, m0, rows, row_base;
   if (p.offsets) {
     const int total = p.mtile_start[p.G];
     if (gm >= total) return false;
@@ -79,19 +83,19 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int wave, int NWC
       int mid = (lo + hi) >> 1;
       if (p.mtile_start[mid] <= gm) lo = mid; else hi = mid;
     }
-    t.g = lo;
-    t.row_base = p.offsets[lo];
-    t.rows = p.offsets[lo + 1] - t.row_base;
-    t.m0 = (gm - p.mtile_start[lo]) * MT;
+    g = lo;
+    row_base = p.offsets[lo];
+    rows = p.offsets[lo + 1] - row_base;
+    m0 = (gm - p.mtile_start[lo]) * MT;
   } else {
     const int mpg = (p.M + MT - 1) / MT;
-    t.g = gm / mpg;
-    if (t.g >= p.G) return false;
-    t.m0 = (gm - t.g * mpg) * MT;
-    t.rows = p.M;
-    t.row_base = 0;
+    g = gm / mpg;
+    if (g >= p.G) return false;
+    m0 = (gm - g * mpg) * MT;
+    rows = p.M;
+    row_base = 0;
   }
-  t.n0 = nt * NT + wave * NWC;
+  t = Tile{g, m0, rows, row_base, nt * NT + wave * NWC};
   return true;
 }
 
@@ -184,9 +188,22 @@ __global__ void __launch_bounds__(256) bf16_splitk_kernel(const GemmArgs p, cons
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
+  // Dense tiles only (the launcher checks): workgroup -> (group, M-tile,
+  // N-tile), straight-line so the tile stays in registers.  Workgroup-uniform:
+  // every wave of a workgroup returns here or none does.
   Tile t;
-  // Workgroup-uniform: every wave of a workgroup returns here or none does.
-  if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;
+  {
+    const int n_ntiles = (p.N + NT - 1) / NT;
+    const int mpg = (p.M + MT - 1) / MT;
+    const int gm = blockIdx.x / n_ntiles;
+    const int nt = blockIdx.x - gm * n_ntiles;
+    t.g = gm / mpg;
+    if (t.g >= p.G) return;
+    t.m0 = (gm - t.g * mpg) * MT;
+    t.rows = p.M;
+    t.row_base = 0;
+    t.n0 = nt * NT + wave * 16 * NW;
+  }
   const int slice = blockIdx.y;
   const GemmSeg& sg = p.seg[sp.seg[slice]];
   const int K = sg.K;

@@ -200,3 +200,19 @@ def test_bf16_map_mid_decode_two_shared_experts():
     import dataclasses
     cfg = dataclasses.replace(synth.config("mid", T=48), name="mid_bf16", precision="bf16")
     _layer_case(cfg, check_codes=False)
+
+
+def test_repeated_decode_forwards_bitwise_equal():
+    """Eight forwards of the same 48-token batch (bf16 map, two shared
+    experts: the K-split path reuses one partial-sum buffer for several
+    GEMMs) give bitwise equal outputs and latents."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.config("mid", T=48), name="mid_bf16", precision="bf16")
+    lay, _ = gpu_layer(cfg)
+    x = synth.gen_hidden(cfg)
+    y0, t0 = run_traced(lay, x)
+    for _ in range(7):
+        y, t = run_traced(lay, x)
+        assert np.array_equal(y, y0)
+        assert np.array_equal(t["z"], t0["z"])
+    lay.close()
