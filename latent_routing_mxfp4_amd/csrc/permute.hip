@@ -17,6 +17,8 @@
 //           tokens of the block that chose the same expert (a token never
 //           picks one expert twice).  row = offset[e] + base[b][e] + rank.
 //
+// A batch of at most 64 tokens (one block) runs all three in one workgroup.
+//
 // No atomics touch global memory and nothing depends on scheduling order, so
 // the permutation is bitwise reproducible and stable (token order inside each
 // segment).
@@ -126,11 +128,80 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
   }
 }
 
+// All of count, scan and scatter in one workgroup when the batch is one
+// block of at most 64 tokens (decode): the same bitmask counting sort, with
+// the per-expert masks and segment offsets kept in LDS.
+__global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int mt0, int32_t* __restrict__ ms0, int mt1,
+                                                         int32_t* __restrict__ ms1, int32_t* __restrict__ row_of_pair,
+                                                         int32_t* __restrict__ pair_of_row) {
+  extern __shared__ unsigned long long masks[];            // [E], then int32 offsets [E]
+  int32_t* soff = reinterpret_cast<int32_t*>(masks + E);
+  __shared__ int32_t part[3][1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) masks[e] = 0ull;
+  __syncthreads();
+  if (tid < T)
+    for (int j = 0; j < k; ++j) atomicOr(&masks[ids[(int64_t)tid * k + j]], 1ull << tid);
+  __syncthreads();
+  // exclusive scans over experts of count, ceil(count/mt0), ceil(count/mt1);
+  // thread tid owns the contiguous experts [lo, hi).
+  const int per = (E + 1023) / 1024;
+  const int lo = tid * per < E ? tid * per : E;
+  const int hi = lo + per < E ? lo + per : E;
+  int s0 = 0, s1 = 0, s2 = 0;
+  for (int e = lo; e < hi; ++e) {
+    const int c = __popcll(masks[e]);
+    s0 += c;
+    s1 += (c + mt0 - 1) / mt0;
+    s2 += (c + mt1 - 1) / mt1;
+  }
+  part[0][tid] = s0; part[1][tid] = s1; part[2][tid] = s2;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan over the 1024 partials
+    int a0 = 0, a1 = 0, a2 = 0;
+    if (tid >= o) { a0 = part[0][tid - o]; a1 = part[1][tid - o]; a2 = part[2][tid - o]; }
+    __syncthreads();
+    part[0][tid] += a0; part[1][tid] += a1; part[2][tid] += a2;
+    __syncthreads();
+  }
+  int r0 = tid ? part[0][tid - 1] : 0;
+  int r1 = tid ? part[1][tid - 1] : 0;
+  int r2 = tid ? part[2][tid - 1] : 0;
+  for (int e = lo; e < hi; ++e) {
+    const int c = __popcll(masks[e]);
+    counts[e] = c;
+    offsets[e] = r0; ms0[e] = r1; ms1[e] = r2;
+    soff[e] = r0;
+    r0 += c;
+    r1 += (c + mt0 - 1) / mt0;
+    r2 += (c + mt1 - 1) / mt1;
+  }
+  if (tid == 1023) { offsets[E] = part[0][1023]; ms0[E] = part[1][1023]; ms1[E] = part[2][1023]; }
+  __syncthreads();
+  if (tid < T) {  // rank of a pair = earlier tokens of the block that chose the same expert
+    const unsigned long long below = (1ull << tid) - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int64_t pair = (int64_t)tid * k + j;
+      const int e = ids[pair];
+      const int row = soff[e] + __popcll(masks[e] & below);
+      row_of_pair[pair] = row;
+      pair_of_row[row] = (int32_t)pair;
+    }
+  }
+}
+
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* scratch, int32_t* counts,
                            int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row, int mt0,
                            int32_t* ms0, int mt1, int32_t* ms1, hipStream_t s) {
   const int nblk = (T + kTokBlock - 1) / kTokBlock;
   const size_t smem = (size_t)E * sizeof(unsigned long long);
+  if (nblk == 1) {  // one block of tokens: one launch
+    perm_small_kernel<<<dim3(1), dim3(1024), smem + (size_t)E * sizeof(int32_t), s>>>(
+        ids, T, E, k, counts, offsets, mt0, ms0, mt1, ms1, row_of_pair, pair_of_row);
+    return hipGetLastError();
+  }
   if (nblk > 0) {
     perm_count_kernel<<<dim3(nblk), dim3(64), smem, s>>>(ids, T, E, k, scratch);
     hipError_t err = hipGetLastError();

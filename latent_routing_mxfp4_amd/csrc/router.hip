@@ -416,14 +416,26 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 
   float bk = -INFINITY;
   int bi = 0x7fffffff;
-  for (int e = lane; e < E; e += 64) {
-    const float sc = softmax ? lrow[e] : sigmoidf(lrow[e]);
-    float key = sc;
-    if (sel_bias) key += sel_bias[e];
-    key = fmaxf(key, -FLT_MAX);  // NaN / -inf inputs rank last but stay above "taken" (-inf)
-    keys[e] = key;
-    scores[e] = sc;
-    if (better(key, e, bk, bi)) { bk = key; bi = e; }
+  for (int e0 = lane; e0 < E; e0 += 64 * 8) {
+    float lv[8], bv[8];  // eight loads in flight, then their keys
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = min(e0 + 64 * j, E - 1);
+      lv[j] = lrow[e];
+      bv[j] = sel_bias ? sel_bias[e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + 64 * j;
+      if (e >= E) break;
+      const float sc = softmax ? lv[j] : sigmoidf(lv[j]);
+      float key = sc;
+      if (sel_bias) key += bv[j];
+      key = fmaxf(key, -FLT_MAX);  // NaN / -inf inputs rank last but stay above "taken" (-inf)
+      keys[e] = key;
+      scores[e] = sc;
+      if (better(key, e, bk, bi)) { bk = key; bi = e; }
+    }
   }
   float ssum = 0.f;
   float mys = 0.f;  // raw score of the winner of slot `lane`
@@ -469,15 +481,25 @@ __global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__
   float key[KPL], scr[KPL];
   float bk = -INFINITY;
   int bi = 0x7fffffff;
+  // All of the lane's loads first (indices past E re-read the last logit and
+  // are discarded below), so they are in flight together instead of one
+  // memory latency per key.
+  float lv[KPL], bv[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = min(lane + 64 * j, E - 1);
+    lv[j] = lrow[e];
+    bv[j] = sel_bias ? sel_bias[e] : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int e = lane + 64 * j;
     key[j] = -INFINITY;  // past E: never selected (k <= E finite keys exist)
     scr[j] = 0.f;
     if (e < E) {
-      const float sc = softmax ? lrow[e] : sigmoidf(lrow[e]);
+      const float sc = softmax ? lv[j] : sigmoidf(lv[j]);
       float kk = sc;
-      if (sel_bias) kk += sel_bias[e];
+      if (sel_bias) kk += bv[j];
       kk = fmaxf(kk, -FLT_MAX);
       key[j] = kk;
       scr[j] = sc;
