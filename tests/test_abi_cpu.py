@@ -186,3 +186,29 @@ def test_round_bf16_argument_errors():
     assert lib.moe_round_bf16(FAKE, 8, FAKE + 2, None) == _lib.MOE_ERR_INVALID_ARG # out alignment
     assert lib.moe_round_bf16(None, 8, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_round_bf16(FAKE, 0, FAKE, None) == _lib.MOE_OK
+
+
+# --------------------------------------------------------------------------- layer without a latent
+
+
+def test_non_latent_create_needs_no_latent_projections():
+    """identity_latent: d_latent must equal d_model and W_down / W_up may be
+    NULL; softmax_gates is a plain flag."""
+    cfg = _lib.MoeLayerConfig(7168, 7168, 384, 8, 1, 2048, 2048, 8192, 1, 1, 0)
+    t = _lib.MoeMxTensor(FAKE, FAKE)
+    z = _lib.MoeMxTensor(None, None)
+    w = _lib.MoeLayerWeights(z, z, FAKE, None, None, t, t, t, t, t, t)
+    assert _create_status(cfg, w) == _lib.MOE_OK
+    cfg.d_latent = 3584                              # a latent width without latent projections
+    assert _create_status(cfg, w) == _lib.MOE_ERR_INVALID_ARG
+    cfg.d_latent, cfg.identity_latent = 7168, 0      # a latent layer needs W_down and W_up
+    assert _create_status(cfg, w) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_non_latent_workspace_has_no_latent_buffers():
+    """Without a latent the workspace holds no z, zq, y_lat or yq, so it is
+    smaller than that of the latent layer of the same model width."""
+    lat = _lib.MoeLayerConfig(7168, 7168, 384, 8, 1, 2048, 2048, 8192, 0, 1, 0)
+    non = _lib.MoeLayerConfig(7168, 7168, 384, 8, 1, 2048, 2048, 8192, 1, 1, 0)
+    for T in (1, 64, 8192):
+        assert _lib.moe_layer_workspace_size(non, T) < _lib.moe_layer_workspace_size(lat, T)

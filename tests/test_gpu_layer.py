@@ -216,3 +216,13 @@ def test_repeated_decode_forwards_bitwise_equal():
         assert np.array_equal(y, y0)
         assert np.array_equal(t["z"], t0["z"])
     lay.close()
+
+
+def test_no_shared_expert_latent_layers():
+    """n_shared = 0 on the latent layer: the output GEMM is the up-projection
+    alone (MX map and higher-precision map, few and many tokens)."""
+    import dataclasses
+    for name in ("tiny", "tiny_bf16"):
+        for T in (40, 300):
+            cfg = dataclasses.replace(synth.config(name, T=T), n_shared=0)
+            _layer_case(cfg, check_codes=False)
