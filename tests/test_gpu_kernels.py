@@ -110,12 +110,9 @@ def test_single_mfma_tile_matches_exact_product(LY):
     got, ref, bound, a, b = _gemm_case(LY, rng, 16, 16, 128)
     exact = mx.mx_matmul_exact(a.codes, a.scales, "e4m3", b.codes, b.scales, "e2m1")
     assert np.array_equal(ref, exact)
-    if not np.all(np.abs(got - ref) <= bound):
-        import os
-        os.makedirs("gpurun_out", exist_ok=True)
-        np.savez("gpurun_out/mfma_probe.npz", a_codes=a.codes, a_scales=a.scales, b_codes=b.codes,
-                 b_scales=b.scales, got=got, ref=ref)
-    assert np.all(np.abs(got - ref) <= bound), f"max err {np.abs(got - ref).max()}"
+    bad = np.argwhere(np.abs(got - ref) > bound)
+    assert len(bad) == 0, (f"{len(bad)} outputs outside the bound, first at {bad[:4].tolist()}; "
+                           f"max err {np.abs(got - ref).max()}")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (17, 80, 256), (64, 256, 512), (300, 384, 1024),
