@@ -9,15 +9,21 @@
 // L2 -> LDS traffic per MFMA.  A 128 x 512 tile moves 48 KB of codes per
 // 128-deep K-step for 16.8 MFLOP -- half the bytes per flop of a 128 x 128
 // tile -- and a 3 x 50.5 KB ring keeps two K-steps (64 KB of weights) in
-// flight per CU.  Eight waves (two per SIMD) compute 64 x 128 each, so one
-// wave's LDS reads and barrier wait overlap the other's MFMAs; every wave
-// reads 16 KB of LDS per 32 MFMAs (about 63 B/clk/CU at the MFMA rate, plus
-// 25 B/clk of staging writes, inside the ~117 B/clk LDS read rate).
+// flight per CU.  Eight waves (two per SIMD) compute 64 x 128 each; every
+// wave reads 16 KB of LDS per 32 MFMAs (about 63 B/clk/CU at the MFMA rate,
+// plus 25 B/clk of staging writes, inside the ~117 B/clk LDS read rate).
+//
+// Ping-pong.  A K-step is a read half (LDS -> registers, then the next loads)
+// and an MFMA half, each opened by a workgroup barrier, and the two waves of
+// a SIMD (one from each M-half of the tile) run half a step apart: while one
+// issues its 32 MFMAs the other reads its fragments, so the matrix core of
+// the SIMD is fed across every barrier instead of idling while both waves
+// wait for the barrier and then for LDS.
 //
 // Loads are direct global -> LDS (inline assembly, waits placed by hand; see
 // lds_pipe.hpp): per K-step each wave issues 2 A-code, 4 B-code, one A-scale
-// (16 lanes) and one B-scale load, and the stage for step ks+2 is issued
-// right after the barrier of step ks.
+// (16 lanes) and one B-scale load, and the stage for step ks+2 is issued at
+// the end of the read half of step ks.
 //
 // The weights are stored in fragment order (kernels.hpp): one 16 x 128 block
 // of codes is 1 KB contiguous in MFMA lane order, so each B load instruction
@@ -155,10 +161,8 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
       gbs = (up ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + 4 * (int64_t)c;
     }
     const int64_t bs_kstride = 4 * (int64_t)p.N;  // bytes between K-steps of the B scales
-    // Stage loads in four parts (2 A-code; 2 B-code; 2 B-code; A-scale and
-    // B-scale), issued between the MFMA groups of the step before, so that
-    // the direct loads queue behind MFMAs instead of stalling the waves in
-    // one burst after the barrier.
+    // A stage's loads of one wave, in four parts: 2 A-code; 2 B-code; 2
+    // B-code; A-scale and B-scale.
     auto issue_part = [&](int ks, int part) {
       uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
       if (part == 0) {
@@ -189,12 +193,29 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
       return av;
     };
 
-    // One K-step; with_issue (a compile-time tag) also issues the stage two
-    // steps ahead, so the steady-state loop has no branch between its MFMA
-    // groups and its loads.
-    auto step = [&](int ks, auto with_issue) {
-      if (ks + 1 < ksteps) wait_vmcnt<WD_LOADS>(); else wait_vmcnt<0>();
+    // One K-step in two halves, each opened by a barrier: a read half (the
+    // step's scales and all A and B fragments from LDS into registers, then
+    // the loads of the stage two steps ahead) and an MFMA half.  The tile's
+    // two M-halves (waves 0-3 and 4-7: one wave of each per SIMD) run half a
+    // step apart -- the second half passes one extra barrier before its first
+    // step, the first half one after its last -- so on every SIMD one wave
+    // issues MFMAs while the other reads LDS, and the barriers no longer stop
+    // both waves of a SIMD at once.
+    // Hazards.  Stage ks is complete in every wave before the barrier that
+    // opens the first half's read of step ks: the first half waits for its
+    // loads at the top of the step, the second half at the end of its read
+    // half of step ks - 1 (or before its extra barrier, for stage 0).  The
+    // loads of stage ks + 2 overwrite the buffer of step ks - 1; both halves
+    // have finished reading it by then, because barrier_lds drains a wave's
+    // LDS reads before it arrives.
+    const bool late = wm == 1;
+    auto step = [&](int ks) {
+      if (!late) {
+        if (ks + 1 < ksteps) wait_vmcnt<WD_LOADS>(); else wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
       barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
       const uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
       const int sh = 8 * g4;
       const uint4 asd =
@@ -205,49 +226,49 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
       for (int ni = 0; ni < 8; ++ni)
         bs_all[ni] = *reinterpret_cast<const uint32_t*>(buf + WD_OFF_BS + 4 * b_row(wn, ni, r16));
       v8i bf[8];
-      auto rd_b = [&](int ni) {
+#pragma unroll
+      for (int ni = 0; ni < 8; ++ni) {
         const int blk = b_row(wn, ni, 0) >> 4;
         const uint4 v = *reinterpret_cast<const uint4*>(buf + WD_OFF_B + 1024 * blk + 16 * lane);
         bf[ni][0] = (int)v.x; bf[ni][1] = (int)v.y; bf[ni][2] = (int)v.z; bf[ni][3] = (int)v.w;
         bf[ni][4] = 0; bf[ni][5] = 0; bf[ni][6] = 0; bf[ni][7] = 0;
-      };
-      // The first MFMAs wait only for half of the B fragments and A fragment
-      // 0: all eight waves read right after the barrier, so a smaller first
-      // batch shortens the time the matrix cores wait for LDS.
+      }
+      v8i av[4];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) rd_b(ni);
-      v8i av = rd_a(buf, 0);
+      for (int mi = 0; mi < 4; ++mi) av[mi] = rd_a(buf, mi);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 2 < ksteps) issue(ks + 2);
+      if (late) {  // stage ks + 1, leaving stage ks + 2 in flight
+        if (ks + 2 < ksteps) wait_vmcnt<WD_LOADS>(); else wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ni = 4; ni < 8; ++ni) rd_b(ni);
-#pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        v8i an;
-        if (mi < 3) an = rd_a(buf, mi + 1);  // next fragment's read overlaps these MFMAs
         const int sa = (int)(as_all[mi] >> sh);
         if (mi < mvalid) {  // fragments wholly past the group's last row are skipped
 #pragma unroll
           for (int ni = 0; ni < 8; ++ni) {
             const int sb = (int)(bs_all[ni] >> sh);
-            if (SWI) acc[mi][ni & 3][ni >> 2] = mfma_f8f4(av, bf[ni], acc[mi][ni & 3][ni >> 2], sa, sb);
-            else acc[mi][ni][0] = mfma_f8f4(av, bf[ni], acc[mi][ni][0], sa, sb);
+            if (SWI) acc[mi][ni & 3][ni >> 2] = mfma_f8f4(av[mi], bf[ni], acc[mi][ni & 3][ni >> 2], sa, sb);
+            else acc[mi][ni][0] = mfma_f8f4(av[mi], bf[ni], acc[mi][ni][0], sa, sb);
           }
         }
-        if constexpr (decltype(with_issue)::value) {
-          __builtin_amdgcn_sched_barrier(0);
-          issue_part(ks + 2, mi);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (mi < 3) av = an;
       }
     };
 
+    // Every wave passes 2 * ksteps + 2 barriers per segment (the segment's
+    // first, two per step, and its half's extra one), so the counts match.
     __syncthreads();  // the previous segment's stages are no longer read
     issue(0);
     if (ksteps > 1) issue(1);
-    int ks = 0;
-    for (; ks + 2 < ksteps; ++ks) step(ks, std::true_type{});
-    for (; ks < ksteps; ++ks) step(ks, std::false_type{});
+    if (late) {
+      if (ksteps > 1) wait_vmcnt<WD_LOADS>(); else wait_vmcnt<0>();
+      barrier_lds();
+    }
+    for (int ks = 0; ks < ksteps; ++ks) step(ks);
+    if (!late) barrier_lds();
   }
 
   Tile t;
