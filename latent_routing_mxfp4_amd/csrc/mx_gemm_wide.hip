@@ -360,36 +360,60 @@ __global__ void __launch_bounds__(512) bf16_gemm_wide_kernel(const GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) gl_lds16(gb[i] + 128 * ks, buf + WB_OFF_B + 1024 * (4 * wave + i));
     };
-    // A new segment refills buffers the previous one's last K-steps were read
-    // from: every wave must be past those reads first.
+    // Ping-pong as in the MX kernel: each K-step is a read half (all of the
+    // step's fragments into registers, then the loads two steps ahead) and
+    // an MFMA half, the tile's two M-halves half a step apart (the second
+    // half passes an extra barrier before its first step, the first half one
+    // after its last).  A new segment refills buffers the previous one's
+    // last K-steps were read from, so every wave passes a barrier first.
+    const bool late = wm == 1;
     if (si > 0) barrier_lds();
     issue(0);
     if (ksteps > 1) issue(1);
-    for (int ks = 0; ks < ksteps; ++ks) {
-      if (ks + 1 < ksteps) wait_vmcnt<WB_LOADS>(); else wait_vmcnt<0>();
+    if (late) {
+      if (ksteps > 1) wait_vmcnt<WB_LOADS>(); else wait_vmcnt<0>();
       barrier_lds();
-      if (ks + 2 < ksteps) issue(ks + 2);
+    }
+    for (int ks = 0; ks < ksteps; ++ks) {
+      if (!late) {
+        if (ks + 1 < ksteps) wait_vmcnt<WB_LOADS>(); else wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
       const uint8_t* buf = lds + (ks % WB_NBUF) * WB_STAGE;
+      bf16x8_t bfr[2][4], afr[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        bf16x8_t bfr[4];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           const int trow = wn * 64 + 16 * ni + r16;
-          bfr[ni] = as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + WB_OFF_B + trow * 128 +
-                                                               (((4 * u + g4) ^ (trow & 7)) << 4)));
+          bfr[u][ni] = as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + WB_OFF_B + trow * 128 +
+                                                                  (((4 * u + g4) ^ (trow & 7)) << 4)));
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
           const int r = wm * 64 + 16 * mi + r16;
-          const bf16x8_t av =
-              as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + r * 128 + (((4 * u + g4) ^ (r & 7)) << 4)));
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bfr[ni], acc[mi][ni][0], 0, 0, 0);
+          afr[u][mi] = as_bf16x8_w(*reinterpret_cast<const uint4*>(buf + r * 128 + (((4 * u + g4) ^ (r & 7)) << 4)));
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 2 < ksteps) issue(ks + 2);
+      if (late) {  // stage ks + 1, leaving stage ks + 2 in flight
+        if (ks + 2 < ksteps) wait_vmcnt<WB_LOADS>(); else wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[u][mi], bfr[u][ni], acc[mi][ni][0], 0, 0, 0);
     }
+    if (!late) barrier_lds();
   }
   Tile t;
   t.g = g;
