@@ -48,12 +48,18 @@ __device__ __forceinline__ bool decode_lds_tile(const GemmArgs& p, int ncol, int
   const int lin = (blockIdx.x & 7) * per + slot;
   if (lin >= total) return false;
   if (routed) {
-    int lo = 0, hi = p.G;  // mtile_start[lo]*n_nt <= lin < mtile_start[hi]*n_nt
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.mtile_start[mid] * n_nt <= lin) lo = mid; else hi = mid;
+    if (p.mtile_group) {
+      // lin = mtile_start[g]*n_nt + nt*mte + mt with nt*mte + mt < n_nt*mte, so
+      // lin / n_nt is one of the group's M-tiles.
+      g = p.mtile_group[lin / n_nt];
+    } else {
+      int lo = 0, hi = p.G;  // mtile_start[lo]*n_nt <= lin < mtile_start[hi]*n_nt
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.mtile_start[mid] * n_nt <= lin) lo = mid; else hi = mid;
+      }
+      g = lo;
     }
-    g = lo;
     const int mte = p.mtile_start[g + 1] - p.mtile_start[g];
     const int local = lin - p.mtile_start[g] * n_nt;
     nt = local / mte;

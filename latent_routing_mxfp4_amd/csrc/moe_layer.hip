@@ -44,7 +44,7 @@ constexpr int64_t kFewRows = 256;  // decode-shaped batches: weight-streaming ke
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, wrpl, ids, gates, dscr, counts, offsets, ms0, ms1, rop, por, hq, hqs, ye,
+  size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, wrpl, ids, gates, dscr, counts, offsets, ms0, ms1, tg1, rop, por, hq, hqs, ye,
       ylat, yq, yqs, hs, hss, xb, yb, hb, dpart, total;
 };
 
@@ -142,6 +142,10 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   p.offsets = take((E + 1) * 4);
   p.ms0 = take((E + 1) * 4);
   p.ms1 = take((E + 1) * 4);
+  {  // group of each M-tile of the LDS-staged kernels: at most P / mt + min(P, E) tiles
+    const size_t mt = (size_t)moe::gemm_mtile(moe::GEMM_WIDE);
+    p.tg1 = take((P / mt + (P < (size_t)E ? P : (size_t)E) + 1) * 4);
+  }
   p.rop = take(P * 4);
   p.por = take(P * 4);
   p.hq = take(P * F);
@@ -282,6 +286,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   int32_t* offsets = at<int32_t>(ws, pl.offsets);
   int32_t* ms0 = at<int32_t>(ws, pl.ms0);
   int32_t* ms1 = at<int32_t>(ws, pl.ms1);
+  int32_t* tg1 = at<int32_t>(ws, pl.tg1);
   int32_t* rop = at<int32_t>(ws, pl.rop);
   int32_t* por = at<int32_t>(ws, pl.por);
   uint8_t* hq = at<uint8_t>(ws, pl.hq);
@@ -379,7 +384,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
   MOE_HIP(mark(MOE_EV_TOPK));
 
   // 5. dispatch
-  MOE_HIP(moe::launch_dispatch(ids, T, E, k, dscr, counts, offsets, rop, por, mt_small, ms0, mt_big, ms1, s));
+  MOE_HIP(moe::launch_dispatch(ids, T, E, k, dscr, counts, offsets, rop, por, mt_small, ms0, mt_big, ms1, tg1, s));
   MOE_HIP(mark(MOE_EV_DISPATCH));
 
   const int mt_r = moe::gemm_mtile(routed_shape);
@@ -402,6 +407,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
                 L};
     a.offsets = offsets;
     a.mtile_start = ms_r;
+    a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? nullptr : tg1;
     a.G = E;
     a.N = F;
     a.gather = por;
@@ -423,6 +429,7 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
                 (int64_t)L * F / 32, F};
     a.offsets = offsets;
     a.mtile_start = ms_r;
+    a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? nullptr : tg1;
     a.G = E;
     a.N = L;
     a.c = ye;
