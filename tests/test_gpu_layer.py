@@ -111,6 +111,20 @@ def test_mid_layer_parity():
     _layer_case(synth.config("mid"))
 
 
+def test_mid_concentrated_routing():
+    """A selection bias of +10 on experts 0..k-2: every token picks those seven
+    (2048 rows each: 16 full 128-row M-tiles per expert in the prefill GEMMs),
+    and its last slot goes to one of the other 121 experts by score (about 17
+    rows each, a single part-filled tile); the M-tile-to-expert table, the
+    permutation and the ragged tails all against the oracle."""
+    cfg = synth.config("mid", T=2048)
+    b = np.zeros(cfg.n_routed, np.float32)
+    b[: cfg.top_k - 1] = 10.0
+    rep, y, tr, o = _layer_case(cfg, selection_bias=b, check_codes=False)
+    ids = tr["ids"]
+    assert np.all(np.sort(ids, axis=1)[:, : cfg.top_k - 1] == np.arange(cfg.top_k - 1)[None, :])
+
+
 def test_tiny_many_experts_lds_topk():
     """More than 1024 routed experts: top-k keeps its keys in LDS instead of
     registers (the K3 router has 896)."""
