@@ -15,6 +15,8 @@ Modules
            SwiGLU experts, gate-weighted combine, up-projection, shared experts;
            plus a brute-force "all experts, then mask" variant.
 ``weights``oracle-side quantisation of the seeded synthetic weights.
+``balance``Quantile Balancing of the selection bias (a reading of the pages;
+           its pins check the reading's consequences, not printed values).
 
 Pins (what the oracle is checked against; see ``tests/test_oracle_*.py``)
 -------------------------------------------------------------------------
