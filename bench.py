@@ -204,6 +204,38 @@ def k2_report(steps, warmup, hip, say):
             "stage_ms": kst, "step_events_ms": kwork["step_events_ms"]}
 
 
+def qb_report(steps, warmup, say):
+    """Quantile Balancing of the selection bias at the K3 prefill shape (16384
+    tokens x 896 experts, top-16) on seeded N(0, 1) logits: time per update and
+    the rate at which it consumes the logits (read once by the threshold pass
+    and once by the margin pass; the per-expert selection reads the transposed
+    margins eight times, mostly from L2).  A report line beside the headline."""
+    import numpy as np
+    import torch
+
+    from latent_routing_mxfp4_amd import layer as LY
+
+    T, E, k = 16384, 896, 16
+    rng = np.random.default_rng(1004)
+    lg = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).cuda()
+    bias = torch.zeros(E, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(bias)
+    ws = torch.empty(LY._lib.moe_quantile_balance_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
+    for _ in range(max(warmup, 1)):
+        LY.quantile_balance(lg, bias, k, 0.5, out=out, workspace=ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record()
+        LY.quantile_balance(lg, bias, k, 0.5, out=out, workspace=ws)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))[steps // 2]
+    say(f"quantile balance at T={T}, E={E}, k={k}: {ms:.3f} ms per update")
+    logit_bytes = T * E * 4
+    return {"workload": f"quantile balance: T={T}, E={E}, top-{k}", "ms_per_update": ms,
+            "logits_gbs": 2 * logit_bytes / (ms / 1e3) / 1e9, "logits_bytes": logit_bytes}
+
+
 def cpu_baseline(name, n_tokens, say):
     """The oracle, as it stands, on the first n_tokens of the workload."""
     import numpy as np
@@ -371,6 +403,8 @@ def main():
                     help="steps of the non-latent K2-like 8192-token layer reported under 'k2' (0: skip)")
     ap.add_argument("--bf16-steps", type=int, default=5,
                     help="steps of the higher-precision map (bf16 dense weights) reported under 'bf16_map' (0: skip)")
+    ap.add_argument("--qb-steps", type=int, default=10,
+                    help="Quantile Balancing updates at the K3 prefill shape reported under 'quantile_balance' (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2)
@@ -492,6 +526,8 @@ def main():
     torch.cuda.empty_cache()
     if args.k2_steps > 0 and args.workload == "k3_prefill":
         out["k2"] = k2_report(args.k2_steps, args.warmup, hip, say)
+    if args.qb_steps > 0:
+        out["quantile_balance"] = qb_report(args.qb_steps, args.warmup, say)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_tokens, say)
     print(json.dumps(out), flush=True)

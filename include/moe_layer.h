@@ -247,6 +247,27 @@ int moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t G, 
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
 int moe_round_bf16(const float* in, int64_t n, uint16_t* out, void* stream);
 
+/* Quantile Balancing of the selection bias from one batch of router logits.
+ * The pages ("Kimi K3 and the New Open-Weights Moat: Inference Efficiency",
+ * "How the router picks 16 of 896", Fig. 2 and the paragraph after it; "What
+ * Kimi K3 asks of the hardware", "Width: 896 experts and the interconnect")
+ * say only that each expert's bias is updated from the distribution of its
+ * score margins so that its routed count approaches a target load.  Reading:
+ * key = sigmoid(logit) + bias; an expert's margin on a token is its key minus
+ * the k-th largest key among the token's other experts; n = round(T*k/E)
+ * clamped to [1, T-1]; Q[e] = midpoint of expert e's n-th and (n+1)-th
+ * largest margins over the batch; bias_out = bias_in - eta * Q.
+ * logits: device fp32 [T][E] (the router's logits, before the sigmoid);
+ * bias_in / bias_out: device fp32 [E] (may be the same buffer); quantile_out:
+ * device fp32 [E] or NULL; 2 <= T, 1 <= k < E <= 4096, 0 < eta <= 1.
+ * ws: device buffer of moe_quantile_balance_workspace_bytes(T, E) bytes,
+ * 16-byte aligned, owned by the caller.  Asynchronous on `stream`.
+ * Errors: MOE_ERR_INVALID_ARG (sizes, eta, null or misaligned pointers),
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+size_t moe_quantile_balance_workspace_bytes(int32_t T, int32_t E);
+int moe_quantile_balance(const float* logits, int32_t T, int32_t E, int32_t k, const float* bias_in, float eta,
+                         float* bias_out, float* quantile_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Dense MX GEMM c[M][N] = deq(a) deq(b)^T in fp32, a = E4M3 [M][K] (row-major),
  * b = E2M1 [N][K] in fragment order, N a positive multiple of 16, K of 128.
  * This is the block-scaled matrix-core kernel the layer's projections run on,

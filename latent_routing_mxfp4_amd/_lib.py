@@ -31,6 +31,8 @@ EXPORTED = (
     "moe_mx_quantize_weights",
     "moe_mx_pack_weights",
     "moe_mx_gemm",
+    "moe_quantile_balance_workspace_bytes",
+    "moe_quantile_balance",
 )
 
 
@@ -126,6 +128,10 @@ def load() -> ctypes.CDLL:
     lib.moe_mx_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
     lib.moe_round_bf16.restype = ctypes.c_int
     lib.moe_round_bf16.argtypes = [vp, i64, vp, vp]
+    lib.moe_quantile_balance_workspace_bytes.restype = sz
+    lib.moe_quantile_balance_workspace_bytes.argtypes = [i32, i32]
+    lib.moe_quantile_balance.restype = ctypes.c_int
+    lib.moe_quantile_balance.argtypes = [vp, i32, i32, i32, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -184,3 +190,13 @@ def moe_mx_gemm(a_codes: int, a_scales: int, b_codes: int, b_scales: int, M: int
 
 def moe_round_bf16(src: int, n: int, out: int, stream: int = 0) -> None:
     _check(load().moe_round_bf16(src, int(n), out, stream), "moe_round_bf16")
+
+
+def moe_quantile_balance_workspace_bytes(T: int, E: int) -> int:
+    return int(load().moe_quantile_balance_workspace_bytes(int(T), int(E)))
+
+
+def moe_quantile_balance(logits: int, T: int, E: int, k: int, bias_in: int, eta: float, bias_out: int,
+                         quantile_out: int, ws: int, ws_bytes: int, stream: int = 0) -> None:
+    _check(load().moe_quantile_balance(logits, int(T), int(E), int(k), bias_in, float(eta), bias_out,
+                                       quantile_out, ws, int(ws_bytes), stream), "moe_quantile_balance")

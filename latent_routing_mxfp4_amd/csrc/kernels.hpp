@@ -162,6 +162,17 @@ hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, int shape, hipStre
 int gemm_wide_mtile();
 hipError_t launch_mx_gemm_wide(const GemmArgs& args, int epilogue, hipStream_t s);
 
+// ---- Quantile Balancing (balance.hip) ----------------------------------------
+// New selection bias from one batch of router logits [T][E] (sigmoid keys):
+// b_out = b_in - eta * Q, Q[e] the midpoint of expert e's n-th and (n+1)-th
+// largest score margins, n = quantile_balance_target(T, E, k).  ws holds
+// quantile_balance_workspace_floats(T, E) floats; q_out may be null; b_out may
+// be b_in.  Requires 2 <= T, 1 <= k < E <= 4096.
+size_t quantile_balance_workspace_floats(int T, int E);
+int quantile_balance_target(int T, int E, int k);
+hipError_t launch_quantile_balance(const float* logits, int T, int E, int k, const float* bias_in, float eta,
+                                   float* bias_out, float* q_out, float* ws, hipStream_t s);
+
 // ---- Combine (combine.hip) --------------------------------------------------
 // y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then
 // yq = MXFP8(y_lat) per row and/or yb = bf16(y_lat); any output may be null.

@@ -637,6 +637,26 @@ int moe_round_bf16(const float* in, int64_t n, uint16_t* out, void* stream) {
   return MOE_OK;
 }
 
+size_t moe_quantile_balance_workspace_bytes(int32_t T, int32_t E) {
+  if (T < 0 || E < 0) return 0;
+  return moe::quantile_balance_workspace_floats(T, E) * sizeof(float);
+}
+
+int moe_quantile_balance(const float* logits, int32_t T, int32_t E, int32_t k, const float* bias_in, float eta,
+                         float* bias_out, float* quantile_out, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 2 || E < 2 || E > 4096 || k < 1 || k >= E) return MOE_ERR_INVALID_ARG;
+  if (!(eta > 0.0f && eta <= 1.0f)) return MOE_ERR_INVALID_ARG;
+  if (!logits || !bias_in || !bias_out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(bias_in, 4) || !aligned(bias_out, 4) ||
+      (quantile_out && !aligned(quantile_out, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 16) || ws_bytes < moe_quantile_balance_workspace_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  if (moe::launch_quantile_balance(logits, T, E, k, bias_in, eta, bias_out, quantile_out,
+                                   static_cast<float*>(ws), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
                 int32_t M, int32_t N, int32_t K, float* c, void* stream) {
   if (M < 0 || N < 0 || N % 16 || K <= 0 || K % 128) return MOE_ERR_INVALID_ARG;

@@ -121,6 +121,25 @@ def mx_gemm(a_codes, a_scales, b_codes, b_scales) -> torch.Tensor:
     return c
 
 
+def quantile_balance(logits: torch.Tensor, bias: torch.Tensor, k: int, eta: float = 1.0,
+                     out: Optional[torch.Tensor] = None, quantiles: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One Quantile Balancing step (``moe_quantile_balance``): the new fp32
+    selection bias [E] from router logits [T][E] and the current bias.
+    ``out`` may be ``bias`` itself; ``quantiles`` ([E] fp32) receives Q."""
+    T, E = logits.shape
+    assert logits.dtype == torch.float32 and logits.is_contiguous() and bias.dtype == torch.float32
+    if out is None:
+        out = torch.empty_like(bias)
+    nbytes = _lib.moe_quantile_balance_workspace_bytes(T, E)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=logits.device)
+    _lib.moe_quantile_balance(logits.data_ptr(), T, E, int(k), bias.data_ptr(), float(eta), out.data_ptr(),
+                              0 if quantiles is None else quantiles.data_ptr(), workspace.data_ptr(), nbytes,
+                              _stream())
+    return out
+
+
 def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray], device="cuda",
                    extra: Optional[Dict[str, Optional[np.ndarray]]] = None, workers: int = 8,
                    progress: Optional[Callable[[int, int], None]] = None,

@@ -212,3 +212,25 @@ def test_non_latent_workspace_has_no_latent_buffers():
     non = _lib.MoeLayerConfig(7168, 7168, 384, 8, 1, 2048, 2048, 8192, 1, 1, 0)
     for T in (1, 64, 8192):
         assert _lib.moe_layer_workspace_size(non, T) < _lib.moe_layer_workspace_size(lat, T)
+
+
+def test_quantile_balance_rejects_bad_arguments_before_any_launch():
+    lib = _lib.load()
+    T, E, k = 16384, 896, 16
+    need = lib.moe_quantile_balance_workspace_bytes(T, E)
+    assert need == 4 * (2 * T + E * T)
+    assert lib.moe_quantile_balance_workspace_bytes(-1, E) == 0
+
+    def call(T=T, E=E, k=k, eta=0.5, ws=FAKE, ws_bytes=need, logits=FAKE, bias=FAKE, out=FAKE):
+        return lib.moe_quantile_balance(logits, T, E, k, bias, eta, out, None, ws, ws_bytes, None)
+
+    bad = _lib.MOE_ERR_INVALID_ARG
+    assert call(T=1) == bad
+    assert call(k=0) == bad and call(k=E) == bad
+    assert call(E=4097, k=16) == bad
+    assert call(eta=0.0) == bad and call(eta=1.5) == bad and call(eta=float("nan")) == bad
+    assert call(logits=None) == bad and call(bias=None) == bad and call(out=None) == bad
+    assert call(logits=FAKE + 2) == bad
+    assert call(ws=None) == _lib.MOE_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == _lib.MOE_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == _lib.MOE_ERR_WORKSPACE
