@@ -268,6 +268,15 @@ size_t moe_quantile_balance_workspace_bytes(int32_t T, int32_t E);
 int moe_quantile_balance(const float* logits, int32_t T, int32_t E, int32_t k, const float* bias_in, float eta,
                          float* bias_out, float* quantile_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement, not part of the layer: the block-scaled FP8 x FP4 matrix-core
+ * rate of this GPU.  `workgroups` x 4 waves each issue 8 * iters independent
+ * 16x16x128 E4M3 x E2M1 MFMAs (2 * 16 * 16 * 128 flops each) on operands of
+ * 1.0; out (device fp32 [workgroups * 4]) receives one checksum per wave
+ * (a sum of accumulators, not meant to be read).  Time it with
+ * events on `stream`.  1 <= iters <= 2^24, 1 <= workgroups <= 2^20.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
+int moe_mfma_rate_probe(int32_t iters, int32_t workgroups, float* out, void* stream);
+
 /* Dense MX GEMM c[M][N] = deq(a) deq(b)^T in fp32, a = E4M3 [M][K] (row-major),
  * b = E2M1 [N][K] in fragment order, N a positive multiple of 16, K of 128.
  * This is the block-scaled matrix-core kernel the layer's projections run on,

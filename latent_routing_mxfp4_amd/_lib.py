@@ -33,6 +33,7 @@ EXPORTED = (
     "moe_mx_gemm",
     "moe_quantile_balance_workspace_bytes",
     "moe_quantile_balance",
+    "moe_mfma_rate_probe",
 )
 
 
@@ -130,6 +131,8 @@ def load() -> ctypes.CDLL:
     lib.moe_round_bf16.argtypes = [vp, i64, vp, vp]
     lib.moe_quantile_balance_workspace_bytes.restype = sz
     lib.moe_quantile_balance_workspace_bytes.argtypes = [i32, i32]
+    lib.moe_mfma_rate_probe.restype = ctypes.c_int
+    lib.moe_mfma_rate_probe.argtypes = [i32, i32, vp, vp]
     lib.moe_quantile_balance.restype = ctypes.c_int
     lib.moe_quantile_balance.argtypes = [vp, i32, i32, i32, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     _lib = lib
@@ -200,3 +203,7 @@ def moe_quantile_balance(logits: int, T: int, E: int, k: int, bias_in: int, eta:
                          quantile_out: int, ws: int, ws_bytes: int, stream: int = 0) -> None:
     _check(load().moe_quantile_balance(logits, int(T), int(E), int(k), bias_in, float(eta), bias_out,
                                        quantile_out, ws, int(ws_bytes), stream), "moe_quantile_balance")
+
+
+def moe_mfma_rate_probe(iters: int, workgroups: int, out: int, stream: int = 0) -> None:
+    _check(load().moe_mfma_rate_probe(int(iters), int(workgroups), out, stream), "moe_mfma_rate_probe")

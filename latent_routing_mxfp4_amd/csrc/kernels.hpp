@@ -173,6 +173,11 @@ int quantile_balance_target(int T, int E, int k);
 hipError_t launch_quantile_balance(const float* logits, int T, int E, int k, const float* bias_in, float eta,
                                    float* bias_out, float* q_out, float* ws, hipStream_t s);
 
+// ---- Matrix-core rate probe (mfma_rate.hip) ---------------------------------
+// workgroups x 4 waves, each issuing 8 * iters independent FP8 x FP4 MFMAs of
+// 16x16x128; out[workgroups * 4] receives one checksum per wave.
+hipError_t launch_mfma_rate(int iters, int workgroups, float* out, hipStream_t s);
+
 // ---- Combine (combine.hip) --------------------------------------------------
 // y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then
 // yq = MXFP8(y_lat) per row and/or yb = bf16(y_lat); any output may be null.

@@ -657,6 +657,14 @@ int moe_quantile_balance(const float* logits, int32_t T, int32_t E, int32_t k, c
   return MOE_OK;
 }
 
+int moe_mfma_rate_probe(int32_t iters, int32_t workgroups, float* out, void* stream) {
+  if (iters < 1 || iters > (1 << 24) || workgroups < 1 || workgroups > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  if (!out || !aligned(out, 4)) return MOE_ERR_INVALID_ARG;
+  if (moe::launch_mfma_rate(iters, workgroups, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
                 int32_t M, int32_t N, int32_t K, float* c, void* stream) {
   if (M < 0 || N < 0 || N % 16 || K <= 0 || K % 128) return MOE_ERR_INVALID_ARG;

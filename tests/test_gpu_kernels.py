@@ -121,3 +121,15 @@ def test_mx_gemm_shapes(LY, M, N, K):
     rng = np.random.default_rng(M * 7919 + N * 31 + K)
     got, ref, bound, _, _ = _gemm_case(LY, rng, M, N, K)
     assert np.all(np.abs(got - ref) <= bound), f"max err/bound {np.max(np.abs(got - ref) / bound)}"
+
+
+def test_mfma_rate_probe_checksum(LY):
+    """The matrix-core rate probe really issues its MFMAs: every accumulator
+    element gains 128 (128 products of 1.0 x 1.0 at scale 1) per MFMA, so each
+    wave's checksum (8 accumulators x 4 values per lane, lane 0) is 4096 * iters."""
+    from latent_routing_mxfp4_amd import _lib
+    wg, iters = 8, 100
+    out = torch.zeros(wg * 4, dtype=torch.float32, device="cuda")
+    _lib.moe_mfma_rate_probe(iters, wg, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.all(out == 4096.0 * iters), out[:4]
