@@ -472,6 +472,8 @@ def main():
             "traffic": None if tp is None else tp["bytes"],
             "algorithmic_bytes": work["expert_up_bytes"]}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the same kernel against the matrix-core rate measured on this GPU just before
+    roof["frac_of_probe"] = roof["achieved"] / mfma_tflops
     out = {
         "metric": "LatentMoE layer tokens/s (K3 width); HBM GB/s decode, MFMA % prefill vs peak",
         "value": value,
