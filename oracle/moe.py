@@ -215,19 +215,16 @@ def dispatch(ids: np.ndarray, n_experts: int) -> Dispatch:
 # --------------------------------------------------------------------------- experts
 
 
-def swiglu_expert(aq, wg, wu, wd, decide=np.float32, full=False, pick=None, hfmt="e4m3"):
+def swiglu_expert(aq, wg, wu, wd, decide=np.float32, full=False, hfmt="e4m3"):
     """down(SiLU(gate a) * (up a)) with the hidden h re-encoded in ``hfmt``
     (MXFP8, or bfloat16 for a higher-precision expert).
 
-    Returns (y, h, hq), plus (g, u) when ``full``.  ``pick(g, u, h, hq)`` may
-    replace the codes of hq (see ``forward``'s ``resolve``).
+    Returns (y, h, hq), plus (g, u) when ``full``.
     """
     g = mm(aq, wg)
     u = mm(aq, wu)
     h = silu(g) * u
     hq = quant(h, hfmt, decide)
-    if pick is not None:
-        hq = pick(g, u, h, hq)
     if full:
         return mm(hq, wd), h, hq, g, u
     return mm(hq, wd), h, hq
@@ -260,17 +257,8 @@ class Trace:
 
 
 def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
-            expert_weights=None, ids_override=None, resolve=None) -> Trace:
-    """The whole layer.  ``expert_weights(e)`` may supply (wg, wu, wd) lazily.
-
-    ``resolve`` (tests only) is consulted at every MX re-quantisation of a
-    computed tensor -- ``zq(z, zq)``, ``hq(e, rows, a, wg, wu, wd, g, u, h, hq)``,
-    ``yq(y_lat, yq, routing, dispatch, ye_rows)``, ``hs(s, wg, wu, wd, g, u, h, hq)``
-    -- and returns the codes to continue with.  The arithmetic of every step
-    is unchanged; a test uses it to replay the layer along the admissible
-    choices another implementation made where a value sits within its proven
-    error of a rounding boundary.
-    """
+            expert_weights=None) -> Trace:
+    """The whole layer.  ``expert_weights(e)`` may supply (wg, wu, wd) lazily."""
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
     E = W.w_router.shape[0]
@@ -283,14 +271,9 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
     xq = quant(x, "bf16" if hp else "e4m3", decide)                 # step 1 (xb under the bf16 map)
     z = mm(xq, W.w_down) if latent else x.astype(np.float64)        # step 2 (latent only)
     r = route(z, W.w_router, top_k, W.logit_bias, W.selection_bias, decide, W.gating)   # steps 3-5
-    if ids_override is not None:
-        ids = np.asarray(ids_override, dtype=np.int32)
-        r = Routing(r.scores, r.sel, ids, winner_gates(r.scores, ids, W.gating), r.gap)
     disp = dispatch(r.ids, E)                                       # step 6
     if latent:
         zq = quant(z, "e4m3", decide)
-        if resolve is not None:
-            zq = resolve.zq(z, zq)
     else:
         zq = xq                                                     # the experts read xq
     sfmt = "bf16" if hp else "e4m3"                                 # shared hidden state, up-projection input
@@ -310,11 +293,7 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
             wg, wu, wd = W.w_gate_e[e], W.w_up_e[e], W.w_down_e[e]
         toks = disp.pair_of_row[lo:hi] // top_k
         a = zq[toks]
-        pick = None
-        if resolve is not None:
-            pick = (lambda g_, u_, h_, hq_, e=e, lo=lo, hi=hi, a=a, wg=wg, wu=wu, wd=wd:
-                    resolve.hq(e, (lo, hi), a, wg, wu, wd, g_, u_, h_, hq_))
-        ye, h, hq, g, u = swiglu_expert(a, wg, wu, wd, decide, full=True, pick=pick)
+        ye, h, hq, g, u = swiglu_expert(a, wg, wu, wd, decide, full=True)
         if h_rows is None:
             F = h.shape[1]
             h_rows = np.zeros((P, F))
@@ -336,8 +315,6 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
 
     if latent:                                                      # step 9
         yq = quant(y_lat, sfmt, decide)
-        if resolve is not None:
-            yq = resolve.yq(y_lat, yq, r, disp, ye_rows)
         y_up = mm(yq, W.w_up)
     else:
         yq, y_up = None, y_lat.copy()
@@ -345,12 +322,8 @@ def forward(x: np.ndarray, W: LayerWeights, top_k: int, decide=np.float32,
     y = y_up.copy()                                                 # step 10
     hs_l, hsq_l, ys_l, gs_l, us_l = [], [], [], [], []
     for s in range(len(W.w_gate_s)):
-        pick = None
-        if resolve is not None:
-            pick = (lambda g_, u_, h_, hq_, s=s: resolve.hs(s, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s],
-                                                              g_, u_, h_, hq_))
         ys, hs, hsq, gs, us = swiglu_expert(xq, W.w_gate_s[s], W.w_up_s[s], W.w_down_s[s], decide, full=True,
-                                            pick=pick, hfmt=sfmt)
+                                            hfmt=sfmt)
         y += ys
         hs_l.append(hs)
         gs_l.append(gs)

@@ -21,7 +21,8 @@ def gpu_weights(cfg, selection_bias=None, workers=8):
     shape = LY.LayerShape.of(cfg)
     extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg),
              "selection_bias": selection_bias}
-    return shape, LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra, workers=workers)
+    return shape, LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra, workers=workers,
+                                    progress=lambda j, n: say(f"    {j} of {n} weight matrices encoded"))
 
 
 def gpu_layer(cfg, max_tokens=None, selection_bias=None, weights=None):
@@ -69,8 +70,24 @@ def run_traced_tokens(layer, x_np: np.ndarray, tokens):
     for n in ("hs", "hs_codes", "hs_scales", "hs_bf16"):
         if n in tr:
             sub[n] = to_np(tr[n][:, tok])
-    full = {n: to_np(tr[n]) for n in ("ids", "gates", "counts", "offsets", "pair_of_row", "row_of_pair")}
+    full = {n: to_np(tr[n]) for n in ("ids", "gates", "counts", "offsets", "pair_of_row", "row_of_pair", "z",
+                                      "zq_codes", "zq_scales", "xq_codes", "xq_scales", "xb") if n in tr}
     ysub = to_np(y[tok])
     del tr, y, x
     torch.cuda.empty_cache()
     return ysub, sub, full
+
+
+def token_subset(tr: dict, tokens, k: int) -> dict:
+    """From a whole-batch numpy trace: the sampled tokens' per-token rows, the
+    per-row (sorted) rows of their k pairs in (token, slot) order, and their
+    shared hidden states -- the layout ``tests.parity.check_tokens`` takes."""
+    tok = np.asarray(tokens, np.int64)
+    pairs = (tok[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    rows = np.asarray(tr["row_of_pair"], np.int64)[pairs]
+    sub = {n: tr[n][tok] for n in PER_TOKEN if n in tr}
+    sub.update({n: tr[n][rows] for n in PER_ROW})
+    for n in ("hs", "hs_codes", "hs_scales", "hs_bf16"):
+        if n in tr:
+            sub[n] = tr[n][:, tok]
+    return sub

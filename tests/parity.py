@@ -4,46 +4,56 @@ What is compared
 ----------------
 1. MX codes of the inputs (x) and weights: bit-exact.
 2. The latent z (bf16 matrix cores on exactly decoded operands): within the
-   fp32 accumulation bound K * 2^-24 * ||a_row|| * ||b_row||.
-3. Expert ids: the same set per token unless the oracle's gap between the k-th
-   and (k+1)-th selection key is below 1e-6 (a flagged near-tie, where the GPU's
-   set must still be a valid top-k within 1e-6); gates within max(1e-6, the
-   error the z bound propagates through the fp32 router).
-4. Dispatch: counts, offsets and permutation equal the stable sort of the
+   fp32 accumulation bound K * 2^-24 * sum |a_i b_i|.
+3. Re-quantisation of every computed tensor, bound-free: the oracle's own
+   quantiser applied to the GPU's fp32 z, h, y_lat and shared hidden states
+   reproduces the GPU's MXFP8 codes and scales (or, under the higher-precision
+   map, its bfloat16 roundings) bit for bit.  Against the oracle's own
+   (unconditioned) zq, every differing code must lie in a block that the z
+   bound leaves ambiguous; those are counted.
+4. Expert ids: the same set per token unless the oracle's gap between the
+   k-th and (k+1)-th selection key is below 1e-6 (a flagged near-tie, where
+   the GPU's set must still be a valid top-k within 1e-6); gates within
+   max(1e-6, the error the z bound propagates through the fp32 router).
+5. Dispatch: counts, offsets and permutation equal the stable sort of the
    GPU's ids, bit-exactly.
-5. Replay.  Every MXFP8 re-quantisation of a computed tensor (zq, hq, yq, hs;
-   under the higher-precision map the bfloat16 roundings of y_lat and hs)
-   turns any accumulation difference that straddles a rounding boundary into a
-   whole-step code change, and such changes cascade through the later stages:
-   even fp32-level noise in the oracle itself moves its own output by ~1e-3
-   (relative L2).  Where several codes are correct, the unique part is
-   compared and the rest is checked for validity: the oracle re-runs the layer
-   (same fp64 arithmetic) and, only in blocks where ITS OWN value lies within
-   the proven error bound of a boundary, continues with the GPU's block after
-   checking that block is an admissible quantisation of some value inside that
-   bound.  Against this replay every GPU code must then match bit-exactly and
-   every fp32 tensor (h, y_e, y_lat, y) must lie within its bound, and the
-   output must meet the tolerance (relative L2 <= 5e-3, max-abs <= 5e-2 rms).
-6. The unconditioned oracle output: relative L2 <= 5e-3 (its max-abs error is
-   reported).
+6. Replay (``tests/replay.py``): the oracle's steps re-run on the GPU's ids,
+   continuing with the GPU's block only where the oracle's own value is within
+   its proven error bound of a boundary and the GPU's block is an admissible
+   quantisation there (counted per tensor: ambiguous and adopted blocks).
+   Against the replay every GPU code matches bit-exactly, every fp32 tensor
+   (h, y_e, y_lat, y) lies within its bound, and the output meets relative
+   L2 <= 5e-3 and max-abs <= 5e-2 rms.
+7. The unconditioned oracle output, over every token whose ids equal the
+   oracle's (a flagged routing near-tie that the GPU resolved the other way
+   is checked against the replay alone): relative L2 <= 5e-3 and max-abs <=
+   5e-2 rms(output) per token.  A token above the max-abs limit is excused
+   only if its path took an admissible choice at a rounding boundary (a
+   quantiser near-tie: some re-quantised code differs from the oracle's own,
+   inside the bound); it is counted and held to the replay at that limit.  A
+   single such code step moves outputs by a few percent of rms: two correct
+   runs whose accumulations differ by 1e-6 relative already differ by ~0.03
+   rms at the mid size (tests/test_requant_cascade_cpu.py).
 
 Error bounds
 ------------
-* bf16 matrix cores: fp32 accumulation, K * 2^-24 * sum |a_i b_i| (bounded by
-  Cauchy-Schwarz).
-* block-scaled MX matrix cores (measured on gfx950 with single-instruction
-  probes): within one 32-element block the products are summed in a window
-  ending 14 bits below the block's largest product (truncated); block sums
-  accumulate in fp32.  Bound: 2^-9 * sum_b amax_a[b] * amax_b[b] (32 products,
-  each off by less than 2^-14 of the block's largest product) plus
-  (K/32 + 2) * 2^-24 * sum |a_i b_i|.
+* bf16 matrix cores: products exact in fp32, at most K roundings of 2^-24:
+  K * 2^-24 * sum |a_i b_i|.
+* block-scaled MX matrix cores: the instruction model pinned by
+  ``tests/test_gpu_mfma_model.py`` (``tests/mfma_model.py``): per-product
+  truncation inside groups of 8 (bounded without forming the products) plus
+  17 * 2^-24 * sum over instructions of (|partial sum| + sum |a_i b_i|).
 """
 
 from __future__ import annotations
 
+import threading
+
 import numpy as np
 
 from oracle import moe, mx
+from tests import mfma_model
+from tests.replay import replay_forward
 
 EPS32 = 2.0 ** -24
 NEAR_TIE = 1e-6
@@ -54,14 +64,15 @@ MAXABS_FRAC = 5e-2
 # --------------------------------------------------------------------------- bounds
 
 
-def row_norms(t: moe.MXTensor) -> np.ndarray:
-    return np.sqrt((t.deq() ** 2).sum(-1))
+def sum_abs(a, b) -> np.ndarray:
+    """sum_i |a_i b_i| for every output of deq(a) deq(b)^T."""
+    return np.abs(a.deq()) @ np.abs(b.deq()).T
 
 
-def gemm_bound(a: moe.MXTensor, b: moe.MXTensor, value: np.ndarray) -> np.ndarray:
+def gemm_bound(a, b, value: np.ndarray) -> np.ndarray:
     """fp32-accumulation bound (the bf16 matrix-core path)."""
     K = a.deq().shape[-1]
-    return K * EPS32 * np.outer(row_norms(a), row_norms(b)) + EPS32 * np.abs(value)
+    return K * EPS32 * sum_abs(a, b) + EPS32 * np.abs(value)
 
 
 def concat_gemm_bound(pairs, value: np.ndarray) -> np.ndarray:
@@ -69,27 +80,23 @@ def concat_gemm_bound(pairs, value: np.ndarray) -> np.ndarray:
     segments ``pairs`` = [(a, b), ...]: (total K) * 2^-24 * sum |a_i b_i| over
     every segment, plus the final rounding."""
     K = sum(a.deq().shape[-1] for a, _ in pairs)
-    sab = sum(np.outer(row_norms(a), row_norms(b)) for a, b in pairs)
-    return K * EPS32 * sab + EPS32 * np.abs(value)
+    return K * EPS32 * sum(sum_abs(a, b) for a, b in pairs) + EPS32 * np.abs(value)
+
+
+def mx_mfma_bound(a: moe.MXTensor, b: moe.MXTensor, value=None) -> np.ndarray:
+    """Bound for one block-scaled MX GEMM (module docstring)."""
+    return mfma_model.mfma_bound(a, b, value)
+
+
+def mx_concat_bound(pairs, value: np.ndarray, extra_roundings: int = 0) -> np.ndarray:
+    """Block-scaled GEMM over K = the concatenation of ``pairs``' K segments,
+    one accumulator throughout (the output projection)."""
+    return mfma_model.mfma_bound_segments(pairs, value, extra_roundings)
 
 
 def u16(a) -> np.ndarray:
     """bfloat16 patterns as uint16 (the trace holds them in int16 tensors)."""
     return np.ascontiguousarray(a).view(np.uint16)
-
-
-def block_amax(t: moe.MXTensor) -> np.ndarray:
-    v = np.abs(t.deq())
-    return v.reshape(*v.shape[:-1], -1, 32).max(-1)
-
-
-def mx_mfma_bound(a: moe.MXTensor, b: moe.MXTensor, value=None) -> np.ndarray:
-    """Bound for the block-scaled MFMA path (module docstring)."""
-    K = a.codes.shape[-1]
-    sab = np.abs(a.deq()) @ np.abs(b.deq()).T
-    win = 2.0 ** -9 * (block_amax(a) @ block_amax(b).T)
-    out = win + (K // 32 + 2) * EPS32 * sab
-    return out + EPS32 * (sab if value is None else np.abs(value))
 
 
 def swiglu_bound(g, u, bg, bu, h):
@@ -106,18 +113,134 @@ def swiglu_bound(g, u, bg, bu, h):
     return prop + (9 + 2 * (np.abs(g) + bg)) * EPS32 * (np.abs(h) + prop) + 1e-30
 
 
-def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray):
+def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray, rms=None):
     diff = y_gpu.astype(np.float64) - y_ref
     rel = np.linalg.norm(diff) / max(np.linalg.norm(y_ref), 1e-300)
-    rms = np.sqrt((y_ref ** 2).mean())
-    return float(rel), float(np.abs(diff).max()), float(rms)
+    if rms is None:
+        rms = np.sqrt((y_ref ** 2).mean())
+    return float(rel), float(np.abs(diff).max()) if diff.size else 0.0, float(rms)
 
 
-# --------------------------------------------------------------------------- replay
+def ambiguous_blocks(v, bound) -> np.ndarray:
+    """MXFP8 blocks whose codes or scale are not fixed by v to within +-bound."""
+    v32 = np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
+    amb = moe.ambiguous_codes(v32, np.asarray(bound, np.float64) + EPS32 * np.abs(v32) + 1e-300)
+    return amb.reshape(*amb.shape[:-1], -1, mx.BLOCK).any(-1)
+
+
+# --------------------------------------------------------------------------- rule (ii): re-quantisation
+
+
+def check_requant(name, v32, codes, scales, rep, fmt="e4m3"):
+    """The oracle's quantiser on the GPU's own fp32 tensor gives the GPU's codes."""
+    v32 = np.asarray(v32, np.float32)
+    if fmt == "bf16":
+        want = mx.bf16_bits(v32)
+        nbad = int((u16(codes) != want).sum())
+        assert nbad == 0, f"bf16({name}) of the GPU's own fp32 values: {nbad} mismatches"
+    else:
+        q = moe.quant(v32, "e4m3")
+        nbad = int((q.codes != codes).sum()) + int((q.scales != scales).sum())
+        if nbad:
+            where = np.argwhere(q.codes != codes)[:3].tolist()
+            raise AssertionError(f"MXFP8({name}) of the GPU's own fp32 values: {nbad} code/scale mismatches "
+                                 f"(first at {where})")
+    rep.setdefault("requant_exact", []).append(name)
+
+
+# --------------------------------------------------------------------------- routing
+
+
+def check_routing(W: moe.LayerWeights, o_z, o_routing: moe.Routing, bz, tr: dict, k: int, rep: dict):
+    """Ids (as sets, near-ties flagged), gates and dispatch of a trace against
+    the oracle's routing of its own latent ``o_z`` (bound ``bz`` on the GPU's
+    z).  Returns (per-slot gate tolerance, per-token 'same ids')."""
+    gi = np.asarray(tr["ids"])
+    T = gi.shape[0]
+    E = W.w_router.shape[0]
+    ri = o_routing.ids
+    assert gi.min() >= 0 and gi.max() < E, "expert id out of range"
+    srt = np.sort(gi, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1]), "repeated expert in a token's top-k"
+    same = np.all(np.sort(ri, axis=1) == srt, axis=1)
+    near = o_routing.gap < NEAR_TIE
+    bad = np.where(~(same | near))[0]
+    assert len(bad) == 0, f"ids differ on tokens {bad[:10]} without a near-tie"
+    for t in np.where(~same)[0]:   # flagged near-ties: the GPU's choice must still be a valid top-k
+        kth = np.sort(o_routing.sel[t])[::-1][k - 1]
+        assert np.all(o_routing.sel[t, gi[t]] >= kth - NEAR_TIE), ("invalid near-tie choice", t)
+    rep["tokens_routed"] = rep.get("tokens_routed", 0) + int(T)
+    rep["near_tie_tokens"] = rep.get("near_tie_tokens", 0) + int(near.sum())
+    rep["ids_differ_flagged"] = rep.get("ids_differ_flagged", 0) + int((~same).sum())
+
+    # logit error from the z bound through the fp32 router
+    Wr = np.abs(W.w_router.astype(np.float64))
+    zw = np.abs(o_z) @ Wr.T
+    dlog = bz @ Wr.T + W.w_router.shape[1] * EPS32 * zw + 2 * EPS32 * (1 + zw)
+    gates = np.asarray(tr["gates"], np.float64)
+    sc = np.take_along_axis(o_routing.scores, gi, axis=1)          # oracle scores of the GPU's set
+    dl = np.take_along_axis(dlog, gi, axis=1)
+    if W.gating == "softmax":
+        # softmax over the winners' logits: a logit error d_j moves gate j by a
+        # factor within exp(+-(d_j + max_i d_i)); the fp32 evaluation adds the
+        # subtraction of the maximum (2^-24 |l - m| inside exp), exp itself,
+        # the k-term sum and the division.
+        ref = moe.winner_gates(o_routing.scores, gi, "softmax")
+        spread = (sc.max(1) - sc.min(1))[:, None]
+        tol = np.maximum(1e-6, ref * (np.expm1(dl + dl.max(1, keepdims=True)) + (k + 6 + 2 * spread) * EPS32))
+    else:
+        ssum = sc.sum(1, keepdims=True)
+        ref = sc / ssum                                             # the oracle's gates of the GPU's set
+        ds = 0.25 * dl + 2 * EPS32                                  # |sigmoid'| <= 1/4
+        tol = np.maximum(1e-6, (ds + ref * ds.sum(1, keepdims=True)) / ssum + 4 * EPS32)
+    err = np.abs(gates - ref)
+    badg = np.argwhere(err > tol)
+    assert len(badg) == 0, ("gate", badg[:4].tolist(), err[tuple(badg[0])], tol[tuple(badg[0])])
+    rep["max_gate_err"] = max(rep.get("max_gate_err", 0.0), float(err.max()))
+    assert np.all(np.abs(gates.sum(1) - 1) <= 1e-6), "gates do not sum to 1"
+
+    d = moe.dispatch(gi, E)
+    for name, want in (("counts", d.counts), ("offsets", d.offsets), ("pair_of_row", d.pair_of_row),
+                       ("row_of_pair", d.row_of_pair)):
+        if name in tr:
+            assert np.array_equal(tr[name], want), name
+    return tol, same
+
+
+def check_latent(W, o_xq, o_z, o_zq, tr, rep):
+    """x codes, z against the oracle's z, zq re-quantisation (rule ii) and the
+    differences from the oracle's own zq.  Returns the bound on z."""
+    if W.precision == "bf16":
+        assert np.array_equal(u16(tr["xb"]), o_xq.bits), "bf16(x)"
+    else:
+        assert np.array_equal(tr["xq_codes"], o_xq.codes), "xq codes"
+        assert np.array_equal(tr["xq_scales"], o_xq.scales), "xq scales"
+    if W.w_down is None:   # no latent: the router reads x, the experts xq
+        assert np.array_equal(tr["z"].astype(np.float64), o_z), "router input is not x"
+        if "zq_codes" in tr:
+            assert np.array_equal(tr["zq_codes"], o_xq.codes) and np.array_equal(tr["zq_scales"], o_xq.scales)
+        return np.zeros_like(o_z)
+    bz = gemm_bound(o_xq, W.w_down, o_z)
+    dz = np.abs(tr["z"].astype(np.float64) - o_z)
+    assert np.all(dz <= bz), f"z outside the fp32 bound: worst ratio {np.max(dz / bz):.3g}"
+    rep["z_err_over_bound"] = max(rep.get("z_err_over_bound", 0.0), float(np.max(dz / bz)))
+    check_requant("z", tr["z"], tr["zq_codes"], tr["zq_scales"], rep)
+    differs = (tr["zq_scales"] != o_zq.scales) | (tr["zq_codes"] != o_zq.codes).reshape(
+        *o_zq.scales.shape, mx.BLOCK).any(-1)
+    amb = ambiguous_blocks(o_z, bz)
+    assert not np.any(differs & ~amb), "zq differs from the oracle's own codes outside an ambiguous block"
+    st = rep.setdefault("zq_vs_oracle", {"blocks": 0, "ambiguous": 0, "differ": 0})
+    st["blocks"] += int(amb.size)
+    st["ambiguous"] += int(amb.sum())
+    st["differ"] += int(differs.sum())
+    return bz
+
+
+# --------------------------------------------------------------------------- replay chooser
 
 
 class Replay:
-    """``resolve`` hooks for ``oracle.moe.forward``: adopt the GPU's block where
+    """Chooser for ``tests.replay.replay_forward``: adopt the GPU's block where
     the oracle's own value is within its bound of a rounding boundary and the
     GPU's block is an admissible quantisation there."""
 
@@ -125,12 +248,22 @@ class Replay:
         self.tr, self.W, self.k, self.dgate, self.xq = tr, W, k, dgate, xq
         self.hp = W.precision == "bf16"   # bfloat16 latent projections and shared experts
         self.stats = {}
+        self.lock = threading.Lock()
         P = tr["hq_codes"].shape[0]
         L = tr["y_e"].shape[1]
         self.h_bound = np.zeros(tr["hq_codes"].shape)
         self.ye_bound = np.zeros((P, L))
         self.ylat_bound = None
         self.hs_bound = []
+
+    def _count(self, name, blocks, amb, use, differs, valid):
+        with self.lock:
+            st = self.stats.setdefault(name, {"blocks": 0, "ambiguous_blocks": 0, "adopted_blocks": 0,
+                                              "inadmissible_blocks": 0})
+            st["blocks"] += int(blocks)
+            st["ambiguous_blocks"] += int(amb.sum())
+            st["adopted_blocks"] += int((use & differs).sum())
+            st["inadmissible_blocks"] += int((amb & ~valid & differs).sum())
 
     def _adopt(self, name, v, bound, ref: moe.MXTensor, gcodes, gscales) -> moe.MXTensor:
         v32 = np.asarray(v, np.float64).astype(np.float32).astype(np.float64)   # the value the oracle quantised
@@ -151,11 +284,8 @@ class Replay:
         ok_el = (gm >= c_lo) & (gm <= c_hi) & ((np.signbit(v32) == (gcodes >= 0x80)) | (mag <= bound))
         valid = ok_scale & ok_el.reshape(*shp[:-1], nb, 32).all(-1)
         use = amb_blk & valid
-        st = self.stats.setdefault(name, {"ambiguous_blocks": 0, "adopted_blocks": 0, "inadmissible_blocks": 0})
-        st["ambiguous_blocks"] += int(amb_blk.sum())
         differs = (gscales != ref.scales) | (gcodes != ref.codes).reshape(*shp[:-1], nb, 32).any(-1)
-        st["adopted_blocks"] += int((use & differs).sum())
-        st["inadmissible_blocks"] += int((amb_blk & ~valid & differs).sum())
+        self._count(name, amb_blk.size, amb_blk, use, differs, valid)
         codes = np.where(np.repeat(use, 32, axis=-1).reshape(shp), gcodes, ref.codes).astype(np.uint8)
         scales = np.where(use, gscales, ref.scales).astype(np.uint8)
         return moe.MXTensor(codes, scales, "e4m3")
@@ -175,13 +305,10 @@ class Replay:
         valid = (g >= lo) & (g <= hi)
         use = amb & valid
         differs = gbits != ref.bits
-        st = self.stats.setdefault(name, {"ambiguous_blocks": 0, "adopted_blocks": 0, "inadmissible_blocks": 0})
-        st["ambiguous_blocks"] += int(amb.sum())
-        st["adopted_blocks"] += int((use & differs).sum())
-        st["inadmissible_blocks"] += int((amb & ~valid & differs).sum())
+        self._count(name, amb.size, amb, use, differs, valid)
         return moe.BF16Tensor(np.where(use, gbits, ref.bits).astype(np.uint16))
 
-    # hooks -----------------------------------------------------------------
+    # choices ---------------------------------------------------------------
     def zq(self, z, zq):
         bound = gemm_bound(self.xq, self.W.w_down, z)
         return self._adopt("zq", z, bound, zq, self.tr["zq_codes"], self.tr["zq_scales"])
@@ -230,91 +357,35 @@ class Replay:
 
 
 def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict, x=None, say=print,
-                expert_weights=None) -> dict:
+                expert_weights=None, workers: int = 1) -> dict:
     """Assert the GPU trace against the oracle (``o`` is its unconditioned run)."""
-    T, k, E = y.shape[0], cfg.top_k, cfg.n_routed
+    T, k = y.shape[0], cfg.top_k
+    hp = W.precision == "bf16"
+    latent = W.w_down is not None
     rep = {}
 
-    # 1. input codes (MXFP8, or bfloat16 under the higher-precision map): bit-exact
-    hp = W.precision == "bf16"
-    if hp:
-        assert np.array_equal(u16(tr["xb"]), o.xq.bits), "bf16(x)"
-    else:
-        assert np.array_equal(tr["xq_codes"], o.xq.codes), "xq codes"
-        assert np.array_equal(tr["xq_scales"], o.xq.scales), "xq scales"
-
-    # 2. latent down-projection (bf16 matrix cores); without a latent the
-    #    router reads x and the experts xq, unchanged
-    latent = W.w_down is not None
+    # 1-3. inputs, latent, re-quantisation of every computed tensor (bound-free)
+    bz = check_latent(W, o.xq, o.z, o.zq, tr, rep)
+    check_requant("h", tr["h"], tr["hq_codes"], tr["hq_scales"], rep)
     if latent:
-        bz = gemm_bound(o.xq, W.w_down, o.z)
-        dz = np.abs(tr["z"].astype(np.float64) - o.z)
-        assert np.all(dz <= bz), f"z outside the fp32 bound: worst ratio {np.max(dz / bz):.3g}"
-        rep["z_err_over_bound"] = float(np.max(dz / bz))
-    else:
-        bz = np.zeros_like(o.z)
-        assert np.array_equal(tr["z"].astype(np.float64), o.z), "router input is not x"
-        assert np.array_equal(tr["zq_codes"], o.xq.codes) and np.array_equal(tr["zq_scales"], o.xq.scales)
+        if hp:
+            check_requant("y_lat", tr["y_lat"], tr["yb"], None, rep, fmt="bf16")
+        else:
+            check_requant("y_lat", tr["y_lat"], tr["yq_codes"], tr["yq_scales"], rep)
+    for s in range(len(W.w_gate_s)):
+        if hp:
+            check_requant(f"hs{s}", tr["hs"][s], tr["hs_bf16"][s], None, rep, fmt="bf16")
+        else:
+            check_requant(f"hs{s}", tr["hs"][s], tr["hs_codes"][s], tr["hs_scales"][s], rep)
 
-    # 3. routing
-    gi, ri = tr["ids"], o.routing.ids
-    for t in range(T):
-        assert len(set(gi[t].tolist())) == k and gi[t].min() >= 0 and gi[t].max() < E
-    same = np.array([set(gi[t]) == set(ri[t]) for t in range(T)])
-    near = o.routing.gap < NEAR_TIE
-    assert np.all(same | near), f"ids differ on tokens {np.where(~(same | near))[0][:10]} without a near-tie"
-    for t in np.where(~same)[0]:   # flagged near-ties: the GPU's choice must still be a valid top-k
-        kth = np.sort(o.routing.sel[t])[::-1][k - 1]
-        assert np.all(o.routing.sel[t, gi[t]] >= kth - NEAR_TIE), ("invalid near-tie choice", t)
-    rep["near_tie_tokens"] = int(near.sum())
-    rep["ids_differ_flagged"] = int((~same).sum())
-    Wr = np.abs(W.w_router.astype(np.float64))
-    zw = np.abs(o.z) @ Wr.T
-    dlog = bz @ Wr.T + W.w_router.shape[1] * EPS32 * zw + 2 * EPS32 * (1 + zw)
-    ds = 0.25 * dlog + 2 * EPS32
-    dgate = np.zeros((T, k))
-    worst_gate = 0.0
-    if W.gating == "softmax":
-        # softmax over the winners' logits: a logit error d_j moves gate j by a
-        # factor within exp(+-(d_j + max_i d_i)); the fp32 evaluation adds the
-        # subtraction of the maximum (EPS32 |l - m| inside exp), exp itself,
-        # the k-term sum and the division.
-        for t in range(T):
-            gates_t = moe.winner_gates(o.routing.scores[t:t + 1], gi[t:t + 1], "softmax")[0]
-            lw = o.routing.scores[t, gi[t]]
-            dl = dlog[t, gi[t]]
-            spread = float(lw.max() - lw.min())
-            for j in range(k):
-                tol = max(1e-6, gates_t[j] * (np.expm1(dl[j] + dl.max()) + (k + 6 + 2 * spread) * EPS32))
-                dgate[t, j] = tol
-                err = abs(float(tr["gates"][t, j]) - gates_t[j])
-                worst_gate = max(worst_gate, err)
-                assert err <= tol, ("gate", t, j, err, tol)
-    for t in range(T if W.gating == "sigmoid" else 0):
-        ssum = o.routing.scores[t, gi[t]].sum()
-        gates_t = o.routing.scores[t, gi[t]] / ssum          # the oracle's gates of the GPU's set
-        dsum = ds[t, gi[t]].sum()
-        for j in range(k):
-            e = int(gi[t, j])
-            tol = max(1e-6, (ds[t, e] + gates_t[j] * dsum) / ssum + 4 * EPS32)
-            dgate[t, j] = tol
-            err = abs(float(tr["gates"][t, j]) - gates_t[j])
-            worst_gate = max(worst_gate, err)
-            assert err <= tol, ("gate", t, j, err, tol)
-    rep["max_gate_err"] = worst_gate
-    assert np.all(np.abs(tr["gates"].astype(np.float64).sum(1) - 1) <= 1e-6)
+    # 4-5. routing and dispatch
+    dgate, same = check_routing(W, o.z, o.routing, bz, tr, k, rep)
+    gi = tr["ids"]
 
-    # 4. dispatch = stable sort of the GPU's ids (bit-exact)
-    d = moe.dispatch(gi, E)
-    assert np.array_equal(tr["counts"], d.counts), "counts"
-    assert np.array_equal(tr["offsets"], d.offsets), "offsets"
-    assert np.array_equal(tr["pair_of_row"], d.pair_of_row), "pair_of_row"
-    assert np.array_equal(tr["row_of_pair"], d.row_of_pair), "row_of_pair"
-
-    # 5. replay along the GPU's admissible choices
+    # 6. replay along the GPU's admissible choices
     if x is not None:
         rp = Replay(tr, W, k, dgate, o.xq)
-        c = moe.forward(x, W, k, ids_override=gi, resolve=rp, expert_weights=expert_weights)
+        c = replay_forward(x, W, k, gi, rp, expert_weights=expert_weights, workers=workers)
         for name, st in rp.stats.items():
             assert st["inadmissible_blocks"] == 0, (name, st)
         rep["replay"] = rp.stats
@@ -347,14 +418,14 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
         assert np.all(dye <= rp.ye_bound), f"y_e outside its bound on {(dye > rp.ye_bound).sum()} elements"
         dyl = np.abs(tr["y_lat"].astype(np.float64) - c.y_lat)
         assert np.all(dyl <= rp.ylat_bound), f"y_lat outside its bound on {(dyl > rp.ylat_bound).sum()} elements"
+        S = len(W.w_gate_s)
         if hp:   # one bf16 GEMM over K = [L | Fs ...]
-            by = concat_gemm_bound([(c.yq, W.w_up)] + [(c.hq_shared[s], W.w_down_s[s])
-                                                      for s in range(len(W.w_gate_s))], c.y)
-        else:
-            by = mx_mfma_bound(c.yq, W.w_up) if latent else rp.ylat_bound
-            for s in range(len(W.w_gate_s)):
-                by = by + mx_mfma_bound(c.hq_shared[s], W.w_down_s[s])
-            by = by + (1 + len(W.w_gate_s)) * EPS32 * np.abs(c.y)
+            by = concat_gemm_bound([(c.yq, W.w_up)] + [(c.hq_shared[s], W.w_down_s[s]) for s in range(S)], c.y)
+        else:    # one MX GEMM over K = [L | Fs ...] (without a latent: y = y_lat + sum_s, accumulated in place)
+            pairs = ([(c.yq, W.w_up)] if latent else []) + [(c.hq_shared[s], W.w_down_s[s]) for s in range(S)]
+            by = mx_concat_bound(pairs, c.y, extra_roundings=0 if latent else 1) if pairs else 0
+            if not latent:
+                by = by + rp.ylat_bound
         dy = np.abs(y.astype(np.float64) - c.y)
         assert np.all(dy <= by), f"y outside its bound on {(dy > by).sum()} elements"
         rel, maxabs, rms = output_errors(y, c.y)
@@ -362,34 +433,96 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
         assert rel <= REL_L2, f"relative L2 vs replay {rel:.3g}"
         assert maxabs <= MAXABS_FRAC * rms, f"max abs vs replay {maxabs:.3g} (rms {rms:.3g})"
 
-    # 6. unconditioned oracle output
-    rel, maxabs, rms = output_errors(y, o.y)
-    rep.update(rel_l2=rel, max_abs_over_rms=maxabs / rms, rms=rms)
-    say("parity report:", rep)
+    # 7. unconditioned oracle output, over every token the GPU routed as the
+    #    oracle does: relative L2, and max-abs per token.  A token above the
+    #    max-abs limit is excused only if its path took an admissible choice at
+    #    a rounding boundary (a quantiser near-tie: some re-quantised code
+    #    differs from the oracle's own), as routing near-ties are; it is then
+    #    held to the replay above at the same limit, and counted.
+    rms = float(np.sqrt((o.y ** 2).mean()))
+    rel, maxabs, _ = output_errors(y[same], o.y[same], rms)
+    clean = codes_equal_oracle(W, o, tr, k, same)
+    dev = np.abs(y.astype(np.float64) - o.y).max(axis=1) if y.size else np.zeros(T)
+    over = same & (dev > MAXABS_FRAC * rms)
+    excused = over & ~clean
+    keep = same & ~excused
+    rep.update(rel_l2=rel, max_abs_over_rms=maxabs / rms,
+               max_abs_over_rms_unexcused=float(dev[keep].max() / rms) if keep.any() else 0.0, rms=rms,
+               tokens_vs_oracle=int(same.sum()), tokens_codes_equal_oracle=int(clean.sum()),
+               tokens_quantiser_near_tie=int((same & ~clean).sum()), tokens_excused_over_max_abs=int(excused.sum()))
+    say("parity report:", {key: v for key, v in rep.items()})
+    rep["_y"] = (y[same].astype(np.float64), o.y[same], clean[same])   # for figures over several subsets
     assert rel <= REL_L2, f"relative L2 {rel:.3g}"
+    assert not np.any(over & clean), (f"max abs {dev[over & clean].max():.3g} against the oracle (rms {rms:.3g}) "
+                                      f"on tokens {np.where(over & clean)[0][:8]}")
     return rep
 
 
-# --------------------------------------------------------------------------- sampled tokens
+def codes_equal_oracle(W, o: moe.Trace, tr: dict, k: int, same_ids) -> np.ndarray:
+    """Per token: the GPU chose exactly the oracle's ids (in slot order) and
+    every re-quantised code on the token's path -- zq, the hq rows of its k
+    pairs, yq, the shared hidden states -- equals the oracle's own."""
+    gi = np.asarray(tr["ids"])
+    T = gi.shape[0]
+    ok = same_ids & np.all(gi == o.routing.ids, axis=1)
+    hp = W.precision == "bf16"
+
+    def rows_equal(gc, gs, rc, rs):
+        eq = np.all(gc == rc, axis=-1)
+        return eq if gs is None else eq & np.all(gs == rs, axis=-1)
+
+    if W.w_down is not None:
+        ok &= rows_equal(tr["zq_codes"], tr["zq_scales"], o.zq.codes, o.zq.scales)
+        if hp:
+            ok &= rows_equal(u16(tr["yb"]), None, o.yq.bits, None)
+        else:
+            ok &= rows_equal(tr["yq_codes"], tr["yq_scales"], o.yq.codes, o.yq.scales)
+    for s in range(len(W.w_gate_s)):
+        if hp:
+            ok &= rows_equal(u16(tr["hs_bf16"][s]), None, o.hq_shared[s].bits, None)
+        else:
+            ok &= rows_equal(tr["hs_codes"][s], tr["hs_scales"][s], o.hq_shared[s].codes, o.hq_shared[s].scales)
+    if o.hq_rows is not None:
+        idx = np.where(ok)[0]
+        pairs = (idx[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+        gr = np.asarray(tr["row_of_pair"], np.int64)[pairs]
+        orr = o.disp.row_of_pair[pairs]
+        eq = rows_equal(tr["hq_codes"][gr], tr["hq_scales"][gr], o.hq_rows.codes[orr], o.hq_rows.scales[orr])
+        ok[idx] = eq.reshape(-1, k).all(1)
+    return ok
 
 
-def check_full_dispatch(full: dict, E: int, k: int):
-    """Batch-wide properties that are unique and cheap: every token routes to k
-    distinct valid experts, gates sum to one, and the GPU's dispatch is exactly
-    the stable expert-sorted permutation of its own ids."""
-    ids = full["ids"]
-    T = ids.shape[0]
-    assert ids.min() >= 0 and ids.max() < E, "expert id out of range"
-    srt = np.sort(ids, axis=1)
-    assert np.all(srt[:, 1:] != srt[:, :-1]), "repeated expert in a token's top-k"
-    assert np.all(np.abs(full["gates"].astype(np.float64).sum(1) - 1) <= 1e-6), "gates do not sum to 1"
-    d = moe.dispatch(ids, E)
-    assert np.array_equal(full["counts"], d.counts), "counts"
-    assert np.array_equal(full["offsets"], d.offsets), "offsets"
-    assert np.array_equal(full["pair_of_row"], d.pair_of_row), "pair_of_row"
-    assert np.array_equal(full["row_of_pair"], d.row_of_pair), "row_of_pair"
-    return {"tokens": int(T), "pairs": int(T * k), "touched_experts": int((d.counts > 0).sum()),
-            "max_expert_rows": int(d.counts.max())}
+# --------------------------------------------------------------------------- whole batches, token subsets
+
+
+def check_batch_routing(cfg, W: moe.LayerWeights, x: np.ndarray, full: dict, workers: int = 16, say=print) -> dict:
+    """Every token of a whole batch: x codes, z, zq (re-quantisation and
+    against the oracle's own), ids, gates and dispatch, against the oracle's
+    latent and router computed for all tokens (``full`` holds the GPU's
+    xq/z/zq/ids/gates/dispatch for the batch)."""
+    from concurrent.futures import ThreadPoolExecutor
+    T = x.shape[0]
+    chunks = [slice(i, min(T, i + 256)) for i in range(0, T, 256)]
+    fmt = "bf16" if W.precision == "bf16" else "e4m3"
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(lambda sl: moe.quant(x[sl], fmt), chunks))
+    if fmt == "bf16":
+        xq = moe.BF16Tensor(np.concatenate([p.bits for p in parts]))
+    else:
+        xq = moe.MXTensor(np.concatenate([p.codes for p in parts]), np.concatenate([p.scales for p in parts]),
+                          "e4m3")
+    z = moe.mm(xq, W.w_down) if W.w_down is not None else x.astype(np.float64)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        zparts = list(ex.map(lambda sl: moe.quant(z[sl], "e4m3"), chunks))
+    zq = moe.MXTensor(np.concatenate([p.codes for p in zparts]), np.concatenate([p.scales for p in zparts]), "e4m3")
+    r = moe.route(z, W.w_router, cfg.top_k, W.logit_bias, W.selection_bias, np.float32, W.gating)
+    rep = {}
+    bz = check_latent(W, xq, z, zq, full, rep)
+    check_routing(W, z, r, bz, full, cfg.top_k, rep)
+    d = moe.dispatch(full["ids"], cfg.n_routed)
+    rep.update(touched_experts=int((d.counts > 0).sum()), max_expert_rows=int(d.counts.max()))
+    say("  batch routing:", rep)
+    return rep
 
 
 def subset_trace(sub: dict, E: int, k: int) -> dict:
@@ -408,11 +541,30 @@ def subset_trace(sub: dict, E: int, k: int) -> dict:
     return tr
 
 
-def check_tokens(cfg, W, x_sub, y_sub, sub, expert_weights, say=print) -> dict:
+def check_tokens(cfg, W, x_sub, y_sub, sub, expert_weights, say=print, workers: int = 1) -> dict:
     """The sampled tokens' full path against the oracle, with the same checks
     as check_layer (replay included) on the subset's trace."""
     import dataclasses as _dc
     tr = subset_trace(sub, cfg.n_routed, cfg.top_k)
     csub = _dc.replace(cfg, T=x_sub.shape[0])
     o = moe.forward(x_sub, W, cfg.top_k, expert_weights=expert_weights)
-    return check_layer(csub, W, o, y_sub, tr, x=x_sub, say=say, expert_weights=expert_weights)
+    return check_layer(csub, W, o, y_sub, tr, x=x_sub, say=say, expert_weights=expert_weights, workers=workers)
+
+
+def merge_reports(reps) -> dict:
+    """Totals and worst cases over the reports of several token subsets."""
+    out = {"subsets": len(reps)}
+    for key in ("tokens_routed", "near_tie_tokens", "ids_differ_flagged", "tokens_vs_oracle",
+                "tokens_codes_equal_oracle", "tokens_quantiser_near_tie", "tokens_excused_over_max_abs"):
+        out[key] = sum(r.get(key, 0) for r in reps)
+    for key in ("z_err_over_bound", "max_gate_err", "replay_max_abs_over_rms", "max_abs_over_rms",
+                "max_abs_over_rms_unexcused", "rel_l2"):
+        out[key] = max(r.get(key, 0.0) for r in reps)
+    rp = {}
+    for r in reps:
+        for name, st in r.get("replay", {}).items():
+            acc = rp.setdefault(name, {})
+            for k2, v in st.items():
+                acc[k2] = acc.get(k2, 0) + v
+    out["replay"] = rp
+    return out

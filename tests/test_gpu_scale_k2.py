@@ -2,9 +2,10 @@
 
 The 8192-token batch of the non-latent layer (7168 wide, 384 experts, top-8,
 softmax-over-winners gates, one shared expert) runs whole on the GPU in the
-configuration the benchmark times.  Routing and dispatch are checked exactly
-for every token; the full data path of a few sampled tokens against the fp64
-oracle.
+configuration the benchmark times.  Every token's routing (router input,
+ids as sets with near-ties flagged, gates, dispatch) is checked against the
+oracle's router on the whole batch; the full data path of a few sampled tokens
+against the fp64 oracle.
 """
 
 import os
@@ -37,9 +38,9 @@ def test_k2_prefill_8192_tokens():
     lay.close()
     del gw
     torch.cuda.empty_cache()
-    rep = parity.check_full_dispatch(full, cfg.n_routed, cfg.top_k)
-    say("  batch:", rep)
     W = weights.layer(cfg, experts="lazy")
+    rep = parity.check_batch_routing(cfg, W, x, full, workers=min(16, len(os.sched_getaffinity(0))), say=say)
+    assert rep["tokens_routed"] == cfg.T
     cache = weights.ExpertCache(cfg, maxsize=64)
     need = sorted(set(sub["ids"].reshape(-1).tolist()))
     with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
