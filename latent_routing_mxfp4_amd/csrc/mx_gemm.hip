@@ -21,6 +21,7 @@
 // all of them in gemm_epilogue.hpp.  MX weights are read in fragment order
 // (kernels.hpp), except W_down, which the bf16 paths read row-major.
 #include "kernels.hpp"
+#include "launch_attr.hpp"
 #include "mx_device.hpp"
 #include "lds_pipe.hpp"
 #include "gemm_epilogue.hpp"
@@ -610,15 +611,11 @@ hipError_t launch_bf16_splitk(const GemmArgs& a, bool bf16_b, const SplitPlan& s
   const dim3 gd((unsigned)grid, (unsigned)sp.n);
   constexpr int D = 4;
   constexpr size_t lds1 = splitk_lds_bytes<1, D>(), lds4 = splitk_lds_bytes<4, D>();
-  static bool attr_set = false;  // per process, before the first launch
-  if (!attr_set) {
-    for (const void* f : {reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, false>),
-                          reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, true>)}) {
-      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds4);
-      if (e != hipSuccess) return e;
-    }
-    attr_set = true;
-  }
+  static DeviceOnce attr;
+  hipError_t ea = lds_limit_once(attr, {reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, false>),
+                                        reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, true>)},
+                                 (int)lds4);
+  if (ea != hipSuccess) return ea;
   if (bf16_b) {
     if (small) bf16_splitk_kernel<1, 2, D, false><<<gd, dim3(256), lds1, s>>>(a, sp, part);
     else bf16_splitk_kernel<4, 2, D, false><<<gd, dim3(256), lds4, s>>>(a, sp, part);

@@ -44,6 +44,7 @@
 
 #include "gemm_epilogue.hpp"
 #include "kernels.hpp"
+#include "launch_attr.hpp"
 #include "lds_pipe.hpp"
 #include "mx_device.hpp"
 
@@ -447,13 +448,9 @@ hipError_t launch_wide_cfg(const GemmArgs& a, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   constexpr size_t smem = (size_t)WD_NBUF * WD_STAGE;
-  static bool attr_set = false;  // per process, before the first launch
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mx_gemm_wide_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static DeviceOnce attr;
+  hipError_t e = lds_limit_once(attr, {reinterpret_cast<const void*>(&mx_gemm_wide_kernel<EPI>)}, (int)smem);
+  if (e != hipSuccess) return e;
   mx_gemm_wide_kernel<EPI><<<dim3((unsigned)tiles), dim3(512), smem, s>>>(a);
   return hipGetLastError();
 }
@@ -473,13 +470,9 @@ hipError_t launch_bf16_wide_cfg(const GemmArgs& a, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   constexpr size_t smem = (size_t)WB_NBUF * WB_STAGE;
-  static bool attr_set = false;  // per process, before the first launch
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bf16_gemm_wide_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static DeviceOnce attr;
+  hipError_t e = lds_limit_once(attr, {reinterpret_cast<const void*>(&bf16_gemm_wide_kernel<EPI>)}, (int)smem);
+  if (e != hipSuccess) return e;
   bf16_gemm_wide_kernel<EPI><<<dim3((unsigned)tiles), dim3(512), smem, s>>>(a);
   return hipGetLastError();
 }

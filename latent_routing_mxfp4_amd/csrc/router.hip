@@ -20,6 +20,7 @@
 #include <float.h>
 
 #include "kernels.hpp"
+#include "launch_attr.hpp"
 #include "mx_device.hpp"
 
 namespace moe {
@@ -323,13 +324,9 @@ hipError_t launch_router_logits(const float* z, const float* w, const float* bia
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr size_t smem = 2 * BOP;
-    static bool attr_set = false;  // per process, before the first launch
-    if (!attr_set) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_logits_bf16x3_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static DeviceOnce attr;
+    e = lds_limit_once(attr, {reinterpret_cast<const void*>(&router_logits_bf16x3_kernel)}, (int)smem);
+    if (e != hipSuccess) return e;
     dim3 grid((E + BE - 1) / BE, (T + BT - 1) / BT);
     router_logits_bf16x3_kernel<<<grid, dim3(256), smem, s>>>(z, wplanes, bias, T, E, L, logits);
     return hipGetLastError();
@@ -546,13 +543,9 @@ hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E,
     return hipGetLastError();
   }
   const size_t smem = (size_t)4 * 2 * E * sizeof(float);  // 4 waves x (keys + scores): 128 KB at E = 4096
-  static bool attr_set = false;                          // per process, before the first launch
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 2 * 4096 * (int)sizeof(float));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static DeviceOnce attr;  // the largest E (4096) once per device
+  hipError_t e = lds_limit_once(attr, {reinterpret_cast<const void*>(&topk_kernel)}, 4 * 2 * 4096 * (int)sizeof(float));
+  if (e != hipSuccess) return e;
   topk_kernel<<<dim3((T + 3) / 4), dim3(256), smem, s>>>(logits, sel_bias, T, E, k, softmax_gates, ids, gates);
   return hipGetLastError();
 }
