@@ -213,6 +213,28 @@ int moe_layer_workspace_size(const moe_layer_config* cfg, int32_t T, size_t* byt
 int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y,
                       void* ws, size_t ws_bytes, void* stream, const moe_layer_trace* trace);
 
+/* Largest workspace moe_layer_forward_noalloc takes from the library's static
+ * scratch: 96 MiB, enough for the Kimi-K3-width forward of up to 192 tokens. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* moe_layer_forward for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc: the same forward (same kernels, same results), with its
+ * workspace taken from a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.  It
+ * calls no hipMalloc, hipFree or other allocating routine.  The first call on
+ * a device looks that device's array up (make one call there before capturing
+ * a graph).  All calls on one GPU share its array, which keeps the last
+ * call's intermediates: calls that overlap on one GPU (other streams, other
+ * threads, other handles) race and must be ordered by the caller.  Nothing in
+ * the array needs clearing between calls.
+ * Errors: as moe_layer_forward; MOE_ERR_WORKSPACE when the forward over T
+ * tokens needs more than MOE_NOALLOC_SCRATCH_BYTES (moe_layer_workspace_size
+ * gives the need); MOE_ERR_HIP when the array cannot be found on the current
+ * device. */
+int moe_layer_forward_noalloc(moe_layer_t layer, const float* x, int32_t T, float* y, void* stream,
+                              const moe_layer_trace* trace);
+
 /* Free the host-side handle (the weights are not touched).  NULL is a no-op. */
 int moe_layer_destroy(moe_layer_t layer);
 

@@ -25,6 +25,7 @@ EXPORTED = (
     "moe_layer_create",
     "moe_layer_workspace_size",
     "moe_layer_forward",
+    "moe_layer_forward_noalloc",
     "moe_layer_destroy",
     "moe_mx_quantize",
     "moe_round_bf16",
@@ -117,6 +118,8 @@ def load() -> ctypes.CDLL:
     lib.moe_layer_workspace_size.argtypes = [ctypes.POINTER(MoeLayerConfig), i32, ctypes.POINTER(sz)]
     lib.moe_layer_forward.restype = ctypes.c_int
     lib.moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, sz, vp, ctypes.POINTER(MoeLayerTrace)]
+    lib.moe_layer_forward_noalloc.restype = ctypes.c_int
+    lib.moe_layer_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, ctypes.POINTER(MoeLayerTrace)]
     lib.moe_layer_destroy.restype = ctypes.c_int
     lib.moe_layer_destroy.argtypes = [vp]
     lib.moe_mx_quantize.restype = ctypes.c_int
@@ -164,6 +167,15 @@ def moe_layer_forward(handle: int, x: int, T: int, y: int, ws: int, ws_bytes: in
                       trace: MoeLayerTrace | None = None) -> None:
     tr = ctypes.byref(trace) if trace is not None else None
     _check(load().moe_layer_forward(handle, x, int(T), y, ws, int(ws_bytes), stream, tr), "moe_layer_forward")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def moe_layer_forward_noalloc(handle: int, x: int, T: int, y: int, stream: int = 0,
+                              trace: MoeLayerTrace | None = None) -> None:
+    tr = ctypes.byref(trace) if trace is not None else None
+    _check(load().moe_layer_forward_noalloc(handle, x, int(T), y, stream, tr), "moe_layer_forward_noalloc")
 
 
 def moe_layer_destroy(handle: int) -> None:

@@ -26,6 +26,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe_layer.h"
@@ -254,15 +256,17 @@ int moe_layer_destroy(moe_layer_t layer) {
     if ((expr) != hipSuccess) return MOE_ERR_HIP;     \
   } while (0)
 
-int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes,
-                      void* stream, const moe_layer_trace* tr) {
-  if (!layer) return MOE_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// The forward over a validated layer, T > 0, and a workspace of at least the
+// plan's size (aligned to kAlign).  Every byte of the workspace that a kernel
+// reads was written earlier in the same forward, so nothing needs clearing.
+int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* ws, void* stream,
+                 const moe_layer_trace* tr) {
   const moe_layer_config& c = layer->cfg;
-  if (T < 0 || T > c.max_tokens) return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
   const Plan pl = make_plan(c, T);
-  if (!ws || !aligned(ws, kAlign) || ws_bytes < pl.total) return MOE_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe_layer_weights& w = layer->w;
@@ -589,6 +593,72 @@ int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, vo
     }
   }
   return MOE_OK;
+}
+
+// ---- static scratch of the no-allocation forward ---------------------------
+//
+// One array per GPU the library runs on (a __device__ variable has a copy on
+// every device), held until the process ends.  In host code `scratch` names
+// a host-side stand-in, not a device address: the device address is looked
+// up per device with hipGetSymbolAddress and only that pointer is used.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// The current device's copy of `scratch` (looked up on the first call there).
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p || !aligned(p, kAlign)) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(moe_layer_t layer, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes,
+                      void* stream, const moe_layer_trace* tr) {
+  if (!layer) return MOE_ERR_INVALID_ARG;
+  const moe_layer_config& c = layer->cfg;
+  if (T < 0 || T > c.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, kAlign) || ws_bytes < make_plan(c, T).total) return MOE_ERR_WORKSPACE;
+  return forward_impl(layer, x, T, y, ws, stream, tr);
+}
+
+int moe_layer_forward_noalloc(moe_layer_t layer, const float* x, int32_t T, float* y, void* stream,
+                              const moe_layer_trace* tr) {
+  if (!layer) return MOE_ERR_INVALID_ARG;
+  const moe_layer_config& c = layer->cfg;
+  if (T < 0 || T > c.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  if (make_plan(c, T).total > kScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return forward_impl(layer, x, T, y, ws, stream, tr);
 }
 
 int moe_mx_quantize(const float* in, int64_t rows, int32_t K, int32_t fmt, uint8_t* codes, uint8_t* scales,

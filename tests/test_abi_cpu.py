@@ -115,6 +115,27 @@ def test_forward_argument_errors_need_no_gpu():
     assert _lib.load().moe_layer_destroy(None) == _lib.MOE_OK
 
 
+def test_noalloc_forward_argument_errors_need_no_gpu():
+    """The no-allocation forward checks its arguments, and refuses a batch whose
+    workspace exceeds the static scratch, before any HIP call."""
+    cfg = _k3(max_tokens=16384)
+    h = _lib.moe_layer_create(cfg, _weights())
+    try:
+        lib = _lib.load()
+        fwd = lib.moe_layer_forward_noalloc
+        assert fwd(h, None, 0, None, None, None) == _lib.MOE_OK
+        assert fwd(None, FAKE, 1, FAKE, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert fwd(h, FAKE, 16385, FAKE, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert fwd(h, FAKE, 8, None, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert fwd(h, FAKE + 4, 8, FAKE, None, None) == _lib.MOE_ERR_INVALID_ARG
+        assert _lib.moe_layer_workspace_size(cfg, 1024) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+        assert fwd(h, FAKE, 1024, FAKE, None, None) == _lib.MOE_ERR_WORKSPACE
+        # the K3-width forward of up to 192 tokens fits the scratch
+        assert _lib.moe_layer_workspace_size(cfg, 192) <= _lib.MOE_NOALLOC_SCRATCH_BYTES
+    finally:
+        _lib.moe_layer_destroy(h)
+
+
 def test_quantize_and_gemm_argument_errors():
     lib = _lib.load()
     assert lib.moe_mx_quantize(FAKE, 4, 48, 0, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
