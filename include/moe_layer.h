@@ -276,7 +276,7 @@ int moe_round_bf16(const float* in, int64_t n, uint16_t* out, void* stream);
  * say only that each expert's bias is updated from the distribution of its
  * score margins so that its routed count approaches a target load.  Reading:
  * key = sigmoid(logit) + bias; an expert's margin on a token is its key minus
- * the k-th largest key among the token's other experts; n = round(T*k/E)
+ * the k-th largest key among the token's other experts; n = round(T*k/E) (ties to even)
  * clamped to [1, T-1]; Q[e] = midpoint of expert e's n-th and (n+1)-th
  * largest margins over the batch; bias_out = bias_in - eta * Q.
  * logits: device fp32 [T][E] (the router's logits, before the sigmoid);

@@ -210,9 +210,10 @@ __global__ void __launch_bounds__(256) qb_select_kernel(const float* __restrict_
 
 size_t quantile_balance_workspace_floats(int T, int E) { return 2 * (size_t)T + (size_t)E * T; }
 
+// round(T k / E) with ties to the even integer, in exact integer arithmetic.
 int quantile_balance_target(int T, int E, int k) {
-  const double c = (double)T * k / E;
-  long n = lround(c);
+  const int64_t tk = (int64_t)T * k, q = tk / E, r = tk % E;
+  int64_t n = q + ((2 * r > E) || (2 * r == E && (q & 1)) ? 1 : 0);
   if (n < 1) n = 1;
   if (n > T - 1) n = T - 1;
   return (int)n;

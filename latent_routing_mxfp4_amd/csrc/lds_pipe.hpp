@@ -14,6 +14,9 @@ namespace moe {
 // wait-count pass would otherwise treat every in-flight LDS load as aliasing
 // every LDS read and drain the whole pipeline (vmcnt(0)) before each fragment
 // read.  Ordering is kept by hand: wait_vmcnt<N>() after issue, then a barrier.
+// The sequences write m0, which the compiler cannot be told about (it is not
+// an allocatable clobber); no compiler-generated instruction of these kernels
+// uses m0, which a test checks on the built gfx950 assembly.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -12,8 +12,8 @@ the hardware", section "Width: 896 experts and the interconnect").  No formula
 is printed.  The reading taken here is the plainest one those sentences
 support:
 
-* target load: ``n = round(T * k / E)`` tokens per expert, clamped to
-  ``[1, T - 1]`` (a uniform load);
+* target load: ``n = round(T * k / E)`` tokens per expert (an exact half
+  goes to the even integer), clamped to ``[1, T - 1]`` (a uniform load);
 * margin of expert ``e`` on token ``t``: its selection key (sigmoid score plus
   selection bias) minus the k-th largest key among the token's *other*
   experts -- expert ``e`` is routed token ``t`` exactly when its margin is

@@ -45,7 +45,8 @@ def _gpu(LY, lg, bias, k, eta=1.0, inplace=False):
 # (300, 1280): more experts than the threshold pass keeps in registers (keys in
 # LDS); (16500, 24): more tokens than the selection keeps in registers (counts
 # re-read from global memory).
-@pytest.mark.parametrize("T,E,k", [(240, 16, 4), (1000, 64, 6), (513, 128, 8), (300, 1280, 6), (16500, 24, 2)])
+@pytest.mark.parametrize("T,E,k", [(240, 16, 4), (1000, 64, 6), (513, 128, 8), (300, 1280, 6), (16500, 24, 2),
+                                   (140, 896, 16), (20, 8, 1), (60, 8, 1)])   # the last three: T k / E ends in .5
 def test_quantiles_and_bias_match_the_oracle(LY, T, E, k):
     say(f"quantile balance T={T} E={E} k={k}")
     lg, bias = _logits(T, E, seed=T + E)

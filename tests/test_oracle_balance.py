@@ -37,6 +37,12 @@ def test_target_load_of_the_k3_shape():
     assert qb.target_load(10, 1000, 1) == 1            # clamped to at least one token
 
 
+def test_target_load_ties_go_to_the_even_count():
+    assert qb.target_load(140, 896, 16) == 2           # 2.5
+    assert qb.target_load(20, 8, 1) == 2               # 2.5
+    assert qb.target_load(60, 8, 1) == 8               # 7.5
+
+
 def test_quantile_shift_gives_one_expert_exactly_the_target():
     lg, bias = _case()
     T, E, k = lg.shape[0], lg.shape[1], 4
