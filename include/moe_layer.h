@@ -28,11 +28,17 @@
  *   E2M1 codes: [rows][K/2] bytes, element 2i in the low nibble of byte i;
  *   E4M3 codes: [rows][K] bytes;
  *   scales:     [rows][K/32] bytes, E8M0 (value 2^(c-127)).
- * Weight matrices are [out][in] (nn.Linear orientation).  The weights the MX
- * GEMMs read are stored in FRAGMENT ORDER instead, which keeps the same bytes
- * per matrix but puts each operand of one 16x16x128 block-scaled MFMA in one
- * contiguous 1 KB block (the kernels' hot loops then load whole cache lines
- * and need no shuffling).  For G matrices [N][K], N % 16 == 0, K % 128 == 0:
+ * Weight matrices are [out][in] (nn.Linear orientation; x @ W[e] of the MoE
+ * data-path toy, Kimi K3: 2.8 Trillion Parameters, Four Bits at a Time,
+ * section "What it takes to serve it").  The layer reads its MX weights in
+ * either of two layouts, chosen by moe_layer_config.weight_layout:
+ *   MOE_WEIGHTS_ROW_MAJOR: the row-major storage above, as a checkpoint holds
+ *     the MXFP4 codes (consumed as stored);
+ *   MOE_WEIGHTS_FRAGMENT: FRAGMENT ORDER, which keeps the same bytes per matrix
+ *     but puts each operand of one 16x16x128 block-scaled MFMA in one
+ *     contiguous 1 KB block (the prefill kernels then move whole cache lines
+ *     per load; the faster layout).
+ * For G matrices [N][K], N % 16 == 0, K % 128 == 0, fragment order is:
  *   codes:  matrix g starts at g*N*K/2; block (nb, kb) = rows 16nb..16nb+15,
  *           elements 128kb..128kb+127 sits at (nb*(K/128) + kb)*1024; inside
  *           it, bytes 16l..16l+15 (l = r + 16q, r < 16, q < 4) are the E2M1
@@ -71,10 +77,15 @@ enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(int status);
 
+/* Layouts of the MX weight tensors (see the top of this file). */
+enum { MOE_WEIGHTS_ROW_MAJOR = 0, MOE_WEIGHTS_FRAGMENT = 1 };
+
 /* Layer shape.  d_model, d_latent, d_ff_routed, d_ff_shared must be positive
- * multiples of 128 (whole MFMA K-steps); 1 <= top_k <= n_routed <= 4096;
- * 0 <= n_shared <= 8; 1 <= max_tokens <= 2^20.  The Kimi-K3 width is
- * {7168, 3584, 896, 16, 2, 3072, 3072, T}. */
+ * multiples of 128: every one of them is the contraction of some MX GEMM,
+ * which the block-scaled instruction consumes 128 elements (four MX blocks)
+ * at a time (the pages' widths 7168, 3584 and the 3072 estimate all are);
+ * 1 <= top_k <= n_routed <= 4096; 0 <= n_shared <= 8; 1 <= max_tokens <=
+ * 2^20.  The Kimi-K3 width is {7168, 3584, 896, 16, 2, 3072, 3072, T}. */
 typedef struct {
   int32_t d_model;     /* d:  model width                        */
   int32_t d_latent;    /* L:  routed latent width                */
@@ -106,6 +117,9 @@ typedef struct {
    *     y  = bf16(y_lat) W_up^T + sum_s hs W_down_s^T.
    * The router, top-k, dispatch and routed experts are unchanged. */
   int32_t dense_bf16;
+  /* Layout of every MX weight tensor of moe_layer_weights: MOE_WEIGHTS_ROW_MAJOR
+   * (0, the zero default) or MOE_WEIGHTS_FRAGMENT. */
+  int32_t weight_layout;
 } moe_layer_config;
 
 /* One MXFP4 (E2M1) tensor: packed codes and E8M0 scales, device memory. */
@@ -116,8 +130,9 @@ typedef struct {
 
 /* Layer weights.  Non-owning: every buffer must outlive the handle and must
  * not change while a forward that reads it is in flight.  Expert tensors are
- * the E (or S) matrices stored back to back.  w_down is row-major; every other
- * MX tensor is in fragment order (see the top of this file). */
+ * the E (or S) matrices stored back to back (per-expert matrices W[E] of the
+ * MoE data-path toy).  Every MX tensor is in the layout the config names;
+ * codes 16-byte and scales 4-byte aligned. */
 typedef struct {
   moe_mx_tensor w_down;            /* [L][d]      latent down-projection (row-major) */
   moe_mx_tensor w_up;              /* [d][L]      latent up-projection          */
@@ -190,19 +205,32 @@ typedef struct {
 
 typedef struct moe_layer* moe_layer_t;
 
-/* Validate the shape and record the (non-owning) weight pointers.  Host-side
- * only: launches nothing.  *out is written only on success.
+/* Validate the shape and record the (non-owning) weight pointers of one
+ * LatentMoE layer (Kimi K3 and the New Open-Weights Moat, "Sparse
+ * computation: latent experts and routing": the latent routed path and the
+ * shared branch).  Host-side only: launches nothing.  *out is written only on
+ * success.
  * Errors: MOE_ERR_INVALID_ARG for null pointers (the two biases may be NULL;
  * the shared tensors may be NULL when n_shared == 0) or out-of-range sizes;
  * MOE_ERR_UNSUPPORTED when a width is not a multiple of 128. */
 int moe_layer_create(const moe_layer_config* cfg, const moe_layer_weights* w, moe_layer_t* out);
 
 /* Device workspace, in bytes, that a forward over T tokens needs
- * (0 <= T <= cfg->max_tokens).  Pure function of (cfg, T).
- * Errors: MOE_ERR_INVALID_ARG (cfg or bytes NULL, T out of range). */
+ * (0 <= T <= cfg->max_tokens): every intermediate of the layer's steps (the
+ * permuted buffer of T*k rows, Four Bits at a Time, "What it takes to serve
+ * it").  Pure function of (cfg, T).
+ * Errors: MOE_ERR_INVALID_ARG (cfg or bytes NULL, T out of range), or the
+ * shape's error from moe_layer_create. */
 int moe_layer_workspace_size(const moe_layer_config* cfg, int32_t T, size_t* bytes);
 
-/* The forward pass: y[T][d] (fp32, fully overwritten) from x[T][d] (fp32).
+/* The same figure as a plain return value: the workspace bytes a forward over
+ * T tokens needs, or 0 when cfg is NULL or invalid or T is out of range. */
+size_t moe_layer_workspace_bytes(const moe_layer_config* cfg, int32_t T);
+
+/* The forward pass (the formula at the top of this file: Moat page, "How the
+ * router picks 16 of 896", Fig. 2, with the latent path of "Sparse
+ * computation: latent experts and routing"): y[T][d] (fp32, fully overwritten)
+ * from x[T][d] (fp32).
  * ws must be a device buffer of at least moe_layer_workspace_size(T) bytes,
  * 256-byte aligned; it is scratch owned by the caller and must not be shared
  * by two forwards in flight at once.  T == 0 returns MOE_OK and launches

@@ -20,10 +20,14 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 
+MOE_WEIGHTS_ROW_MAJOR = 0
+MOE_WEIGHTS_FRAGMENT = 1
+
 EXPORTED = (
     "moe_status_string",
     "moe_layer_create",
     "moe_layer_workspace_size",
+    "moe_layer_workspace_bytes",
     "moe_layer_forward",
     "moe_layer_forward_noalloc",
     "moe_layer_destroy",
@@ -47,7 +51,7 @@ class MoEError(RuntimeError):
 class MoeLayerConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "d_latent", "n_routed", "top_k", "n_shared", "d_ff_routed", "d_ff_shared", "max_tokens",
-        "identity_latent", "softmax_gates", "dense_bf16")]
+        "identity_latent", "softmax_gates", "dense_bf16", "weight_layout")]
 
 
 class MoeMxTensor(ctypes.Structure):
@@ -116,6 +120,8 @@ def load() -> ctypes.CDLL:
                                      ctypes.POINTER(vp)]
     lib.moe_layer_workspace_size.restype = ctypes.c_int
     lib.moe_layer_workspace_size.argtypes = [ctypes.POINTER(MoeLayerConfig), i32, ctypes.POINTER(sz)]
+    lib.moe_layer_workspace_bytes.restype = sz
+    lib.moe_layer_workspace_bytes.argtypes = [ctypes.POINTER(MoeLayerConfig), i32]
     lib.moe_layer_forward.restype = ctypes.c_int
     lib.moe_layer_forward.argtypes = [vp, vp, i32, vp, vp, sz, vp, ctypes.POINTER(MoeLayerTrace)]
     lib.moe_layer_forward_noalloc.restype = ctypes.c_int
@@ -161,6 +167,10 @@ def moe_layer_workspace_size(cfg: MoeLayerConfig, T: int) -> int:
     n = ctypes.c_size_t()
     _check(load().moe_layer_workspace_size(ctypes.byref(cfg), int(T), ctypes.byref(n)), "moe_layer_workspace_size")
     return n.value
+
+
+def moe_layer_workspace_bytes(cfg: MoeLayerConfig, T: int) -> int:
+    return int(load().moe_layer_workspace_bytes(ctypes.byref(cfg), int(T)))
 
 
 def moe_layer_forward(handle: int, x: int, T: int, y: int, ws: int, ws_bytes: int, stream: int = 0,

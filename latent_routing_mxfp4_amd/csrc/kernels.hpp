@@ -25,9 +25,11 @@ hipError_t launch_quantize(const float* in, int64_t rows, int K, int fmt, uint8_
 // Row-major E2M1 codes [G*N][K/2] + scales [G*N][K/32] -> fragment order.
 hipError_t launch_pack_e2m1(const uint8_t* codes, const uint8_t* scales, int64_t G, int N, int K,
                             uint8_t* out_codes, uint8_t* out_scales, hipStream_t s);
-// E2M1 packed [rows][K/2] + scales [rows][K/32] -> exact bf16 [rows][K].
+// E2M1 codes + scales of one [rows][K] matrix -> exact bf16 [rows][K]; the
+// input row-major (codes [rows][K/2], scales [rows][K/32]) or, with
+// frag != 0, in fragment order (rows % 16 == 0, K % 128 == 0).
 hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
-                                   uint16_t* out, hipStream_t s);
+                                   uint16_t* out, hipStream_t s, int frag = 0);
 // fp32 [n] -> bfloat16 [n], round to nearest even (n % 4 == 0, in 16-byte and
 // out 8-byte aligned).
 hipError_t launch_round_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);
@@ -79,6 +81,7 @@ struct GemmSeg {
   int64_t b_gstride;   // bytes between groups' code matrices
   int64_t bs_gstride;  // bytes between groups' scale matrices
   int K;
+  int b_rm;            // MX B (and b2) row-major: codes [N][K/2], scales [N][K/32]; 0 = fragment order
 };
 
 struct GemmArgs {

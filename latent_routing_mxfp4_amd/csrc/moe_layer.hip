@@ -171,6 +171,7 @@ int check_config(const moe_layer_config* c) {
   if (c->n_shared > 0 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
   if (c->identity_latent && c->d_latent != c->d_model) return MOE_ERR_INVALID_ARG;
   if (c->dense_bf16 && c->identity_latent) return MOE_ERR_UNSUPPORTED;  // the map is the latent layer's
+  if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_FRAGMENT) return MOE_ERR_INVALID_ARG;
   if (c->n_routed > 4096 || c->top_k > 64) return MOE_ERR_UNSUPPORTED;
   if (c->d_model % 128 || c->d_latent % 128 || c->d_ff_routed % 128) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 0 && c->d_ff_shared % 128) return MOE_ERR_UNSUPPORTED;
@@ -246,6 +247,11 @@ int moe_layer_workspace_size(const moe_layer_config* cfg, int32_t T, size_t* byt
   return MOE_OK;
 }
 
+size_t moe_layer_workspace_bytes(const moe_layer_config* cfg, int32_t T) {
+  size_t bytes = 0;
+  return moe_layer_workspace_size(cfg, T, &bytes) == MOE_OK ? bytes : 0;
+}
+
 int moe_layer_destroy(moe_layer_t layer) {
   delete layer;
   return MOE_OK;
@@ -307,6 +313,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
   float* dpart = at<float>(ws, pl.dpart);
   const bool hp = c.dense_bf16 != 0;
   const bool few = T <= kFewRows;
+  const int wrm = c.weight_layout == MOE_WEIGHTS_ROW_MAJOR ? 1 : 0;  // MX weights row-major [out][in]
   auto u8 = [](const void* p) { return reinterpret_cast<const uint8_t*>(p); };
 
   // Kernel shapes: weight streaming when a group has few rows (decode), the
@@ -356,14 +363,14 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
     moe::GemmArgs a = {};
     a.nseg = 1;
     a.seg[0] = {reinterpret_cast<const uint8_t*>(xdq), nullptr, d, w.w_down.codes, w.w_down.scales,
-                nullptr, nullptr, 0, 0, d};
+                nullptr, nullptr, 0, 0, d, wrm};
     a.G = 1;
     a.M = T;
     a.N = L;
     a.ldc = L;
     MOE_HIP(moe::launch_bf16_mx_splitk(a, zpart, moe::bf16_mx_splitk_slices(T, L, d), z, zq, zqs, s));
   } else {
-    MOE_HIP(moe::launch_decode_e2m1_bf16(w.w_down.codes, w.w_down.scales, L, d, wdn16, s));
+    MOE_HIP(moe::launch_decode_e2m1_bf16(w.w_down.codes, w.w_down.scales, L, d, wdn16, s, 1 - wrm));
     moe::GemmArgs a = {};
     a.nseg = 1;
     a.seg[0] = {reinterpret_cast<const uint8_t*>(xdq), nullptr, d, reinterpret_cast<const uint8_t*>(wdn16),
@@ -408,7 +415,8 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
                 w.w_up_e.scales,
                 (int64_t)F * L / 2,
                 (int64_t)F * L / 32,
-                L};
+                L,
+                wrm};
     a.offsets = offsets;
     a.mtile_start = ms_r;
     a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? nullptr : tg1;
@@ -430,7 +438,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
     moe::GemmArgs a = {};
     a.nseg = 1;
     a.seg[0] = {hq, hqs, F, w.w_down_e.codes, w.w_down_e.scales, nullptr, nullptr, (int64_t)L * F / 2,
-                (int64_t)L * F / 32, F};
+                (int64_t)L * F / 32, F, wrm};
     a.offsets = offsets;
     a.mtile_start = ms_r;
     a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? nullptr : tg1;
@@ -487,7 +495,8 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
                 w.w_up_s.scales,
                 (int64_t)Fs * d / 2,
                 (int64_t)Fs * d / 32,
-                d};
+                d,
+                wrm};
     a.G = S;
     a.M = T;
     a.N = Fs;
@@ -527,7 +536,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
     moe::GemmArgs a = {};
     const int s0 = latent ? 1 : 0;
     a.nseg = s0 + S;
-    if (latent) a.seg[0] = {yq, yqs, L, w.w_up.codes, w.w_up.scales, nullptr, nullptr, 0, 0, L};
+    if (latent) a.seg[0] = {yq, yqs, L, w.w_up.codes, w.w_up.scales, nullptr, nullptr, 0, 0, L, wrm};
     a.c_accumulate = latent ? 0 : 1;
     for (int i = 0; i < S; ++i)
       a.seg[s0 + i] = {hs + (int64_t)i * T * Fs,
@@ -539,7 +548,8 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
                       nullptr,
                       0,
                       0,
-                      Fs};
+                      Fs,
+                      wrm};
     a.G = 1;
     a.M = T;
     a.N = d;

@@ -230,14 +230,19 @@ __global__ void __launch_bounds__(256) bf16_splitk_kernel(const GemmArgs p, cons
     const bool up = sg.b2 != nullptr && c >= half;
     const int cc = up ? c - half : c;
     const uint8_t* base = (up ? sg.b2 : sg.b) + (int64_t)t.g * sg.b_gstride;
-    if (MXB) {
+    if (MXB && sg.b_rm) {  // row cc, MX block 4 ks + g4: 16 bytes of the row, its scale byte
       gb[ni] = base + (int64_t)cc * (K >> 1) + 64 * ks0 + 16 * g4;
       gs[ni] = (up ? sg.b2s : sg.bs) + (int64_t)t.g * sg.bs_gstride + (int64_t)cc * (K >> 5) + 4 * ks0 + g4;
+    } else if (MXB) {      // the same block in fragment order (lane chunk cc % 16 + 16 g4 of block (cc / 16, ks))
+      gb[ni] = base + ((int64_t)(cc >> 4) * (K >> 7) + ks0) * 1024 + 16 * ((cc & 15) + 16 * g4);
+      gs[ni] = (up ? sg.b2s : sg.bs) + (int64_t)t.g * sg.bs_gstride + ((int64_t)ks0 * p.N + cc) * 4 + g4;
     } else {
       gb[ni] = base + ((int64_t)cc * K + 128 * ks0 + 8 * g4) * 2;
       gs[ni] = nullptr;
     }
   }
+  const int64_t b_k = sg.b_rm ? 64 : 1024;              // MX weights: bytes between K-steps of a lane's codes
+  const int64_t bs_k = sg.b_rm ? 4 : 4 * (int64_t)p.N;  // and of its scale
   struct BSlot {
     uint4 v[NW][BQ];
     int sc[NW];
@@ -252,8 +257,8 @@ __global__ void __launch_bounds__(256) bf16_splitk_kernel(const GemmArgs p, cons
 #pragma unroll
     for (int ni = 0; ni < NW; ++ni) {
       if (MXB) {
-        q.v[ni][0] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gb[ni] + 64 * ks)));
-        q.sc[ni] = gs[ni][4 * ks];
+        q.v[ni][0] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(gb[ni] + b_k * ks)));
+        q.sc[ni] = gs[ni][bs_k * ks];
       } else {
 #pragma unroll
         for (int u = 0; u < BQ; ++u)
@@ -454,17 +459,24 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
       ap[mi] = sg.a + arow[mi] * sg.lda + 16 * g4;
       asp[mi] = sg.as + arow[mi] * kb + g4;
     }
+    // Weight operand of lane (r16, g4): row fcol + r16, elements 32 g4 .. +31
+    // of the K-step -- 16 bytes at 16 lane of the fragment-order block, or
+    // bytes 16 g4 of the row's 64 for the K-step when row-major.
+    const bool brm = sg.b_rm != 0;
     const uint8_t* bp[NW][NB];
     const uint8_t* bsp[NW][NB];
 #pragma unroll
     for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
       for (int h = 0; h < NB; ++h) {
-        bp[ni][h] = (h == 0 ? sg.b : sg.b2) + (int64_t)t.g * sg.b_gstride + (int64_t)(fcol[ni] >> 4) * nks * 1024 +
-                    16 * lane;
-        bsp[ni][h] = (h == 0 ? sg.bs : sg.b2s) + (int64_t)t.g * sg.bs_gstride + 4 * (int64_t)(fcol[ni] + r16) + g4;
+        const uint8_t* cb = (h == 0 ? sg.b : sg.b2) + (int64_t)t.g * sg.b_gstride;
+        const uint8_t* sb = (h == 0 ? sg.bs : sg.b2s) + (int64_t)t.g * sg.bs_gstride;
+        bp[ni][h] = brm ? cb + (int64_t)(fcol[ni] + r16) * (K >> 1) + 16 * g4
+                        : cb + (int64_t)(fcol[ni] >> 4) * nks * 1024 + 16 * lane;
+        bsp[ni][h] = brm ? sb + (int64_t)(fcol[ni] + r16) * kb + g4 : sb + 4 * (int64_t)(fcol[ni] + r16) + g4;
       }
-    const int64_t bs_k = 4 * (int64_t)p.N;  // bytes between K-steps of the scales
+    const int64_t b_k = brm ? 64 : 1024;                // bytes between K-steps of a lane's codes
+    const int64_t bs_k = brm ? 4 : 4 * (int64_t)p.N;    // bytes between K-steps of the scales
 
     // Register ring of D K-steps: slot j holds the operands of step ks + j
     // (weight block and scale per fragment, activation fragment and scale per
@@ -482,7 +494,7 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
       for (int ni = 0; ni < NW; ++ni)
 #pragma unroll
         for (int h = 0; h < NB; ++h) {
-          q.b[ni][h] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni][h] + 1024 * ks)));
+          q.b[ni][h] = to_uint4(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[ni][h] + b_k * ks)));
           q.bs[ni][h] = bsp[ni][h][bs_k * ks];
         }
 #pragma unroll

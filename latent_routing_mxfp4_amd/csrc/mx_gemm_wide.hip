@@ -147,21 +147,30 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
     const uint8_t* ga[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) ga[i] = sg.a + a_row[i] * sg.lda + 16 * a_chunk[i];
+    // Weight source addresses.  Fragment order: the block of 16 rows x 128
+    // elements is 1 KB contiguous and lane l takes bytes 16 l; row-major: lane
+    // l = r + 16 q takes bytes 16 q of row r's 64 bytes for the K-step.  Either
+    // way the LDS stage receives the block in fragment order.
+    const bool brm = sg.b_rm != 0;
     const uint8_t* gb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int up;
       const int c = b_col(16 * (4 * wave + i), up, p.N - 16);  // first row of the block
-      gb[i] = (up ? sg.b2 : sg.b) + (int64_t)g * sg.b_gstride + (int64_t)(c >> 4) * ksteps * 1024 + 16 * lane;
+      const uint8_t* base = (up ? sg.b2 : sg.b) + (int64_t)g * sg.b_gstride;
+      gb[i] = brm ? base + (int64_t)(c + (lane & 15)) * (K >> 1) + 16 * (lane >> 4)
+                  : base + (int64_t)(c >> 4) * ksteps * 1024 + 16 * lane;
     }
+    const int64_t b_kstride = brm ? 64 : 1024;  // bytes between K-steps of a lane's weight codes
     const uint8_t* gas = sg.as + as_row * (sg.lda >> 5);
     const uint8_t* gbs;
     {
       int up;
       const int c = b_col(64 * wave + lane, up, p.N - 1);
-      gbs = (up ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride + 4 * (int64_t)c;
+      const uint8_t* base = (up ? sg.b2s : sg.bs) + (int64_t)g * sg.bs_gstride;
+      gbs = brm ? base + (int64_t)c * kb : base + 4 * (int64_t)c;
     }
-    const int64_t bs_kstride = 4 * (int64_t)p.N;  // bytes between K-steps of the B scales
+    const int64_t bs_kstride = brm ? 4 : 4 * (int64_t)p.N;  // bytes between K-steps of the B scales
     // A stage's loads of one wave, in four parts: 2 A-code; 2 B-code; 2
     // B-code; A-scale and B-scale.
     auto issue_part = [&](int ks, int part) {
@@ -173,7 +182,7 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int i = 2 * (part - 1) + j;
-          gl_lds16(gb[i] + 1024 * ks, buf + WD_OFF_B + 1024 * (4 * wave + i));
+          gl_lds16(gb[i] + b_kstride * ks, buf + WD_OFF_B + 1024 * (4 * wave + i));
         }
       } else {
         gl_lds4(gas + 4 * ks, buf + WD_OFF_AS + 256 * wave);

@@ -93,13 +93,25 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
 }
 
 // E2M1 (packed) + E8M0 -> bf16, one thread per 32-element block.
+// One thread per MX block (row, j) of the output order: block b = row * K/32 + j.
+// Fragment-order input (frag != 0, N rows): its 16 code bytes are lane chunk
+// (row % 16) + 16 (j % 4) of block (row / 16, j / 4), its scale byte j % 4 of
+// dword (j / 4) * N + row.
 __global__ void __launch_bounds__(256) decode_e2m1_bf16_kernel(const uint4* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales, int64_t nblk,
-                                                              uint4* __restrict__ out) {
+                                                              uint4* __restrict__ out, int frag, int N, int K) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int kblk = K >> 5;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-    const uint4 c = codes[b];
-    const int e = (int)scales[b] - 127;
+    int64_t cb = b, sb = b;
+    if (frag) {
+      const int64_t row = b / kblk;
+      const int j = (int)(b - row * kblk);
+      cb = ((row >> 4) * (K >> 7) + (j >> 2)) * 64 + (row & 15) + 16 * (j & 3);
+      sb = ((int64_t)(j >> 2) * N + row) * 4 + (j & 3);
+    }
+    const uint4 c = codes[cb];
+    const int e = (int)scales[sb] - 127;
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {  // 8 elements per dword
@@ -137,13 +149,15 @@ hipError_t launch_round_bf16(const float* in, int64_t n, uint16_t* out, hipStrea
 }
 
 hipError_t launch_decode_e2m1_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K, uint16_t* out,
-                                   hipStream_t s) {
+                                   hipStream_t s, int frag) {
   const int64_t nblk = rows * (int64_t)K / 32;
   if (nblk == 0) return hipSuccess;
+  if (frag && (rows % 16 || K % 128 || rows > 0x7fffffff)) return hipErrorInvalidValue;
   int64_t blocks = (nblk + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   decode_e2m1_bf16_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(reinterpret_cast<const uint4*>(codes), scales,
-                                                                        nblk, reinterpret_cast<uint4*>(out));
+                                                                        nblk, reinterpret_cast<uint4*>(out), frag,
+                                                                        (int)rows, K);
   return hipGetLastError();
 }
 

@@ -43,12 +43,13 @@ class LayerShape:
     latent: bool = True          # False: no latent projections (d_latent == d_model)
     softmax_gates: bool = False  # gates = softmax over the winners' logits
     dense_bf16: bool = False     # latent projections and shared experts in bfloat16
+    weight_layout: int = _lib.MOE_WEIGHTS_FRAGMENT   # or MOE_WEIGHTS_ROW_MAJOR ([out][in] as stored)
 
     @classmethod
-    def of(cls, cfg) -> "LayerShape":
+    def of(cls, cfg, weight_layout: int = _lib.MOE_WEIGHTS_FRAGMENT) -> "LayerShape":
         return cls(cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k, cfg.n_shared, cfg.d_ff_routed,
                    cfg.d_ff_shared, bool(getattr(cfg, "latent", True)), getattr(cfg, "gating", "sigmoid") == "softmax",
-                   getattr(cfg, "precision", "mx") == "bf16")
+                   getattr(cfg, "precision", "mx") == "bf16", int(weight_layout))
 
     def matrix_shape(self, name: str) -> Tuple[int, int]:
         d, L, F, Fs = self.d_model, self.d_latent, self.d_ff_routed, self.d_ff_shared
@@ -65,7 +66,7 @@ class LayerShape:
     def c_config(self, max_tokens: int) -> _lib.MoeLayerConfig:
         return _lib.MoeLayerConfig(self.d_model, self.d_latent, self.n_routed, self.top_k, self.n_shared,
                                    self.d_ff_routed, self.d_ff_shared, int(max_tokens), int(not self.latent),
-                                   int(self.softmax_gates), int(self.dense_bf16))
+                                   int(self.softmax_gates), int(self.dense_bf16), int(self.weight_layout))
 
 
 # --------------------------------------------------------------------------- MX helpers
@@ -148,9 +149,8 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
 
     ``host_fp32(name, index)`` returns the fp32 ``[out][in]`` matrix (numpy);
     matrices are produced by a thread pool, copied to the device one at a
-    time and encoded there: ``w_down`` row-major (``moe_mx_quantize``, it feeds
-    the bf16 latent projection), every other matrix in fragment order
-    (``moe_mx_quantize_weights``, read by the MX GEMMs).  Under the
+    time and encoded there to MXFP4 in the shape's weight layout: row-major
+    (``moe_mx_quantize``) or fragment order (``moe_mx_quantize_weights``).  Under the
     higher-precision map the latent projections and shared experts are
     rounded to bfloat16 instead (``moe_round_bf16``), stored row-major under
     ``<name>_bf16`` (their MX entries are None).
@@ -193,7 +193,7 @@ def encode_weights(shape: LayerShape, host_fp32: Callable[[str, int], np.ndarray
             dev = torch.from_numpy(np.ascontiguousarray(host, dtype=np.float32)).to(device, non_blocking=False)
             if scales is None:
                 _lib.moe_round_bf16(dev.data_ptr(), dev.numel(), codes.data_ptr(), _stream())
-            elif name == "w_down":
+            elif shape.weight_layout == _lib.MOE_WEIGHTS_ROW_MAJOR:
                 mx_quantize(dev, FMT_E2M1, out=(codes, scales))
             else:
                 mx_quantize_weights(dev, out=(codes, scales))

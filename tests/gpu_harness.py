@@ -17,19 +17,19 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_weights(cfg, selection_bias=None, workers=8):
-    shape = LY.LayerShape.of(cfg)
+def gpu_weights(cfg, selection_bias=None, workers=8, weight_layout=None):
+    shape = LY.LayerShape.of(cfg) if weight_layout is None else LY.LayerShape.of(cfg, weight_layout)
     extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg),
              "selection_bias": selection_bias}
     return shape, LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra, workers=workers,
                                     progress=lambda j, n: say(f"    {j} of {n} weight matrices encoded"))
 
 
-def gpu_layer(cfg, max_tokens=None, selection_bias=None, weights=None):
+def gpu_layer(cfg, max_tokens=None, selection_bias=None, weights=None, weight_layout=None):
     if weights is None:
-        shape, weights = gpu_weights(cfg, selection_bias)
+        shape, weights = gpu_weights(cfg, selection_bias, weight_layout=weight_layout)
     else:
-        shape = LY.LayerShape.of(cfg)
+        shape = LY.LayerShape.of(cfg) if weight_layout is None else LY.LayerShape.of(cfg, weight_layout)
     return LY.LatentMoE(shape, weights, max_tokens or cfg.T), weights
 
 

@@ -255,3 +255,22 @@ def test_quantile_balance_rejects_bad_arguments_before_any_launch():
     assert call(ws=None) == _lib.MOE_ERR_WORKSPACE
     assert call(ws_bytes=need - 1) == _lib.MOE_ERR_WORKSPACE
     assert call(ws=FAKE + 8) == _lib.MOE_ERR_WORKSPACE
+
+
+def test_weight_layout_and_workspace_bytes():
+    """The config names the MX weight layout (row-major = 0, the zero default,
+    or fragment order); any other value is refused.  moe_layer_workspace_bytes
+    returns moe_layer_workspace_size's figure, and 0 where that is an error."""
+    lib = _lib.load()
+    for layout in (_lib.MOE_WEIGHTS_ROW_MAJOR, _lib.MOE_WEIGHTS_FRAGMENT):
+        cfg = _k3()
+        cfg.weight_layout = layout
+        assert _create_status(cfg, _weights()) == _lib.MOE_OK
+        for T in (0, 1, 64, 16384):
+            assert _lib.moe_layer_workspace_bytes(cfg, T) == _lib.moe_layer_workspace_size(cfg, T)
+    cfg = _k3()
+    cfg.weight_layout = 2
+    assert _create_status(cfg, _weights()) == _lib.MOE_ERR_INVALID_ARG
+    assert _lib.moe_layer_workspace_bytes(cfg, 64) == 0
+    assert _lib.moe_layer_workspace_bytes(_k3(), 16385) == 0
+    assert lib.moe_layer_workspace_bytes(None, 64) == 0

@@ -20,9 +20,9 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _check_weight_codes(cfg, gw, W):
-    """The GPU-encoded weights equal the oracle's codes: w_down row-major, the
-    rest in fragment order (read back through the layout's numpy statement)."""
+def _check_weight_codes(cfg, gw, W, row_major=False):
+    """The GPU-encoded MX weights equal the oracle's codes, in fragment order
+    (read back through the layout's numpy statement) or row-major."""
     from oracle import mx
     if W.precision == "bf16":   # bfloat16 dense weights: the oracle's own rounding of the same fp32
         for name in ("w_down", "w_up", "w_gate_s", "w_up_s", "w_down_s"):
@@ -39,7 +39,7 @@ def _check_weight_codes(cfg, gw, W):
             continue
         c, s = gw[name]
         c, s = c.cpu().numpy(), s.cpu().numpy()
-        if name != "w_down":
+        if not row_major:
             c, s = from_fragment_order(c, s)
         ref = getattr(W, name)
         assert np.array_equal(s, ref.scales), name
@@ -49,7 +49,9 @@ def _check_weight_codes(cfg, gw, W):
         if not lst or not isinstance(lst[0], moe.MXTensor):
             continue
         c, s = gw[name]
-        c, s = from_fragment_order(c.cpu().numpy(), s.cpu().numpy())
+        c, s = c.cpu().numpy(), s.cpu().numpy()
+        if not row_major:
+            c, s = from_fragment_order(c, s)
         for i, ref in enumerate(lst):
             assert np.array_equal(s[i], ref.scales), (name, i)
             assert np.array_equal(c[i], mx.pack_e2m1(ref.codes)), (name, i)
@@ -240,3 +242,60 @@ def test_no_shared_expert_latent_layers():
         for T in (40, 300):
             cfg = dataclasses.replace(synth.config(name, T=T), n_shared=0)
             _layer_case(cfg, check_codes=False)
+
+
+# --------------------------------------------------------------------------- weight layouts
+
+
+def _y(lay, x):
+    xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    y = lay.forward(xt)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("mid", 48), ("mid", 600), ("tiny_bf16", 300), ("k2_tiny", 64)])
+def test_row_major_weights_give_the_fragment_order_result(name, T):
+    """MX weights handed over row-major [out][in] (weight_layout = ROW_MAJOR,
+    the codes as a checkpoint stores them) give bit for bit the forward on the
+    same codes in fragment order: the kernels stage identical operands and
+    only their global addresses differ.  48 tokens run the weight-streaming
+    and K-split kernels, 600 the LDS-staged ones and the bf16 image of
+    W_down."""
+    from latent_routing_mxfp4_amd import _lib
+    cfg = synth.config(name, T=T)
+    say(f"row-major weights {name} T={T}")
+    W = weights.layer(cfg)
+    lay_f, _ = gpu_layer(cfg)
+    lay_r, gw_r = gpu_layer(cfg, weight_layout=_lib.MOE_WEIGHTS_ROW_MAJOR)
+    _check_weight_codes(cfg, gw_r, W, row_major=True)
+    x = synth.gen_hidden(cfg)
+    yf, yr = _y(lay_f, x), _y(lay_r, x)
+    lay_f.close()
+    lay_r.close()
+    assert np.array_equal(yf.view(np.uint32), yr.view(np.uint32))
+
+
+def test_checkpoint_row_major_weights_packed_to_fragment_order():
+    """Row-major MXFP4 weights (as stored) converted by moe_mx_pack_weights and
+    run in fragment order: the oracle's result, and bit for bit the row-major
+    forward on the unpacked codes."""
+    from latent_routing_mxfp4_amd import _lib
+    from latent_routing_mxfp4_amd import layer as LY
+    cfg = synth.config("tiny")
+    say(f"packed checkpoint weights {cfg.name} T={cfg.T}")
+    W = weights.layer(cfg)
+    lay_r, gw_r = gpu_layer(cfg, weight_layout=_lib.MOE_WEIGHTS_ROW_MAJOR)
+    packed = dict(gw_r)
+    for name in LY.DENSE + LY.ROUTED + LY.SHARED:
+        if gw_r.get(name) is not None:
+            packed[name] = LY.mx_pack_weights(*gw_r[name])
+    _check_weight_codes(cfg, packed, W)
+    lay_p = LY.LatentMoE(LY.LayerShape.of(cfg), packed, cfg.T)
+    x = synth.gen_hidden(cfg)
+    y, tr = run_traced(lay_p, x)
+    o = moe.forward(x, W, cfg.top_k)
+    parity.check_layer(cfg, W, o, y, tr, x=x, say=say)
+    assert np.array_equal(y.view(np.uint32), _y(lay_r, x).view(np.uint32))
+    lay_p.close()
+    lay_r.close()

@@ -143,3 +143,27 @@ def test_k3_bf16_map_decode_64_tokens(k3):
 def test_k3_bf16_map_prefill_16384_tokens(k3):
     """The higher-precision map at K3 width, 16384 tokens (LDS bf16 GEMMs)."""
     _run(k3, "k3_prefill_bf16")
+
+
+def test_k3_row_major_weights_bitwise(k3):
+    """The K3-width weights handed over row-major give bit for bit the
+    fragment-order forward, at the decode and prefill batch sizes (the
+    weight-streaming, K-split and LDS-staged kernels)."""
+    LY, shape, gw, W, cache = k3
+    from latent_routing_mxfp4_amd import _lib
+    base = synth.config("k3_prefill")
+    say("K3: encoding all weights row-major on the GPU")
+    rshape, gr = gpu_weights(base, workers=16, weight_layout=_lib.MOE_WEIGHTS_ROW_MAJOR)
+    for name in ("k3_decode", "k3_prefill"):
+        cfg = synth.config(name)
+        say(f"  {name}: T={cfg.T}, row-major against fragment order")
+        x = torch.from_numpy(synth.gen_hidden(cfg)).cuda()
+        outs = []
+        for sh, w in ((shape, gw), (rshape, gr)):
+            lay = LY.LatentMoE(sh, w, cfg.T)
+            outs.append(lay.forward(x).cpu())
+            torch.cuda.synchronize()
+            lay.close()
+        assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32)), name
+    del gr
+    torch.cuda.empty_cache()
