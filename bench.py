@@ -131,7 +131,9 @@ def run_workload(name, steps, warmup, weights, hip, say, logit_bias=None):
 
     stage_ms = {}
     for si, sname in enumerate(_lib.STAGES):
-        stage_ms[sname] = statistics.mean(evs.elapsed(i, si, si + 1) for i in range(steps))
+        # median over the timed steps (a slow first step or a stray hiccup does
+        # not move it; the profile summary takes the median the same way)
+        stage_ms[sname] = statistics.median(evs.elapsed(i, si, si + 1) for i in range(steps))
     # per-step forward time between the first and the last stage event
     per_step = sorted(evs.elapsed(i, 0, len(_lib.STAGES)) for i in range(steps))
     pick = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
@@ -204,6 +206,31 @@ def k2_report(steps, warmup, hip, say):
             "stage_ms": kst, "step_events_ms": kwork["step_events_ms"]}
 
 
+def small_report(name, steps, warmup, hip, say):
+    """The small parity workloads (tiny: 64 tokens; mid: 4096 tokens, 128
+    experts): throughput and the MX matrix-core share, on their own weights.
+    Report lines beside the headline; launch-bound (tiny) or short (mid)."""
+    import torch
+
+    import synth
+    from latent_routing_mxfp4_amd import layer as LY
+
+    cfg = synth.config(name)
+    shape = LY.LayerShape.of(cfg)
+    extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg)}
+    weights = LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra,
+                                workers=min(16, len(os.sched_getaffinity(0))))
+    c, ms, st, work, counts = run_workload(name, steps, warmup, weights, hip, say)
+    del weights
+    torch.cuda.empty_cache()
+    return {"workload": f"{c.name}: T={c.T}, d={c.d_model}, latent={c.d_latent}, E={c.n_routed} top-{c.top_k}, "
+                        f"{c.n_shared} shared, d_ff={c.d_ff_routed}",
+            "value": c.T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+            "mx_tflops": work["mx_flops"] / (ms / 1e3) / 1e12,
+            "mx_frac": work["mx_flops"] / (ms / 1e3) / 1e12 / PEAK_MX_TFLOPS,
+            "stage_ms": st, "step_events_ms": work["step_events_ms"]}
+
+
 def qb_report(steps, warmup, say):
     """Quantile Balancing of the selection bias at the K3 prefill shape (16384
     tokens x 896 experts, top-16) on seeded N(0, 1) logits: time per update and
@@ -236,8 +263,22 @@ def qb_report(steps, warmup, say):
             "logits_gbs": 2 * logit_bytes / (ms / 1e3) / 1e9, "logits_bytes": logit_bytes}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(name, n_tokens, say):
-    """The oracle, as it stands, on the first n_tokens of the workload."""
+    """The oracle, as it stands, on the workload: the routing and dispatch of
+    EVERY token of the batch (quantise x, latent, router, top-k, gates, expert
+    sort), timed in full; the expert FFNs, combine, up-projection and shared
+    experts on the first ``n_tokens`` tokens (tokens are independent: the layer
+    is dropless), timed and extrapolated per token to the whole batch; and the
+    same sample again with one BLAS thread.  Expert weights are encoded
+    beforehand (load-time work, untimed)."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
 
@@ -245,37 +286,60 @@ def cpu_baseline(name, n_tokens, say):
     from oracle import moe, weights
 
     cfg = synth.config(name)
-    x = synth.gen_hidden(cfg, T=n_tokens)
+    T = cfg.T
+    x = synth.gen_hidden(cfg)
     W = weights.layer(cfg, experts="lazy")
-    cache = weights.ExpertCache(cfg, maxsize=n_tokens * cfg.top_k + 8)
-    # find the experts the sample needs and encode them beforehand (not timed:
-    # weight encoding is load-time work on the GPU side too)
-    z = moe.mm(moe.quant(x), W.w_down)
+    cores = _blas_threads()
+    # 1. routing and dispatch of every token
+    t0 = time.perf_counter()
+    xq = moe.quant(x)
+    z = moe.mm(xq, W.w_down)
     r = moe.route(z, W.w_router, cfg.top_k, W.logit_bias, W.selection_bias)
-    need = sorted(set(r.ids.reshape(-1).tolist()))
+    moe.dispatch(r.ids, cfg.n_routed)
+    t_route = time.perf_counter() - t0
+    say(f"cpu oracle: routing and dispatch of all {T} tokens in {t_route:.2f} s ({cores} BLAS threads)")
+    # 2. the whole layer on the sample (its experts encoded first, untimed)
+    xs = x[:n_tokens]
+    cache = weights.ExpertCache(cfg, maxsize=n_tokens * cfg.top_k + 8)
+    need = sorted(set(r.ids[:n_tokens].reshape(-1).tolist()))
     with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
         list(ex.map(cache, need))
     t0 = time.perf_counter()
-    moe.forward(x, W, cfg.top_k, expert_weights=cache)
-    dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
+    moe.forward(xs, W, cfg.top_k, expert_weights=cache)
+    t_sample = time.perf_counter() - t0
+    t_single = None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            moe.forward(xs, W, cfg.top_k, expert_weights=cache)
+            t_single = time.perf_counter() - t0
+    except ImportError:
         pass
-    say(f"cpu oracle: {n_tokens} tokens of {name} in {dt:.2f} s ({cores} threads)")
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of the {name} batch through the fp64 oracle forward "
-                      f"({len(need)} routed experts, weights pre-encoded outside the timed call); "
-                      f"{dt:.1f} s wall"}
+    per_tok = t_sample / n_tokens
+    total = t_route + per_tok * T     # routing of the batch + the sample's per-token cost for every token
+    say(f"cpu oracle: whole layer on {n_tokens} tokens in {t_sample:.2f} s ({per_tok:.2f} s/token); "
+        f"batch extrapolated {total:.0f} s")
+    out = {"value": T / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": (f"{name}: routing and dispatch of all {T} tokens timed ({t_route:.1f} s); the whole layer "
+                      f"on the first {n_tokens} tokens timed ({t_sample:.1f} s, {len(need)} routed experts, "
+                      f"weights encoded beforehand) and extrapolated per token to {T} tokens: value is "
+                      f"EXTRAPOLATED"),
+           "routing_all_tokens_s": t_route, "sample_tokens": n_tokens, "layer_s_per_token": per_tok,
+           "extrapolated": True}
+    if t_single is not None:
+        out["single_thread_layer_s_per_token"] = t_single / n_tokens
+        out["single_thread_sample_tokens_per_s"] = n_tokens / t_single
+    return out
 
 
 # --------------------------------------------------------------------------- rocprofv3 summaries
 
 PROFILE_MD = os.path.join(ROOT, "profiles", "k3_layer_kernels_and_hbm_traffic.md")
 PROFILE_CMD = ("python3 /root/repo/bench.py --steps 3 --warmup 1 --decode-steps 5 --no-cpu-baseline "
-               "--k2-steps 0 --bf16-steps 0 --copy-probe")
+               "--skew-steps 0 --k2-steps 0 --bf16-steps 0 --qb-steps 0 --small-steps 0")
+SIMDS = 1024    # MI355X: 256 compute units x 4 SIMDs (the MfmaUtil denominator)
+XCDS = 8        # the counter CSV holds GRBM_GUI_ACTIVE summed over the 8 XCDs' instances
 
 
 def source_digest() -> str:
@@ -304,12 +368,14 @@ def _grid(r):
     return int(r.get("Grid_Size_X", 1)) * int(r.get("Grid_Size_Y", 1)) * int(r.get("Grid_Size_Z", 1))
 
 
-def summarize_profiles(stats_dir, fetch_dir, write_dir) -> str:
-    """Markdown summary of three rocprofv3 runs of PROFILE_CMD: per (kernel,
-    grid) the dispatch count, mean duration, FETCH_SIZE and WRITE_SIZE per
-    dispatch, and HBM bytes per launch scaled by the same counters on the
-    1 GiB copy kernel (--copy-probe); plus the machine-readable traffic lines
-    the benchmark reads."""
+def summarize_profiles(stats_dir, fetch_dir, write_dir, mfma_dir=None) -> str:
+    """Markdown summary of the rocprofv3 runs of PROFILE_CMD: per (kernel,
+    grid) the dispatch count, the median duration over the dispatches after the
+    first (the warm-up step), FETCH_SIZE and WRITE_SIZE per dispatch, HBM bytes
+    per launch scaled by the same counters on the 1 GiB copy kernel the
+    benchmark runs first, and the matrix cores' busy share
+    (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs)); plus the
+    machine-readable traffic lines the benchmark reads."""
     import csv
     import collections
     import re
@@ -321,15 +387,26 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir) -> str:
 
     trace = one(stats_dir, "kernel_trace.csv")
     dur = collections.defaultdict(list)
-    for r in trace:
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
         dur[(r["Kernel_Name"], _grid(r))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
-    cnt = {}
-    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        agg = collections.defaultdict(list)
-        for r in one(d, "counter_collection.csv"):
-            if r["Counter_Name"] == name:
-                agg[(r["Kernel_Name"], _grid(r))].append(float(r["Counter_Value"]))
-        cnt[name] = {k: sum(v) / len(v) for k, v in agg.items()}
+
+    def counters(d, names):
+        # per dispatch (rocprofv3 writes each counter's instances already summed)
+        agg = collections.defaultdict(lambda: collections.defaultdict(float))
+        rows = one(d, "counter_collection.csv")
+        for r in rows:
+            n = r["Counter_Name"]
+            if n in names:
+                agg[(r["Kernel_Name"], _grid(r), r.get("Dispatch_Id", ""))][n] += float(r["Counter_Value"])
+        per = collections.defaultdict(lambda: collections.defaultdict(list))
+        for (kn, gr, _), v in agg.items():
+            for n, x in v.items():
+                per[(kn, gr)][n].append(x)
+        return {k: {n: sum(x) / len(x) for n, x in v.items()} for k, v in per.items()}
+
+    cnt = {"FETCH_SIZE": {k: v["FETCH_SIZE"] for k, v in counters(fetch_dir, {"FETCH_SIZE"}).items()},
+           "WRITE_SIZE": {k: v["WRITE_SIZE"] for k, v in counters(write_dir, {"WRITE_SIZE"}).items()}}
+    mfma = counters(mfma_dir, {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"}) if mfma_dir else {}
     # calibration: torch.mul over 2^28 floats reads 1 GiB and writes 1 GiB
     probe = [k for k in cnt["FETCH_SIZE"] if "MulFunctor" in k[0]]   # the only torch.mul of the run
     assert probe, "no copy-probe dispatch in the counter runs"
@@ -344,22 +421,35 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir) -> str:
     for key, ds in dur.items():
         fk, wk = cnt["FETCH_SIZE"].get(key), cnt["WRITE_SIZE"].get(key)
         hbm = None if fk is None or wk is None else (fk * f_fac + wk * w_fac) * 1024
-        rows.append((sum(ds), short(key[0]), key[1], len(ds), sum(ds) / len(ds), fk, wk, hbm))
+        med = statistics.median(ds[1:] if len(ds) > 1 else ds)
+        m = mfma.get(key)
+        util = None
+        if m and m.get("GRBM_GUI_ACTIVE"):   # busy cycles over (the GPU's active cycles x SIMDs)
+            util = 100.0 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (m["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+        rows.append((sum(ds), short(key[0]), key[1], len(ds), med, fk, wk, hbm, util))
     rows.sort(reverse=True)
-    out = ["# K3 LatentMoE layer on MI355X: kernel times and HBM traffic", "",
+    out = ["# K3 LatentMoE layer on MI355X: kernel times, HBM traffic and matrix-core busy share", "",
            "Commands (run from /tmp with TMPDIR=/tmp; the benchmark runs the 16384-token prefill batch, "
            "then the 64-token decode batch, both at K3 width):", "",
            "    rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/p_stats -o run -- " + PROFILE_CMD,
            "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/p_fetch -o run -- " + PROFILE_CMD,
            "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/p_write -o run -- " + PROFILE_CMD,
-           "    python3 /root/repo/bench.py --summarize /tmp/p_stats /tmp/p_fetch /tmp/p_write", "",
+           "    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d /tmp/p_mfma -o run -- "
+           + PROFILE_CMD,
+           "    python3 /root/repo/bench.py --summarize /tmp/p_stats /tmp/p_fetch /tmp/p_write /tmp/p_mfma", "",
            f"Counter calibration (1 GiB read + 1 GiB write elementwise kernel): FETCH_SIZE x {f_fac:.3f}, "
-           f"WRITE_SIZE x {w_fac:.3f} (KiB per dispatch -> KiB moved).", "",
-           "| kernel | grid (threads) | dispatches | mean ms | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB/launch |",
-           "|---|---:|---:|---:|---:|---:|---:|"]
-    for tot, name, grid, n, mean, fk, wk, hbm in rows[:24]:
-        out.append(f"| {name} | {grid} | {n} | {mean:.4f} | {fk if fk is None else round(fk)} | "
-                   f"{wk if wk is None else round(wk)} | {'-' if hbm is None else f'{hbm / 1e6:.1f}'} |")
+           f"WRITE_SIZE x {w_fac:.3f} (KiB per dispatch -> KiB moved).  Median ms: over the dispatches after the "
+           f"first of each (kernel, grid) (the first belongs to the warm-up step).  MFMA busy: "
+           f"SQ_VALU_MFMA_BUSY_CYCLES / (GPU active cycles x {SIMDS} SIMDs) per dispatch, averaged; the CSV "
+           f"holds GRBM_GUI_ACTIVE summed over the {XCDS} XCDs (a 0.154 ms fill kernel reads 8 x its 367 k "
+           f"cycles), so the active cycles are GRBM_GUI_ACTIVE / {XCDS}.  The matrix-core rate probe "
+           f"(moe::mfma_rate_kernel, back-to-back FP8 x FP4 MFMAs) reads about 79% busy at 3.9 PFLOP/s.", "",
+           "| kernel | grid (threads) | dispatches | median ms | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB/launch | MFMA busy % |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for tot, name, grid, n, med, fk, wk, hbm, util in rows[:24]:
+        out.append(f"| {name} | {grid} | {n} | {med:.4f} | {fk if fk is None else round(fk)} | "
+                   f"{wk if wk is None else round(wk)} | {'-' if hbm is None else f'{hbm / 1e6:.1f}'} | "
+                   f"{'-' if util is None else f'{util:.1f}'} |")
     # the dominant kernels: expert_up = largest-grid dispatch of the prefill / decode gate-up kernels
     out += ["", "Dominant kernels (expert_up: routed gate/up GEMM + SwiGLU + MXFP8), machine-readable:", ""]
     dig = source_digest()
@@ -368,7 +458,7 @@ def summarize_profiles(stats_dir, fetch_dir, write_dir) -> str:
         if not cand:
             continue
         r = max(cand, key=lambda r: r[2])
-        out.append(f"    traffic {wl} expert_up mean_ms={r[4]:.4f} hbm_bytes={0 if r[7] is None else int(r[7])} "
+        out.append(f"    traffic {wl} expert_up median_ms={r[4]:.4f} hbm_bytes={0 if r[7] is None else int(r[7])} "
                    f"sources={dig}")
     return "\n".join(out) + "\n"
 
@@ -381,15 +471,15 @@ def profiled_traffic(workload: str):
     except OSError:
         return None
     import re
-    m = re.search(rf"traffic {workload} expert_up mean_ms=([0-9.]+) hbm_bytes=([0-9]+) sources=([0-9a-f]+)", text)
+    m = re.search(rf"traffic {workload} expert_up median_ms=([0-9.]+) hbm_bytes=([0-9]+) sources=([0-9a-f]+)", text)
     if not m or m.group(3) != source_digest():
         return None
     return {"bytes": int(m.group(2)), "profiled_ms": float(m.group(1))}
 
 
 def main():
-    if len(sys.argv) == 5 and sys.argv[1] == "--summarize":
-        sys.stdout.write(summarize_profiles(*sys.argv[2:5]))
+    if len(sys.argv) in (5, 6) and sys.argv[1] == "--summarize":
+        sys.stdout.write(summarize_profiles(*sys.argv[2:]))
         return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,7 +497,11 @@ def main():
                     help="Quantile Balancing updates at the K3 prefill shape reported under 'quantile_balance' (0: skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=2,
+                    help="tokens of the batch the CPU oracle runs the whole layer on (extrapolated)")
+    ap.add_argument("--small-steps", type=int, default=20,
+                    help="steps of the tiny (64-token) and mid (4096-token) layers reported under 'tiny' and 'mid' "
+                         "(0: skip)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="kept for the profile command: the copy probe now always runs first")
@@ -472,8 +566,6 @@ def main():
             "traffic": None if tp is None else tp["bytes"],
             "algorithmic_bytes": work["expert_up_bytes"]}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # the same kernel against the matrix-core rate measured on this GPU just before
-    roof["frac_of_probe"] = roof["achieved"] / mfma_tflops
     out = {
         "metric": "LatentMoE layer tokens/s (K3 width); HBM GB/s decode, MFMA % prefill vs peak",
         "value": value,
@@ -541,6 +633,9 @@ def main():
     torch.cuda.empty_cache()
     if args.k2_steps > 0 and args.workload == "k3_prefill":
         out["k2"] = k2_report(args.k2_steps, args.warmup, hip, say)
+    if args.small_steps > 0 and args.workload == "k3_prefill":
+        for name in ("tiny", "mid"):
+            out[name] = small_report(name, args.small_steps, args.warmup, hip, say)
     if args.qb_steps > 0:
         out["quantile_balance"] = qb_report(args.qb_steps, args.warmup, say)
     if not args.no_cpu_baseline:
