@@ -109,6 +109,8 @@ struct GemmArgs {
   uint16_t* ob;                // EPI_SWIGLU_BF16: bfloat16 [rows][N]
   int64_t ob_gstride;          // elements between dense groups' bf16 outputs
   int max_mtiles;              // upper bound of M-tiles (grid size / n-tiles)
+  int kchains;                 // weight-streaming dense GEMMs: 4 = the K-steps are split over the 4 waves
+                               // of a workgroup (summed in wave order), 0 or 1 = one accumulator per output
 };
 
 // Kernel configurations: weight streaming with 16 or 64 rows per M-tile (few

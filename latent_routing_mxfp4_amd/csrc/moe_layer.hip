@@ -508,6 +508,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
     a.q_gstride = (int64_t)T * Fs;
     a.qs_gstride = (int64_t)T * Fs / 32;
     a.max_mtiles = S * ((T + mt_dense - 1) / mt_dense);
+    a.kchains = dense_shape == moe::GEMM_STREAM16 ? 4 : 1;  // few rows: K split over each workgroup's waves
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, dense_shape, s));
   }
   MOE_HIP(mark(MOE_EV_SHARED_UP));
@@ -556,6 +557,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
     a.c = y;
     a.ldc = d;
     a.max_mtiles = (T + mt_dense - 1) / mt_dense;
+    a.kchains = dense_shape == moe::GEMM_STREAM16 ? 4 : 1;
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, dense_shape, s));
   }
   MOE_HIP(mark(MOE_EV_OUT));

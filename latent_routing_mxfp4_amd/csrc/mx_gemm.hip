@@ -403,15 +403,23 @@ __global__ void __launch_bounds__(256) splitk_swiglu_kernel(const float* __restr
 // non-temporally) and the 64 contiguous scale bytes of the block's 16 rows,
 // D K-steps ahead of the MFMAs, together with the few activation rows
 // (L2-resident), read in the E4M3 operand layout straight from global memory.
-template <int MW, int NW, int EPI>
+//
+// KS = 4 (dense GEMMs of few rows, where one accumulator per output leaves too
+// few waves to keep enough weight bytes in flight): the workgroup's four
+// waves own the same columns and each takes a contiguous quarter of the
+// K-steps (counted over all K segments); waves 1-3 hand their accumulators to
+// wave 0 through LDS, which adds them in wave order (deterministic) and runs
+// the epilogue.
+template <int MW, int NW, int EPI, int KS = 1>
 __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   // K-steps in flight per wave: as many as keep two waves per SIMD.
   constexpr int D = MW == 1 ? (NW <= 2 ? 4 : 2) : 1;
   constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
   constexpr int NB = SWI ? 2 : 1;
   constexpr int MT = 16 * MW;
-  constexpr int NT = 4 * 16 * NW;
+  constexpr int NT = (KS == 1 ? 4 : 1) * 16 * NW;
   static_assert(EPI == EPI_F32 || NW % 2 == 0, "quantising epilogues need whole 32-column blocks per wave");
+  static_assert(KS == 1 || KS == 4, "one accumulator chain, or one per wave");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -419,7 +427,15 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   Tile t;
-  if (!decode_tile<MT, NT>(p, wave, 16 * NW, t)) return;  // uniform across the workgroup
+  if (!decode_tile<MT, NT>(p, wave, KS == 1 ? 16 * NW : 0, t)) return;  // uniform across the workgroup
+  // This wave's K-steps [kc0, kc1) of the concatenated segments.
+  int kc0 = 0, kc1 = 1 << 30;
+  if (KS > 1) {
+    int total = 0;
+    for (int s = 0; s < p.nseg; ++s) total += p.seg[s].K >> 7;
+    kc0 = (int)((int64_t)total * wave / KS);
+    kc1 = (int)((int64_t)total * (wave + 1) / KS);
+  }
 
   int64_t arow[MW];
 #pragma unroll
@@ -447,17 +463,22 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
 #pragma unroll
       for (int h = 0; h < NB; ++h) acc[mi][ni][h] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  int kseg = 0;  // K-steps of the segments before this one
   for (int s = 0; s < p.nseg; ++s) {
     const GemmSeg& sg = p.seg[s];
     const int K = sg.K;
-    const int nks = K >> 7;
     const int kb = K >> 5;
+    // this wave's steps of the segment: [k0, k0 + nks)
+    const int k0 = KS == 1 ? 0 : max(kc0 - kseg, 0);
+    const int nks = KS == 1 ? K >> 7 : min(kc1 - kseg, K >> 7) - k0;
+    kseg += K >> 7;
+    if (KS > 1 && nks <= 0) continue;
     const uint8_t* ap[MW];
     const uint8_t* asp[MW];
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi) {
-      ap[mi] = sg.a + arow[mi] * sg.lda + 16 * g4;
-      asp[mi] = sg.as + arow[mi] * kb + g4;
+      ap[mi] = sg.a + arow[mi] * sg.lda + 16 * g4 + 128 * k0;
+      asp[mi] = sg.as + arow[mi] * kb + g4 + 4 * k0;
     }
     // Weight operand of lane (r16, g4): row fcol + r16, elements 32 g4 .. +31
     // of the K-step -- 16 bytes at 16 lane of the fragment-order block, or
@@ -472,11 +493,18 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
         const uint8_t* cb = (h == 0 ? sg.b : sg.b2) + (int64_t)t.g * sg.b_gstride;
         const uint8_t* sb = (h == 0 ? sg.bs : sg.b2s) + (int64_t)t.g * sg.bs_gstride;
         bp[ni][h] = brm ? cb + (int64_t)(fcol[ni] + r16) * (K >> 1) + 16 * g4
-                        : cb + (int64_t)(fcol[ni] >> 4) * nks * 1024 + 16 * lane;
+                        : cb + (int64_t)(fcol[ni] >> 4) * (K >> 7) * 1024 + 16 * lane;
         bsp[ni][h] = brm ? sb + (int64_t)(fcol[ni] + r16) * kb + g4 : sb + 4 * (int64_t)(fcol[ni] + r16) + g4;
       }
     const int64_t b_k = brm ? 64 : 1024;                // bytes between K-steps of a lane's codes
     const int64_t bs_k = brm ? 4 : 4 * (int64_t)p.N;    // bytes between K-steps of the scales
+#pragma unroll
+    for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+      for (int h = 0; h < NB; ++h) {   // to this wave's first step
+        bp[ni][h] += b_k * k0;
+        bsp[ni][h] += bs_k * k0;
+      }
 
     // Register ring of D K-steps: slot j holds the operands of step ks + j
     // (weight block and scale per fragment, activation fragment and scale per
@@ -538,18 +566,51 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
     for (int j = 0; j < D; ++j)
       if (ks + j < nks) compute(sl[j]);
   }
+  if (KS > 1) {  // waves 1..3 hand their partial sums to wave 0, which adds them in order
+    constexpr int NV = MW * NW * NB * 4;  // floats per lane
+    __shared__ float red[KS > 1 ? KS - 1 : 1][NV][64];
+    if (wave > 0) {
+      int i = 0;
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+          for (int h = 0; h < NB; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[wave - 1][i++][lane] = acc[mi][ni][h][e];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KS - 1; ++w) {
+      int i = 0;
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NW; ++ni)
+#pragma unroll
+          for (int h = 0; h < NB; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[mi][ni][h][e] += red[w][i++][lane];
+    }
+  }
   epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
 template <int MW, int NW, int EPI>
 static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int NT = 4 * 16 * NW;
+  const bool chains = a.kchains == 4;
+  if (a.kchains != 0 && a.kchains != 1 && !chains) return hipErrorInvalidValue;
+  if (chains && a.offsets != nullptr) return hipErrorInvalidValue;  // dense GEMMs only
+  const int NT = (chains ? 1 : 4) * 16 * NW;
   if (a.N % 16 != 0) return hipErrorInvalidValue;  // fragment-order weights
   const int n_ntiles = (a.N + NT - 1) / NT;
   const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  mx_gemm_stream_kernel<MW, NW, EPI><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  if (chains) mx_gemm_stream_kernel<MW, NW, EPI, 4><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+  else mx_gemm_stream_kernel<MW, NW, EPI, 1><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -88,10 +88,16 @@ def mx_mfma_bound(a: moe.MXTensor, b: moe.MXTensor, value=None) -> np.ndarray:
     return mfma_model.mfma_bound(a, b, value)
 
 
+# The dense MX GEMMs of few-row batches (shared gate/up, output projection)
+# split their K-steps over up to 4 accumulator chains, one per wave of a
+# workgroup, added in wave order.
+DENSE_CHAINS = 4
+
+
 def mx_concat_bound(pairs, value: np.ndarray, extra_roundings: int = 0) -> np.ndarray:
-    """Block-scaled GEMM over K = the concatenation of ``pairs``' K segments,
-    one accumulator throughout (the output projection)."""
-    return mfma_model.mfma_bound_segments(pairs, value, extra_roundings)
+    """Block-scaled dense GEMM over K = the concatenation of ``pairs``' K
+    segments (the output projection)."""
+    return mfma_model.mfma_bound_segments(pairs, value, extra_roundings, chains=DENSE_CHAINS)
 
 
 def u16(a) -> np.ndarray:
@@ -348,7 +354,8 @@ class Replay:
             bh = swiglu_bound(g, u, gemm_bound(self.xq, wg, g), gemm_bound(self.xq, wu, u), h)
             self.hs_bound.append(bh)
             return self._adopt_bf16(f"hs{s}", h, bh, hq, self.tr["hs_bf16"][s])
-        bh = swiglu_bound(g, u, mx_mfma_bound(self.xq, wg, g), mx_mfma_bound(self.xq, wu, u), h)
+        bh = swiglu_bound(g, u, mfma_model.mfma_bound(self.xq, wg, g, chains=DENSE_CHAINS),
+                          mfma_model.mfma_bound(self.xq, wu, u, chains=DENSE_CHAINS), h)
         self.hs_bound.append(bh)
         return self._adopt(f"hs{s}", h, bh, hq, self.tr["hs_codes"][s], self.tr["hs_scales"][s])
 
