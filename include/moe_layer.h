@@ -334,6 +334,28 @@ int moe_mfma_rate_probe(int32_t iters, int32_t workgroups, float* out, void* str
 int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                 const uint8_t* b_scales, int32_t M, int32_t N, int32_t K, float* c, void* stream);
 
+/* The router's top-k selection (Kimi K3 and the New Open-Weights Moat, "How
+ * the router picks 16 of 896", Fig. 2), exposed for stage-level checks: per
+ * token t, score = sigmoid(logit) (softmax_gates = 0) or the logit itself
+ * (softmax_gates != 0); key = score + selection_bias[e] (NULL: zeros), NaN
+ * and -inf keys ranking last; ids[t][0..k) = the k best experts by (key
+ * descending, id ascending), in that order; gates = the winners' scores over
+ * their sum in slot order, or the softmax of the winners' logits.
+ * logits: device fp32 [T][E]; ids: device int32 [T][k]; gates: device fp32
+ * [T][k].  1 <= k <= min(E, 64), E <= 4096.  Asynchronous on `stream`.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
+int moe_router_topk(const float* logits, const float* selection_bias, int32_t T, int32_t E, int32_t k,
+                    int32_t softmax_gates, int32_t* ids, float* gates, void* stream);
+
+/* The same selection on the router's K-slice partial sums, as the layer runs
+ * it for few tokens: logits[t][e] = (partial[0][t][e] + partial[1][t][e] +
+ * ... + partial[nz-1][t][e], added in that order in fp32) + logit_bias[e]
+ * (NULL: + 0), written to `logits`, then the top-k above.  partial: device
+ * fp32 [nz][T][E], 1 <= nz; E <= 1024; other arguments as above. */
+int moe_router_reduce_topk(const float* partial, int32_t nz, const float* logit_bias, const float* selection_bias,
+                           int32_t T, int32_t E, int32_t k, int32_t softmax_gates, float* logits, int32_t* ids,
+                           float* gates, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,8 @@ EXPORTED = (
     "moe_quantile_balance_workspace_bytes",
     "moe_quantile_balance",
     "moe_mfma_rate_probe",
+    "moe_router_topk",
+    "moe_router_reduce_topk",
 )
 
 
@@ -136,6 +138,10 @@ def load() -> ctypes.CDLL:
     lib.moe_mx_pack_weights.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
     lib.moe_mx_gemm.restype = ctypes.c_int
     lib.moe_mx_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.moe_router_topk.restype = ctypes.c_int
+    lib.moe_router_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_router_reduce_topk.restype = ctypes.c_int
+    lib.moe_router_reduce_topk.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.moe_round_bf16.restype = ctypes.c_int
     lib.moe_round_bf16.argtypes = [vp, i64, vp, vp]
     lib.moe_quantile_balance_workspace_bytes.restype = sz
@@ -211,6 +217,19 @@ def moe_mx_gemm(a_codes: int, a_scales: int, b_codes: int, b_scales: int, M: int
                 stream: int = 0) -> None:
     _check(load().moe_mx_gemm(a_codes, a_scales, b_codes, b_scales, int(M), int(N), int(K), c, stream),
            "moe_mx_gemm")
+
+
+def moe_router_topk(logits: int, selection_bias: int, T: int, E: int, k: int, softmax_gates: bool, ids: int,
+                    gates: int, stream: int = 0) -> None:
+    _check(load().moe_router_topk(logits, selection_bias, int(T), int(E), int(k), int(bool(softmax_gates)), ids,
+                                  gates, stream), "moe_router_topk")
+
+
+def moe_router_reduce_topk(partial: int, nz: int, logit_bias: int, selection_bias: int, T: int, E: int, k: int,
+                           softmax_gates: bool, logits: int, ids: int, gates: int, stream: int = 0) -> None:
+    _check(load().moe_router_reduce_topk(partial, int(nz), logit_bias, selection_bias, int(T), int(E), int(k),
+                                         int(bool(softmax_gates)), logits, ids, gates, stream),
+           "moe_router_reduce_topk")
 
 
 def moe_round_bf16(src: int, n: int, out: int, stream: int = 0) -> None:

@@ -43,13 +43,24 @@ hipError_t launch_round_bf16(const float* in, int64_t n, uint16_t* out, hipStrea
 // small.
 int router_split(int T, int E, int L);
 bool router_bf16x3(int T, int E, int L);
+// leave_partial (with router_reduce_in_topk(T, E, L)): the K-slice sums stay
+// in `partial` for launch_router_reduce_topk, which adds them.
 hipError_t launch_router_logits(const float* z, const float* w, const float* logit_bias, int T, int E,
-                                int L, float* logits, float* partial, uint16_t* wplanes, hipStream_t s);
+                                int L, float* logits, float* partial, uint16_t* wplanes, hipStream_t s,
+                                bool leave_partial = false);
+bool router_reduce_in_topk(int T, int E, int L);
+int router_slices(int T, int E, int L);  // K-slice sums written to `partial` (<= router_split)
 // Per token: s = sigmoid(logit), key = s + sel_bias, top-k by (key desc, id asc),
 // gates = s / sum(s over the k winners).  softmax_gates: key = logit + sel_bias,
 // gates = softmax over the k winners' logits.
 hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, bool softmax_gates,
                        int32_t* ids, float* gates, hipStream_t s);
+// The same selection on the router's nz = router_split(T, E, L) K-slice sums
+// (E <= 1024): logits = sum of the slices in slice order + logit_bias, written
+// to `logits`, then top-k as launch_topk.
+hipError_t launch_router_reduce_topk(const float* partial, int nz, const float* logit_bias, const float* sel_bias,
+                                     int T, int E, int k, bool softmax_gates, float* logits, int32_t* ids,
+                                     float* gates, hipStream_t s);
 
 // ---- Dispatch (permute.hip) -------------------------------------------------
 size_t dispatch_scratch_ints(int T, int E);
@@ -118,6 +129,10 @@ struct GemmArgs {
 // rows per group: prefill; 128 x 512 for MX, 128 x 256 for bf16).
 enum GemmShape : int { GEMM_STREAM16 = 0, GEMM_STREAM64 = 1, GEMM_WIDE = 4 };
 int gemm_mtile(int shape);
+// Two weight-streaming GEMMs (GEMM_STREAM16 shape, EPI_F32 or
+// EPI_SWIGLU_QUANT, one accumulator chain each) in one launch: the dense
+// `pre` on the first workgroups, then `a` (dense or routed).
+hipError_t launch_mx_gemm_pair(const GemmArgs& pre, const GemmArgs& a, int epi, hipStream_t s);
 
 // Dense bf16 GEMM on the 512-thread 128 x 256 kernel (mx_gemm_wide.hip): G
 // dense groups of M rows, A = bf16 [M][K] per K segment (seg[i].a, shared by

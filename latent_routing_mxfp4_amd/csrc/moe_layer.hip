@@ -17,7 +17,11 @@
 // Step 10 runs the up-projection and every shared down-projection as one
 // GEMM whose K dimension is the concatenation [L | Fs | Fs ...], so the sum of
 // the routed and shared branches (Moat page, Fig. 2) happens in the fp32
-// accumulators instead of an extra pass over y.
+// accumulators instead of an extra pass over y.  With MX weights and few
+// rows (weight-streaming kernels) the shared experts ride in the routed
+// experts' launches instead: step 9 in the workgroups of step 6 that come
+// before the routed ones, the shared down-projections in step 7's (writing
+// y), and step 10 adds only the up-projection to y.
 //
 // Higher-precision map (dense_bf16): step 1 rounds x to bf16 (xb), and steps
 // 2, 9 and 10 are bf16 GEMMs on bfloat16 weights (LDS-staged 512-thread
@@ -388,10 +392,17 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
   MOE_HIP(mark(MOE_EV_DOWN));
 
   // 3-4. router
+  // (few tokens: the K-slice sums of the logits are added by the top-k kernel)
+  const bool reduce_in_topk = moe::router_reduce_in_topk(T, E, L);
   MOE_HIP(moe::launch_router_logits(zr, w.w_router, w.router_logit_bias, T, E, L, logits,
-                                    at<float>(ws, pl.rpart), at<uint16_t>(ws, pl.wrpl), s));
+                                    at<float>(ws, pl.rpart), at<uint16_t>(ws, pl.wrpl), s, reduce_in_topk));
   MOE_HIP(mark(MOE_EV_LOGITS));
-  MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, c.softmax_gates != 0, ids, gates, s));
+  if (reduce_in_topk)
+    MOE_HIP(moe::launch_router_reduce_topk(at<float>(ws, pl.rpart), moe::router_slices(T, E, L),
+                                           w.router_logit_bias, w.selection_bias, T, E, k, c.softmax_gates != 0,
+                                           logits, ids, gates, s));
+  else
+    MOE_HIP(moe::launch_topk(logits, w.selection_bias, T, E, k, c.softmax_gates != 0, ids, gates, s));
   MOE_HIP(mark(MOE_EV_TOPK));
 
   // 5. dispatch
@@ -402,7 +413,68 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
   const int32_t* ms_r = routed_shape == moe::GEMM_STREAM16 ? ms0 : ms1;
   const int64_t max_mt_r = P / mt_r + (P < E ? P : E) + 1;
 
-  // 6. routed GEMM1 + SwiGLU + MXFP8
+  // The shared experts' gate/up GEMM (step 9) on MX weights, as arguments.
+  auto shared_up_args = [&]() {
+    moe::GemmArgs a = {};
+    a.nseg = 1;
+    a.seg[0] = {xq,
+                xqs,
+                d,
+                w.w_gate_s.codes,
+                w.w_gate_s.scales,
+                w.w_up_s.codes,
+                w.w_up_s.scales,
+                (int64_t)Fs * d / 2,
+                (int64_t)Fs * d / 32,
+                d,
+                wrm};
+    a.G = S;
+    a.M = T;
+    a.N = Fs;
+    a.c = tr ? tr->hs : nullptr;
+    a.ldc = Fs;
+    a.c_gstride = (int64_t)T * Fs;
+    a.q = hs;
+    a.qs = hss;
+    a.q_gstride = (int64_t)T * Fs;
+    a.qs_gstride = (int64_t)T * Fs / 32;
+    a.max_mtiles = S * ((T + mt_dense - 1) / mt_dense);
+    return a;
+  };
+  // The shared experts' down-projections (the K segments of step 10 after
+  // the latent one): y = sum_s hs_s W_down_s^T.
+  auto shared_down_args = [&]() {
+    moe::GemmArgs a = {};
+    a.nseg = S;
+    for (int i = 0; i < S; ++i)
+      a.seg[i] = {hs + (int64_t)i * T * Fs,
+                  hss + (int64_t)i * T * Fs / 32,
+                  Fs,
+                  w.w_down_s.codes + (int64_t)i * d * Fs / 2,
+                  w.w_down_s.scales + (int64_t)i * d * Fs / 32,
+                  nullptr,
+                  nullptr,
+                  0,
+                  0,
+                  Fs,
+                  wrm};
+    a.G = 1;
+    a.M = T;
+    a.N = d;
+    a.c = y;
+    a.ldc = d;
+    a.max_mtiles = (T + mt_dense - 1) / mt_dense;
+    return a;
+  };
+  // Few rows: every GEMM after the router streams its weights, so the
+  // shared experts' halves (which need only x, then hs) run in the routed
+  // experts' launches -- gate/up with step 6, the down-projections with step
+  // 7 (y = shared part, to which step 10 adds the up-projection) -- rather
+  // than in launches of their own bound by memory latency.
+  const bool shared_with_routed =
+      !hp && S > 0 && dense_shape == moe::GEMM_STREAM16 && routed_shape == moe::GEMM_STREAM16;
+
+  // 6. routed GEMM1 + SwiGLU + MXFP8 (+ the shared experts' gate/up)
   {
     moe::GemmArgs a = {};
     a.nseg = 1;
@@ -429,7 +501,8 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
     a.q = hq;
     a.qs = hqs;
     a.max_mtiles = (int)max_mt_r;
-    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, routed_shape, s));
+    if (shared_with_routed) MOE_HIP(moe::launch_mx_gemm_pair(shared_up_args(), a, moe::EPI_SWIGLU_QUANT, s));
+    else MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, routed_shape, s));
   }
   MOE_HIP(mark(MOE_EV_EXPERT_UP));
 
@@ -447,7 +520,8 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
     a.c = ye;
     a.ldc = L;
     a.max_mtiles = (int)max_mt_r;
-    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, routed_shape, s));
+    if (shared_with_routed && latent) MOE_HIP(moe::launch_mx_gemm_pair(shared_down_args(), a, moe::EPI_F32, s));
+    else MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, routed_shape, s));
   }
   MOE_HIP(mark(MOE_EV_EXPERT_DOWN));
 
@@ -464,7 +538,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
   }
   MOE_HIP(mark(MOE_EV_COMBINE));
 
-  // 9. shared experts, first half
+  // 9. shared experts, first half (with MX weights at few rows: in step 6's launch)
   if (S > 0 && hp) {  // bfloat16 gate/up on bf16(x), hidden state rounded to bf16
     moe::GemmArgs a = hp_shared_args(c, T, few);
     a.seg[0].a = u8(xb);
@@ -483,31 +557,8 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
       a.max_mtiles = S * ((T + moe::gemm_mtile(moe::GEMM_WIDE) - 1) / moe::gemm_mtile(moe::GEMM_WIDE));
       MOE_HIP(moe::launch_bf16_gemm_wide(a, moe::EPI_SWIGLU_BF16, s));
     }
-  } else if (S > 0) {
-    moe::GemmArgs a = {};
-    a.nseg = 1;
-    a.seg[0] = {xq,
-                xqs,
-                d,
-                w.w_gate_s.codes,
-                w.w_gate_s.scales,
-                w.w_up_s.codes,
-                w.w_up_s.scales,
-                (int64_t)Fs * d / 2,
-                (int64_t)Fs * d / 32,
-                d,
-                wrm};
-    a.G = S;
-    a.M = T;
-    a.N = Fs;
-    a.c = tr ? tr->hs : nullptr;
-    a.ldc = Fs;
-    a.c_gstride = (int64_t)T * Fs;
-    a.q = hs;
-    a.qs = hss;
-    a.q_gstride = (int64_t)T * Fs;
-    a.qs_gstride = (int64_t)T * Fs / 32;
-    a.max_mtiles = S * ((T + mt_dense - 1) / mt_dense);
+  } else if (S > 0 && !shared_with_routed) {
+    moe::GemmArgs a = shared_up_args();
     a.kchains = dense_shape == moe::GEMM_STREAM16 ? 4 : 1;  // few rows: K split over each workgroup's waves
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, dense_shape, s));
   }
@@ -533,6 +584,19 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
       a.max_mtiles = (T + moe::gemm_mtile(moe::GEMM_WIDE) - 1) / moe::gemm_mtile(moe::GEMM_WIDE);
       MOE_HIP(moe::launch_bf16_gemm_wide(a, moe::EPI_F32, s));
     }
+  } else if (latent && shared_with_routed) {  // y (the shared part, step 7) += yq W_up^T
+    moe::GemmArgs a = {};
+    a.nseg = 1;
+    a.seg[0] = {yq, yqs, L, w.w_up.codes, w.w_up.scales, nullptr, nullptr, 0, 0, L, wrm};
+    a.c_accumulate = 1;
+    a.G = 1;
+    a.M = T;
+    a.N = d;
+    a.c = y;
+    a.ldc = d;
+    a.max_mtiles = (T + mt_dense - 1) / mt_dense;
+    a.kchains = 4;
+    MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_F32, dense_shape, s));
   } else if (latent || S > 0) {
     moe::GemmArgs a = {};
     const int s0 = latent ? 1 : 0;
@@ -765,6 +829,34 @@ int moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* 
   a.ldc = N;
   a.max_mtiles = (M + moe::gemm_mtile(shape) - 1) / moe::gemm_mtile(shape);
   if (moe::launch_mx_gemm(a, moe::EPI_F32, shape, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_router_topk(const float* logits, const float* selection_bias, int32_t T, int32_t E, int32_t k,
+                    int32_t softmax_gates, int32_t* ids, float* gates, void* stream) {
+  if (T < 0 || E < 1 || E > 4096 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !ids || !gates || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(gates, 4) ||
+      (selection_bias && !aligned(selection_bias, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (moe::launch_topk(logits, selection_bias, T, E, k, softmax_gates != 0, ids, gates,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_router_reduce_topk(const float* partial, int32_t nz, const float* logit_bias, const float* selection_bias,
+                           int32_t T, int32_t E, int32_t k, int32_t softmax_gates, float* logits, int32_t* ids,
+                           float* gates, void* stream) {
+  if (T < 0 || nz < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!partial || !logits || !ids || !gates || !aligned(partial, 4) || !aligned(logits, 4) || !aligned(ids, 4) ||
+      !aligned(gates, 4) || (logit_bias && !aligned(logit_bias, 4)) ||
+      (selection_bias && !aligned(selection_bias, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (moe::launch_router_reduce_topk(partial, nz, logit_bias, selection_bias, T, E, k, softmax_gates != 0, logits,
+                                     ids, gates, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }

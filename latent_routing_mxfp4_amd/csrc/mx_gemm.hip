@@ -65,16 +65,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& f) {
 
 }  // namespace
 
-// Map a workgroup to (group, M-tile, N-tile).  Returns false for workgroups
+// Map workgroup `bid` to (group, M-tile, N-tile).  Returns false for workgroups
 // past the last M-tile (the grid is sized for the worst case).  The fields
 // are computed in locals and stored once, so the tile stays in registers
 // (filling them branch by branch through the reference left the tile in
 // per-lane scratch memory).
 template <int MT, int NT>
-__device__ __forceinline__ bool decode_tile(const GemmArgs& p, int wave, int NWC, Tile& t) {
+__device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bid, int wave, int NWC, Tile& t) {
   const int n_ntiles = (p.N + NT - 1) / NT;
-  const int gm = blockIdx.x / n_ntiles;
-  const int nt = blockIdx.x - gm * n_ntiles;
+  const int gm = bid / n_ntiles;
+  const int nt = bid - gm * n_ntiles;
   int g, m0, rows, row_base;
   if (p.offsets) {
     const int total = p.mtile_start[p.G];
@@ -410,10 +410,10 @@ __global__ void __launch_bounds__(256) splitk_swiglu_kernel(const float* __restr
 // K-steps (counted over all K segments); waves 1-3 hand their accumulators to
 // wave 0 through LDS, which adds them in wave order (deterministic) and runs
 // the epilogue.
-template <int MW, int NW, int EPI, int KS = 1>
-__global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
+template <int MW, int NW, int EPI, int KS>
+__device__ __forceinline__ void stream_gemm(const GemmArgs& p, int bid) {
   // K-steps in flight per wave: as many as keep two waves per SIMD.
-  constexpr int D = MW == 1 ? (NW <= 2 ? 4 : 2) : 1;
+  constexpr int D = MW == 1 ? (NW <= 2 ? 4 : 3) : 1;
   constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
   constexpr int NB = SWI ? 2 : 1;
   constexpr int MT = 16 * MW;
@@ -427,7 +427,7 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   Tile t;
-  if (!decode_tile<MT, NT>(p, wave, KS == 1 ? 16 * NW : 0, t)) return;  // uniform across the workgroup
+  if (!decode_tile<MT, NT>(p, bid, wave, KS == 1 ? 16 * NW : 0, t)) return;  // uniform across the workgroup
   // This wave's K-steps [kc0, kc1) of the concatenated segments.
   int kc0 = 0, kc1 = 1 << 30;
   if (KS > 1) {
@@ -566,7 +566,7 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
     for (int j = 0; j < D; ++j)
       if (ks + j < nks) compute(sl[j]);
   }
-  if (KS > 1) {  // waves 1..3 hand their partial sums to wave 0, which adds them in order
+  if constexpr (KS > 1) {  // waves 1..3 hand their partial sums to wave 0, which adds them in order
     constexpr int NV = MW * NW * NB * 4;  // floats per lane
     __shared__ float red[KS > 1 ? KS - 1 : 1][NV][64];
     if (wave > 0) {
@@ -598,6 +598,25 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
   epilogue<MW, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
+template <int MW, int NW, int EPI, int KS = 1>
+__global__ void __launch_bounds__(256) mx_gemm_stream_kernel(const GemmArgs p) {
+  stream_gemm<MW, NW, EPI, KS>(p, blockIdx.x);
+}
+
+// Two weight-streaming GEMMs with the same epilogue in one launch: workgroups
+// [0, npre) compute `pre` (a dense GEMM, one accumulator chain per output),
+// the rest `p`.  At decode the shared experts' gate/up GEMM, which needs only
+// x, rides along with the routed experts' one: its few hundred workgroups
+// stream their weights while the routed ones do, instead of a launch of its
+// own bound by memory latency.
+template <int MW, int NW, int EPI>
+__global__ void __launch_bounds__(256) mx_gemm_stream_pair_kernel(const GemmArgs pre, int npre,
+                                                                  const GemmArgs p) {
+  const int b = blockIdx.x;
+  if (b < npre) stream_gemm<MW, NW, EPI, 1>(pre, b);
+  else stream_gemm<MW, NW, EPI, 1>(p, b - npre);
+}
+
 template <int MW, int NW, int EPI>
 static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
   const bool chains = a.kchains == 4;
@@ -623,6 +642,34 @@ int gemm_mtile(int shape) {
 // of fp32 output under 4 GB.
 static bool epilogue_dims_ok(const GemmArgs& a) {
   return a.N > 0 && a.N < (1 << 22) && a.ldc >= 0 && a.ldc < (1 << 22);
+}
+
+// Workgroups of one weight-streaming problem in the one-accumulator layout.
+template <int NW>
+static int64_t stream_grid(const GemmArgs& a) {
+  const int n_ntiles = (a.N + 4 * 16 * NW - 1) / (4 * 16 * NW);
+  return (int64_t)a.max_mtiles * n_ntiles;
+}
+
+template <int MW, int NW, int EPI>
+static hipError_t launch_stream_pair_cfg(const GemmArgs& pre, const GemmArgs& a, hipStream_t s) {
+  if (pre.offsets != nullptr || (pre.kchains != 0 && pre.kchains != 1) || (a.kchains != 0 && a.kchains != 1))
+    return hipErrorInvalidValue;
+  if (pre.N % 16 != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
+  const int64_t g0 = stream_grid<NW>(pre), g1 = stream_grid<NW>(a);
+  if (g0 < 0 || g1 < 0 || g0 + g1 > 0x7fffffff) return hipErrorInvalidValue;
+  if (g0 + g1 == 0) return hipSuccess;
+  mx_gemm_stream_pair_kernel<MW, NW, EPI><<<dim3((unsigned)(g0 + g1)), dim3(256), 0, s>>>(pre, (int)g0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm_pair(const GemmArgs& pre, const GemmArgs& a, int epi, hipStream_t s) {
+  if (!epilogue_dims_ok(pre) || !epilogue_dims_ok(a)) return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_F32: return launch_stream_pair_cfg<1, 4, EPI_F32>(pre, a, s);
+    case EPI_SWIGLU_QUANT: return launch_stream_pair_cfg<1, 2, EPI_SWIGLU_QUANT>(pre, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {

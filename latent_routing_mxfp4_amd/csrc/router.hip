@@ -12,11 +12,14 @@
 //     tiles staged through LDS; for few tiles (decode) the K range is split
 //     over extra workgroups and the slices summed in a fixed order.
 //   topk: one wave per token (sigmoid scores, or the logits themselves with
-//     softmax gates); the E selection keys and raw scores sit in LDS,
-//     each lane keeps the best key of its strided slice, and k rounds of a
-//     64-lane (key desc, id asc) reduction (DPP within rows, readlane across)
-//     pick the winners in slot order; only the winning lane rescans its
-//     slice.  k <= 64 (slot j is held by lane j).
+//     softmax gates).  Up to 1024 experts the keys sit in registers, a
+//     threshold (the k-th largest of the lanes' maxima) cuts them to a few
+//     candidates, and each candidate's slot is the number of better ones;
+//     otherwise (and when too many keys tie) k rounds of a 64-lane
+//     (key desc, id asc) reduction (DPP within rows, readlane across) pick
+//     the winners in slot order.  k <= 64 (slot j is held by lane j).  For
+//     few tokens the K-slice sums of the logits are added by the top-k
+//     kernel itself (one workgroup per token).
 #include <float.h>
 
 #include "kernels.hpp"
@@ -312,8 +315,19 @@ bool router_bf16x3(int T, int E, int L) {
   return L % BK == 0 && (int64_t)((T + BT - 1) / BT) * ((E + BE - 1) / BE) >= 128;
 }
 
+// Number of K slices the fp32 router kernel writes (1: it writes the logits).
+int router_slices(int T, int E, int L) {
+  if (T <= 0 || router_bf16x3(T, E, L)) return 1;
+  const int split = router_split(T, E, L);
+  const int kslice = ((L / RK + split - 1) / split) * RK;
+  return (L + kslice - 1) / kslice;
+}
+
+bool router_reduce_in_topk(int T, int E, int L) { return E <= 1024 && router_slices(T, E, L) > 1; }
+
 hipError_t launch_router_logits(const float* z, const float* w, const float* bias, int T, int E, int L,
-                                float* logits, float* partial, uint16_t* wplanes, hipStream_t s) {
+                                float* logits, float* partial, uint16_t* wplanes, hipStream_t s,
+                                bool leave_partial) {
   if (T == 0) return hipSuccess;
   if (router_bf16x3(T, E, L) && wplanes != nullptr) {
     const int64_t n4 = (int64_t)E * L / 4;
@@ -341,7 +355,7 @@ hipError_t launch_router_logits(const float* z, const float* w, const float* bia
   }
   router_logits_kernel<<<grid, dim3(256), 0, s>>>(z, w, bias, T, E, L, kslice, partial);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || leave_partial) return e;
   const int64_t n = (int64_t)T * E;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
@@ -461,51 +475,110 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   }
 }
 
-// Same selection with each lane's keys and raw scores in registers (expert
-// e = lane + 64 j in slot j, E <= 64 * KPL): the winner's lane marks it taken
-// and rescans its KPL keys without touching memory, and the winner's score is
-// broadcast by readlane.  Same keys, same order of comparisons and sums as
-// topk_kernel, so the same ids and gates.
+// Order-preserving map of a float to uint32 (for non-NaN values: a < b as
+// floats implies map(a) < map(b); -0 maps below +0).
+__device__ __forceinline__ uint32_t orderable(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Top-k of one token held by a wave: lane l holds expert e = l + 64 j in slot
+// j (selection key key[j], -inf past E, and raw score scr[j]).  On return lane
+// r < k holds the winner of slot r (id, raw score) and every lane the sum of
+// the k winners' raw scores in slot order.  The winners are the k best by
+// (key desc, id asc), in that order -- the same as k rounds of "take the best
+// remaining", which is what the fallback below does.
+//
+// Threshold first: let theta be the k-th largest of the 64 lane maxima (a
+// radix select over its bit pattern: 32 ballots).  At least k lanes hold a key
+// >= theta, so no key below theta can be among the k best; the candidates are
+// the keys >= theta, typically a little over k.  If there are at most 64, they
+// are packed one per lane through LDS (`cand`: 3 x 64 words per wave), each
+// counts the candidates better than itself -- its slot -- and the slots are
+// filled through LDS again.  Otherwise (many equal keys) the round-based
+// selection runs on the registers.
 template <int KPL>
-__global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__ logits,
-                                                      const float* __restrict__ sel_bias, int T, int E, int k,
-                                                      bool softmax, int32_t* __restrict__ ids,
-                                                      float* __restrict__ gates) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const float* lrow = logits + (int64_t)t * E;
-  float key[KPL], scr[KPL];
+__device__ __forceinline__ void wave_topk(float (&key)[KPL], const float (&scr)[KPL], int lane, int k,
+                                          float* cand, int& myid, float& mys, float& ssum) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) m = fmaxf(m, key[j]);
+  const uint32_t um = orderable(m);
+  uint32_t th = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = th | (1u << bit);
+    if (__popcll(__ballot(um >= c)) >= k) th = c;
+  }
+  const float theta = from_orderable(th);
+  uint32_t cm = 0;  // this lane's candidate slots
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) cm |= (key[j] >= theta && key[j] > -INFINITY) ? (1u << j) : 0u;
+  const int n = __popc(cm);
+  int pos = 0, total = 0;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) {  // prefix sum over lanes of n (<= 16 < 32) bit by bit
+    const uint64_t bb = __ballot((n >> b) & 1);
+    pos += lanes_below(bb) << b;
+    total += __popcll(bb) << b;
+  }
+  ssum = 0.f;
+  if (total <= 64) {
+    float* ck = cand;
+    int* ci = reinterpret_cast<int*>(cand + 64);
+    float* cs = cand + 128;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (cm & (1u << j)) {
+        ck[pos] = key[j];
+        ci[pos] = lane + 64 * j;
+        cs[pos] = scr[j];
+        ++pos;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool have = lane < total;
+    const float kk = have ? ck[lane] : -INFINITY;
+    const int ii = have ? ci[lane] : 0x7fffffff;
+    const float ss = have ? cs[lane] : 0.f;
+    int rank = 0;
+    for (int j = 0; j < total; ++j) {
+      const float kj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kk), j));
+      const int ij = __builtin_amdgcn_readlane(ii, j);
+      rank += better(kj, ij, kk, ii) ? 1 : 0;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (have && rank < k) {  // slot `rank`
+      ci[rank] = ii;
+      cs[rank] = ss;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    myid = lane < k ? ci[lane] : 0;
+    mys = lane < k ? cs[lane] : 0.f;
+    for (int r = 0; r < k; ++r)  // every lane adds the same values in slot order
+      ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mys), r));
+    return;
+  }
+  // Round-based selection: the winner's lane marks it taken and rescans its
+  // KPL keys without touching memory; the winner's score is broadcast by
+  // readlane.
   float bk = -INFINITY;
   int bi = 0x7fffffff;
-  // All of the lane's loads first (indices past E re-read the last logit and
-  // are discarded below), so they are in flight together instead of one
-  // memory latency per key.
-  float lv[KPL], bv[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int e = min(lane + 64 * j, E - 1);
-    lv[j] = lrow[e];
-    bv[j] = sel_bias ? sel_bias[e] : 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = -INFINITY;  // past E: never selected (k <= E finite keys exist)
-    scr[j] = 0.f;
-    if (e < E) {
-      const float sc = softmax ? lv[j] : sigmoidf(lv[j]);
-      float kk = sc;
-      if (sel_bias) kk += bv[j];
-      kk = fmaxf(kk, -FLT_MAX);
-      key[j] = kk;
-      scr[j] = sc;
-      if (better(kk, e, bk, bi)) { bk = kk; bi = e; }
-    }
-  }
-  float ssum = 0.f;
-  float mys = 0.f;
-  int myid = 0;
+  for (int j = 0; j < KPL; ++j)
+    if (better(key[j], lane + 64 * j, bk, bi)) { bk = key[j]; bi = lane + 64 * j; }
+  mys = 0.f;
+  myid = 0;
   for (int r = 0; r < k; ++r) {
     float wk = bk;
     int wi = bi;
@@ -527,11 +600,132 @@ __global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__
       }
     }
   }
+}
+
+// Same selection as topk_kernel with each lane's keys and raw scores in
+// registers (expert e = lane + 64 j in slot j, E <= 64 * KPL): same keys, same
+// order of comparisons and sums, so the same ids and gates.
+template <int KPL>
+__global__ void __launch_bounds__(256) topk_reg_kernel(const float* __restrict__ logits,
+                                                      const float* __restrict__ sel_bias, int T, int E, int k,
+                                                      bool softmax, int32_t* __restrict__ ids,
+                                                      float* __restrict__ gates) {
+  __shared__ float cand[4][3 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // no block-level barrier below
+  const float* lrow = logits + (int64_t)t * E;
+  float key[KPL], scr[KPL];
+  // All of the lane's loads first (indices past E re-read the last logit and
+  // are discarded below), so they are in flight together instead of one
+  // memory latency per key.
+  float lv[KPL], bv[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = min(lane + 64 * j, E - 1);
+    lv[j] = lrow[e];
+    bv[j] = sel_bias ? sel_bias[e] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {  // (selects, not branches: the arrays stay in plain registers)
+    const bool in = lane + 64 * j < E;
+    const float sc = softmax ? lv[j] : sigmoidf(lv[j]);
+    const float kk = fmaxf(sel_bias ? sc + bv[j] : sc, -FLT_MAX);  // NaN / -inf rank last, above "taken"
+    key[j] = in ? kk : -INFINITY;  // past E: never selected (k <= E finite keys exist)
+    scr[j] = in ? sc : 0.f;
+  }
+  int myid;
+  float mys, ssum;
+  wave_topk<KPL>(key, scr, lane, k, cand[wave], myid, mys, ssum);
   const float gt = winner_gate(softmax, k, lane, mys, ssum);
   if (lane < k) {
     ids[(int64_t)t * k + lane] = myid;
     gates[(int64_t)t * k + lane] = gt;
   }
+}
+
+// Few tokens: the router's K-slice partial sums, reduced here instead of in a
+// kernel of their own.  One workgroup per token: its 256 threads add the
+// slices of the token's E logits in slice order and add the logit bias (the
+// reduce kernel's arithmetic, so the same logits), write them out and to LDS;
+// then the first wave selects the top k from LDS (E <= 1024).
+__global__ void __launch_bounds__(256) router_reduce_topk_kernel(const float* __restrict__ part, int nz,
+                                                                const float* __restrict__ logit_bias,
+                                                                const float* __restrict__ sel_bias, int T, int E,
+                                                                int k, bool softmax, float* __restrict__ logits,
+                                                                int32_t* __restrict__ ids,
+                                                                float* __restrict__ gates) {
+  constexpr int EPT = 4;    // logits per thread (E <= 1024)
+  constexpr int SB = 32;    // slices loaded per batch (all in flight)
+  __shared__ float lg[256 * EPT];
+  __shared__ float cand[3 * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int t = blockIdx.x;
+  const int64_t n = (int64_t)T * E;
+  int64_t o[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) o[i] = (int64_t)t * E + min(tid + 256 * i, E - 1);
+  float v[EPT];
+  for (int s0 = 0; s0 < nz; s0 += SB) {
+    float p[EPT][SB];
+#pragma unroll
+    for (int s = 0; s < SB; ++s) {
+      const int64_t so = (int64_t)min(s0 + s, nz - 1) * n;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) p[i][s] = part[so + o[i]];
+    }
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const int sl = s0 + s;
+        v[i] = sl == 0 ? p[i][s] : (sl < nz ? v[i] + p[i][s] : v[i]);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid + 256 * i;
+    if (e < E) {
+      const float l = v[i] + (logit_bias ? logit_bias[e] : 0.f);
+      logits[(int64_t)t * E + e] = l;
+      lg[e] = l;
+    }
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  constexpr int KPL = 16;
+  float key[KPL], scr[KPL];
+  float bv[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) bv[j] = sel_bias ? sel_bias[min(lane + 64 * j, E - 1)] : 0.f;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = lane + 64 * j;
+    const bool in = e < E;
+    const float lv = lg[in ? e : E - 1];
+    const float sc = softmax ? lv : sigmoidf(lv);
+    const float kk = fmaxf(sel_bias ? sc + bv[j] : sc, -FLT_MAX);
+    key[j] = in ? kk : -INFINITY;
+    scr[j] = in ? sc : 0.f;
+  }
+  int myid;
+  float mys, ssum;
+  wave_topk<KPL>(key, scr, lane, k, cand, myid, mys, ssum);
+  const float gt = winner_gate(softmax, k, lane, mys, ssum);
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = myid;
+    gates[(int64_t)t * k + lane] = gt;
+  }
+}
+
+hipError_t launch_router_reduce_topk(const float* partial, int nz, const float* logit_bias, const float* sel_bias,
+                                     int T, int E, int k, bool softmax_gates, float* logits, int32_t* ids,
+                                     float* gates, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!partial || nz < 1 || E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return hipErrorInvalidValue;
+  router_reduce_topk_kernel<<<dim3((unsigned)T), dim3(256), 0, s>>>(partial, nz, logit_bias, sel_bias, T, E, k,
+                                                                   softmax_gates, logits, ids, gates);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, const float* sel_bias, int T, int E, int k, bool softmax_gates,

@@ -88,16 +88,18 @@ def mx_mfma_bound(a: moe.MXTensor, b: moe.MXTensor, value=None) -> np.ndarray:
     return mfma_model.mfma_bound(a, b, value)
 
 
-# The dense MX GEMMs of few-row batches (shared gate/up, output projection)
-# split their K-steps over up to 4 accumulator chains, one per wave of a
-# workgroup, added in wave order.
+# The dense MX GEMMs of few-row batches split their K-steps over up to 4
+# accumulator chains, one per wave of a workgroup, added in wave order.  The
+# output projection at few rows: the shared down-projections form one more
+# chain (computed into y first, then y += the up-projection's chains).
 DENSE_CHAINS = 4
+OUT_CHAINS = DENSE_CHAINS + 1
 
 
 def mx_concat_bound(pairs, value: np.ndarray, extra_roundings: int = 0) -> np.ndarray:
     """Block-scaled dense GEMM over K = the concatenation of ``pairs``' K
     segments (the output projection)."""
-    return mfma_model.mfma_bound_segments(pairs, value, extra_roundings, chains=DENSE_CHAINS)
+    return mfma_model.mfma_bound_segments(pairs, value, extra_roundings, chains=OUT_CHAINS)
 
 
 def u16(a) -> np.ndarray:
@@ -388,11 +390,13 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
     # 4-5. routing and dispatch
     dgate, same = check_routing(W, o.z, o.routing, bz, tr, k, rep)
     gi = tr["ids"]
+    say("  latent, re-quantisation and routing checked")
 
     # 6. replay along the GPU's admissible choices
     if x is not None:
         rp = Replay(tr, W, k, dgate, o.xq)
         c = replay_forward(x, W, k, gi, rp, expert_weights=expert_weights, workers=workers)
+        say("  replay along the GPU's choices done")
         for name, st in rp.stats.items():
             assert st["inadmissible_blocks"] == 0, (name, st)
         rep["replay"] = rp.stats
@@ -439,6 +443,7 @@ def check_layer(cfg, W: moe.LayerWeights, o: moe.Trace, y: np.ndarray, tr: dict,
         rep.update(replay_rel_l2=rel, replay_max_abs_over_rms=maxabs / rms)
         assert rel <= REL_L2, f"relative L2 vs replay {rel:.3g}"
         assert maxabs <= MAXABS_FRAC * rms, f"max abs vs replay {maxabs:.3g} (rms {rms:.3g})"
+        say("  every tensor within its bound of the replay")
 
     # 7. unconditioned oracle output, over every token the GPU routed as the
     #    oracle does: relative L2, and max-abs per token.  A token above the

@@ -274,3 +274,23 @@ def test_weight_layout_and_workspace_bytes():
     assert _lib.moe_layer_workspace_bytes(cfg, 64) == 0
     assert _lib.moe_layer_workspace_bytes(_k3(), 16385) == 0
     assert lib.moe_layer_workspace_bytes(None, 64) == 0
+
+
+def test_topk_stage_argument_errors_need_no_gpu():
+    """The top-k stage entries check sizes and pointers before any HIP call."""
+    lib = _lib.load()
+    topk, fused = lib.moe_router_topk, lib.moe_router_reduce_topk
+    E_ = _lib.MOE_ERR_INVALID_ARG
+    assert topk(None, None, 0, 896, 16, 0, None, None, None) == _lib.MOE_OK       # T = 0: no-op
+    assert topk(FAKE, None, 4, 896, 0, 0, FAKE, FAKE, None) == E_                  # k < 1
+    assert topk(FAKE, None, 4, 896, 65, 0, FAKE, FAKE, None) == E_                 # k > 64
+    assert topk(FAKE, None, 4, 8, 9, 0, FAKE, FAKE, None) == E_                    # k > E
+    assert topk(FAKE, None, 4, 4097, 16, 0, FAKE, FAKE, None) == E_                # E > 4096
+    assert topk(None, None, 4, 896, 16, 0, FAKE, FAKE, None) == E_                 # null logits
+    assert topk(FAKE + 2, None, 4, 896, 16, 0, FAKE, FAKE, None) == E_             # misaligned
+    assert topk(FAKE, FAKE + 1, 4, 896, 16, 0, FAKE, FAKE, None) == E_
+    assert fused(None, 2, None, None, 0, 896, 16, 0, None, None, None, None) == _lib.MOE_OK
+    assert fused(FAKE, 0, None, None, 4, 896, 16, 0, FAKE, FAKE, FAKE, None) == E_  # nz < 1
+    assert fused(FAKE, 2, None, None, 4, 1025, 16, 0, FAKE, FAKE, FAKE, None) == E_  # E > 1024
+    assert fused(FAKE, 2, None, None, 4, 896, 16, 0, None, FAKE, FAKE, None) == E_  # null logits out
+    assert fused(FAKE, 2, FAKE + 2, None, 4, 896, 16, 0, FAKE, FAKE, FAKE, None) == E_

@@ -95,12 +95,18 @@ def _run(k3, name):
             if (i + 1) % 64 == 0:
                 say(f"    {i + 1} of {len(need)} experts encoded by the oracle")
     say(f"  full data path of {len(tokens)} token(s) in {len(subs)} subset(s)")
+
+    def check(i):
+        tok, sub, ys = subs[i]
+        # each subset's stage lines, not its full report
+        quiet = lambda *a: None if str(a[0]).startswith("parity report") else say(f"    subset {i}:", *a)
+        return parity.check_tokens(cfg, Wc, x[tok], ys, sub, cache, say=quiet)
+
     with ThreadPoolExecutor(max_workers=WORKERS) as ex:
         reps = []
-        for r in ex.map(lambda t: parity.check_tokens(cfg, Wc, x[t[0]], t[2], t[1], cache,
-                                                       say=lambda *a: None), subs):
+        for r in ex.map(check, range(len(subs))):
             reps.append(r)
-            say(f"    subset {len(reps)} of {len(subs)} checked")
+            say(f"    subset {len(reps) - 1} of {len(subs)} checked")
     merged = parity.merge_reports(reps)
     # figures over all the checked tokens together (rms of the oracle's output
     # over them): relative L2, and max-abs per token, where a token above the
