@@ -535,9 +535,20 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
     del a, b
+    # Read-only stream of 4 GiB with 16-byte non-temporal loads (what the
+    # decode expert GEMMs do with their weights): the reference for their GB/s.
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    rbuf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    rfold = torch.empty(16 * n_cu * 256, dtype=torch.int32, device="cuda")
+    LY._lib.moe_hbm_read_probe(rbuf.data_ptr(), rbuf.numel(), 16 * n_cu, rfold.data_ptr(), LY._stream())
+    e0.record()
+    LY._lib.moe_hbm_read_probe(rbuf.data_ptr(), rbuf.numel(), 16 * n_cu, rfold.data_ptr(), LY._stream())
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = rbuf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del rbuf, rfold
     # Matrix-core probe on the same GPU: back-to-back independent FP8 x FP4
     # block-scaled 16x16x128 MFMAs, two waves per SIMD on every CU.
-    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     wg, iters = 2 * n_cu, 400
     mf = torch.empty(wg * 4, dtype=torch.float32, device="cuda")
     LY._lib.moe_mfma_rate_probe(20, wg, mf.data_ptr(), LY._stream())
@@ -618,6 +629,7 @@ def main():
     if args.bf16_steps > 0 and args.workload == "k3_prefill":
         out["bf16_map"] = bf16_map_report(weights, args.bf16_steps, args.decode_steps, args.warmup, hip, say)
     out["hbm_copy_probe_gbs"] = copy_gbs
+    out["hbm_read_probe_gbs"] = read_gbs
     out["mfma_fp8xfp4_probe_tflops"] = mfma_tflops
     if args.workload == "k3_decode":
         dom = stages["expert_up"]

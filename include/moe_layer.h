@@ -327,6 +327,15 @@ int moe_quantile_balance(const float* logits, int32_t T, int32_t E, int32_t k, c
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
 int moe_mfma_rate_probe(int32_t iters, int32_t workgroups, float* out, void* stream);
 
+/* Measurement, not part of the layer: how fast this GPU streams HBM with plain
+ * 16-byte non-temporal loads (the decode expert GEMMs' whole job is such a
+ * stream of weights).  Reads `bytes` (a positive multiple of 16) from the
+ * device buffer buf (16-byte aligned) with `workgroups` x 256 threads;
+ * out (device uint32 [workgroups * 256]) receives one fold of the data per
+ * thread, not meant to be read.  Time it with events on `stream`.
+ * 1 <= workgroups <= 2^20.  Errors: MOE_ERR_INVALID_ARG, MOE_ERR_HIP. */
+int moe_hbm_read_probe(const void* buf, size_t bytes, int32_t workgroups, uint32_t* out, void* stream);
+
 /* Dense MX GEMM c[M][N] = deq(a) deq(b)^T in fp32, a = E4M3 [M][K] (row-major),
  * b = E2M1 [N][K] in fragment order, N a positive multiple of 16, K of 128.
  * This is the block-scaled matrix-core kernel the layer's projections run on,

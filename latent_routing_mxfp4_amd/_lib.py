@@ -41,6 +41,7 @@ EXPORTED = (
     "moe_mfma_rate_probe",
     "moe_router_topk",
     "moe_router_reduce_topk",
+    "moe_hbm_read_probe",
 )
 
 
@@ -148,6 +149,8 @@ def load() -> ctypes.CDLL:
     lib.moe_quantile_balance_workspace_bytes.argtypes = [i32, i32]
     lib.moe_mfma_rate_probe.restype = ctypes.c_int
     lib.moe_mfma_rate_probe.argtypes = [i32, i32, vp, vp]
+    lib.moe_hbm_read_probe.restype = ctypes.c_int
+    lib.moe_hbm_read_probe.argtypes = [vp, sz, i32, vp, vp]
     lib.moe_quantile_balance.restype = ctypes.c_int
     lib.moe_quantile_balance.argtypes = [vp, i32, i32, i32, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     _lib = lib
@@ -244,6 +247,10 @@ def moe_quantile_balance(logits: int, T: int, E: int, k: int, bias_in: int, eta:
                          quantile_out: int, ws: int, ws_bytes: int, stream: int = 0) -> None:
     _check(load().moe_quantile_balance(logits, int(T), int(E), int(k), bias_in, float(eta), bias_out,
                                        quantile_out, ws, int(ws_bytes), stream), "moe_quantile_balance")
+
+
+def moe_hbm_read_probe(buf: int, nbytes: int, workgroups: int, out: int, stream: int = 0) -> None:
+    _check(load().moe_hbm_read_probe(buf, int(nbytes), int(workgroups), out, stream), "moe_hbm_read_probe")
 
 
 def moe_mfma_rate_probe(iters: int, workgroups: int, out: int, stream: int = 0) -> None:

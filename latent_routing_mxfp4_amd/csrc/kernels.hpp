@@ -182,6 +182,22 @@ hipError_t launch_mx_gemm(const GemmArgs& args, int epilogue, int shape, hipStre
 int gemm_wide_mtile();
 hipError_t launch_mx_gemm_wide(const GemmArgs& args, int epilogue, hipStream_t s);
 
+// Operands of the gate-weighted combine (launch_combine's arguments, MXFP8
+// output): y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t][j]] in slot order.
+struct CombineArgs {
+  const float* y_e;
+  const float* gates;
+  const int32_t* row_of_pair;
+  int T, k, L;
+  float* y_lat;  // nullable
+  uint8_t* yq;
+  uint8_t* yqs;
+};
+// The 512-thread MX kernel's dense SwiGLU + MXFP8 GEMM (the shared experts'
+// gate/up at prefill) and the combine in one launch: the combine runs on a
+// fraction of the workgroups spread through the launch, the GEMM on the rest.
+hipError_t launch_mx_gemm_wide_combine(const GemmArgs& args, const CombineArgs& c, hipStream_t s);
+
 // ---- Quantile Balancing (balance.hip) ----------------------------------------
 // New selection bias from one batch of router logits [T][E] (sigmoid keys):
 // b_out = b_in - eta * Q, Q[e] the midpoint of expert e's n-th and (n+1)-th
@@ -197,6 +213,9 @@ hipError_t launch_quantile_balance(const float* logits, int T, int E, int k, con
 // workgroups x 4 waves, each issuing 8 * iters independent FP8 x FP4 MFMAs of
 // 16x16x128; out[workgroups * 4] receives one checksum per wave.
 hipError_t launch_mfma_rate(int iters, int workgroups, float* out, hipStream_t s);
+// Plain HBM read stream: `bytes` (a multiple of 16) from buf by `workgroups` x
+// 256 threads; out[workgroups * 256] receives one fold per thread.
+hipError_t launch_hbm_read(const void* buf, int64_t bytes, int workgroups, uint32_t* out, hipStream_t s);
 
 // ---- Combine (combine.hip) --------------------------------------------------
 // y_lat[t] = sum_j gates[t][j] * y_e[row_of_pair[t*k+j]] (slot order), then

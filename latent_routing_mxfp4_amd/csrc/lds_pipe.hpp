@@ -37,18 +37,19 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(
 
 // Tile decode shared by the LDS-staged kernels: the flat tile list (group,
 // weight column-tile, M-tile; M fastest) is cut into 8 contiguous chunks, one
-// per XCD (workgroup i runs on XCD i % 8).  False for workgroups past the end.
+// per XCD (workgroup bid runs on XCD bid % 8).  False for workgroups past the
+// end.
 template <int MT>
-__device__ __forceinline__ bool decode_lds_tile(const GemmArgs& p, int ncol, int& g, int& mt, int& nt, int& rows,
-                                                int& row_base) {
+__device__ __forceinline__ bool decode_lds_tile(const GemmArgs& p, int bid, int ncol, int& g, int& mt, int& nt,
+                                                int& rows, int& row_base) {
   const int n_nt = (p.N + ncol - 1) / ncol;
   const bool routed = p.offsets != nullptr;
   const int mpg = routed ? 0 : (p.M + MT - 1) / MT;
   const int total = routed ? p.mtile_start[p.G] * n_nt : p.G * mpg * n_nt;
   const int per = (total + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
+  const int slot = bid >> 3;
   if (slot >= per) return false;
-  const int lin = (blockIdx.x & 7) * per + slot;
+  const int lin = (bid & 7) * per + slot;
   if (lin >= total) return false;
   if (routed) {
     if (p.mtile_group) {

@@ -21,7 +21,8 @@
 // rows (weight-streaming kernels) the shared experts ride in the routed
 // experts' launches instead: step 9 in the workgroups of step 6 that come
 // before the routed ones, the shared down-projections in step 7's (writing
-// y), and step 10 adds only the up-projection to y.
+// y), and step 10 adds only the up-projection to y.  With many rows, steps 8
+// and 9 share one launch (the combine on some of the GEMM's workgroups).
 //
 // Higher-precision map (dense_bf16): step 1 rounds x to bf16 (xb), and steps
 // 2, 9 and 10 are bf16 GEMMs on bfloat16 weights (LDS-staged 512-thread
@@ -527,8 +528,15 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
 
   // 8. combine
   // The fp32 combined latent is only kept for a trace; yq is what the
-  // up-projection reads.
-  if (hp) {
+  // up-projection reads.  Many tokens with MX shared experts: the combine
+  // (HBM-bound) runs in the same launch as the shared gate/up GEMM (matrix
+  // cores), on a fraction of its workgroups.
+  const bool combine_with_shared = !hp && latent && S > 0 && dense_shape == moe::GEMM_WIDE;
+  if (combine_with_shared) {
+    moe::GemmArgs a = shared_up_args();
+    const moe::CombineArgs cb = {ye, gates, rop, (int)T, k, L, tr && tr->y_lat ? ylat : nullptr, yq, yqs};
+    MOE_HIP(moe::launch_mx_gemm_wide_combine(a, cb, s));
+  } else if (hp) {
     MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, tr && tr->y_lat ? ylat : nullptr, nullptr, nullptr, s, yb));
   } else if (latent) {
     MOE_HIP(moe::launch_combine(ye, gates, rop, T, k, L, tr && tr->y_lat ? ylat : nullptr, yq, yqs, s));
@@ -557,7 +565,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
       a.max_mtiles = S * ((T + moe::gemm_mtile(moe::GEMM_WIDE) - 1) / moe::gemm_mtile(moe::GEMM_WIDE));
       MOE_HIP(moe::launch_bf16_gemm_wide(a, moe::EPI_SWIGLU_BF16, s));
     }
-  } else if (S > 0 && !shared_with_routed) {
+  } else if (S > 0 && !shared_with_routed && !combine_with_shared) {
     moe::GemmArgs a = shared_up_args();
     a.kchains = dense_shape == moe::GEMM_STREAM16 ? 4 : 1;  // few rows: K split over each workgroup's waves
     MOE_HIP(moe::launch_mx_gemm(a, moe::EPI_SWIGLU_QUANT, dense_shape, s));
@@ -807,6 +815,14 @@ int moe_mfma_rate_probe(int32_t iters, int32_t workgroups, float* out, void* str
   if (iters < 1 || iters > (1 << 24) || workgroups < 1 || workgroups > (1 << 20)) return MOE_ERR_INVALID_ARG;
   if (!out || !aligned(out, 4)) return MOE_ERR_INVALID_ARG;
   if (moe::launch_mfma_rate(iters, workgroups, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_hbm_read_probe(const void* buf, size_t bytes, int32_t workgroups, uint32_t* out, void* stream) {
+  if (!buf || !out || bytes == 0 || bytes % 16 || workgroups < 1 || workgroups > (1 << 20)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return MOE_ERR_INVALID_ARG;
+  if (moe::launch_hbm_read(buf, (int64_t)bytes, workgroups, out, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -42,6 +42,7 @@
 // tile is 512 output columns and wave wn owns col0 + 128 wn .. +127.
 #include <type_traits>
 
+#include "combine_device.hpp"
 #include "gemm_epilogue.hpp"
 #include "kernels.hpp"
 #include "launch_attr.hpp"
@@ -62,7 +63,7 @@ constexpr int WD_NBUF = 3;
 constexpr int WD_LOADS = 8;  // direct loads per wave per K-step
 
 template <int EPI>
-__global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
+__device__ __forceinline__ void wide_mx_tile(const GemmArgs& p, int bid) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr bool SWI = EPI == EPI_SWIGLU_QUANT;
   constexpr int NB = SWI ? 2 : 1;              // accumulators per fragment (gate, up)
@@ -76,7 +77,7 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
 
   const bool routed = p.offsets != nullptr;
   int g, mt, nt, rows, row_base;
-  if (!decode_lds_tile<WD_M>(p, NCOL, g, mt, nt, rows, row_base)) return;
+  if (!decode_lds_tile<WD_M>(p, bid, NCOL, g, mt, nt, rows, row_base)) return;
   const int m0 = mt * WD_M;
   const int col0 = nt * NCOL;
   // 16-row fragments of this wave that hold at least one row of the group
@@ -290,6 +291,58 @@ __global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
   epilogue<4, NW, NB, EPI>(p, t, acc, r16, g4);
 }
 
+template <int EPI>
+__global__ void __launch_bounds__(512) mx_gemm_wide_kernel(const GemmArgs p) {
+  wide_mx_tile<EPI>(p, blockIdx.x);
+}
+
+// Prefill: the combine (HBM-bound) beside the shared experts' gate/up GEMM
+// (matrix-core bound), which it does not depend on, in one launch.  Groups of
+// 8 consecutive workgroups (one per XCD) are "slots"; every R-th slot is a
+// combine slot whose 8 workgroups each combine `chunk` tokens, the others
+// run the GEMM's tiles in their own order (GEMM slot = slot - slot / R), so
+// a few CUs at a time stream the expert outputs while the rest keep the
+// matrix cores busy.  The combine's arithmetic is the combine kernel's.
+__device__ __forceinline__ void combine_chunk(const CombineArgs& c, int chunk, int ci) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int64_t t0 = (int64_t)ci * chunk;
+  if (t0 >= c.T) return;  // uniform over the workgroup
+  const int nt = (int)min((int64_t)chunk, (int64_t)c.T - t0);
+  int32_t* rows = reinterpret_cast<int32_t*>(lds);
+  float* gs = reinterpret_cast<float*>(lds) + chunk * c.k;
+  for (int i = threadIdx.x; i < nt * c.k; i += blockDim.x) {
+    rows[i] = c.row_of_pair[t0 * c.k + i];
+    gs[i] = c.gates[t0 * c.k + i];
+  }
+  __syncthreads();
+  // Two (token, feature-quad) items per thread at a time, so 2k row loads are
+  // in flight per thread (the combine kernel's arithmetic for each item).
+  const int n4 = c.L >> 2;  // a multiple of 8, and so is n4 * nt: MX blocks stay whole
+  const int items = nt * n4;
+  const int bs = blockDim.x;
+  for (int it = threadIdx.x; it < items; it += 2 * bs) {
+    const int ib = it + bs;
+    const bool two = ib < items;  // the same for the 8 lanes of an MX block
+    const int ta = it / n4, fa = it - ta * n4;
+    const int tb = two ? ib / n4 : ta, fb = two ? ib - tb * n4 : fa;
+    float4 acc_a = make_float4(0.f, 0.f, 0.f, 0.f), acc_b = acc_a;
+    for (int j0 = 0; j0 < c.k; j0 += 16) {
+      combine_rows16(c.y_e, rows + ta * c.k, gs + ta * c.k, c.k, c.L, j0, fa, acc_a);
+      combine_rows16(c.y_e, rows + tb * c.k, gs + tb * c.k, c.k, c.L, j0, fb, acc_b);
+    }
+    combine_store(acc_a, c.L, t0 + ta, fa, c.y_lat, c.yq, c.yqs, nullptr);
+    if (two) combine_store(acc_b, c.L, t0 + tb, fb, c.y_lat, c.yq, c.yqs, nullptr);
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(512) mx_gemm_wide_combine_kernel(const GemmArgs p, const CombineArgs c,
+                                                                   int chunk, int R) {
+  const int slot = blockIdx.x >> 3, x = blockIdx.x & 7;
+  if (slot % R == R - 1) combine_chunk(c, chunk, 8 * (slot / R) + x);
+  else wide_mx_tile<EPI>(p, 8 * (slot - slot / R) + x);
+}
+
 // Dense bf16 GEMM: the latent down-projection on exact bf16 images of the MX
 // operands (the reason it runs on bf16 matrix cores is in mx_gemm.hip), and
 // the bfloat16 latent projections and shared experts of the higher-precision
@@ -331,7 +384,7 @@ __global__ void __launch_bounds__(512) bf16_gemm_wide_kernel(const GemmArgs p) {
   const int r16 = lane & 15, g4 = lane >> 4;
   const int wm = wave >> 2, wn = wave & 3;
   int g, mt, nt, rows, row_base;
-  if (!decode_lds_tile<WB_M>(p, NCOL, g, mt, nt, rows, row_base)) return;
+  if (!decode_lds_tile<WB_M>(p, blockIdx.x, NCOL, g, mt, nt, rows, row_base)) return;
   const int m0 = mt * WB_M;
   const int col0 = nt * NCOL;
   v4f acc[4][4][1];
@@ -464,6 +517,37 @@ hipError_t launch_wide_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Combine chunks of 32 tokens (7.3 MB of expert outputs at K3 width); one
+// combine slot per R slots, R from the two counts so that both kinds of
+// work are spread over the whole launch.
+constexpr int kCombineChunk = 32;
+
+hipError_t launch_wide_combine(const GemmArgs& a, const CombineArgs& c, hipStream_t s) {
+  constexpr int EPI = EPI_SWIGLU_QUANT;
+  constexpr int NCOL = WD_B / 2;
+  if (a.N % 16 != 0 || a.offsets != nullptr) return hipErrorInvalidValue;  // a dense GEMM
+  if (c.T <= 0 || c.k < 1 || c.k > 64 || c.L <= 0 || c.L % 32 != 0 || !c.y_e || !c.gates || !c.row_of_pair ||
+      !c.yq || !c.yqs)
+    return hipErrorInvalidValue;
+  const int n_nt = (a.N + NCOL - 1) / NCOL;
+  const int64_t tiles = (int64_t)a.max_mtiles * n_nt;
+  const int64_t gemm_slots = (tiles + 7) / 8;
+  const int64_t comb_slots = ((c.T + kCombineChunk - 1) / kCombineChunk + 7) / 8;
+  if (gemm_slots <= 0) return hipErrorInvalidValue;
+  int64_t R = (gemm_slots + comb_slots) / comb_slots;
+  R = R < 2 ? 2 : R;  // (at least every other slot a GEMM slot, so the loop below ends)
+  int64_t S = gemm_slots + comb_slots;
+  while (S - S / R < gemm_slots || S / R < comb_slots) ++S;
+  if (8 * S > 0x7fffffff) return hipErrorInvalidValue;
+  constexpr size_t smem = (size_t)WD_NBUF * WD_STAGE;  // (the combine uses 2 * 32 * k * 4 bytes of it)
+  static DeviceOnce attr;
+  hipError_t e =
+      lds_limit_once(attr, {reinterpret_cast<const void*>(&mx_gemm_wide_combine_kernel<EPI>)}, (int)smem);
+  if (e != hipSuccess) return e;
+  mx_gemm_wide_combine_kernel<EPI><<<dim3((unsigned)(8 * S)), dim3(512), smem, s>>>(a, c, kCombineChunk, (int)R);
+  return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_bf16_wide_cfg(const GemmArgs& a, hipStream_t s) {
   if (a.nseg < 1 || a.nseg > 9 || a.offsets != nullptr) return hipErrorInvalidValue;
@@ -497,6 +581,11 @@ hipError_t launch_bf16_gemm_wide(const GemmArgs& a, int epi, hipStream_t s) {
     case EPI_SWIGLU_BF16: return launch_bf16_wide_cfg<EPI_SWIGLU_BF16>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_mx_gemm_wide_combine(const GemmArgs& a, const CombineArgs& c, hipStream_t s) {
+  if (a.N <= 0 || a.N >= (1 << 22) || a.ldc < 0 || a.ldc >= (1 << 22)) return hipErrorInvalidValue;
+  return launch_wide_combine(a, c, s);
 }
 
 hipError_t launch_mx_gemm_wide(const GemmArgs& a, int epi, hipStream_t s) {
