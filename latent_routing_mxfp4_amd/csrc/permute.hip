@@ -54,15 +54,24 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int nblk, int E, int32_
                                                         int32_t* __restrict__ offsets, int mt0,
                                                         int32_t* __restrict__ ms0, int mt1,
                                                         int32_t* __restrict__ ms1, int32_t* __restrict__ tg1) {
-  __shared__ int32_t part[3][1024];
+  __shared__ int32_t part[3][16];
   const int tid = threadIdx.x;
-  // 1) per expert: exclusive scan over blocks (in place), total = count.
+  // 1) per expert: exclusive scan over blocks (in place), total = count; the
+  //    blocks' counts are loaded 32 at a time, all in flight (one load at a
+  //    time made this a chain of nblk memory latencies).
+  constexpr int NB = 32;
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk[(int64_t)b * E + e];
-      blk[(int64_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += NB) {
+      int c[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) c[i] = b0 + i < nblk ? blk[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (b0 + i < nblk) {
+          blk[(int64_t)(b0 + i) * E + e] = run;
+          run += c[i];
+        }
     }
     counts[e] = run;
   }
@@ -79,19 +88,22 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int nblk, int E, int32_
     s1 += (c + mt0 - 1) / mt0;
     s2 += (c + mt1 - 1) / mt1;
   }
-  part[0][tid] = s0; part[1][tid] = s1; part[2][tid] = s2;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partials.
-  for (int o = 1; o < 1024; o <<= 1) {
-    int a0 = 0, a1 = 0, a2 = 0;
-    if (tid >= o) { a0 = part[0][tid - o]; a1 = part[1][tid - o]; a2 = part[2][tid - o]; }
-    __syncthreads();
-    part[0][tid] += a0; part[1][tid] += a1; part[2][tid] += a2;
-    __syncthreads();
+  // Exclusive scan of the 1024 partials: inclusive within each wave by lane
+  // shuffles, then the totals of the waves before this one (16 waves).
+  const int lane = tid & 63, wave = tid >> 6;
+  int i0 = s0, i1 = s1, i2 = s2;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a0 = __shfl_up(i0, o, 64), a1 = __shfl_up(i1, o, 64), a2 = __shfl_up(i2, o, 64);
+    if (lane >= o) { i0 += a0; i1 += a1; i2 += a2; }
   }
-  int r0 = tid ? part[0][tid - 1] : 0;
-  int r1 = tid ? part[1][tid - 1] : 0;
-  int r2 = tid ? part[2][tid - 1] : 0;
+  if (lane == 63) { part[0][wave] = i0; part[1][wave] = i1; part[2][wave] = i2; }
+  __syncthreads();
+  int r0 = i0 - s0, r1 = i1 - s1, r2 = i2 - s2;
+  int t0 = 0, t1 = 0, t2 = 0;  // totals over all experts
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) { r0 += part[0][w]; r1 += part[1][w]; r2 += part[2][w]; }
+    t0 += part[0][w]; t1 += part[1][w]; t2 += part[2][w];
+  }
   for (int e = lo; e < hi; ++e) {
     const int c = counts[e];
     offsets[e] = r0; ms0[e] = r1; ms1[e] = r2;
@@ -102,7 +114,7 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int nblk, int E, int32_
     r1 += (c + mt0 - 1) / mt0;
     r2 += n1;
   }
-  if (tid == 1023) { offsets[E] = part[0][1023]; ms0[E] = part[1][1023]; ms1[E] = part[2][1023]; }
+  if (tid == 1023) { offsets[E] = t0; ms0[E] = t1; ms1[E] = t2; }
 }
 
 __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -142,7 +154,7 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
                                                          int32_t* __restrict__ pair_of_row) {
   extern __shared__ unsigned long long masks[];            // [E], then int32 offsets [E]
   int32_t* soff = reinterpret_cast<int32_t*>(masks + E);
-  __shared__ int32_t part[3][1024];
+  __shared__ int32_t part[3][16];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) masks[e] = 0ull;
   __syncthreads();
@@ -161,18 +173,22 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
     s1 += (c + mt0 - 1) / mt0;
     s2 += (c + mt1 - 1) / mt1;
   }
-  part[0][tid] = s0; part[1][tid] = s1; part[2][tid] = s2;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan over the 1024 partials
-    int a0 = 0, a1 = 0, a2 = 0;
-    if (tid >= o) { a0 = part[0][tid - o]; a1 = part[1][tid - o]; a2 = part[2][tid - o]; }
-    __syncthreads();
-    part[0][tid] += a0; part[1][tid] += a1; part[2][tid] += a2;
-    __syncthreads();
+  // Exclusive scan of the 1024 partials: inclusive within each wave by lane
+  // shuffles, then the totals of the waves before this one (16 waves).
+  const int lane = tid & 63, wave = tid >> 6;
+  int i0 = s0, i1 = s1, i2 = s2;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a0 = __shfl_up(i0, o, 64), a1 = __shfl_up(i1, o, 64), a2 = __shfl_up(i2, o, 64);
+    if (lane >= o) { i0 += a0; i1 += a1; i2 += a2; }
   }
-  int r0 = tid ? part[0][tid - 1] : 0;
-  int r1 = tid ? part[1][tid - 1] : 0;
-  int r2 = tid ? part[2][tid - 1] : 0;
+  if (lane == 63) { part[0][wave] = i0; part[1][wave] = i1; part[2][wave] = i2; }
+  __syncthreads();
+  int r0 = i0 - s0, r1 = i1 - s1, r2 = i2 - s2;
+  int t0 = 0, t1 = 0, t2 = 0;  // totals over all experts
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) { r0 += part[0][w]; r1 += part[1][w]; r2 += part[2][w]; }
+    t0 += part[0][w]; t1 += part[1][w]; t2 += part[2][w];
+  }
   for (int e = lo; e < hi; ++e) {
     const int c = __popcll(masks[e]);
     counts[e] = c;
@@ -185,7 +201,7 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
     r1 += (c + mt0 - 1) / mt0;
     r2 += n1;
   }
-  if (tid == 1023) { offsets[E] = part[0][1023]; ms0[E] = part[1][1023]; ms1[E] = part[2][1023]; }
+  if (tid == 1023) { offsets[E] = t0; ms0[E] = t1; ms1[E] = t2; }
   __syncthreads();
   if (tid < T) {  // rank of a pair = earlier tokens of the block that chose the same expert
     const unsigned long long below = (1ull << tid) - 1ull;
