@@ -8,14 +8,6 @@
 
 namespace moe {
 
-// Maximum over each group of 8 neighbouring lanes (pairs, quads, half-rows).
-__device__ __forceinline__ uint32_t lane8_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
-  return v;
-}
-
 // y_lat (if given), bf16 (yb, if given) and MXFP8 codes (yq, if given) of
 // features 4f .. 4f+3 of token t from their fp32 sum `acc`.  With yq, the 8
 // lanes holding f = 8b .. 8b+7 must be active together: they form MX block b.

@@ -29,17 +29,6 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + t) * u;
 }
 
-// Two E4M3 codes (bits 0-7 and 8-15) of v0, v1 under block exponent e: the
-// hardware fp32 -> E4M3 conversion, which rounds to nearest with ties to even
-// on the OCP grid, of v * 2^-e clamped to +-448.  Scaling by a power of two is
-// exact and the clamp is the quantiser's clip to the largest magnitude, so the
-// codes equal the integer encoder's (enc_e4m3) for every finite input.
-__device__ __forceinline__ uint32_t e4m3x2(float v0, float v1, int e) {
-  const float a = fminf(fmaxf(ldexpf(v0, -e), -448.0f), 448.0f);
-  const float b = fminf(fmaxf(ldexpf(v1, -e), -448.0f), 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
-}
-
 // Maximum over each row of 16 lanes with DPP lane swaps (no LDS round trip):
 // swap within pairs, then pairs within quads, then quads within half-rows
 // (half-row mirror), then half-rows (row mirror).

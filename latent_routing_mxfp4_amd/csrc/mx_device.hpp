@@ -83,8 +83,28 @@ __device__ __forceinline__ uint32_t mx_encode(float v, int e) {
 __device__ __forceinline__ uint32_t enc_e4m3(float v, int e) { return mx_encode<3, -6, 0x7E, 7>(v, e); }
 __device__ __forceinline__ uint32_t enc_e2m1(float v, int e) { return mx_encode<1, 0, 0x7, 3>(v, e); }
 
+// Two E4M3 codes (bits 0-7 and 8-15) of v0, v1 under block exponent e: the
+// hardware fp32 -> E4M3 conversion, which rounds to nearest with ties to even
+// on the OCP grid, of v * 2^-e clamped to +-448.  Scaling by a power of two is
+// exact and the clamp is the quantiser's clip to the largest magnitude, so the
+// codes equal the integer encoder's (enc_e4m3) for every finite input.
+__device__ __forceinline__ uint32_t e4m3x2(float v0, float v1, int e) {
+  const float a = fminf(fmaxf(ldexpf(v0, -e), -448.0f), 448.0f);
+  const float b = fminf(fmaxf(ldexpf(v1, -e), -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
 // ---------------------------------------------------------------------------
 // Wave helpers.
+
+// Maximum over each group of 8 neighbouring lanes (pairs, quads, half-rows).
+__device__ __forceinline__ uint32_t lane8_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return v;
+}
+
 
 // Max over aligned groups of W lanes (W a power of two <= 64), via xor shuffles.
 template <int W>

@@ -6,7 +6,7 @@
 //
 // Layout: one thread per 4 consecutive floats (one 16-byte load), so 8
 // neighbouring lanes hold one 32-element block and agree on its maximum with
-// three xor shuffles.  Reads and writes are fully coalesced; the kernel is
+// three lane swaps.  Reads and writes are fully coalesced; the kernel is
 // HBM-bound (4 B read, 1.03 B (E4M3) or 0.53 B (E2M1) written per element).
 // For E4M3 it can also write the exact dequantised values as bf16 (the
 // operand of the bf16 latent down-projection).
@@ -58,12 +58,15 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4* __restrict_
     float4 v = in[i];
     uint32_t m = max(max(__float_as_uint(v.x) & 0x7fffffffu, __float_as_uint(v.y) & 0x7fffffffu),
                      max(__float_as_uint(v.z) & 0x7fffffffu, __float_as_uint(v.w) & 0x7fffffffu));
-    m = group_max_u32<8>(m);  // non-negative floats order like their bit patterns
+    // non-negative floats order like their bit patterns; the 8 lanes of a
+    // block are neighbours (DPP swaps for E4M3, shuffles for the weights)
+    m = FMT == 0 ? lane8_max_u32(m) : group_max_u32<8>(m);
     if (FMT == 0) {
       int sc = mx_scale_code<8>(m);
       int e = sc - 127;
-      uint32_t w = enc_e4m3(v.x, e) | (enc_e4m3(v.y, e) << 8) | (enc_e4m3(v.z, e) << 16) |
-                   (enc_e4m3(v.w, e) << 24);
+      // the hardware conversion of the clamped, scaled values: the same codes
+      // as the integer encoder (enc_e4m3) for every finite input (e4m3x2)
+      uint32_t w = e4m3x2(v.x, v.y, e) | (e4m3x2(v.z, v.w, e) << 16);
       reinterpret_cast<uint32_t*>(codes)[i] = w;
       if ((i & 7) == 0) scales[i >> 3] = (uint8_t)sc;
       if (deq) {  // bf16 copy of the dequantised values (exact), for the bf16 matrix cores
