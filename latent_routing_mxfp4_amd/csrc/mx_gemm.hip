@@ -118,17 +118,41 @@ __device__ __forceinline__ uint32_t e2m1_bf16_slow(uint32_t c, int sc) {
   const float v = ldexpf((float)(E ? 2 + m : m), (E ? E - 2 : -1) + sc - 127);
   return __float_as_uint((c & 0x8) ? -v : v) >> 16;
 }
-__device__ __forceinline__ void e2m1_block_bf16(const uint4& codes, int sc, uint4 (&out)[4]) {
+struct Bf16Block {
+  uint4 u[4];
+};
+// The general path for a whole block, out of line: inlined at every unrolled
+// K-step it multiplied the kernel's code several times over (tens of KB of
+// branches that never run), which then missed the instruction cache.
+__device__ __noinline__ Bf16Block e2m1_block_bf16_general(uint4 codes, int sc) {
+  Bf16Block r;
   const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
-  const bool fast = sc >= 2 && sc <= 252;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    uint32_t* o = &r.u[u].x;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t lo = (w[u] >> (8 * h)) & 0xf, hi = (w[u] >> (8 * h + 4)) & 0xf;
+      o[h] = e2m1_bf16_slow(lo, sc) | (e2m1_bf16_slow(hi, sc) << 16);
+    }
+  }
+  return r;
+}
+__device__ __forceinline__ void e2m1_block_bf16(const uint4& codes, int sc, uint4 (&out)[4]) {
+  if (sc < 2 || sc > 252) {  // never for the weight encoder's blocks of useful size
+    const Bf16Block r = e2m1_block_bf16_general(codes, sc);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) out[u] = r.u[u];
+    return;
+  }
+  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     uint32_t* o = &out[u].x;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const uint32_t lo = (w[u] >> (8 * h)) & 0xf, hi = (w[u] >> (8 * h + 4)) & 0xf;
-      o[h] = fast ? (e2m1_bf16_fast(lo, sc) | (e2m1_bf16_fast(hi, sc) << 16))
-                  : (e2m1_bf16_slow(lo, sc) | (e2m1_bf16_slow(hi, sc) << 16));
+      o[h] = e2m1_bf16_fast(lo, sc) | (e2m1_bf16_fast(hi, sc) << 16);
     }
   }
 }
