@@ -145,14 +145,31 @@ __device__ __forceinline__ void e2m1_block_bf16(const uint4& codes, int sc, uint
     for (int u = 0; u < 4; ++u) out[u] = r.u[u];
     return;
   }
+  // The block's eight magnitudes as two byte tables (low and high bytes of
+  // the bf16 patterns, entry m = byte m, m = 0 giving 0), then per code byte
+  // two byte permutes: each pair of elements costs a handful of instructions
+  // instead of the formula per element.
+  uint32_t B[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) B[m] = m == 0 ? 0u : e2m1_bf16_fast((uint32_t)m, sc);
+  const uint32_t Llo = (B[0] & 0xffu) | ((B[1] & 0xffu) << 8) | ((B[2] & 0xffu) << 16) | ((B[3] & 0xffu) << 24);
+  const uint32_t Lhi = (B[4] & 0xffu) | ((B[5] & 0xffu) << 8) | ((B[6] & 0xffu) << 16) | ((B[7] & 0xffu) << 24);
+  const uint32_t Hlo = (B[0] >> 8) | ((B[1] >> 8) << 8) | ((B[2] >> 8) << 16) | ((B[3] >> 8) << 24);
+  const uint32_t Hhi = (B[4] >> 8) | ((B[5] >> 8) << 8) | ((B[6] >> 8) << 16) | ((B[7] >> 8) << 24);
   const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     uint32_t* o = &out[u].x;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const uint32_t lo = (w[u] >> (8 * h)) & 0xf, hi = (w[u] >> (8 * h + 4)) & 0xf;
-      o[h] = e2m1_bf16_fast(lo, sc) | (e2m1_bf16_fast(hi, sc) << 16);
+      const uint32_t b = (w[u] >> (8 * h)) & 0xffu;  // elements 8u + 2h (low nibble) and 8u + 2h + 1
+      // selector bytes: magnitude of the low element in byte 0, of the high
+      // one in byte 2 (bytes 1 and 3 select entry 0, which is 0); the same
+      // shifted up a byte places the high-byte table's entries
+      const uint32_t sel = (b & 7u) | ((b & 0x70u) << 12);
+      const uint32_t lo = __builtin_amdgcn_perm(Lhi, Llo, sel);
+      const uint32_t hi = __builtin_amdgcn_perm(Hhi, Hlo, sel << 8);
+      o[h] = lo | hi | ((b & 8u) << 12) | ((b & 0x80u) << 24);  // the two sign bits
     }
   }
 }
