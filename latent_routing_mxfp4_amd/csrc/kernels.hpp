@@ -157,7 +157,7 @@ struct SplitPlan {
   int16_t ks0[kMaxSlices];    // its first K-step (128 wide) in the segment
   int16_t nks[kMaxSlices];    // its K-steps
 };
-SplitPlan splitk_plan(const GemmArgs& args, int max_cuts = 8);
+SplitPlan splitk_plan(const GemmArgs& args);
 hipError_t launch_bf16_splitk(const GemmArgs& args, bool bf16_b, const SplitPlan& sp, float* part, hipStream_t s);
 // c[M][N] = sum of the S partials in slice order; with q, its MXFP8 codes along N.
 hipError_t launch_splitk_reduce(const float* part, int S, int M, int N, float* c, uint8_t* q, uint8_t* qs,

@@ -718,13 +718,15 @@ hipError_t launch_bf16_gemm_quant(const GemmArgs& a, int shape, hipStream_t s) {
   return launch_bf16_gemm_wide(a, EPI_F32_QUANT, s);
 }
 
-SplitPlan splitk_plan(const GemmArgs& a, int max_cuts) {
-  // About 2048 waves in all, at most max_cuts slices' worth of K cuts (the
-  // partial sums stay small next to the weights); segments are cut separately.
+SplitPlan splitk_plan(const GemmArgs& a) {
+  // About 2048 waves in all, at most 8 slices' worth of K cuts (the partial
+  // sums stay small next to the weights; at 64 tokens the MX down-projection
+  // with its reduce measured 27 us at 8 slices against 31 us at 14); segments
+  // are cut separately.
   const int MT = a.M <= 16 ? 16 : 64;
   const int tiles = a.G * ((a.N + 127) / 128) * ((a.M + MT - 1) / MT);
   int target = (2048 + 4 * tiles - 1) / (4 * tiles);
-  target = target < 1 ? 1 : (target > max_cuts ? max_cuts : target);
+  target = target < 1 ? 1 : (target > 8 ? 8 : target);
   int total = 0;
   for (int i = 0; i < a.nseg; ++i) total += a.seg[i].K / 128;
   const int kper = (total + target - 1) / target;
@@ -805,11 +807,6 @@ hipError_t launch_splitk_swiglu(const float* part, int S, int G, int M, int F, f
   return hipGetLastError();
 }
 
-// The latent down-projection at decode: 14 cuts (4 K-steps per slice at
-// d = 7168) measured faster than 8 on its own (28 vs 35 us at 64 tokens;
-// with the reduce 38 vs 41 us) despite the larger partial-sum buffer.
-constexpr int kMxDownCuts = 14;
-
 int bf16_mx_splitk_slices(int M, int N, int K) {
   GemmArgs a = {};
   a.nseg = 1;
@@ -817,13 +814,13 @@ int bf16_mx_splitk_slices(int M, int N, int K) {
   a.G = 1;
   a.M = M;
   a.N = N;
-  return splitk_plan(a, kMxDownCuts).n;
+  return splitk_plan(a).n;
 }
 
 hipError_t launch_bf16_mx_splitk(const GemmArgs& a, float* part, int S, float* z, uint8_t* zq, uint8_t* zqs,
                                  hipStream_t s) {
   if (a.nseg != 1 || a.G != 1) return hipErrorInvalidValue;
-  const SplitPlan sp = splitk_plan(a, kMxDownCuts);
+  const SplitPlan sp = splitk_plan(a);
   if (sp.n != S) return hipErrorInvalidValue;  // the partial buffer was sized for S slices
   hipError_t e = launch_bf16_splitk(a, false, sp, part, s);
   if (e != hipSuccess) return e;
