@@ -239,6 +239,32 @@ def small_report(name, steps, warmup, hip, say):
             "stage_ms": st, "step_events_ms": work["step_events_ms"]}
 
 
+def ep8_share_report(steps, warmup, hip, say):
+    """One GPU's share of an 8-way expert-parallel K3 decode step (112 local
+    experts, 1024 token copies, ~9 rows per expert; latent, router and shared
+    experts on the GPU's own 64 tokens), on the same kernels; the all-to-all
+    exchange is not modelled.  Reported beside the headline, not counted."""
+    import torch
+
+    import synth
+    from latent_routing_mxfp4_amd import layer as LY
+
+    cfg = synth.config("k3_ep8_share")
+    shape = LY.LayerShape.of(cfg)
+    extra = {"w_router": synth.gen_router(cfg), "router_logit_bias": synth.gen_logit_bias(cfg)}
+    weights = LY.encode_weights(shape, lambda n, i: synth.gen_weight(cfg, n, i), extra=extra,
+                                workers=min(16, len(os.sched_getaffinity(0))))
+    c, ms, st, work, counts = run_workload(cfg.name, steps, warmup, weights, hip, say)
+    del weights
+    torch.cuda.empty_cache()
+    return {"workload": f"{c.name}: T={c.T} own tokens, E={c.n_routed} local experts top-{c.top_k} "
+                        f"({c.T * c.top_k} copies), {c.n_shared} shared, d_ff={c.d_ff_routed}",
+            "value": c.T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+            "layer_gbs": work["layer_bytes"] / (ms / 1e3) / 1e9,
+            "expert_up_gbs": work["expert_up_launch_bytes"] / (st["expert_up"] / 1e3) / 1e9,
+            "max_expert_rows": int(counts.max()), "stage_ms": st, "step_events_ms": work["step_events_ms"]}
+
+
 def qb_report(steps, warmup, say):
     """Quantile Balancing of the selection bias at the K3 prefill shape (16384
     tokens x 896 experts, top-16) on seeded N(0, 1) logits: time per update and
@@ -345,7 +371,7 @@ def cpu_baseline(name, n_tokens, say):
 
 PROFILE_MD = os.path.join(ROOT, "profiles", "k3_layer_kernels_and_hbm_traffic.md")
 PROFILE_CMD = ("python3 /root/repo/bench.py --steps 3 --warmup 1 --decode-steps 5 --no-cpu-baseline "
-               "--skew-steps 0 --k2-steps 0 --bf16-steps 0 --qb-steps 0 --small-steps 0")
+               "--skew-steps 0 --k2-steps 0 --bf16-steps 0 --qb-steps 0 --small-steps 0 --ep8-steps 0")
 SIMDS = 1024    # MI355X: 256 compute units x 4 SIMDs (the MfmaUtil denominator)
 XCDS = 8        # the counter CSV holds GRBM_GUI_ACTIVE summed over the 8 XCDs' instances
 
@@ -512,6 +538,9 @@ def main():
     ap.add_argument("--small-steps", type=int, default=20,
                     help="steps of the tiny (64-token) and mid (4096-token) layers reported under 'tiny' and 'mid' "
                          "(0: skip)")
+    ap.add_argument("--ep8-steps", type=int, default=20,
+                    help="steps of one GPU's share of an 8-way expert-parallel K3 decode (112 local experts) "
+                         "reported under 'ep8_share' (0: skip)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="kept for the profile command: the copy probe now always runs first")
@@ -658,6 +687,8 @@ def main():
     if args.small_steps > 0 and args.workload == "k3_prefill":
         for name in ("tiny", "mid"):
             out[name] = small_report(name, args.small_steps, args.warmup, hip, say)
+    if args.ep8_steps > 0 and args.workload == "k3_prefill":
+        out["ep8_share"] = ep8_share_report(args.ep8_steps, args.warmup, hip, say)
     if args.qb_steps > 0:
         out["quantile_balance"] = qb_report(args.qb_steps, args.warmup, say)
     if not args.no_cpu_baseline:

@@ -115,6 +115,13 @@ CONFIGS = {
                                    top_k=16, n_shared=2, d_ff_shared=3072, d_ff_routed=3072,
                                    router_init="normal", logit_bias="none", seed_x=1004, seed_w=1003,
                                    precision="bf16"),
+    # One GPU's share of an 8-way expert-parallel K3 decode step: 112 local
+    # experts (the first 112 of the K3 set, same seeds) receiving 1024 token
+    # copies, about 9 rows each; the latent projections, router and shared
+    # experts run on the GPU's own 64 tokens.  The exchange is not modelled.
+    "k3_ep8_share": LayerConfig("k3_ep8_share", T=64, d_model=7168, d_latent=3584, n_routed=112,
+                                top_k=16, n_shared=2, d_ff_shared=3072, d_ff_routed=3072,
+                                router_init="normal", logit_bias="none", seed_x=1003, seed_w=1003),
     "k2_prefill": LayerConfig("k2_prefill", T=8192, d_model=7168, d_latent=7168, n_routed=384, top_k=8,
                               n_shared=1, d_ff_shared=2048, d_ff_routed=2048, router_init="normal",
                               logit_bias="none", seed_x=1007, seed_w=1007, latent=False, gating="softmax"),
