@@ -66,12 +66,12 @@ hipError_t launch_router_reduce_topk(const float* partial, int nz, const float* 
 size_t dispatch_scratch_ints(int T, int E);
 // counts[E], offsets[E+1], row_of_pair[T*k], pair_of_row[T*k], and, for each of
 // the two M-tile heights mt0/mt1, mtile_start_x[E+1] (prefix of ceil(count/mt)).
-// mtile_group1 (nullable, mtile_start1[E] entries): the group of each M-tile of
-// height mt1, so that a workgroup finds its group with one load.
+// mtile_group0/1 (nullable, mtile_start0/1[E] entries): the group of each
+// M-tile of height mt0/mt1, so that a workgroup finds its group with one load.
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* scratch, int32_t* counts,
                            int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row, int mt0,
-                           int32_t* mtile_start0, int mt1, int32_t* mtile_start1, int32_t* mtile_group1,
-                           hipStream_t s);
+                           int32_t* mtile_start0, int32_t* mtile_group0, int mt1, int32_t* mtile_start1,
+                           int32_t* mtile_group1, hipStream_t s);
 
 // ---- MX GEMM (mx_gemm.hip) --------------------------------------------------
 enum Epilogue : int {
@@ -102,7 +102,7 @@ struct GemmArgs {
   // M-tiles are [mtile_start[g], mtile_start[g+1]).  Dense: G groups of M rows.
   const int32_t* offsets;      // null => dense
   const int32_t* mtile_start;  // routed only
-  const int32_t* mtile_group;  // routed, LDS-staged kernels: group of each M-tile (null: binary search)
+  const int32_t* mtile_group;  // routed: group of each M-tile (null: binary search over mtile_start)
   int G;
   int M;                       // dense rows per group
   int N;                       // output columns (per matrix)

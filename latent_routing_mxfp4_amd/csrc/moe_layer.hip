@@ -51,8 +51,8 @@ constexpr int64_t kFewRows = 256;  // decode-shaped batches: weight-streaming ke
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, wrpl, ids, gates, dscr, counts, offsets, ms0, ms1, tg1, rop, por, hq, hqs, ye,
-      ylat, yq, yqs, hs, hss, xb, yb, hb, dpart, total;
+  size_t xq, xqs, xdq, wdn16, zpart, z, zq, zqs, logits, rpart, wrpl, ids, gates, dscr, counts, offsets, ms0, ms1,
+      tg0, tg1, rop, por, hq, hqs, ye, ylat, yq, yqs, hs, hss, xb, yb, hb, dpart, total;
 };
 
 // The bf16 GEMMs of the higher-precision map (operand pointers left null:
@@ -149,9 +149,11 @@ Plan make_plan(const moe_layer_config& c, int64_t T) {
   p.offsets = take((E + 1) * 4);
   p.ms0 = take((E + 1) * 4);
   p.ms1 = take((E + 1) * 4);
-  {  // group of each M-tile of the LDS-staged kernels: at most P / mt + min(P, E) tiles
-    const size_t mt = (size_t)moe::gemm_mtile(moe::GEMM_WIDE);
-    p.tg1 = take((P / mt + (P < (size_t)E ? P : (size_t)E) + 1) * 4);
+  {  // group of each M-tile of the routed GEMMs: at most P / mt + min(P, E) tiles
+    const size_t mt0 = (size_t)moe::gemm_mtile(moe::GEMM_STREAM16), mt1 = (size_t)moe::gemm_mtile(moe::GEMM_WIDE);
+    const size_t pe = P < (size_t)E ? P : (size_t)E;
+    p.tg0 = take(P <= (size_t)16 * E ? (P / mt0 + pe + 1) * 4 : 0);  // weight-streaming shape only
+    p.tg1 = take((P / mt1 + pe + 1) * 4);
   }
   p.rop = take(P * 4);
   p.por = take(P * 4);
@@ -301,6 +303,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
   int32_t* offsets = at<int32_t>(ws, pl.offsets);
   int32_t* ms0 = at<int32_t>(ws, pl.ms0);
   int32_t* ms1 = at<int32_t>(ws, pl.ms1);
+  int32_t* tg0 = at<int32_t>(ws, pl.tg0);
   int32_t* tg1 = at<int32_t>(ws, pl.tg1);
   int32_t* rop = at<int32_t>(ws, pl.rop);
   int32_t* por = at<int32_t>(ws, pl.por);
@@ -407,7 +410,8 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
   MOE_HIP(mark(MOE_EV_TOPK));
 
   // 5. dispatch
-  MOE_HIP(moe::launch_dispatch(ids, T, E, k, dscr, counts, offsets, rop, por, mt_small, ms0, mt_big, ms1, tg1, s));
+  MOE_HIP(moe::launch_dispatch(ids, T, E, k, dscr, counts, offsets, rop, por, mt_small, ms0,
+                               routed_shape == moe::GEMM_STREAM16 ? tg0 : nullptr, mt_big, ms1, tg1, s));
   MOE_HIP(mark(MOE_EV_DISPATCH));
 
   const int mt_r = moe::gemm_mtile(routed_shape);
@@ -492,7 +496,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
                 wrm};
     a.offsets = offsets;
     a.mtile_start = ms_r;
-    a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? nullptr : tg1;
+    a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? tg0 : tg1;
     a.G = E;
     a.N = F;
     a.gather = por;
@@ -515,7 +519,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
                 (int64_t)L * F / 32, F, wrm};
     a.offsets = offsets;
     a.mtile_start = ms_r;
-    a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? nullptr : tg1;
+    a.mtile_group = routed_shape == moe::GEMM_STREAM16 ? tg0 : tg1;
     a.G = E;
     a.N = L;
     a.c = ye;

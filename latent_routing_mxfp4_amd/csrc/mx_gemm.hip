@@ -73,26 +73,42 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& f) {
 template <int MT, int NT>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int bid, int wave, int NWC, Tile& t) {
   const int n_ntiles = (p.N + NT - 1) / NT;
-  const int gm = bid / n_ntiles;
-  const int nt = bid - gm * n_ntiles;
-  int g, m0, rows, row_base;
+  int g, m0, rows, row_base, nt;
   if (p.offsets) {
+    const int gm = bid / n_ntiles;
+    nt = bid - gm * n_ntiles;
     const int total = p.mtile_start[p.G];
     if (gm >= total) return false;
-    int lo = 0, hi = p.G;  // mtile_start[lo] <= gm < mtile_start[hi]
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if (p.mtile_start[mid] <= gm) lo = mid; else hi = mid;
+    int lo = 0;
+    if (p.mtile_group) {  // the dispatch's table: one load instead of a chain of ten
+      lo = p.mtile_group[gm];
+    } else {
+      int hi = p.G;  // mtile_start[lo] <= gm < mtile_start[hi]
+      while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (p.mtile_start[mid] <= gm) lo = mid; else hi = mid;
+      }
     }
     g = lo;
     row_base = p.offsets[lo];
     rows = p.offsets[lo + 1] - row_base;
     m0 = (gm - p.mtile_start[lo]) * MT;
   } else {
+    // Dense: workgroups are dealt to the 8 XCDs in turn (bid % 8); each XCD
+    // takes a contiguous run of tiles, M-tiles of one N-tile adjacent, so the
+    // M-tiles that share a weight tile run together on one XCD and its L2
+    // serves the weights to all of them.  The grid is 8 * ceil(tiles / 8).
     const int mpg = (p.M + MT - 1) / MT;
-    g = gm / mpg;
-    if (g >= p.G) return false;
-    m0 = (gm - g * mpg) * MT;
+    const int total = p.G * mpg * n_ntiles;
+    const int per = (total + 7) >> 3;
+    const int slot = bid >> 3;
+    if (slot >= per) return false;
+    const int lin = (bid & 7) * per + slot;
+    if (lin >= total) return false;
+    const int gn = lin / mpg;  // group * n_ntiles + N-tile
+    g = gn / n_ntiles;
+    nt = gn - g * n_ntiles;
+    m0 = (lin - gn * mpg) * MT;
     rows = p.M;
     row_base = 0;
   }
@@ -658,6 +674,17 @@ __global__ void __launch_bounds__(256) mx_gemm_stream_pair_kernel(const GemmArgs
   else stream_gemm<MW, NW, EPI, 1>(p, b - npre);
 }
 
+// Workgroups of a weight-streaming launch with NT-column tiles: one per
+// (M-tile, N-tile) of a routed GEMM (max_mtiles bounds its M-tiles); a dense
+// GEMM's tiles rounded up to whole rounds of the 8 XCDs (see decode_tile).
+template <int MW>
+static int64_t stream_tiles(const GemmArgs& a, int NT) {
+  const int64_t n_ntiles = (a.N + NT - 1) / NT;
+  if (a.offsets) return (int64_t)a.max_mtiles * n_ntiles;
+  const int64_t mpg = (a.M + 16 * MW - 1) / (16 * MW);
+  return ((int64_t)a.G * mpg * n_ntiles + 7) / 8 * 8;
+}
+
 template <int MW, int NW, int EPI>
 static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
   const bool chains = a.kchains == 4;
@@ -665,8 +692,8 @@ static hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t s) {
   if (chains && a.offsets != nullptr) return hipErrorInvalidValue;  // dense GEMMs only
   const int NT = (chains ? 1 : 4) * 16 * NW;
   if (a.N % 16 != 0) return hipErrorInvalidValue;  // fragment-order weights
-  const int n_ntiles = (a.N + NT - 1) / NT;
-  const int64_t grid = (int64_t)a.max_mtiles * n_ntiles;
+  if (a.M < 0 || a.G < 0) return hipErrorInvalidValue;
+  const int64_t grid = stream_tiles<MW>(a, NT);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (chains) mx_gemm_stream_kernel<MW, NW, EPI, 4><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
@@ -685,19 +712,14 @@ static bool epilogue_dims_ok(const GemmArgs& a) {
   return a.N > 0 && a.N < (1 << 22) && a.ldc >= 0 && a.ldc < (1 << 22);
 }
 
-// Workgroups of one weight-streaming problem in the one-accumulator layout.
-template <int NW>
-static int64_t stream_grid(const GemmArgs& a) {
-  const int n_ntiles = (a.N + 4 * 16 * NW - 1) / (4 * 16 * NW);
-  return (int64_t)a.max_mtiles * n_ntiles;
-}
 
 template <int MW, int NW, int EPI>
 static hipError_t launch_stream_pair_cfg(const GemmArgs& pre, const GemmArgs& a, hipStream_t s) {
   if (pre.offsets != nullptr || (pre.kchains != 0 && pre.kchains != 1) || (a.kchains != 0 && a.kchains != 1))
     return hipErrorInvalidValue;
   if (pre.N % 16 != 0 || a.N % 16 != 0) return hipErrorInvalidValue;
-  const int64_t g0 = stream_grid<NW>(pre), g1 = stream_grid<NW>(a);
+  if (pre.M < 0 || pre.G < 0) return hipErrorInvalidValue;
+  const int64_t g0 = stream_tiles<MW>(pre, 4 * 16 * NW), g1 = stream_tiles<MW>(a, 4 * 16 * NW);
   if (g0 < 0 || g1 < 0 || g0 + g1 > 0x7fffffff) return hipErrorInvalidValue;
   if (g0 + g1 == 0) return hipSuccess;
   mx_gemm_stream_pair_kernel<MW, NW, EPI><<<dim3((unsigned)(g0 + g1)), dim3(256), 0, s>>>(pre, (int)g0, a);

@@ -52,8 +52,9 @@ __global__ void __launch_bounds__(64) perm_count_kernel(const int32_t* __restric
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int nblk, int E, int32_t* __restrict__ blk,
                                                         int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ offsets, int mt0,
-                                                        int32_t* __restrict__ ms0, int mt1,
-                                                        int32_t* __restrict__ ms1, int32_t* __restrict__ tg1) {
+                                                        int32_t* __restrict__ ms0, int32_t* __restrict__ tg0,
+                                                        int mt1, int32_t* __restrict__ ms1,
+                                                        int32_t* __restrict__ tg1) {
   __shared__ int32_t part[3][16];
   const int tid = threadIdx.x;
   // 1) per expert: exclusive scan over blocks (in place), total = count; the
@@ -107,11 +108,13 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int nblk, int E, int32_
   for (int e = lo; e < hi; ++e) {
     const int c = counts[e];
     offsets[e] = r0; ms0[e] = r1; ms1[e] = r2;
-    const int n1 = (c + mt1 - 1) / mt1;
+    const int n0 = (c + mt0 - 1) / mt0, n1 = (c + mt1 - 1) / mt1;
+    if (tg0)
+      for (int q = 0; q < n0; ++q) tg0[r1 + q] = e;
     if (tg1)
       for (int q = 0; q < n1; ++q) tg1[r2 + q] = e;
     r0 += c;
-    r1 += (c + mt0 - 1) / mt0;
+    r1 += n0;
     r2 += n1;
   }
   if (tid == 1023) { offsets[E] = t0; ms0[E] = t1; ms1[E] = t2; }
@@ -148,7 +151,8 @@ __global__ void __launch_bounds__(64) perm_scatter_kernel(const int32_t* __restr
 // the per-expert masks and segment offsets kept in LDS.
 __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                         int mt0, int32_t* __restrict__ ms0, int mt1,
+                                                         int mt0, int32_t* __restrict__ ms0,
+                                                         int32_t* __restrict__ tg0, int mt1,
                                                          int32_t* __restrict__ ms1, int32_t* __restrict__ tg1,
                                                          int32_t* __restrict__ row_of_pair,
                                                          int32_t* __restrict__ pair_of_row) {
@@ -194,11 +198,13 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
     counts[e] = c;
     offsets[e] = r0; ms0[e] = r1; ms1[e] = r2;
     soff[e] = r0;
-    const int n1 = (c + mt1 - 1) / mt1;
+    const int n0 = (c + mt0 - 1) / mt0, n1 = (c + mt1 - 1) / mt1;
+    if (tg0)
+      for (int q = 0; q < n0; ++q) tg0[r1 + q] = e;
     if (tg1)
       for (int q = 0; q < n1; ++q) tg1[r2 + q] = e;
     r0 += c;
-    r1 += (c + mt0 - 1) / mt0;
+    r1 += n0;
     r2 += n1;
   }
   if (tid == 1023) { offsets[E] = t0; ms0[E] = t1; ms1[E] = t2; }
@@ -217,12 +223,12 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
 
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* scratch, int32_t* counts,
                            int32_t* offsets, int32_t* row_of_pair, int32_t* pair_of_row, int mt0,
-                           int32_t* ms0, int mt1, int32_t* ms1, int32_t* tg1, hipStream_t s) {
+                           int32_t* ms0, int32_t* tg0, int mt1, int32_t* ms1, int32_t* tg1, hipStream_t s) {
   const int nblk = (T + kTokBlock - 1) / kTokBlock;
   const size_t smem = (size_t)E * sizeof(unsigned long long);
   if (nblk == 1) {  // one block of tokens: one launch
     perm_small_kernel<<<dim3(1), dim3(1024), smem + (size_t)E * sizeof(int32_t), s>>>(
-        ids, T, E, k, counts, offsets, mt0, ms0, mt1, ms1, tg1, row_of_pair, pair_of_row);
+        ids, T, E, k, counts, offsets, mt0, ms0, tg0, mt1, ms1, tg1, row_of_pair, pair_of_row);
     return hipGetLastError();
   }
   if (nblk > 0) {
@@ -230,7 +236,8 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* scr
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  perm_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(nblk, E, scratch, counts, offsets, mt0, ms0, mt1, ms1, tg1);
+  perm_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(nblk, E, scratch, counts, offsets, mt0, ms0, tg0, mt1, ms1,
+                                                   tg1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
   perm_scatter_kernel<<<dim3(nblk), dim3(64), smem, s>>>(ids, T, E, k, scratch, offsets, row_of_pair,
