@@ -8,8 +8,11 @@ shared experts) over one batch of synthetic tokens already resident in HBM.
 
 Default workload: the 16384-token prefill batch (matrix-core bound); the
 64-token decode batch (HBM bound) is measured in the same run and reported
-under "decode".  Per-stage times come from HIP events recorded by the library
-on the forward's stream inside the timed region.
+under "decode".  Inside the timed region the library records only the two
+HIP events that bracket the dominant launch (expert_up) on the forward's
+stream; the other per-stage times come from the same steps run again
+untimed with an event at every stage boundary (each event record adds a few
+microseconds to the stream, which would otherwise count in the step time).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -40,14 +43,17 @@ def _hip():
 
 
 class StageEvents:
-    """MOE_TRACE_EVENTS HIP events per step, for K steps."""
+    """MOE_TRACE_EVENTS HIP events per step, for K steps (only those in `only`,
+    if given: the other entries stay NULL and the library skips them)."""
 
-    def __init__(self, hip, n_steps, n_ev):
+    def __init__(self, hip, n_steps, n_ev, only=None):
         self.hip = hip
         self.arrays = []
         for _ in range(n_steps):
             arr = (ctypes.c_void_p * n_ev)()
             for i in range(n_ev):
+                if only is not None and i not in only:
+                    continue
                 e = ctypes.c_void_p()
                 assert hip.hipEventCreate(ctypes.byref(e)) == 0
                 arr[i] = e.value
@@ -61,7 +67,8 @@ class StageEvents:
     def close(self):
         for arr in self.arrays:
             for e in arr:
-                self.hip.hipEventDestroy(e)
+                if e:
+                    self.hip.hipEventDestroy(e)
 
 
 def algorithmic_work(cfg, counts):
@@ -118,9 +125,12 @@ def run_workload(name, steps, warmup, weights, hip, say, logit_bias=None):
     lay.workspace(cfg.T)
     stream = torch.cuda.current_stream().cuda_stream
     nev = _lib.MOE_TRACE_EVENTS
-    evs = StageEvents(hip, steps, nev)
-    traces = [_lib.MoeLayerTrace(*([None] * len(_lib.TRACE_FIELDS)), ctypes.cast(a, ctypes.c_void_p))
-              for a in evs.arrays]
+    dom = _lib.STAGES.index("expert_up")       # stage i lies between events i and i + 1
+    tevs = StageEvents(hip, steps, nev, only=(dom, dom + 1))
+    sevs = StageEvents(hip, steps, nev)
+    mk = lambda evs: [_lib.MoeLayerTrace(*([None] * len(_lib.TRACE_FIELDS)), ctypes.cast(a, ctypes.c_void_p))
+                      for a in evs.arrays]
+    timed_traces, stage_traces = mk(tevs), mk(sevs)
     ws = lay.workspace(cfg.T)
 
     def step(tr=None):
@@ -132,21 +142,28 @@ def run_workload(name, steps, warmup, weights, hip, say, logit_bias=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(traces[i])
+        step(timed_traces[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
+    # the same steps again, untimed, with an event at every stage boundary
+    for i in range(steps):
+        step(stage_traces[i])
+    torch.cuda.synchronize()
 
     stage_ms = {}
     for si, sname in enumerate(_lib.STAGES):
-        # median over the timed steps (a slow first step or a stray hiccup does
-        # not move it; the profile summary takes the median the same way)
-        stage_ms[sname] = statistics.median(evs.elapsed(i, si, si + 1) for i in range(steps))
+        # median over the steps (a slow first step or a stray hiccup does not
+        # move it; the profile summary takes the median the same way)
+        stage_ms[sname] = statistics.median(sevs.elapsed(i, si, si + 1) for i in range(steps))
+    # the dominant launch as timed inside the timed region
+    stage_ms["expert_up"] = statistics.median(tevs.elapsed(i, dom, dom + 1) for i in range(steps))
     # per-step forward time between the first and the last stage event
-    per_step = sorted(evs.elapsed(i, 0, len(_lib.STAGES)) for i in range(steps))
+    per_step = sorted(sevs.elapsed(i, 0, len(_lib.STAGES)) for i in range(steps))
     pick = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     step_stats = {"median": statistics.median(per_step), "p10": pick(0.1), "p90": pick(0.9)}
-    evs.close()
+    tevs.close()
+    sevs.close()
 
     # routing statistics of this batch (outside the timed region)
     tb = {"counts": torch.empty(cfg.n_routed, dtype=torch.int32, device="cuda")}

@@ -177,7 +177,9 @@ enum {
  * the same stream) with the sizes shown, for the T of that call.  Rows in
  * "sorted order" are the (token, slot) pairs stably sorted by expert.
  * `events`, if not NULL, is a HOST array of MOE_TRACE_EVENTS hipEvent_t
- * handles (created by the caller) recorded at the stage boundaries above. */
+ * handles (created by the caller) recorded at the stage boundaries above; a
+ * NULL entry leaves its boundary unrecorded (each record costs the stream a
+ * few microseconds, so a timing run can bracket only the stage it needs). */
 typedef struct {
   uint8_t* xq_codes;   uint8_t* xq_scales;   /* [T][d], [T][d/32]            */
   float* z;                                  /* [T][L] fp32 latent           */

@@ -332,7 +332,7 @@ int forward_impl(moe_layer_t layer, const float* x, int32_t T, float* y, void* w
   const int mt_small = moe::gemm_mtile(moe::GEMM_STREAM16), mt_big = moe::gemm_mtile(moe::GEMM_WIDE);
 
   hipEvent_t const* ev = tr && tr->events ? reinterpret_cast<hipEvent_t const*>(tr->events) : nullptr;
-  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord(ev[i], s) : hipSuccess; };
   MOE_HIP(mark(MOE_EV_START));
 
   // 1. xq (and its exact bf16 image for the latent down-projection)
