@@ -62,29 +62,47 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const float* __restr
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = v4f_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = kbeg; k0 < kend; k0 += RK) {
-    // 64 rows x 32 floats = 512 float4 per operand; 2 per thread.
+  // The K range in rounds of RC chunks: a round's global loads are all
+  // issued first (in flight together, one memory latency per round rather
+  // than per chunk), then each chunk goes through LDS into the MFMAs.
+  constexpr int RC = 4;
+  for (int kr = kbeg; kr < kend; kr += RC * RK) {
+    // per chunk: 64 rows x 32 floats = 512 float4 per operand; 2 per thread
+    float4 vz[RC][2], vw[RC][2];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int f = tid + 256 * it;
-      const int r = f >> 3, c4 = (f & 7) * 4;
-      float4 vz = make_float4(0.f, 0.f, 0.f, 0.f), vw = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t0 + r < T) vz = *reinterpret_cast<const float4*>(z + (int64_t)(t0 + r) * L + k0 + c4);
-      if (e0 + r < E) vw = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + r) * L + k0 + c4);
-      *reinterpret_cast<float4*>(&zs[r][c4]) = vz;
-      *reinterpret_cast<float4*>(&ws[r][c4]) = vw;
-    }
-    __syncthreads();
+    for (int c = 0; c < RC; ++c)
 #pragma unroll
-    for (int kk = 0; kk < RK; kk += 4) {
-      float a0 = zs[wm + r16][kk + g4], a1 = zs[wm + 16 + r16][kk + g4];
-      float b0 = ws[wn + r16][kk + g4], b1 = ws[wn + 16 + r16][kk + g4];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+      for (int it = 0; it < 2; ++it) {
+        const int f = tid + 256 * it;
+        const int r = f >> 3, c4 = (f & 7) * 4;
+        const int k0 = kr + c * RK;
+        vz[c][it] = make_float4(0.f, 0.f, 0.f, 0.f);
+        vw[c][it] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (k0 < kend && t0 + r < T) vz[c][it] = *reinterpret_cast<const float4*>(z + (int64_t)(t0 + r) * L + k0 + c4);
+        if (k0 < kend && e0 + r < E) vw[c][it] = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + r) * L + k0 + c4);
+      }
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+      if (kr + c * RK >= kend) break;  // uniform
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int f = tid + 256 * it;
+        const int r = f >> 3, c4 = (f & 7) * 4;
+        *reinterpret_cast<float4*>(&zs[r][c4]) = vz[c][it];
+        *reinterpret_cast<float4*>(&ws[r][c4]) = vw[c][it];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < RK; kk += 4) {
+        float a0 = zs[wm + r16][kk + g4], a1 = zs[wm + 16 + r16][kk + g4];
+        float b0 = ws[wn + r16][kk + g4], b1 = ws[wn + 16 + r16][kk + g4];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -665,6 +683,10 @@ __global__ void __launch_bounds__(256) router_reduce_topk_kernel(const float* __
   int64_t o[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) o[i] = (int64_t)t * E + min(tid + 256 * i, E - 1);
+  constexpr int KPL = 16;
+  float bv[KPL];  // selection bias of wave 0's keys, loaded beside the slices
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) bv[j] = sel_bias && tid < 64 ? sel_bias[min(lane + 64 * j, E - 1)] : 0.f;
   float v[EPT];
   for (int s0 = 0; s0 < nz; s0 += SB) {
     float p[EPT][SB];
@@ -693,11 +715,7 @@ __global__ void __launch_bounds__(256) router_reduce_topk_kernel(const float* __
   }
   __syncthreads();
   if (tid >= 64) return;
-  constexpr int KPL = 16;
   float key[KPL], scr[KPL];
-  float bv[KPL];
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) bv[j] = sel_bias ? sel_bias[min(lane + 64 * j, E - 1)] : 0.f;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int e = lane + 64 * j;
