@@ -791,14 +791,18 @@ hipError_t launch_bf16_splitk(const GemmArgs& a, bool bf16_b, const SplitPlan& s
   if (!epilogue_dims_ok(q)) return hipErrorInvalidValue;
   const bool small = a.M <= 16;
   const int MT = small ? 16 : 64;
-  const int64_t grid = (int64_t)a.G * ((a.M + MT - 1) / MT) * ((a.N + 127) / 128);
+  // MX weights at 64-row tiles: 16 columns per wave (NT = 64), twice the
+  // workgroups, each decoding one weight fragment per K-step.
+  const bool narrow = !bf16_b && !small;
+  const int NT = narrow ? 64 : 128;
+  const int64_t grid = (int64_t)a.G * ((a.M + MT - 1) / MT) * ((a.N + NT - 1) / NT);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 gd((unsigned)grid, (unsigned)sp.n);
   constexpr int D = 4;
   constexpr size_t lds1 = splitk_lds_bytes<1, D>(), lds4 = splitk_lds_bytes<4, D>();
   static DeviceOnce attr;
   hipError_t ea = lds_limit_once(attr, {reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, false>),
-                                        reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 2, D, true>)},
+                                        reinterpret_cast<const void*>(&bf16_splitk_kernel<4, 1, D, true>)},
                                  (int)lds4);
   if (ea != hipSuccess) return ea;
   if (bf16_b) {
@@ -806,7 +810,7 @@ hipError_t launch_bf16_splitk(const GemmArgs& a, bool bf16_b, const SplitPlan& s
     else bf16_splitk_kernel<4, 2, D, false><<<gd, dim3(256), lds4, s>>>(a, sp, part);
   } else {
     if (small) bf16_splitk_kernel<1, 2, D, true><<<gd, dim3(256), lds1, s>>>(a, sp, part);
-    else bf16_splitk_kernel<4, 2, D, true><<<gd, dim3(256), lds4, s>>>(a, sp, part);
+    else bf16_splitk_kernel<4, 1, D, true><<<gd, dim3(256), lds4, s>>>(a, sp, part);
   }
   return hipGetLastError();
 }
