@@ -229,24 +229,31 @@ __device__ __forceinline__ void wide_mx_tile(const GemmArgs& p, int bid) {
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* buf = lds + (ks % WD_NBUF) * WD_STAGE;
       const int sh = 8 * g4;
-      const uint4 asd =
-          *reinterpret_cast<const uint4*>(buf + WD_OFF_AS + 1024 * wm + 256 * (r16 >> 2) + 16 * (r16 & 3));
-      const uint32_t as_all[4] = {asd.x, asd.y, asd.z, asd.w};
+      uint32_t as_all[4] = {0u, 0u, 0u, 0u};
       uint32_t bs_all[8];
-#pragma unroll
-      for (int ni = 0; ni < 8; ++ni)
-        bs_all[ni] = *reinterpret_cast<const uint32_t*>(buf + WD_OFF_BS + 4 * b_row(wn, ni, r16));
       v8i bf[8];
-#pragma unroll
-      for (int ni = 0; ni < 8; ++ni) {
-        const int blk = b_row(wn, ni, 0) >> 4;
-        const uint4 v = *reinterpret_cast<const uint4*>(buf + WD_OFF_B + 1024 * blk + 16 * lane);
-        bf[ni][0] = (int)v.x; bf[ni][1] = (int)v.y; bf[ni][2] = (int)v.z; bf[ni][3] = (int)v.w;
-        bf[ni][4] = 0; bf[ni][5] = 0; bf[ni][6] = 0; bf[ni][7] = 0;
-      }
       v8i av[4];
+      // A wave with no row of the group (the second M-half of a tail tile of
+      // at most 64 rows) issues no MFMAs, so it reads no fragments either:
+      // LDS data returning into one wave's registers stalls the matrix core
+      // for the other wave of its SIMD too.
+      if (mvalid > 0) {
+        const uint4 asd =
+            *reinterpret_cast<const uint4*>(buf + WD_OFF_AS + 1024 * wm + 256 * (r16 >> 2) + 16 * (r16 & 3));
+        as_all[0] = asd.x; as_all[1] = asd.y; as_all[2] = asd.z; as_all[3] = asd.w;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) av[mi] = rd_a(buf, mi);
+        for (int ni = 0; ni < 8; ++ni)
+          bs_all[ni] = *reinterpret_cast<const uint32_t*>(buf + WD_OFF_BS + 4 * b_row(wn, ni, r16));
+#pragma unroll
+        for (int ni = 0; ni < 8; ++ni) {
+          const int blk = b_row(wn, ni, 0) >> 4;
+          const uint4 v = *reinterpret_cast<const uint4*>(buf + WD_OFF_B + 1024 * blk + 16 * lane);
+          bf[ni][0] = (int)v.x; bf[ni][1] = (int)v.y; bf[ni][2] = (int)v.z; bf[ni][3] = (int)v.w;
+          bf[ni][4] = 0; bf[ni][5] = 0; bf[ni][6] = 0; bf[ni][7] = 0;
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) av[mi] = rd_a(buf, mi);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (ks + 2 < ksteps) issue(ks + 2);
       if (late) {  // stage ks + 1, leaving stage ks + 2 in flight
