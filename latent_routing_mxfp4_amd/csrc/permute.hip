@@ -11,9 +11,7 @@
 //   scan    one workgroup.  Per expert, an exclusive scan over blocks gives
 //           each block's base inside the expert segment; an exclusive scan over
 //           experts gives the segment offsets; the same scan over
-//           ceil(count / MT) gives the M-tile prefix the grouped GEMM walks,
-//           and (optionally) each M-tile is labelled with its expert, so a
-//           GEMM workgroup finds its expert with one load.
+//           ceil(count / MT) gives the M-tile prefix the grouped GEMM walks.
 //   scatter recomputes the block masks; the rank of a pair inside its block
 //           is popcount(mask & lanes-below-me), i.e. the number of earlier
 //           tokens of the block that chose the same expert (a token never
